@@ -1,0 +1,10 @@
+"""fp64 CPU oracle of the Hyena operator -- TEST INFRASTRUCTURE ONLY.
+
+Importable from the tests, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg; never from the product path.
+"""
+from .hyena_oracle import (  # noqa: F401
+    modal_filter, conv_direct, conv_fft, causal_conv, hyena_fwd, fir_fwd,
+    modal_state, chunk_fwd, next_pow2,
+)
+from .metrics import compare, passes, REL_L2_MAX, ELEM_REL_MAX, TAU  # noqa: F401

@@ -1,0 +1,318 @@
+"""Pins of the fp64 oracle against facts other than itself.
+
+Each pin takes the oracle module (or a stand-in with the same functions) and
+raises AssertionError when the oracle disagrees with:
+
+* hand-worked values (tests/golden/hand_worked.json);
+* exact rational brute force (fractions.Fraction) on tiny inputs;
+* closed forms: the geometric-series DFT of the modal filter, the per-mode
+  recurrence s(t) = p s(t-1) + u(t), the impulse response;
+* invariants: linearity, time invariance, scale equivariance, chunked == full;
+* a textbook routine: numpy.convolve.
+
+The same pins are run against oracles with a planted mistake to show that each
+plausible mistake is caught (tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _params(rng, D, N, lam_lo=1e-3):
+    lam = -np.exp(rng.uniform(math.log(lam_lo), 0.0, (D, N)))
+    R = rng.normal(0, 0.25, (D, N))
+    return lam, R
+
+
+# ---------------------------------------------------------------- golden
+def pin_golden(O):
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    for c in g["modal_cases"]:
+        lam = np.log(np.array(c["poles"]))[None, :]
+        R = np.array(c["residues"])[None, :]
+        sh = lambda a: np.array(a, dtype=np.float64)[None, None, :]
+        x1, v, x2 = sh(c["x1"]), sh(c["v"]), sh(c["x2"])
+        skip = np.array([c["skip"]])
+        y = O.hyena_fwd(x1, x2, v, lam, R, skip)
+        assert np.allclose(y[0, 0], c["y"], rtol=0, atol=1e-13), (c["name"], y, c["y"])
+        s = O.modal_state(x1 * v, lam)
+        assert np.allclose(s[0, 0], c["state"], rtol=0, atol=1e-13), (c["name"], s)
+        L = len(c["x1"])
+        for C in (1, L, c.get("chunk", 2)):
+            yc, sc = O.chunk_fwd(x1, x2, v, lam, R, skip, C)
+            assert np.allclose(yc[0, 0], c["y"], rtol=0, atol=1e-13), (c["name"], C, yc)
+            assert np.allclose(sc[0, 0], c["state"], rtol=0, atol=1e-13), (c["name"], C, sc)
+        if "chunk" in c:
+            half = c["chunk"]
+            _, s1 = O.chunk_fwd(x1[..., :half], x2[..., :half], v[..., :half],
+                                lam, R, skip, half)
+            assert np.allclose(s1[0, 0], c["state_after_first_chunk"], rtol=0, atol=1e-13)
+    for c in g["fir_cases"]:
+        sh = lambda a: np.array(a, dtype=np.float64)[None, None, :]
+        y = O.fir_fwd(sh(c["x1"]), sh(c["x2"]), sh(c["v"]),
+                      np.array(c["taps"], dtype=np.float64)[None, :],
+                      np.array([c["skip"]]))
+        assert np.allclose(y[0, 0], c["y"], rtol=0, atol=1e-13), (c["name"], y)
+
+
+# ---------------------------------------------------------------- filter
+def pin_filter_rational(O):
+    """h = sum_n R_n p_n^t with rational p_n, R_n, against exact fractions."""
+    poles = [Fraction(1, 2), Fraction(3, 4), Fraction(7, 8), Fraction(1, 16)]
+    res = [Fraction(1), Fraction(-3, 2), Fraction(5, 4), Fraction(2)]
+    L = 40
+    lam = np.log(np.array([float(p) for p in poles]))[None, :]
+    R = np.array([float(r) for r in res])[None, :]
+    h = O.modal_filter(lam, R, L)[0]
+    for t in range(L):
+        exact = sum(r * p ** t for r, p in zip(res, poles))
+        scale = sum(abs(r) * p ** t for r, p in zip(res, poles))
+        assert abs(h[t] - float(exact)) <= 1e-13 * float(scale), (t, h[t], float(exact))
+    assert h[0] == float(sum(res))
+
+
+def pin_filter_dft(O):
+    """Geometric series: DFT_2L of h[0:L] = sum_n R_n (1 - p^L w^(kL)) / (1 - p w^k)."""
+    rng = _rng(11)
+    D, N, L = 3, 16, 512
+    lam, R = _params(rng, D, N)
+    h = O.modal_filter(lam, R, L)
+    n = 2 * L
+    H = np.fft.rfft(h, n=n, axis=-1)
+    k = np.arange(n // 2 + 1)
+    w = np.exp(-2j * np.pi * k / n)
+    p = np.exp(lam)
+    closed = np.zeros((D, k.size), dtype=complex)
+    for m in range(N):
+        pm = p[:, m:m + 1]
+        closed += R[:, m:m + 1] * (1 - pm ** L * (-1.0) ** k) / (1 - pm * w[None])
+    err = np.linalg.norm(H - closed) / np.linalg.norm(closed)
+    assert err < 1e-11, err
+
+
+def pin_recurrence(O):
+    """Per-mode recurrence s(t) = p s(t-1) + u(t) and z(t) = sum_n R_n s_n(t)."""
+    rng = _rng(12)
+    B, D, N, L = 2, 3, 5, 300
+    lam, R = _params(rng, D, N)
+    x1 = rng.normal(size=(B, D, L))
+    v = rng.normal(size=(B, D, L))
+    u = x1 * v
+    p = np.exp(lam)
+    s = np.zeros((B, D, N))
+    z = np.zeros((B, D, L))
+    for t in range(L):
+        s = p[None] * s + u[:, :, t:t + 1]
+        z[:, :, t] = np.sum(R[None] * s, axis=-1)
+    y = O.hyena_fwd(x1, np.ones_like(x1), v, lam, R, np.zeros(D))
+    assert np.max(np.abs(y - z)) <= 1e-11 * np.max(np.abs(z)), np.max(np.abs(y - z))
+    s_or = O.modal_state(u, lam)
+    assert np.max(np.abs(s_or - s)) <= 1e-11 * np.max(np.abs(s))
+
+
+# ---------------------------------------------------------------- conv
+def pin_impulse(O):
+    rng = _rng(13)
+    D, N, L = 4, 16, 700
+    lam, R = _params(rng, D, N)
+    h = O.modal_filter(lam, R, L)
+    for t0 in (0, 1, 333, L - 1):
+        x1 = np.zeros((1, D, L))
+        x1[..., t0] = 1.0
+        y = O.hyena_fwd(x1, np.ones_like(x1), np.ones_like(x1), lam, R, np.zeros(D))
+        assert np.all(y[..., :t0] == 0.0), t0
+        assert np.allclose(y[0, :, t0:], h[:, :L - t0], rtol=1e-12, atol=1e-14), t0
+        taps = rng.normal(size=(D, 9))
+        yf = O.fir_fwd(x1, np.ones_like(x1), np.ones_like(x1), taps, np.zeros(D))
+        assert np.all(yf[..., :t0] == 0.0)
+        m = min(9, L - t0)
+        assert np.array_equal(yf[0, :, t0:t0 + m], taps[:, :m])
+
+
+def pin_linearity_time_invariance(O):
+    rng = _rng(14)
+    D, N, L = 3, 16, 1500
+    lam, R = _params(rng, D, N)
+    skip = rng.normal(size=D)
+    x1a, x1b = rng.normal(size=(2, 1, D, L))
+    x2 = rng.normal(size=(1, D, L))
+    v = rng.normal(size=(1, D, L))
+    a, b = 0.7, -1.9
+    f = lambda x: O.hyena_fwd(x, x2, v, lam, R, skip)
+    lhs = f(a * x1a + b * x1b)
+    rhs = a * f(x1a) + b * f(x1b)
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
+    # time invariance of the filter part (x2 = 1, v = 1): shifting u shifts z
+    sh = 57
+    g = lambda x: O.hyena_fwd(x, np.ones_like(x), np.ones_like(x), lam, R, np.zeros(D))
+    xs = np.zeros_like(x1a)
+    xs[..., sh:] = x1a[..., :L - sh]
+    assert np.allclose(g(xs)[..., sh:], g(x1a)[..., :L - sh], rtol=1e-11, atol=1e-11)
+    assert np.all(g(xs)[..., :sh] == 0)
+
+
+def pin_numpy_convolve(O):
+    rng = _rng(15)
+    D, N = 2, 16
+    for L in (1, 2, 17, 999, 5000):
+        lam, R = _params(rng, D, N)
+        x1 = rng.normal(size=(1, D, L))
+        y = O.hyena_fwd(x1, np.ones_like(x1), np.ones_like(x1), lam, R, np.zeros(D))
+        h = O.modal_filter(lam, R, L)
+        for c in range(D):
+            ref = np.convolve(x1[0, c], h[c])[:L]
+            assert np.allclose(y[0, c], ref, rtol=1e-10, atol=1e-10 * np.max(np.abs(ref))), (L, c)
+        for K in (1, 7, 128):
+            taps = rng.normal(size=(D, K))
+            yf = O.fir_fwd(x1, np.ones_like(x1), np.ones_like(x1), taps, np.zeros(D))
+            for c in range(D):
+                ref = np.convolve(x1[0, c], taps[c])[:L]
+                assert np.allclose(yf[0, c], ref, rtol=1e-12, atol=1e-12), (L, K, c)
+
+
+def pin_direct_vs_fft(O):
+    rng = _rng(16)
+    u = rng.normal(size=(2, 3, 3000))
+    h = rng.normal(size=(3, 3000)) * np.exp(-np.arange(3000) / 500.0)
+    a = O.conv_direct(u, h[None])
+    b = O.conv_fft(u, h[None])
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+    hs = rng.normal(size=(3, 7))
+    assert np.max(np.abs(O.conv_direct(u, hs[None]) - O.conv_fft(u, hs[None]))) < 1e-12
+
+
+def pin_fraction_bruteforce(O):
+    """Exact rational evaluation of the gated FIR operator on a tiny input."""
+    rng = _rng(17)
+    L, K = 9, 4
+    q = lambda: Fraction(int(rng.integers(-8, 9)), int(rng.integers(1, 5)))
+    x1 = [q() for _ in range(L)]
+    v = [q() for _ in range(L)]
+    x2 = [q() for _ in range(L)]
+    w = [q() for _ in range(K)]
+    sk = q()
+    u = [a * b for a, b in zip(x1, v)]
+    y = []
+    for t in range(L):
+        z = sum((w[k] * u[t - k] for k in range(K) if t - k >= 0), Fraction(0))
+        y.append(x2[t] * z + sk * u[t])
+    f = lambda a: np.array([float(x) for x in a])[None, None, :]
+    yo = O.fir_fwd(f(x1), f(x2), f(v), np.array([float(x) for x in w])[None], np.array([float(sk)]))
+    assert np.allclose(yo[0, 0], [float(x) for x in y], rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------- gate
+def pin_gate_special(O):
+    rng = _rng(18)
+    D, N, L = 3, 16, 200
+    lam, _ = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, 2, D, L))
+    skip = rng.normal(size=D)
+    y = O.hyena_fwd(x1, x2, v, lam, np.zeros((D, N)), skip)
+    assert np.array_equal(y, skip[None, :, None] * (x1 * v))
+    _, R = _params(rng, D, N)
+    y0 = O.hyena_fwd(x1, np.zeros_like(x2), v, lam, R, skip)
+    assert np.array_equal(y0, skip[None, :, None] * (x1 * v))
+
+
+def pin_fir_delta(O):
+    rng = _rng(19)
+    D, L = 3, 300
+    x1, x2, v = rng.normal(size=(3, 1, D, L))
+    skip = rng.normal(size=D)
+    u = x1 * v
+    for K, lag in ((1, 0), (7, 3), (128, 127), (128, 5)):
+        taps = np.zeros((D, K))
+        taps[:, lag] = 1.0
+        y = O.fir_fwd(x1, x2, v, taps, skip)
+        us = np.zeros_like(u)
+        us[..., lag:] = u[..., :L - lag]
+        assert np.array_equal(y, x2 * us + skip[None, :, None] * u), (K, lag)
+
+
+# ---------------------------------------------------------------- chunked
+def pin_chunk_equals_full(O):
+    rng = _rng(20)
+    B, D, N, L = 2, 3, 16, 777
+    lam, R = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, B, D, L))
+    skip = rng.normal(size=D)
+    yf = O.hyena_fwd(x1, x2, v, lam, R, skip)
+    sf = O.modal_state(x1 * v, lam)
+    for C in (1, 2, 64, 100, 256, L, 1000):
+        yc, sc = O.chunk_fwd(x1, x2, v, lam, R, skip, C)
+        assert np.max(np.abs(yc - yf)) <= 1e-10 * np.max(np.abs(yf)), C
+        assert np.max(np.abs(sc - sf)) <= 1e-10 * np.max(np.abs(sf)), C
+
+
+def pin_chunk_resume(O):
+    """Split anywhere, hand the state over, continue: equals the single call."""
+    rng = _rng(21)
+    B, D, N, L = 1, 3, 16, 600
+    lam, R = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, B, D, L))
+    skip = rng.normal(size=D)
+    s0 = rng.normal(size=(B, D, N))
+    y_all, s_all = O.chunk_fwd(x1, x2, v, lam, R, skip, 128, state_in=s0)
+    for cut in (128, 256, 301):
+        ya, sa = O.chunk_fwd(x1[..., :cut], x2[..., :cut], v[..., :cut], lam, R, skip, 128, state_in=s0)
+        yb, sb = O.chunk_fwd(x1[..., cut:], x2[..., cut:], v[..., cut:], lam, R, skip, 128, state_in=sa)
+        y = np.concatenate([ya, yb], axis=-1)
+        assert np.max(np.abs(y - y_all)) <= 1e-10 * np.max(np.abs(y_all)), cut
+        assert np.max(np.abs(sb - s_all)) <= 1e-10 * np.max(np.abs(s_all)), cut
+    # a non-zero initial state adds sum_n R_n p_n^(t+1) s0_n to z
+    y_zero, _ = O.chunk_fwd(x1, x2, v, lam, R, skip, 128)
+    t = np.arange(L)
+    extra = np.einsum("dn,bdn,dnt->bdt", R, s0, np.exp(lam[:, :, None] * (t + 1)))
+    assert np.allclose(y_all - y_zero, x2 * extra, rtol=1e-9, atol=1e-9)
+
+
+def pin_chunk_state_rational(O):
+    """state_out = p^L s_in + sum_k p^(L-1-k) u[k], exactly, with rational p."""
+    poles = [Fraction(1, 2), Fraction(3, 4), Fraction(5, 8)]
+    L, C = 11, 4
+    rng = _rng(22)
+    u = [Fraction(int(rng.integers(-5, 6)), int(rng.integers(1, 4))) for _ in range(L)]
+    s0 = [Fraction(1, 3), Fraction(-2), Fraction(3, 2)]
+    exact = [p ** L * s + sum(p ** (L - 1 - k) * u[k] for k in range(L)) for p, s in zip(poles, s0)]
+    lam = np.log(np.array([float(p) for p in poles]))[None]
+    x1 = np.array([float(x) for x in u])[None, None]
+    ones = np.ones_like(x1)
+    _, s = O.chunk_fwd(x1, ones, ones, lam, np.ones((1, 3)), None, C,
+                       state_in=np.array([float(x) for x in s0])[None, None])
+    assert np.allclose(s[0, 0], [float(e) for e in exact], rtol=1e-13, atol=1e-13), (s, exact)
+
+
+def pin_scale_equivariance(O):
+    rng = _rng(23)
+    D, N, L = 4, 16, 512
+    lam, R = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, 1, D, L))
+    skip = rng.normal(size=D)
+    sc = np.exp(rng.uniform(0, math.log(1e12), D))
+    y = O.hyena_fwd(x1, x2, v, lam, R, skip)
+    ys = O.hyena_fwd(x1 * sc[None, :, None], x2, v, lam, R, skip)
+    ref = y * sc[None, :, None]
+    err = np.max(np.abs(ys - ref), axis=-1) / np.max(np.abs(ref), axis=-1)
+    assert np.all(err <= 1e-12), err
+
+
+ALL_PINS = [
+    pin_golden, pin_filter_rational, pin_filter_dft, pin_recurrence,
+    pin_impulse, pin_linearity_time_invariance, pin_numpy_convolve,
+    pin_direct_vs_fft, pin_fraction_bruteforce, pin_gate_special,
+    pin_fir_delta, pin_chunk_equals_full, pin_chunk_resume,
+    pin_chunk_state_rational, pin_scale_equivariance,
+]

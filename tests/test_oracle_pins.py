@@ -1,0 +1,141 @@
+"""The fp64 oracle against its pins, and the pins against planted mistakes.
+
+A planted mistake lives in a copy of an oracle function, on the CPU; each must
+make at least one pin fail.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle.hyena_oracle as HO
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(HO)
+
+
+# ------------------------------------------------------------ planted mistakes
+def _mutant(**over):
+    """A namespace with the oracle's functions, some replaced, re-bound so the
+    replaced helpers are used by the functions that call them."""
+    ns = {k: getattr(HO, k) for k in dir(HO) if not k.startswith("__")}
+    ns.update(over)
+    mod = types.SimpleNamespace(**ns)
+    # rebuild the composite functions over the (possibly replaced) helpers
+    def hyena_fwd(x1, x2, v, log_poles, residues, skip, conv=None):
+        L = np.asarray(x1).shape[-1]
+        h = mod.modal_filter(log_poles, residues, L)
+        cv = conv or mod.causal_conv
+        return mod._gate(x1, x2, v, lambda u: cv(u, h[None]), skip)
+
+    def fir_fwd(x1, x2, v, taps, skip, conv=None):
+        w = np.asarray(taps, dtype=np.float64)
+        cv = conv or mod.conv_direct
+        return mod._gate(x1, x2, v, lambda u: cv(u, w[None]), skip)
+
+    def causal_conv(u, h):
+        if u.shape[-1] <= HO.DIRECT_MAX_L or h.shape[-1] <= 64:
+            return mod.conv_direct(u, h)
+        return mod.conv_fft(u, h)
+
+    if "hyena_fwd" not in over:
+        mod.hyena_fwd = hyena_fwd
+    if "fir_fwd" not in over:
+        mod.fir_fwd = fir_fwd
+    if "causal_conv" not in over:
+        mod.causal_conv = causal_conv
+    return mod
+
+
+def _filter_shifted(log_poles, residues, L):          # time origin off by one
+    lam = np.asarray(log_poles, float)
+    R = np.asarray(residues, float)
+    t = np.arange(L) + 1.0
+    return np.einsum("dn,dnt->dt", R, np.exp(lam[:, :, None] * t))
+
+
+def _filter_dropped_mode(log_poles, residues, L):     # last mode dropped
+    lam = np.asarray(log_poles, float)[:, :-1]
+    R = np.asarray(residues, float)[:, :-1]
+    t = np.arange(L, dtype=float)
+    if lam.shape[1] == 0:
+        return np.zeros((np.asarray(log_poles).shape[0], L))
+    return np.einsum("dn,dnt->dt", R, np.exp(lam[:, :, None] * t))
+
+
+def _conv_anticausal(u, h):                           # transposed operand
+    u = np.asarray(u, float)
+    h = np.asarray(h, float)
+    L = u.shape[-1]
+    z = np.zeros_like(u)
+    for lag in range(min(L, h.shape[-1])):
+        z[..., :L - lag] += h[..., lag:lag + 1] * u[..., lag:]
+    return z
+
+
+def _conv_fft_circular(u, h):                         # no zero padding
+    import scipy.fft
+    u = np.asarray(u, float)
+    h = np.asarray(h, float)
+    L = u.shape[-1]
+    return scipy.fft.irfft(scipy.fft.rfft(u, n=L) * scipy.fft.rfft(h[..., :L], n=L), n=L)
+
+
+def _gate_skip_inside(x1, x2, v, z_of_u, skip):       # skip inside the x2 gate
+    x1, x2, v = (np.asarray(a, float) for a in (x1, x2, v))
+    u = x1 * v
+    sk = np.zeros(x1.shape[-2]) if skip is None else np.asarray(skip, float)
+    return x2 * (z_of_u(u) + sk[:, None] * u)
+
+
+def _chunk_variant(carry_off=1, decay_off=1, last_len_full=False):
+    """chunk_fwd with a planted mistake in the carried term or state update."""
+    def chunk_fwd(x1, x2, v, log_poles, residues, skip, C, state_in=None, return_states=False):
+        x1, x2, v = (np.asarray(a, float) for a in (x1, x2, v))
+        lam = np.asarray(log_poles, float)
+        R = np.asarray(residues, float)
+        B, D, L = x1.shape
+        s = np.zeros((B, D, lam.shape[1])) if state_in is None else np.array(state_in, float)
+        u = x1 * v
+        z = np.zeros_like(u)
+        h = HO.modal_filter(lam, R, min(C, L))
+        for t0 in range(0, L, C):
+            Cp = min(C, L - t0)
+            uc = u[..., t0:t0 + Cp]
+            zc = HO.conv_direct(uc, h[None, :, :Cp])
+            j = np.arange(Cp, dtype=float)
+            zc += np.einsum("dn,bdn,dnj->bdj", R, s, np.exp(lam[:, :, None] * (j + carry_off)))
+            z[..., t0:t0 + Cp] = zc
+            Cs = C if last_len_full else Cp
+            dec = np.exp(lam[:, :, None] * (Cp - decay_off - j))
+            s = np.exp(lam * Cs)[None] * s + np.einsum("bdj,dnj->bdn", uc, dec)
+        sk = np.zeros(D) if skip is None else np.asarray(skip, float)
+        return x2 * z + sk[:, None] * u, s
+    return chunk_fwd
+
+
+MUTANTS = {
+    "filter_time_origin": dict(modal_filter=_filter_shifted),
+    "filter_dropped_mode": dict(modal_filter=_filter_dropped_mode),
+    "conv_anticausal": dict(conv_direct=_conv_anticausal),
+    "conv_fft_circular": dict(conv_fft=_conv_fft_circular),
+    "gate_skip_inside": dict(_gate=_gate_skip_inside),
+    "chunk_carry_exponent": dict(chunk_fwd=_chunk_variant(carry_off=0)),
+    "chunk_decay_exponent": dict(chunk_fwd=_chunk_variant(decay_off=0)),
+    "chunk_last_length": dict(chunk_fwd=_chunk_variant(last_len_full=True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(**MUTANTS[name])
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
