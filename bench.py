@@ -1,0 +1,189 @@
+"""Benchmark of the Hyena operator on one MI355X.
+
+One step = one pass of the operator over the 32 kb chunked-prefill workload
+(B=1, D=4096, L=32768, bf16 I/O, N=16 modes, chunk 1024 with carried state):
+modal filter generation, input gate, causal long convolution, output gate and
+skip, and the carried modal state -- all in one launch of hyena_chunk_fwd.
+Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  Besides the headline it reports the roofline of the
+dominant kernel (HIP-event timing of the same launches), the other entry points
+at the same shape, and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Hyena op Gtoken·channels/s at D=4096 L=32768 bf16; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "32k_chunked"
+CHUNK = 1024
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["genomic_lm_amd/csrc/chunk_mfma.hip", "genomic_lm_amd/csrc/common.hpp",
+                  "genomic_lm_amd/csrc/launch.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--algo", default="mfma", choices=["mfma", "fft", "auto"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, stream):
+    """Average per-call time (s) over `steps` calls, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def cpu_baseline(w):
+    """The fp64 oracle's chunked prefill on a bounded sample of channels."""
+    import numpy as np
+    import oracle
+    rows = np.arange(4)
+    x1, x2, v = (w.f64(k, rows) for k in ("x1", "x2", "v"))
+    lam = w.log_poles[rows].astype(np.float64)
+    R = w.residues[rows].astype(np.float64)
+    sk = w.skip[rows].astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.chunk_fwd(x1, x2, v, lam, R, sk, CHUNK)
+    dt = time.perf_counter() - t0
+    tc = x1.size
+    return {
+        "value": tc / dt / 1e9, "unit": "Gtoken·channels/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle.chunk_fwd (fp64, chunk {CHUNK}) on {len(rows)} of {w.D} channels "
+                  f"x {w.L} tokens, {dt:.1f} s wall, numpy single thread",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the operator "
+              "shards over channels with no communication, so N GPUs run N independent copies "
+              "of this single-GPU workload.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import genomic_lm_amd as G
+    import workloads as W
+
+    G.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make(WORKLOAD)
+    B, D, L = w.B, w.D, w.L
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    par = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    x1, x2, v = to(w.x1), to(w.x2), to(w.v)
+    lam, res, skip = par(w.log_poles), par(w.residues), par(w.skip)
+    y = torch.empty_like(x1)
+    st = torch.empty((B, D, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo=args.algo, out=y, state_out=st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    t_step = e0.elapsed_time(e1) / 1e3 / args.steps
+    if not torch.isfinite(y.float()).all():
+        raise RuntimeError("non-finite output")
+
+    tc = B * D * L
+    alg_bytes = 8 * tc                       # x1, x2, v read + y written, bf16
+    achieved = alg_bytes / t_step / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("algo") == args.algo:
+            traffic = tr.get("bytes_per_launch")
+
+    comps = {}
+    if not args.no_components:
+        comp_steps = max(3, args.steps // 4)
+        runs = {
+            "chunk_fft": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="fft", out=y, state_out=st),
+            "chunk_mfma": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="mfma", out=y, state_out=st),
+            "fftconv_single_pass": lambda: G.fftconv_fwd(x1, x2, v, lam, res, skip, out=y),
+            "fir7": lambda: G.fir_fwd(x1, x2, v, par(w.taps[7]), skip, out=y),
+            "fir128": lambda: G.fir_fwd(x1, x2, v, par(w.taps[128]), skip, out=y),
+        }
+        for name, fn in runs.items():
+            t = timed(fn, comp_steps, 2, stream)
+            comps[name] = {"ms": round(t * 1e3, 4), "Gtc_per_s": round(tc / t / 1e9, 2),
+                           "hbm_frac": round(alg_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tc / t_step / 1e9, 3),
+        "unit": "Gtoken·channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "32k chunked prefill (B=1 D=4096 L=32768, bf16 I/O, N=16, chunk 1024)",
+                   "entry": "hyena_chunk_fwd", "algo": args.algo, "B": B, "D": D, "L": L,
+                   "chunk": CHUNK, "modes": w.N, "io": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "wall_s_timed": round(t_wall, 3),
+        "components": comps,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

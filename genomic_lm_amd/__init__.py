@@ -1,0 +1,219 @@
+"""genomic_lm_amd -- MI355X (gfx950) Hyena operator, Python binding of libhyena.so.
+
+A thin ctypes layer over the C ABI in include/hyena.h: it checks dtype,
+device and contiguity of torch tensors, passes their device pointers and the
+current HIP stream, and turns status codes into exceptions.  Every step of the
+operator runs in the HIP kernels of libhyena.so; there is no fallback path.
+If the library is not built the functions raise HyenaNotBuilt.
+
+Entry points (names follow the C ABI):
+  modal_filter(log_poles, residues, L)                      -> h (D, L) fp32
+  fir_fwd(x1, x2, v, taps, skip=None)                       -> y
+  fftconv_fwd(x1, x2, v, log_poles, residues, skip=None)    -> y
+  chunk_fwd(x1, x2, v, log_poles, residues, C, skip=None,
+            state_in=None, algo="auto")                      -> (y, state_out)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "HyenaError", "HyenaNotBuilt", "lib", "LIB_PATH", "abi_version",
+    "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
+    "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_LAUNCH",
+    "F32", "BF16", "ALGOS", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+ALGOS = {"auto": 0, "fft": 1, "mfma": 2}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+
+# name -> (restype, argtypes); the full set of symbols include/hyena.h declares
+EXPORTS = {
+    "hyena_abi_version": (_int, []),
+    "hyena_status_string": (ctypes.c_char_p, [_int]),
+    "hyena_modal_filter": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
+    "hyena_fir_fwd": (_int, [_p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int, _p]),
+    "hyena_fftconv_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
+                                 _p, _size, _p]),
+    "hyena_fftconv_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
+    "hyena_chunk_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
+                               _i64, _int, _int, _p]),
+}
+
+
+class HyenaNotBuilt(RuntimeError):
+    pass
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhyena.so, with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise HyenaNotBuilt(
+                f"{LIB_PATH} is missing: build it with `python -m genomic_lm_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().hyena_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().hyena_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise HyenaError(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return _p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else _p(t.data_ptr())
+
+
+def _act(name, t, like=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be (B, D, L), got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if like is not None:
+        if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device:
+            raise ValueError(f"{name} must match x1 in shape, dtype and device")
+    return t
+
+
+def _param(name, t, shape, dev, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _io(t):
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+def modal_filter(log_poles: torch.Tensor, residues: torch.Tensor, L: int) -> torch.Tensor:
+    """h[c, t] = sum_n residues[c, n] * exp(log_poles[c, n] * t), fp32 (D, L)."""
+    if not log_poles.is_cuda:
+        raise ValueError("log_poles must be on a GPU device")
+    D, N = log_poles.shape
+    _param("log_poles", log_poles, (D, N), log_poles.device)
+    _param("residues", residues, (D, N), log_poles.device)
+    h = torch.empty((D, L), dtype=torch.float32, device=log_poles.device)
+    _check("hyena_modal_filter", lib().hyena_modal_filter(
+        _ptr(log_poles), _ptr(residues), D, N, L, _ptr(h), _stream(h)))
+    return h
+
+
+def fir_fwd(x1, x2, v, taps, skip=None, out=None) -> torch.Tensor:
+    """Gated explicit FIR: y = x2 * (taps conv x1*v) + skip * x1*v."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    K = taps.shape[-1] if isinstance(taps, torch.Tensor) and taps.dim() == 2 else -1
+    _param("taps", taps, (D, K), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    _check("hyena_fir_fwd", lib().hyena_fir_fwd(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(taps), K, _ptr(skip), _ptr(y), B, D, L,
+        _io(x1), _stream(x1)))
+    return y
+
+
+def fftconv_workspace_size(B: int, D: int, L: int, N: int, dtype=torch.bfloat16) -> int:
+    return int(lib().hyena_fftconv_workspace_size(B, D, L, N, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def fftconv_fwd(x1, x2, v, log_poles, residues, skip=None, out=None, workspace=None) -> torch.Tensor:
+    """Single-pass modal Hyena operator with a zero-padded FFT convolution."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
+    _param("log_poles", log_poles, (D, N), x1.device)
+    _param("residues", residues, (D, N), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    need = fftconv_workspace_size(B, D, L, N, x1.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x1.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hyena_fftconv_fwd", lib().hyena_fftconv_fwd(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip), _ptr(y),
+        B, D, L, _io(x1), _ptr(workspace), ws_bytes, _stream(x1)))
+    return y
+
+
+def chunk_fwd(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
+              algo: str = "auto", out=None, state_out=None):
+    """Chunked prefill with the modal state carried in and out; returns (y, state_out)."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
+    _param("log_poles", log_poles, (D, N), x1.device)
+    _param("residues", residues, (D, N), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    _param("state_in", state_in, (B, D, N), x1.device, optional=True)
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}")
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    if state_out is None:
+        state_out = torch.empty((B, D, N), dtype=torch.float32, device=x1.device)
+    else:
+        _param("state_out", state_out, (B, D, N), x1.device)
+    _check("hyena_chunk_fwd", lib().hyena_chunk_fwd(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip),
+        _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, int(C), _io(x1), ALGOS[algo],
+        _stream(x1)))
+    return y, state_out

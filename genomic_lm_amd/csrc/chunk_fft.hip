@@ -1,0 +1,272 @@
+// chunk_fft.hip -- chunked prefill with the modal state carried across chunks,
+// the in-chunk convolution done as a zero-padded FFT of length >= 2C.
+//
+// For the chunk [t0, t0 + C'), C' = min(C, L - t0):
+//   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + sum_n R_n p_n^(t-t0+1) s_n
+//   s_n <- p_n^C' s_n + sum_{j<C'} p_n^(C'-1-j) u[t0+j]
+// which makes the chunked output equal the single-pass output for any C
+// (TurboQuant-Bio int4 Evo 2 checkpoints, 'Important: a correctness fix comes
+// with this' and 'Chunk size'; the IIR modal state is the layer's inference
+// cache: Evo2-7B-262K model card, Implementation Notes, 'Custom cache').  The
+// pages' engine runs the in-chunk part through an FFT buffer sized by the
+// chunk ('modal-FFT buffer', TurboQuant-Bio, 'Chunk size'); here that buffer
+// is LDS.
+//
+// One workgroup walks all chunks of one (b, c) row in order.  The spectrum of
+// h[0:C) is built once per row and kept in registers; per chunk there are two
+// forward and two inverse size-S transforms (S = C/2 rounded up to a power of
+// two, the parity-half scheme of fftconv.hip), the rank-N carried term, and a
+// workgroup reduction for the state update.
+#include "common.hpp"
+#include "fft.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+__device__ __forceinline__ float2 real_spectrum_c(float2 ck, float2 cm, float2 w) {
+  float2 a = make_float2(ck.x + cm.x, ck.y - cm.y);
+  float2 b = make_float2(ck.x - cm.x, ck.y + cm.y);
+  return cscale(cadd(a, cmul_mi(cmul(w, b))), 0.5f);
+}
+
+__device__ __forceinline__ float2 inverse_pack_c(float2 zk, float2 zm, float2 w) {
+  float2 a = make_float2(zk.x + zm.x, zk.y - zm.y);
+  float2 b = make_float2(zk.x - zm.x, zk.y + zm.y);
+  return cscale(cadd(a, cmul_pi(cmul(cconj(w), b))), 0.5f);
+}
+
+constexpr int CHUNK_MAXN = 64;
+constexpr int CHUNK_NG = 16;             // modes per reduction group
+
+template <int S, int T, typename IO, bool VEC>
+__global__ __launch_bounds__(T) void chunk_fft_kernel(
+    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const float* __restrict__ lam, const float* __restrict__ res, int N,
+    const float* __restrict__ skip, const float* state_in,
+    float* state_out, IO* __restrict__ y, int D, int L, int C) {
+  constexpr int P = S / T;
+  constexpr int M = 2 * S;
+  constexpr int LG_M = ilog2(M);
+  constexpr int LG_N = LG_M + 1;
+  __shared__ float2 lds[lds_padded_size(S)];
+  __shared__ float s_lam[CHUNK_MAXN], s_res[CHUNK_MAXN], s_st[CHUNK_MAXN];
+  __shared__ float red[T * (CHUNK_NG + 1)];      // partial sums of one mode group
+
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int c = static_cast<int>(row % D);
+  const IO* x1r = x1 + row * L;
+  const IO* x2r = x2 + row * L;
+  const IO* vr = v + row * L;
+  IO* yr = y + row * L;
+  const float sk = skip ? skip[c] : 0.0f;
+
+  for (int n = t; n < N; n += T) {
+    s_lam[n] = lam[static_cast<int64_t>(c) * N + n];
+    s_res[n] = res[static_cast<int64_t>(c) * N + n];
+    s_st[n] = state_in ? state_in[row * N + n] : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- spectrum of h[0:C) for both parity halves, kept for every chunk
+  float2 hs[2][P];
+  float h_nyq = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    float2 a[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) a[i] = make_float2(0.0f, 0.0f);
+    for (int n = 0; n < N; ++n) {
+      const float l = s_lam[n];
+      const float p = expf(l);
+      const float step = expf(l * static_cast<float>(2 * T));
+      float e = s_res[n] * expf(l * static_cast<float>(2 * t));
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        a[i].x += e;
+        a[i].y = fmaf(e, p, a[i].y);
+        e *= step;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int m = t + T * i;
+      if (2 * m >= C) a[i].x = 0.0f;
+      if (2 * m + 1 >= C) a[i].y = 0.0f;
+      if (q) a[i] = cmul(a[i], twiddle(m, LG_M));
+    }
+    fft_forward<S, T>(a, lds, t);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = t + T * i;
+      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+      hs[q][i] = real_spectrum_c(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+    }
+    if (q == 0 && t == 0) h_nyq = a[0].x - a[0].y;
+  }
+
+  const float inv_m = 1.0f / static_cast<float>(M);
+#pragma unroll 1
+  for (int t0 = 0; t0 < L; t0 += C) {
+    const int Cp = min(C, L - t0);
+    const int lim = t0 + Cp;
+    float2 u[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int m = t + T * i;
+      const float2 p1 = ld_pair<IO, VEC>(x1r, t0 + 2 * m, lim);
+      const float2 p2 = ld_pair<IO, VEC>(vr, t0 + 2 * m, lim);
+      u[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
+    }
+    float2 b0[P], a[P];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) a[i] = q ? cmul(u[i], twiddle(t + T * i, LG_M)) : u[i];
+      fft_forward<S, T>(a, lds, t);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
+      __syncthreads();
+      float2 z[P];
+      float zm_nyq = 0.0f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int k = t + T * i;
+        const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+        z[i] = cmul(real_spectrum_c(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)), hs[q][i]);
+      }
+      if (q == 0 && t == 0) zm_nyq = (a[0].x - a[0].y) * h_nyq;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = z[i];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int k = t + T * i;
+        const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+        float2 zmir = lds[lds_pad(kk)];
+        if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
+        a[i] = inverse_pack_c(z[i], zmir, twiddle(2 * k + q, LG_N));
+      }
+      fft_inverse<S, T>(a, lds, t);
+      if (q == 0) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) b0[i] = a[i];
+      }
+    }
+    // in-chunk convolution at positions t0 + 2m, t0 + 2m + 1
+    float2 zz[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      zz[i] = cscale(cadd(b0[i], cmul(cconj(twiddle(t + T * i, LG_M)), a[i])), inv_m);
+
+    // carried term sum_n R_n p_n^(tau+1) s_n (old state), and the state
+    // partials, reduced over the workgroup 16 modes at a time
+    const bool full = (Cp == 2 * S);       // ladder only when the chunk fills the frame
+    for (int n0 = 0; n0 < N; n0 += CHUNK_NG) {
+      const int ng = min(CHUNK_NG, N - n0);
+      for (int g = 0; g < ng; ++g) {
+        const int n = n0 + g;
+        const float l = s_lam[n];
+        const float p = expf(l);
+        const float step = expf(l * static_cast<float>(2 * T));
+        float e = s_res[n] * s_st[n] * expf(l * static_cast<float>(2 * t + 1));
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          zz[i].x += e;
+          zz[i].y = fmaf(e, p, zz[i].y);
+          e *= step;
+        }
+        // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
+        float part = 0.0f;
+        if (full) {
+          float w = expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+#pragma unroll
+          for (int i = P - 1; i >= 0; --i) {
+            part = fmaf(u[i].x, w * p, part);
+            part = fmaf(u[i].y, w, part);
+            w *= step;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < P; ++i) {
+            const int m2 = 2 * (t + T * i);
+            const float w = expf(l * static_cast<float>(max(Cp - 2 - m2, 0)));
+            part = fmaf(u[i].x, (m2 + 1 < Cp) ? w * p : w, part);   // m2 = Cp-1: weight p^0
+            part = fmaf(u[i].y, w, part);                              // zero beyond Cp anyway
+          }
+        }
+        red[t * (CHUNK_NG + 1) + g] = part;
+      }
+      __syncthreads();                     // partials written; old state no longer read
+      for (int g = t; g < ng; g += T) {
+        float tot = 0.0f;
+        for (int j = 0; j < T; ++j) tot += red[j * (CHUNK_NG + 1) + g];
+        const int n = n0 + g;
+        s_st[n] = fmaf(expf(s_lam[n] * static_cast<float>(Cp)), s_st[n], tot);
+      }
+      __syncthreads();                     // red reusable
+    }
+    // gate and store
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int pos = t0 + 2 * (t + T * i);
+      if (pos >= lim) continue;
+      const float2 g = ld_pair<IO, VEC>(x2r, pos, lim);
+      const float2 out = make_float2(fmaf(g.x, zz[i].x, sk * u[i].x), fmaf(g.y, zz[i].y, sk * u[i].y));
+      st_pair<IO, VEC>(yr, pos, lim, out);
+    }
+  }
+  for (int n = t; n < N; n += T) state_out[row * N + n] = s_st[n];
+}
+
+int chunk_fft_S(int64_t C) {
+  int64_t half = (C + 1) / 2;
+  int64_t S = 256;
+  while (S < half) S <<= 1;
+  return S <= 4096 ? static_cast<int>(S) : 0;
+}
+
+template <int S, int T, typename IO>
+static hipError_t launch_chunk_s(const ChunkArgs& a, int C, bool vec) {
+  dim3 grid(static_cast<unsigned>(a.B * a.D)), block(T);
+  const IO* x1 = static_cast<const IO*>(a.x1);
+  const IO* x2 = static_cast<const IO*>(a.x2);
+  const IO* v = static_cast<const IO*>(a.v);
+  IO* y = static_cast<IO*>(a.y);
+  if (vec)
+    chunk_fft_kernel<S, T, IO, true><<<grid, block, 0, a.stream>>>(
+        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L, C);
+  else
+    chunk_fft_kernel<S, T, IO, false><<<grid, block, 0, a.stream>>>(
+        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L, C);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_chunk_io(const ChunkArgs& a, int S, int C, bool vec) {
+  switch (S) {
+    case 256: return launch_chunk_s<256, 64, IO>(a, C, vec);
+    case 512: return launch_chunk_s<512, 64, IO>(a, C, vec);
+    case 1024: return launch_chunk_s<1024, 64, IO>(a, C, vec);
+    case 2048: return launch_chunk_s<2048, 128, IO>(a, C, vec);
+    case 4096: return launch_chunk_s<4096, 256, IO>(a, C, vec);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_chunk_fft(const ChunkArgs& a) {
+  const int C = a.C < a.L ? a.C : a.L;     // a chunk longer than the sequence is one chunk
+  const int S = chunk_fft_S(C);
+  if (S == 0 || a.N > CHUNK_MAXN) return hipErrorInvalidValue;
+  const size_t esz = a.bf16 ? 2 : 4;
+  const bool vec = (a.L % 2 == 0) && (C % 2 == 0) && aligned_all(2 * esz, a.x1, a.x2, a.v, a.y);
+  return a.bf16 ? launch_chunk_io<bf16_t>(a, S, C, vec) : launch_chunk_io<float>(a, S, C, vec);
+}
+
+}  // namespace hyena

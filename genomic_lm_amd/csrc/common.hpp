@@ -1,0 +1,94 @@
+// common.hpp -- element formats, complex arithmetic and twiddles shared by the
+// gfx950 kernels of libhyena.  Device code only; no host state.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hyena {
+
+typedef uint16_t bf16_t;   // bfloat16 bit pattern as stored in memory
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN, overflow
+// goes to +-inf as IEEE rounding says.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// ------------------------------------------------------------------ I/O
+// Element access for the two activation formats.  Loads return fp32, stores
+// round once.
+template <typename T> struct Io;
+
+template <> struct Io<float> {
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+  // two consecutive elements [i, i+1]; requires 8-byte alignment of p + i
+  static __device__ __forceinline__ float2 ld2(const float* p, int64_t i) {
+    return *reinterpret_cast<const float2*>(p + i);
+  }
+  static __device__ __forceinline__ void st2(float* p, int64_t i, float2 x) {
+    *reinterpret_cast<float2*>(p + i) = x;
+  }
+};
+
+template <> struct Io<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+  // requires 4-byte alignment of p + i
+  static __device__ __forceinline__ float2 ld2(const bf16_t* p, int64_t i) {
+    uint32_t w = *reinterpret_cast<const uint32_t*>(p + i);
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+  }
+  static __device__ __forceinline__ void st2(bf16_t* p, int64_t i, float2 x) {
+    uint32_t w = static_cast<uint32_t>(f32_to_bf16(x.x)) |
+                 (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
+    *reinterpret_cast<uint32_t*>(p + i) = w;
+  }
+};
+
+// Elements [i, i+1] of a row of length L, zero beyond the end.  VEC selects
+// the paired access, valid when the row start is aligned to two elements.
+template <typename T, bool VEC>
+__device__ __forceinline__ float2 ld_pair(const T* row, int64_t i, int64_t L) {
+  if (VEC && i + 1 < L) return Io<T>::ld2(row, i);
+  float a = (i < L) ? Io<T>::ld(row, i) : 0.0f;
+  float b = (i + 1 < L) ? Io<T>::ld(row, i + 1) : 0.0f;
+  return make_float2(a, b);
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void st_pair(T* row, int64_t i, int64_t L, float2 x) {
+  if (VEC && i + 1 < L) { Io<T>::st2(row, i, x); return; }
+  if (i < L) Io<T>::st(row, i, x.x);
+  if (i + 1 < L) Io<T>::st(row, i + 1, x.y);
+}
+
+// ------------------------------------------------------------------ complex
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+// multiply by -i and +i
+__device__ __forceinline__ float2 cmul_mi(float2 a) { return make_float2(a.y, -a.x); }
+__device__ __forceinline__ float2 cmul_pi(float2 a) { return make_float2(-a.y, a.x); }
+
+// exp(-2*pi*i * num / 2^lg), num >= 0.  The angle in half-turns, -num/2^(lg-1),
+// is exact in fp32 for num < 2^24, and sincospi keeps the result to a few ulp.
+__device__ __forceinline__ float2 twiddle(int num, int lg) {
+  float x = -ldexpf(static_cast<float>(num), 1 - lg);
+  float s, c;
+  sincospif(x, &s, &c);
+  return make_float2(c, s);
+}
+
+}  // namespace hyena

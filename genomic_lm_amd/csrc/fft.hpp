@@ -1,0 +1,191 @@
+// fft.hpp -- Stockham radix-P complex FFT for one workgroup, gfx950.
+//
+// A size-S transform is held by T threads, P = S / T points each, in
+// "strided natural" order: register i of thread t is element t + T*i.  Each
+// Stockham pass does P/R radix-R butterflies per thread entirely in
+// registers; between passes the data is exchanged through LDS (one write, one
+// read, two barriers).  Input and output are both in strided natural order,
+// so the caller loads from and stores to global memory coalesced without any
+// extra reordering pass.  The butterflies are radix 16 where the size allows
+// (the last pass takes the remaining factor), which keeps the number of LDS
+// round trips at ceil(log_P S) - 1.
+//
+// The pass structure is the auto-sorting Stockham formulation: pass with span
+// Ns and radix R reads x[j + r*S/R], multiplies by exp(-2*pi*i*r*(j mod Ns)/(Ns*R))
+// and writes the length-R DFT to y[(j/Ns)*Ns*R + (j mod Ns) + r*Ns].
+//
+// LDS rows are padded by one complex every 32 (lds_pad), which keeps the
+// 8-byte accesses of every pass within a few percent of conflict-free.
+#pragma once
+
+#include "common.hpp"
+
+namespace hyena {
+
+__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
+__host__ __device__ constexpr int lds_padded_size(int S) { return S + (S >> 5); }
+
+// ------------------------------------------------------------- small DFTs
+// Forward DFT (omega = exp(-2*pi*i/R)), natural order in and out.
+template <int R> struct Dft;
+
+template <> struct Dft<2> {
+  static __device__ __forceinline__ void run(float2* v) {
+    float2 a = v[0], b = v[1];
+    v[0] = cadd(a, b);
+    v[1] = csub(a, b);
+  }
+};
+
+template <> struct Dft<4> {
+  static __device__ __forceinline__ void run(float2* v) {
+    float2 a0 = cadd(v[0], v[2]), a1 = csub(v[0], v[2]);
+    float2 a2 = cadd(v[1], v[3]), a3 = cmul_mi(csub(v[1], v[3]));
+    v[0] = cadd(a0, a2);
+    v[2] = csub(a0, a2);
+    v[1] = cadd(a1, a3);
+    v[3] = csub(a1, a3);
+  }
+};
+
+template <> struct Dft<8> {
+  static __device__ __forceinline__ void run(float2* v) {
+    const float r = 0.70710678118654752f;
+    float2 e[4] = {v[0], v[2], v[4], v[6]};
+    float2 o[4] = {v[1], v[3], v[5], v[7]};
+    Dft<4>::run(e);
+    Dft<4>::run(o);
+    o[1] = make_float2((o[1].x + o[1].y) * r, (o[1].y - o[1].x) * r);   // * exp(-i pi/4)
+    o[2] = cmul_mi(o[2]);                                                // * exp(-i pi/2)
+    o[3] = make_float2((o[3].y - o[3].x) * r, -(o[3].x + o[3].y) * r);  // * exp(-3i pi/4)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = cadd(e[k], o[k]);
+      v[k + 4] = csub(e[k], o[k]);
+    }
+  }
+};
+
+template <> struct Dft<16> {
+  static __device__ __forceinline__ void run(float2* v) {
+    const float c1 = 0.92387953251128674f, s1 = 0.38268343236508977f;
+    const float r = 0.70710678118654752f;
+    float2 e[8], o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      e[k] = v[2 * k];
+      o[k] = v[2 * k + 1];
+    }
+    Dft<8>::run(e);
+    Dft<8>::run(o);
+    // o[k] *= exp(-i pi k / 8)
+    o[1] = cmul(o[1], make_float2(c1, -s1));
+    o[2] = make_float2((o[2].x + o[2].y) * r, (o[2].y - o[2].x) * r);
+    o[3] = cmul(o[3], make_float2(s1, -c1));
+    o[4] = cmul_mi(o[4]);
+    o[5] = cmul(o[5], make_float2(-s1, -c1));
+    o[6] = make_float2((o[6].y - o[6].x) * r, -(o[6].x + o[6].y) * r);
+    o[7] = cmul(o[7], make_float2(-c1, -s1));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = cadd(e[k], o[k]);
+      v[k + 8] = csub(e[k], o[k]);
+    }
+  }
+};
+
+__host__ __device__ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// ------------------------------------------------------------- passes
+template <int S, int T, int NS>
+struct PassRadix {
+  static constexpr int P = S / T;
+  static constexpr int value = (S / NS >= P) ? P : S / NS;
+};
+
+template <int S, int T, int R, int NS>
+__device__ __forceinline__ void pass_compute(float2 (&reg)[S / T], int t) {
+  constexpr int P = S / T;
+  constexpr int NB = P / R;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float2 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = reg[b + r * NB];
+    if constexpr (NS > 1) {
+      const int j = t + T * b;
+      const int k = j & (NS - 1);
+      const float2 w = twiddle(k, ilog2(NS * R));
+      float2 wr = w;
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        v[r] = cmul(v[r], wr);
+        if (r + 1 < R) wr = cmul(wr, w);
+      }
+    }
+    Dft<R>::run(v);
+#pragma unroll
+    for (int r = 0; r < R; ++r) reg[b + r * NB] = v[r];
+  }
+}
+
+template <int S, int T, int R, int NS>
+__device__ __forceinline__ void pass_store(const float2 (&reg)[S / T], float2* lds, int t) {
+  constexpr int P = S / T;
+  constexpr int NB = P / R;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = t + T * b;
+    const int base = (j / NS) * NS * R + (j & (NS - 1));
+#pragma unroll
+    for (int r = 0; r < R; ++r) lds[lds_pad(base + r * NS)] = reg[b + r * NB];
+  }
+}
+
+template <int S, int T, int R>
+__device__ __forceinline__ void pass_load(float2 (&reg)[S / T], const float2* lds, int t) {
+  constexpr int P = S / T;
+  constexpr int NB = P / R;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) reg[b + r * NB] = lds[lds_pad(t + T * b + r * (S / R))];
+  }
+}
+
+template <int S, int T, int NS>
+__device__ __forceinline__ void fft_from(float2 (&reg)[S / T], float2* lds, int t) {
+  constexpr int R = PassRadix<S, T, NS>::value;
+  pass_compute<S, T, R, NS>(reg, t);
+  if constexpr (NS * R < S) {
+    __syncthreads();                    // earlier readers of lds are done
+    pass_store<S, T, R, NS>(reg, lds, t);
+    __syncthreads();
+    constexpr int R2 = PassRadix<S, T, NS * R>::value;
+    pass_load<S, T, R2>(reg, lds, t);
+    fft_from<S, T, NS * R>(reg, lds, t);
+  }
+}
+
+// Forward transform X[k] = sum_m x[m] exp(-2*pi*i*m*k/S), in place in
+// registers (strided natural order), using lds (lds_padded_size(S) complex) as
+// exchange space.  Every thread of the workgroup must call it.  On return lds
+// may still be read by other threads: synchronise before writing to it.
+template <int S, int T>
+__device__ __forceinline__ void fft_forward(float2 (&reg)[S / T], float2* lds, int t) {
+  static_assert(S % T == 0 && (S & (S - 1)) == 0, "power-of-two size, T | S");
+  static_assert(S / T == 4 || S / T == 8 || S / T == 16, "4, 8 or 16 points per thread");
+  fft_from<S, T, 1>(reg, lds, t);
+}
+
+// Unnormalised inverse: x[m] = sum_k X[k] exp(+2*pi*i*m*k/S) = conj(F(conj X)).
+template <int S, int T>
+__device__ __forceinline__ void fft_inverse(float2 (&reg)[S / T], float2* lds, int t) {
+#pragma unroll
+  for (int i = 0; i < S / T; ++i) reg[i].y = -reg[i].y;
+  fft_forward<S, T>(reg, lds, t);
+#pragma unroll
+  for (int i = 0; i < S / T; ++i) reg[i].y = -reg[i].y;
+}
+
+}  // namespace hyena

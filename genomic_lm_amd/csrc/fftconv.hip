@@ -1,0 +1,226 @@
+// fftconv.hip -- single-pass modal Hyena operator, one workgroup per (b, c) row.
+//
+// y = x2 * (h causal-conv u) + skip * u, u = x1 * v, h[t] = sum_n R_n exp(lam_n t),
+// the convolution taken as a zero-padded FFT product of length Nfft = 4S >= 2L
+// ('modal-form IIR via FFT': Evo2-7B-262K model card, Implementation Notes,
+// 'Block dispatch'; 'FFT-based long convolution': Evo1-1.5-7B-8K model card,
+// Implementation Notes, 'Hyena engine').
+//
+// Layout of the transform (all fp32, all on chip):
+//  * the real length-Nfft signals u and h are packed as complex c[m] =
+//    x[2m] + i x[2m+1], m < M = 2S; since x is zero from L <= 2S on, c is zero
+//    on its upper half;
+//  * the first decimation-in-frequency stage of the size-M DFT therefore
+//    splits into two size-S DFTs with no butterflies: C[2k+q] is the DFT of
+//    c[m] * exp(-2*pi*i*q*m/M), q = 0, 1 (the "parity halves");
+//  * the real spectrum U[K], K = 2k+q, comes from C[K] and C[M-K], and M-K
+//    has the same parity, so each parity half is processed on its own;
+//  * Z = U * H, repacked for the inverse real transform, inverse size-S DFT
+//    per parity, and the two halves are recombined with one twiddle:
+//    c_z[m] = (B_0[m] + exp(2*pi*i*m/M) B_1[m]) / M.
+// Only one size-S transform lives in LDS at a time, so S = 16384 (L = 32768)
+// still fits in one CU's 160 KB of LDS.  h is generated per thread with short
+// exp ladders (<= 16 multiplications from an exact anchor) and never touches
+// memory.
+#include "common.hpp"
+#include "fft.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+// U[K] = (C[K] + conj C[M-K]) / 2 - i w (C[K] - conj C[M-K]) / 2, w = exp(-2 pi i K / Nfft)
+__device__ __forceinline__ float2 real_spectrum(float2 ck, float2 cm, float2 w) {
+  float2 a = make_float2(ck.x + cm.x, ck.y - cm.y);
+  float2 b = make_float2(ck.x - cm.x, ck.y + cm.y);
+  float2 r = cadd(a, cmul_mi(cmul(w, b)));
+  return cscale(r, 0.5f);
+}
+
+// C_z[K] = ((Z[K] + conj Z[M-K]) + i conj(w) (Z[K] - conj Z[M-K])) / 2
+__device__ __forceinline__ float2 inverse_pack(float2 zk, float2 zm, float2 w) {
+  float2 a = make_float2(zk.x + zm.x, zk.y - zm.y);
+  float2 b = make_float2(zk.x - zm.x, zk.y + zm.y);
+  float2 r = cadd(a, cmul_pi(cmul(cconj(w), b)));
+  return cscale(r, 0.5f);
+}
+
+// a[i] = (h[2m], h[2m+1]) for m = t + T*i, zero at and beyond L.
+template <int P, int T>
+__device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, const float* res,
+                                            int N, int t, int L) {
+#pragma unroll
+  for (int i = 0; i < P; ++i) a[i] = make_float2(0.0f, 0.0f);
+  for (int n = 0; n < N; ++n) {
+    const float l = lam[n];
+    const float p = expf(l);
+    const float step = expf(l * static_cast<float>(2 * T));
+    float e = res[n] * expf(l * static_cast<float>(2 * t));
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      a[i].x += e;
+      a[i].y = fmaf(e, p, a[i].y);
+      e *= step;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int m2 = 2 * (t + T * i);
+    if (m2 >= L) a[i].x = 0.0f;
+    if (m2 + 1 >= L) a[i].y = 0.0f;
+  }
+}
+
+template <int S, int T, typename IO, bool VEC>
+__global__ __launch_bounds__(T) void fftconv_kernel(
+    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const float* __restrict__ lam, const float* __restrict__ res, int N,
+    const float* __restrict__ skip, IO* __restrict__ y, int D, int L) {
+  constexpr int P = S / T;
+  constexpr int M = 2 * S;
+  constexpr int LG_M = ilog2(M);
+  constexpr int LG_N = LG_M + 1;
+  __shared__ float2 lds[lds_padded_size(S)];
+
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int c = static_cast<int>(row % D);
+  const IO* x1r = x1 + row * L;
+  const IO* x2r = x2 + row * L;
+  const IO* vr = v + row * L;
+  IO* yr = y + row * L;
+  const float* lamc = lam + static_cast<int64_t>(c) * N;
+  const float* resc = res + static_cast<int64_t>(c) * N;
+
+  float2 b0[P];           // inverse transform of the even half, kept for the recombination
+  float zm_nyq = 0.0f;    // Z[M] (real), only used by thread 0
+
+#pragma unroll 1
+  for (int q = 0; q < 2; ++q) {
+    float2 a[P];
+    // ---- u = x1 * v, packed in pairs, parity pre-twiddle
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int m = t + T * i;
+      const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+      const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+      a[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
+      if (q) a[i] = cmul(a[i], twiddle(m, LG_M));
+    }
+    fft_forward<S, T>(a, lds, t);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
+    __syncthreads();
+    float2 z[P];
+    float um_nyq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = t + T * i;
+      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+      z[i] = real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+    }
+    if (q == 0 && t == 0) um_nyq = a[0].x - a[0].y;
+
+    // ---- h, generated on chip, same packing
+    modal_pairs<P, T>(a, lamc, resc, N, t, L);
+    if (q) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) a[i] = cmul(a[i], twiddle(t + T * i, LG_M));
+    }
+    fft_forward<S, T>(a, lds, t);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = t + T * i;
+      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+      z[i] = cmul(z[i], real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)));
+    }
+    if (q == 0 && t == 0) zm_nyq = um_nyq * (a[0].x - a[0].y);
+
+    // ---- repack Z for the inverse real transform
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = z[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = t + T * i;
+      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+      float2 zmir = lds[lds_pad(kk)];
+      if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
+      a[i] = inverse_pack(z[i], zmir, twiddle(2 * k + q, LG_N));
+    }
+    fft_inverse<S, T>(a, lds, t);
+
+    if (q == 0) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) b0[i] = a[i];
+    } else {
+      // ---- recombine, gate, store
+      const float sk = skip ? skip[c] : 0.0f;
+      const float inv_m = 1.0f / static_cast<float>(M);
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int m = t + T * i;
+        if (2 * m >= L) continue;
+        const float2 zz = cscale(cadd(b0[i], cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
+        const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+        const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+        const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
+        const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
+                                       fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
+        st_pair<IO, VEC>(yr, 2 * m, L, out);
+      }
+    }
+  }
+}
+
+template <int S, int T, typename IO>
+static hipError_t launch_s(const FftconvArgs& a, bool vec) {
+  dim3 grid(static_cast<unsigned>(a.B * a.D)), block(T);
+  const IO* x1 = static_cast<const IO*>(a.x1);
+  const IO* x2 = static_cast<const IO*>(a.x2);
+  const IO* v = static_cast<const IO*>(a.v);
+  IO* y = static_cast<IO*>(a.y);
+  if (vec)
+    fftconv_kernel<S, T, IO, true><<<grid, block, 0, a.stream>>>(
+        x1, x2, v, a.lam, a.res, a.N, a.skip, y, a.D, a.L);
+  else
+    fftconv_kernel<S, T, IO, false><<<grid, block, 0, a.stream>>>(
+        x1, x2, v, a.lam, a.res, a.N, a.skip, y, a.D, a.L);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_io(const FftconvArgs& a, int S, bool vec) {
+  switch (S) {
+    case 256: return launch_s<256, 64, IO>(a, vec);
+    case 512: return launch_s<512, 64, IO>(a, vec);
+    case 1024: return launch_s<1024, 64, IO>(a, vec);
+    case 2048: return launch_s<2048, 128, IO>(a, vec);
+    case 4096: return launch_s<4096, 256, IO>(a, vec);
+    case 8192: return launch_s<8192, 512, IO>(a, vec);
+    case 16384: return launch_s<16384, 1024, IO>(a, vec);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int fftconv_onchip_S(int64_t L) {
+  int64_t half = (L + 1) / 2;
+  int64_t S = 256;
+  while (S < half) S <<= 1;
+  return S <= 16384 ? static_cast<int>(S) : 0;
+}
+
+hipError_t launch_fftconv_onchip(const FftconvArgs& a) {
+  const int S = fftconv_onchip_S(a.L);
+  if (S == 0) return hipErrorInvalidValue;
+  const size_t esz = a.bf16 ? 2 : 4;
+  const bool vec = (a.L % 2 == 0) && aligned_all(2 * esz, a.x1, a.x2, a.v, a.y);
+  return a.bf16 ? launch_io<bf16_t>(a, S, vec) : launch_io<float>(a, S, vec);
+}
+
+}  // namespace hyena

@@ -1,0 +1,176 @@
+// hyena_abi.cpp -- the extern "C" entry points declared in include/hyena.h.
+//
+// Host only: every argument is validated before anything is launched, then the
+// call is routed to a kernel launcher (launch.hpp).  Nothing here allocates,
+// prints, throws or synchronises.
+#include "hyena.h"
+
+#include <hip/hip_runtime.h>
+
+#include <limits>
+
+#include "launch.hpp"
+
+namespace {
+
+using hyena::aligned_to;
+
+constexpr int64_t kMaxInt = std::numeric_limits<int>::max();
+
+hyena_status_t from_hip(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH; }
+
+bool valid_io(hyena_dtype_t io) { return io == HYENA_F32 || io == HYENA_BF16; }
+size_t io_size(hyena_dtype_t io) { return io == HYENA_BF16 ? 2 : 4; }
+
+// Common checks of the activation arguments.  Returns HYENA_OK, or the error;
+// `empty` is set when there is no element to compute.
+hyena_status_t check_acts(const void* x1, const void* x2, const void* v, const void* y,
+                          int64_t B, int64_t D, int64_t L, hyena_dtype_t io, bool* empty) {
+  if (!valid_io(io)) return HYENA_ERR_INVALID_ARG;
+  if (B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
+  *empty = (B == 0 || D == 0 || L == 0);
+  if (B > kMaxInt || D > kMaxInt || L > kMaxInt || B * D > kMaxInt) return HYENA_ERR_UNSUPPORTED;
+  if (!*empty && B * D > std::numeric_limits<int64_t>::max() / L) return HYENA_ERR_UNSUPPORTED;
+  if (*empty) return HYENA_OK;
+  if (!x1 || !x2 || !v || !y) return HYENA_ERR_INVALID_ARG;
+  const size_t a = io_size(io);
+  if (!aligned_to(x1, a) || !aligned_to(x2, a) || !aligned_to(v, a) || !aligned_to(y, a))
+    return HYENA_ERR_INVALID_ARG;
+  return HYENA_OK;
+}
+
+hyena_status_t check_modal(const float* lam, const float* res, int64_t N, const float* skip) {
+  if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (!lam || !res) return HYENA_ERR_INVALID_ARG;
+  if (!aligned_to(lam, 4) || !aligned_to(res, 4) || (skip && !aligned_to(skip, 4)))
+    return HYENA_ERR_INVALID_ARG;
+  return HYENA_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hyena_abi_version(void) { return HYENA_ABI_VERSION; }
+
+const char* hyena_status_string(hyena_status_t status) {
+  switch (status) {
+    case HYENA_OK: return "HYENA_OK";
+    case HYENA_ERR_INVALID_ARG: return "HYENA_ERR_INVALID_ARG: null, negative, misaligned or out-of-range argument";
+    case HYENA_ERR_UNSUPPORTED: return "HYENA_ERR_UNSUPPORTED: shape beyond the limits of this build";
+    case HYENA_ERR_WORKSPACE: return "HYENA_ERR_WORKSPACE: workspace missing or too small";
+    case HYENA_ERR_LAUNCH: return "HYENA_ERR_LAUNCH: a HIP launch or runtime call failed";
+  }
+  return "HYENA_ERR_UNKNOWN";
+}
+
+hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
+                                  int64_t N, int64_t L, float* h, void* stream) {
+  if (D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
+  if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (D == 0 || L == 0) return HYENA_OK;
+  if (!log_poles || !residues || !h) return HYENA_ERR_INVALID_ARG;
+  if (!aligned_to(log_poles, 4) || !aligned_to(residues, 4) || !aligned_to(h, 4))
+    return HYENA_ERR_INVALID_ARG;
+  if (D > 65535 || L > kMaxInt || D * L > std::numeric_limits<int64_t>::max() / 4)
+    return HYENA_ERR_UNSUPPORTED;
+  return from_hip(hyena::launch_modal_filter(log_poles, residues, static_cast<int>(D),
+                                             static_cast<int>(N), static_cast<int>(L), h,
+                                             as_stream(stream)));
+}
+
+hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, const float* taps,
+                             int64_t K, const float* skip, void* y, int64_t B, int64_t D,
+                             int64_t L, hyena_dtype_t io, void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  if (st != HYENA_OK) return st;
+  if (K < 1) return HYENA_ERR_INVALID_ARG;
+  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
+  if (empty) return HYENA_OK;
+  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
+  if (B * D > 65535) return HYENA_ERR_UNSUPPORTED;   // grid.y
+  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+  return from_hip(hyena::launch_fir(a));
+}
+
+size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {
+  (void)N;
+  (void)io;
+  if (B <= 0 || D <= 0 || L <= 0) return 0;
+  if (hyena::fftconv_onchip_S(L) != 0) return 0;
+  if (next_pow2(2 * L) > HYENA_MAX_FFT_LEN) return 0;
+  return hyena::fftconv_large_workspace(B, D, L);
+}
+
+hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
+                                 const float* log_poles, const float* residues, int64_t N,
+                                 const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                                 hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  if (st != HYENA_OK) return st;
+  if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (!empty && next_pow2(2 * L) > HYENA_MAX_FFT_LEN) return HYENA_ERR_UNSUPPORTED;
+  if (empty) return HYENA_OK;
+  st = check_modal(log_poles, residues, N, skip);
+  if (st != HYENA_OK) return st;
+  hyena::FftconvArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, y,
+                       static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
+                       io == HYENA_BF16, workspace, ws_bytes, as_stream(stream)};
+  if (hyena::fftconv_onchip_S(L) != 0) return from_hip(hyena::launch_fftconv_onchip(a));
+  const size_t need = hyena::fftconv_large_workspace(B, D, L);
+  if (need == 0) return HYENA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < need || !aligned_to(workspace, 16)) return HYENA_ERR_WORKSPACE;
+  return from_hip(hyena::launch_fftconv_large(a));
+}
+
+hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
+                               const float* log_poles, const float* residues, int64_t N,
+                               const float* skip, const float* state_in, float* state_out,
+                               void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                               hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
+  if (algo != HYENA_CHUNK_AUTO && algo != HYENA_CHUNK_FFT && algo != HYENA_CHUNK_MFMA)
+    return HYENA_ERR_INVALID_ARG;
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  if (L == 0 && B >= 0 && D >= 0 && valid_io(io)) {
+    // no token: the state passes through unchanged
+    if (C < 1 || N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+    if (B == 0 || D == 0) return HYENA_OK;
+    if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
+      return HYENA_ERR_INVALID_ARG;
+    if (B * D > kMaxInt) return HYENA_ERR_UNSUPPORTED;
+    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N, as_stream(stream)));
+  }
+  if (st != HYENA_OK) return st;
+  if (C < 1) return HYENA_ERR_INVALID_ARG;
+  if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (empty) return HYENA_OK;
+  st = check_modal(log_poles, residues, N, skip);
+  if (st != HYENA_OK) return st;
+  if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
+    return HYENA_ERR_INVALID_ARG;
+  const int64_t Ceff = C < L ? C : L;
+  hyena_chunk_algo_t use = algo;
+  if (use == HYENA_CHUNK_AUTO) use = (N <= 16) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
+  if (use == HYENA_CHUNK_MFMA && N > 16) return HYENA_ERR_UNSUPPORTED;
+  if (use == HYENA_CHUNK_FFT && Ceff > HYENA_MAX_FFT_CHUNK) return HYENA_ERR_UNSUPPORTED;
+  hyena::ChunkArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
+                     state_out, y, static_cast<int>(B), static_cast<int>(D),
+                     static_cast<int>(L), static_cast<int>(Ceff), io == HYENA_BF16,
+                     as_stream(stream)};
+  return from_hip(use == HYENA_CHUNK_MFMA ? hyena::launch_chunk_mfma(a) : hyena::launch_chunk_fft(a));
+}
+
+}  // extern "C"

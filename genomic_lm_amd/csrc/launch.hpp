@@ -1,0 +1,85 @@
+// launch.hpp -- internal host-side interface between the C ABI (hyena_abi.cpp)
+// and the kernel launchers in the .hip files.  Arguments arrive here already
+// validated; launchers only pick a kernel variant and launch it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hyena {
+
+inline bool aligned_to(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+template <typename... Ps>
+inline bool aligned_all(size_t a, Ps... ps) {
+  return (aligned_to(ps, a) && ...);
+}
+
+struct FftconvArgs {
+  const void* x1;
+  const void* x2;
+  const void* v;
+  const float* lam;
+  const float* res;
+  int N;
+  const float* skip;
+  void* y;
+  int B, D, L;
+  bool bf16;
+  void* workspace;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+struct FirArgs {
+  const void* x1;
+  const void* x2;
+  const void* v;
+  const float* taps;
+  int K;
+  const float* skip;
+  void* y;
+  int B, D, L;
+  bool bf16;
+  hipStream_t stream;
+};
+
+struct ChunkArgs {
+  const void* x1;
+  const void* x2;
+  const void* v;
+  const float* lam;
+  const float* res;
+  int N;
+  const float* skip;
+  const float* state_in;
+  float* state_out;
+  void* y;
+  int B, D, L, C;
+  bool bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
+                               float* h, hipStream_t stream);
+
+hipError_t launch_fir(const FirArgs& a);
+
+// Sub-transform size S of the on-chip single-pass kernel for length L, or 0
+// when L is too long for it (L > 32768).
+int fftconv_onchip_S(int64_t L);
+hipError_t launch_fftconv_onchip(const FftconvArgs& a);
+
+// Multi-kernel single pass for L > 32768 through a caller workspace.
+size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L);
+hipError_t launch_fftconv_large(const FftconvArgs& a);
+
+hipError_t launch_chunk_fft(const ChunkArgs& a);
+hipError_t launch_chunk_mfma(const ChunkArgs& a);
+
+// state_out <- state_in (or 0 when state_in is null), count floats.
+hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t count,
+                             hipStream_t stream);
+
+}  // namespace hyena

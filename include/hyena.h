@@ -1,0 +1,184 @@
+/*
+ * hyena.h -- C ABI of the MI355X (gfx950) Hyena operator library, libhyena.so.
+ *
+ * The Hyena operator is the data-parallel core of a StripedHyena 2 (Evo 2)
+ * mixer.  Per channel c it computes
+ *
+ *     u      = x1 * v                                   (input gate)
+ *     h[t]   = sum_n R[c,n] * exp(lam[c,n] * t)          (modal long filter)
+ *     z[t]   = sum_{k<=t} h[t-k] * u[k]                  (causal convolution)
+ *     y      = x2 * z + skip[c] * u                      (output gate + skip)
+ *
+ * Sources on the pages:
+ *  - three streams from the 3H input projection and a gated output that feeds
+ *    out_proj: evo2_flash README, layer_names table ('blocks.N.projections',
+ *    'blocks.N.filter');
+ *  - hcl blocks are a modal-form IIR filter evaluated with an FFT, hcm / hcs
+ *    blocks are FIR filters of inner length 128 / 7: Evo2-7B-262K model card,
+ *    Implementation Notes, 'Block dispatch';
+ *  - log_poles / residues are kept in fp32, everything else is bf16:
+ *    Evo2-7B-262K model card, Usage, 'Note on dtype' and Implementation Notes;
+ *  - bf16 is mandatory because the residual stream reaches ~1e12: evo2_flash
+ *    README, Requirements and install;
+ *  - the per-layer inference cache holds the FIR window and the IIR modal
+ *    state: Evo2-7B-262K model card, Implementation Notes, 'Custom cache';
+ *    Evo1-1.5-7B-8K model card, Implementation Notes, 'Cache subclass';
+ *  - chunked prefill must give the single-pass result, whatever the chunk
+ *    size: TurboQuant-Bio int4 Evo 2 checkpoints, 'Important: a correctness
+ *    fix comes with this' and 'Chunk size'.
+ *
+ * Conventions shared by every entry point
+ *  - Activations x1, x2, v, y are channel-major (B, D, L) contiguous arrays
+ *    (time is the fastest axis) of element type `io`: HYENA_F32 (float) or
+ *    HYENA_BF16 (bfloat16 bit patterns, 2 bytes).  Arithmetic is fp32; y is
+ *    rounded once, to nearest even.
+ *  - Parameters are fp32 and shared across the batch: log_poles and residues
+ *    (D, N), skip (D) (NULL means 0), taps (D, K) with taps[c*K + k] the
+ *    coefficient of lag k (PyTorch conv1d weights are the reverse order).
+ *  - The modal state is fp32 (B, D, N): state[b, c, n] = s_n(t) =
+ *    sum_{k<=t} p_n^(t-k) u[k], p_n = exp(lam[c,n]), after the last token.
+ *  - Every pointer argument is a DEVICE pointer of the current HIP device.
+ *    The caller allocates and frees all memory.  Inputs are read only; outputs
+ *    must not overlap inputs (except state_out == state_in, which is allowed).
+ *    Base pointers must be aligned to their element size; 16-byte alignment
+ *    enables the vectorised paths.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call is asynchronous on that stream and never synchronises the
+ *    host; device faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any launch.  Nothing is
+ *    printed and nothing throws across the ABI.  Sizes of 0 are accepted and
+ *    do nothing (except hyena_chunk_fwd with L = 0, which copies state_in to
+ *    state_out, or zeroes it when state_in is NULL).  Non-finite inputs
+ *    propagate to the outputs; they are not an error.
+ *  - The library keeps no global or per-device state and allocates nothing;
+ *    all entry points are reentrant and may be called from several host
+ *    threads.
+ */
+#ifndef HYENA_H_
+#define HYENA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYENA_ABI_VERSION 1
+
+typedef enum hyena_status {
+    HYENA_OK = 0,
+    HYENA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad enum, misalignment, N out of [1, 64] */
+    HYENA_ERR_UNSUPPORTED = 2,   /* valid but beyond what this build implements (limits below) */
+    HYENA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than hyena_fftconv_workspace_size() */
+    HYENA_ERR_LAUNCH = 4,        /* a HIP launch or runtime call failed (hipGetLastError) */
+} hyena_status_t;
+
+typedef enum hyena_dtype {
+    HYENA_F32 = 0,
+    HYENA_BF16 = 1,
+} hyena_dtype_t;
+
+/* Algorithm for hyena_chunk_fwd.  Both compute the same function. */
+typedef enum hyena_chunk_algo {
+    HYENA_CHUNK_AUTO = 0,        /* the faster of the two for the shape */
+    HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms */
+    HYENA_CHUNK_MFMA = 2,        /* blocked Toeplitz on bf16x3 MFMA + modal state scan */
+} hyena_chunk_algo_t;
+
+/* Limits of this build. */
+#define HYENA_MAX_MODES 64               /* N */
+#define HYENA_MAX_FIR_TAPS 1024          /* K */
+#define HYENA_MAX_FFT_LEN (1 << 20)      /* single-pass FFT length, next pow2 >= 2L */
+#define HYENA_MAX_FFT_CHUNK 8192         /* C for HYENA_CHUNK_FFT (FFT length 2C <= 16384) */
+
+int hyena_abi_version(void);
+const char* hyena_status_string(hyena_status_t status);
+
+/*
+ * hyena_modal_filter -- materialise the modal long filter.
+ *   h[c, t] = sum_{n<N} residues[c, n] * exp(log_poles[c, n] * t),  0 <= t < L,
+ * evaluated in fp32 with exp taken directly (no long power recurrence).
+ * The modal form and its fp32 parameters: Evo2-7B-262K model card,
+ * Architecture ('Training dtype') and Implementation Notes ('log_poles /
+ * residues kept in fp32'); Evo1-1.5-7B-8K model card, Architecture.
+ *   log_poles, residues : (D, N) fp32, device
+ *   h                   : (D, L) fp32, device, written
+ * The fused entry points below generate h on chip and never call this; it
+ * exists as a building block and for tests.
+ */
+hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues,
+                                  int64_t D, int64_t N, int64_t L,
+                                  float* h, void* stream);
+
+/*
+ * hyena_fir_fwd -- gated explicit-FIR Hyena operator (hcs: K = 7, hcm: K = 128).
+ *   z[t] = sum_{k<K, k<=t} taps[c, k] * u[t-k],   u = x1 * v,
+ *   y    = x2 * z + skip[c] * u.
+ * Evo2-7B-262K model card, Implementation Notes, 'Block dispatch' (FIR
+ * cascades of inner length 128 and 7); only the single FIR is implemented.
+ *   x1, x2, v : (B, D, L) `io`, device;  y : (B, D, L) `io`, device, written
+ *   taps      : (D, K) fp32, device, 1 <= K <= HYENA_MAX_FIR_TAPS
+ *   skip      : (D) fp32, device, or NULL
+ */
+hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
+                             const float* taps, int64_t K, const float* skip,
+                             void* y, int64_t B, int64_t D, int64_t L,
+                             hyena_dtype_t io, void* stream);
+
+/*
+ * hyena_fftconv_fwd -- single-pass modal Hyena operator.
+ * The causal convolution is a zero-padded FFT product of length
+ * Nfft = next power of two >= 2L ('modal-form IIR via FFT': Evo2-7B-262K
+ * model card, Implementation Notes, 'Block dispatch'; 'FFT-based long
+ * convolution': Evo1-1.5-7B-8K model card, Implementation Notes, 'Hyena
+ * engine').  h is generated on chip; it never touches memory.
+ *   x1, x2, v : (B, D, L) `io`;  y : (B, D, L) `io`, written
+ *   log_poles, residues : (D, N) fp32, 1 <= N <= HYENA_MAX_MODES
+ *   skip : (D) fp32 or NULL
+ *   workspace : device buffer of at least hyena_fftconv_workspace_size(...)
+ *               bytes (may be NULL when that size is 0), contents scratch.
+ * Nfft > HYENA_MAX_FFT_LEN -> HYENA_ERR_UNSUPPORTED.
+ */
+hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
+                                 const float* log_poles, const float* residues,
+                                 int64_t N, const float* skip, void* y,
+                                 int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes hyena_fftconv_fwd needs for this shape (0 when the FFT runs on chip). */
+size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                    hyena_dtype_t io);
+
+/*
+ * hyena_chunk_fwd -- chunked prefill with the modal state carried in and out.
+ * The sequence is processed in chunks [t0, t0 + C') of C tokens (the last
+ * may be shorter); within a chunk
+ *   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + sum_n R_n p_n^(t-t0+1) s_n,
+ * and after it  s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j].
+ * The output equals the single-pass output of the whole sequence started from
+ * the state `state_in` (TurboQuant-Bio int4 Evo 2 checkpoints, 'Important: a
+ * correctness fix comes with this' and 'Chunk size'); the IIR modal state is
+ * the layer's inference cache (Evo2-7B-262K model card, Implementation Notes,
+ * 'Custom cache'; Evo1-1.5-7B-8K model card, Implementation Notes, 'Cache
+ * subclass').  All chunks of the call run in ONE launch; L = C gives one
+ * chunk per call and L = C = 1 is a decode step.
+ *   x1, x2, v : (B, D, L) `io`;  y : (B, D, L) `io`, written
+ *   log_poles, residues : (D, N) fp32;  skip : (D) fp32 or NULL
+ *   state_in  : (B, D, N) fp32 or NULL (zero state)
+ *   state_out : (B, D, N) fp32, written (may equal state_in)
+ *   C >= 1; algo HYENA_CHUNK_FFT needs C <= HYENA_MAX_FFT_CHUNK.
+ */
+hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
+                               const float* log_poles, const float* residues,
+                               int64_t N, const float* skip,
+                               const float* state_in, float* state_out,
+                               void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                               hyena_dtype_t io, hyena_chunk_algo_t algo,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_H_ */

@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+Only calls whose arguments fail validation are made here; those return before
+any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import genomic_lm_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyena.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(G.LIB_PATH):
+        from genomic_lm_amd import build
+        build.build()
+    yield
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(hyena_[a-z0-9_]+)\s*\(", text))
+
+
+def test_header_declares_the_binding_set():
+    assert declared_functions() == set(G.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = declared_functions() - syms
+    assert not missing, missing
+    lib = G.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings():
+    assert G.abi_version() == 1
+    for st in range(5):
+        assert G.status_string(st).startswith("HYENA_")
+    assert "UNKNOWN" in G.status_string(99)
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)            # never dereferenced: every call below fails validation first
+MISALIGNED = P(0x10001)
+
+
+def test_modal_filter_validation():
+    f = G.lib().hyena_modal_filter
+    assert f(None, None, 4, 16, 8, None, None) == G.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, -1, 16, 8, FAKE, None) == G.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 4, 0, 8, FAKE, None) == G.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 4, 65, 8, FAKE, None) == G.ERR_INVALID_ARG
+    assert f(FAKE, MISALIGNED, 4, 16, 8, FAKE, None) == G.ERR_INVALID_ARG
+    assert f(None, None, 0, 16, 8, None, None) == G.OK          # empty: nothing to do
+    assert f(None, None, 4, 16, 0, None, None) == G.OK
+
+
+def test_fir_validation():
+    f = G.lib().hyena_fir_fwd
+    good = (FAKE, FAKE, FAKE, FAKE, 7, None, FAKE, 1, 4, 64, G.BF16, None)
+    bad = list(good); bad[0] = None
+    assert f(*bad) == G.ERR_INVALID_ARG
+    bad = list(good); bad[4] = 0
+    assert f(*bad) == G.ERR_INVALID_ARG
+    bad = list(good); bad[4] = 1025
+    assert f(*bad) == G.ERR_UNSUPPORTED
+    bad = list(good); bad[10] = 7
+    assert f(*bad) == G.ERR_INVALID_ARG
+    bad = list(good); bad[9] = -3
+    assert f(*bad) == G.ERR_INVALID_ARG
+    bad = list(good); bad[1] = MISALIGNED
+    assert f(*bad) == G.ERR_INVALID_ARG
+    bad = list(good); bad[3] = None
+    assert f(*bad) == G.ERR_INVALID_ARG
+    empty = list(good); empty[9] = 0; empty[0] = None
+    assert f(*empty) == G.OK
+
+
+def test_fftconv_validation():
+    f = G.lib().hyena_fftconv_fwd
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, FAKE, 1, 4, 1024, G.BF16, None, 0, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (3, None, G.ERR_INVALID_ARG),
+                           (5, 0, G.ERR_INVALID_ARG), (5, 65, G.ERR_INVALID_ARG),
+                           (10, -1, G.ERR_INVALID_ARG), (11, 2, G.ERR_INVALID_ARG),
+                           (10, 1 << 20, G.ERR_UNSUPPORTED)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    assert G.lib().hyena_fftconv_workspace_size(1, 4, 1024, 16, G.BF16) == 0
+    assert G.lib().hyena_fftconv_workspace_size(0, 4, 1024, 16, G.BF16) == 0
+
+
+def test_chunk_validation():
+    f = G.lib().hyena_chunk_fwd
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, None, FAKE, FAKE, 1, 4, 1024, 1024,
+            G.BF16, 0, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (8, None, G.ERR_INVALID_ARG),
+                           (13, 0, G.ERR_INVALID_ARG), (15, 3, G.ERR_INVALID_ARG),
+                           (5, 65, G.ERR_INVALID_ARG), (8, MISALIGNED, G.ERR_INVALID_ARG)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[5] = 32; a[15] = G.ALGOS["mfma"]        # MFMA kernel holds <= 16 modes
+    assert f(*a) == G.ERR_UNSUPPORTED
+    a = list(good); a[13] = 16384; a[15] = G.ALGOS["fft"]; a[12] = 16384
+    assert f(*a) == G.ERR_UNSUPPORTED                          # FFT chunk > 8192
+    a = list(good); a[10] = 0                                  # empty batch
+    assert f(*a) == G.OK
+
+
+def test_binding_rejects_cpu_tensors_before_any_call():
+    import torch
+    x = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        G.fir_fwd(x, x, x, torch.zeros(2, 7))
+    with pytest.raises(ValueError):
+        G.chunk_fwd(x, x, x, torch.zeros(2, 16), torch.zeros(2, 16), 4)

@@ -1,0 +1,267 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Small cases cover every kernel variant (each FFT size, FIR tap counts, chunk
+sizes, ragged lengths, batch > 1, carried state); the full-size cases run the
+configurations the benchmark uses, in the same launch configuration, and
+compare sampled channels (all time steps) with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import genomic_lm_amd as G
+import oracle
+import workloads as W
+from tests.gpu_util import (DevWorkload, act_to_dev, gate, log, oracle_fir, oracle_modal,
+                            par_to_dev, sample_rows, state_gate, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()                                   # loud failure if the library is missing
+    yield
+
+
+def small(io, D=8, L=1024, B=1, seed_cfg=None, lam_lo=None):
+    name = seed_cfg or ("tiny" if io == "f32" else "7b_layer_set")
+    return W.make(name, B=B, D=D, L=L, lam_lo=lam_lo)
+
+
+# ------------------------------------------------------------------ filter
+@pytest.mark.parametrize("L", [1, 777, 8192])
+def test_modal_filter(L):
+    w = small("f32", D=16, L=L)
+    d = DevWorkload(w)
+    log(f"modal_filter D=16 L={L}")
+    h = to_f64(G.modal_filter(d.lam, d.res, L))
+    ref = oracle.modal_filter(w.log_poles, w.residues, L)
+    err = np.sqrt(np.sum((h - ref) ** 2, -1) / np.sum(ref ** 2, -1))
+    assert np.max(err) < 1e-5, err
+
+
+# ------------------------------------------------------------------ fftconv
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [1, 2, 7, 100, 512, 777, 1000, 1024, 2049, 4096, 8192, 16384, 32768])
+def test_fftconv_small(io, L):
+    B = 2 if L in (777, 4096) else 1
+    w = small(io, D=4, L=L, B=B)
+    d = DevWorkload(w)
+    log(f"fftconv io={io} B={B} D=4 L={L}")
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    ref, _ = oracle_modal(w)
+    gate(y, ref, io, label=f"fftconv L={L}")
+
+
+# ------------------------------------------------------------------ FIR
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("K,L", [(1, 100), (3, 1), (7, 2048), (7, 3001), (8, 4096), (9, 100),
+                                 (128, 2048), (128, 5000), (129, 300), (1024, 4096)])
+def test_fir_small(io, K, L):
+    w = small(io, D=4, L=L, B=2 if K == 7 else 1)
+    d = DevWorkload(w)
+    taps = W.random_taps(K, w.D, seed=K, bf16=(io == "bf16"))
+    log(f"fir io={io} K={K} L={L}")
+    y = G.fir_fwd(d.x1, d.x2, d.v, par_to_dev(taps), d.skip)
+    gate(y, oracle_fir(w, K, taps=taps), io, label=f"fir K={K} L={L}")
+
+
+# ------------------------------------------------------------------ chunked
+CHUNK_CASES = [(1, 50), (7, 300), (64, 1000), (128, 1024), (1000, 4096), (1024, 3000),
+               (1024, 5000), (4096, 8192), (8192, 8192), (2048, 1500)]
+
+
+@pytest.mark.parametrize("algo", ["mfma", "fft"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("C,L", CHUNK_CASES)
+def test_chunk_small(algo, io, C, L):
+    w = small(io, D=4, L=L, B=2 if C == 64 else 1)
+    d = DevWorkload(w)
+    s0 = W.random_state(w.B, w.D, w.N, seed=C + L)
+    log(f"chunk algo={algo} io={io} C={C} L={L}")
+    for state in (None, s0):
+        sin = None if state is None else par_to_dev(state)
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, state_in=sin, algo=algo)
+        ref_y, ref_s = oracle_modal(w, C=C, state_in=state)
+        gate(y, ref_y, io, label=f"chunk/{algo} C={C} L={L} state={'yes' if state is not None else 'no'}")
+        state_gate(s, ref_s, label=f"chunk/{algo} C={C} L={L}")
+
+
+@pytest.mark.parametrize("algo", ["mfma", "fft"])
+def test_chunk_resume_matches_single_call(algo):
+    """Split anywhere, carry the state through the host, continue."""
+    w = small("bf16", D=8, L=5000)
+    d = DevWorkload(w)
+    C = 1024
+    y_all, s_all = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
+    for cut in (1024, 2048, 1500, 4999):
+        log(f"resume algo={algo} cut={cut}")
+        parts = [t[..., :cut].contiguous() for t in (d.x1, d.x2, d.v)]
+        ya, sa = G.chunk_fwd(*parts, d.lam, d.res, C, d.skip, algo=algo)
+        sa_host = sa.cpu()                      # the cache leaves the device and comes back
+        parts = [t[..., cut:].contiguous() for t in (d.x1, d.x2, d.v)]
+        yb, sb = G.chunk_fwd(*parts, d.lam, d.res, C, d.skip, state_in=sa_host.cuda(), algo=algo)
+        y = torch.cat([ya, yb], dim=-1)
+        ref, ref_s = oracle_modal(w)
+        gate(y, ref, "bf16", label=f"resume cut={cut}")
+        state_gate(sb, ref_s, label=f"resume cut={cut}")
+        d_ = (y.float() - y_all.float()).abs().max().item()
+        scale = y_all.float().abs().max().item()
+        assert d_ <= 2e-2 * scale
+
+
+def test_chunked_equals_single_pass_on_gpu():
+    w = small("bf16", D=8, L=32768)
+    d = DevWorkload(w)
+    y_full = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    ref, _ = oracle_modal(w)
+    for algo in ("mfma", "fft"):
+        for C in (1024, 4096):
+            y, _ = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
+            gate(y, ref, "bf16", label=f"chunk/{algo} C={C}")
+            m = oracle.compare(to_f64(y), to_f64(y_full))
+            log(f"  chunk/{algo} C={C} vs fftconv: {m}")
+            assert oracle.passes(m)
+
+
+# ------------------------------------------------------------------ exact special cases
+def test_impulse_is_exactly_causal():
+    D, L = 4, 4096
+    w = small("bf16", D=D, L=L)
+    t0 = 1500
+    x1 = np.zeros((1, D, L), dtype=np.float32)
+    x1[..., t0] = 1.0
+    one = W.f32_to_bf16_bits(np.ones((1, D, L), dtype=np.float32))
+    dx1 = act_to_dev(W.f32_to_bf16_bits(x1), "bf16")
+    dv = act_to_dev(one, "bf16")
+    lam, res = par_to_dev(w.log_poles), par_to_dev(w.residues)
+    h = oracle.modal_filter(w.log_poles, w.residues, L)
+    outs = {
+        "fftconv": G.fftconv_fwd(dx1, dv, dv, lam, res),
+        "chunk/mfma": G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="mfma")[0],
+        "chunk/fft": G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="fft")[0],
+    }
+    for name, y in outs.items():
+        yy = to_f64(y)
+        assert np.all(yy[..., :t0] == 0.0), name
+        ref = np.zeros((1, D, L))
+        ref[0, :, t0:] = h[:, :L - t0]
+        gate(y, ref, "bf16", label=f"impulse {name}")
+    taps = par_to_dev(W.random_taps(7, D, seed=1, bf16=True))
+    yf = to_f64(G.fir_fwd(dx1, dv, dv, taps))
+    assert np.all(yf[..., :t0] == 0.0) and np.all(yf[..., t0 + 7:] == 0.0)
+
+
+def test_zero_residues_give_exact_skip_path():
+    w = small("bf16", D=4, L=3000)
+    d = DevWorkload(w)
+    zero = torch.zeros_like(d.res)
+    u = w.f64("x1") * w.f64("v")
+    expect = W.f32_to_bf16_bits((w.skip[None, :, None].astype(np.float64) * u).astype(np.float32))
+    for name, y in {
+        "fftconv": G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, zero, d.skip),
+        "chunk/mfma": G.chunk_fwd(d.x1, d.x2, d.v, d.lam, zero, 512, d.skip, algo="mfma")[0],
+        "chunk/fft": G.chunk_fwd(d.x1, d.x2, d.v, d.lam, zero, 512, d.skip, algo="fft")[0],
+        "fir": G.fir_fwd(d.x1, d.x2, d.v, torch.zeros(w.D, 7, device=d.x1.device), d.skip),
+    }.items():
+        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, expect), name
+
+
+def test_outputs_fully_written_and_deterministic():
+    w = small("bf16", D=8, L=5000)
+    d = DevWorkload(w)
+    runs = {
+        "fftconv": lambda out: G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip, out=out),
+        "chunk/mfma": lambda out: G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="mfma", out=out)[0],
+        "chunk/fft": lambda out: G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="fft", out=out)[0],
+        "fir128": lambda out: G.fir_fwd(d.x1, d.x2, d.v, d.taps[128], d.skip, out=out),
+    }
+    for name, run in runs.items():
+        first = None
+        for rep in range(3):
+            out = torch.full_like(d.x1, float("nan"))
+            run(out)
+            assert torch.isfinite(out.float()).all(), name
+            bits = out.view(torch.int16).cpu()
+            if first is None:
+                first = bits
+            else:
+                assert torch.equal(bits, first), name
+
+
+def test_empty_sequences():
+    dv = torch.device("cuda:0")
+    D, N = 4, 16
+    lam = torch.full((D, N), -0.1, device=dv)
+    res = torch.ones((D, N), device=dv)
+    x = torch.empty((1, D, 0), dtype=torch.bfloat16, device=dv)
+    s0 = torch.randn(1, D, N, device=dv)
+    y, s = G.chunk_fwd(x, x, x, lam, res, 1024, state_in=s0)
+    assert y.shape == (1, D, 0) and torch.equal(s, s0)
+    _, s = G.chunk_fwd(x, x, x, lam, res, 1024)
+    assert torch.count_nonzero(s) == 0
+    assert G.fftconv_fwd(x, x, x, lam, res).shape == (1, D, 0)
+
+
+# ------------------------------------------------------------------ full-size configurations
+def _full(name):
+    log(f"generating {name}")
+    w = W.make(name)
+    return w, DevWorkload(w)
+
+
+def test_config_tiny_full():
+    w, d = _full("tiny")
+    ref, ref_s = oracle_modal(w)
+    gate(G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip), ref, "f32", label="tiny fftconv")
+    for algo in ("mfma", "fft"):
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 128, d.skip, algo=algo)
+        gate(y, ref, "f32", label=f"tiny chunk/{algo}")
+        state_gate(s, ref_s, label=f"tiny chunk/{algo}")
+
+
+def test_config_7b_layer_set():
+    w, d = _full("7b_layer_set")
+    rows = sample_rows(w.D)
+    for K in (7, 128):
+        y = G.fir_fwd(d.x1, d.x2, d.v, d.taps[K], d.skip)
+        gate(y, oracle_fir(w, K, rows), "bf16", rows, label=f"7b FIR-{K}")
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    ref, _ = oracle_modal(w, rows)
+    gate(y, ref, "bf16", rows, label="7b modal fftconv")
+
+
+@pytest.mark.parametrize("name", ["32k_chunked", "40b_shaped"])
+def test_config_32k(name):
+    w, d = _full(name)
+    rows = sample_rows(w.D)
+    ref, ref_s = oracle_modal(w, rows)
+    C = 1024
+    for algo in ("mfma", "fft"):
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
+        gate(y, ref, "bf16", rows, label=f"{name} chunk/{algo} one launch")
+        state_gate(s, ref_s, rows, label=f"{name} chunk/{algo}")
+    # per-chunk calls with the state handed over between them
+    ys, st = [], None
+    for t0 in range(0, w.L, C):
+        sl = [t[..., t0:t0 + C].contiguous() for t in (d.x1, d.x2, d.v)]
+        yc, st = G.chunk_fwd(*sl, d.lam, d.res, C, d.skip, state_in=st, algo="auto")
+        ys.append(yc)
+    gate(torch.cat(ys, -1), ref, "bf16", rows, label=f"{name} chunk x{w.L // C} calls")
+    state_gate(st, ref_s, rows, label=f"{name} per-chunk calls")
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    gate(y, ref, "bf16", rows, label=f"{name} fftconv N=65536")
+
+
+def test_config_262k_chunked():
+    w, d = _full("262k")
+    rows = sample_rows(w.D, k=4)
+    ref, ref_s = oracle_modal(w, rows)
+    for algo in ("mfma", "fft"):
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 4096, d.skip, algo=algo)
+        gate(y, ref, "bf16", rows, label=f"262k chunk/{algo} C=4096")
+        state_gate(s, ref_s, rows, label=f"262k chunk/{algo}")
