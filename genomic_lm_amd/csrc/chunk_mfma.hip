@@ -17,9 +17,12 @@
 //
 // Mapping: one 64-lane wave per (b, c) row, 1024-token tiles (32 blocks x 32
 // tokens) walked in order.  Per tile: T.U, G.S and the transposed E^T = U^T.P^T
-// are 13 v_mfma_f32_32x32x16_bf16.  Every fp32 operand x is split into
-// bf16 hi = rne(x), lo = rne(x - hi) and products use hi*hi + hi*lo + lo*hi
-// (relative error ~2^-17); u = x1*v of two bf16 values is exactly hi + lo.
+// are v_mfma_f32_32x32x16_bf16 products of fp32 operands split into three
+// bf16 parts x = x0 + x1 + x2 (each the rounded remainder of the previous);
+// every product keeps the part pairs of order <= 2 (x0y0, x0y1, x1y0, x1y1,
+// x0y2, x2y0), which leaves ~2^-24 relative error per term, fp32-like.
+// u = x1*v of two bf16 values is exactly u0 + u1; fp32 inputs take three
+// parts.  22 MFMAs per 1024-token tile for bf16 I/O.
 // The contraction index of T.U is permuted so that each lane's B-operand
 // tokens are exactly the tokens of its output rows: u, x2 and y move in 8-byte
 // runs of 4 tokens and never cross lanes.  The scan runs one mode (hi or lo
@@ -40,9 +43,12 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-  hi = static_cast<__bf16>(x);
-  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+// x = p0 + p1 + p2 + r with p_k = rne_bf16 of the remainder so far; |r| <= 2^-24 |x|
+__device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& p2) {
+  p0 = static_cast<__bf16>(x);
+  const float r1 = x - static_cast<float>(p0);
+  p1 = static_cast<__bf16>(r1);
+  p2 = static_cast<__bf16>(r1 - static_cast<float>(p1));
 }
 
 // token (within a 32-token block) of output register r / operand slot
@@ -91,22 +97,26 @@ __device__ __forceinline__ void st4(IO* row, int64_t i, int64_t L, const float (
     if (i + e < L) Io<IO>::st(row, i + e, o[e]);
 }
 
-// B operand of E^T = U^T . P^T for one lane: column nn (mode nn & 15, part
-// nn >> 4), slots (s, j) -> token blk_tok(8s + j, hf).  Weight of token tok
-// is p^(ref - tok) for tok <= ref, else 0.  Part 0 columns carry hi(w) in
-// `ba` and `bb`; part 1 columns carry lo(w) in `ba` and 0 in `bb`.
+// B operands of E^T = U^T . P^T for one lane: column nn (mode nn & 15, part
+// nn >> 4), slots (s, j) -> token blk_tok(8s + j, hf).  The weight of token
+// tok is w = p^(ref - tok) for tok <= ref, else 0, split as w0 + w1 + w2.
+// Summing columns n and n + 16 of  U0.A + U1.A + U0.B (+ U2.C)  gives every
+// product of order <= 2:  A = [w0 | w1], B = [w2 | 0], C = [w0 | 0].
 __device__ __forceinline__ void build_state_weights(float lam_n, int part, int hf, int ref,
-                                                    bf16x8 (&ba)[2], bf16x8 (&bb)[2]) {
+                                                    bf16x8 (&pa)[2], bf16x8 (&pb)[2],
+                                                    bf16x8 (&pc)[2]) {
+  const __bf16 zero = static_cast<__bf16>(0.0f);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tok = blk_tok(8 * s + j, hf);
       const float w = (tok <= ref) ? expf(lam_n * static_cast<float>(ref - tok)) : 0.0f;
-      __bf16 hi, lo;
-      split_bf16(w, hi, lo);
-      ba[s][j] = part ? lo : hi;
-      bb[s][j] = part ? static_cast<__bf16>(0.0f) : hi;
+      __bf16 w0, w1, w2;
+      split3(w, w0, w1, w2);
+      pa[s][j] = part ? w1 : w0;
+      pb[s][j] = part ? zero : w2;
+      pc[s][j] = part ? zero : w0;
     }
   }
 }
@@ -117,6 +127,8 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, const float* state_in,
     float* state_out, IO* __restrict__ y, int D, int L) {
+  // parts of u: x1*v of two bf16 values is exactly two bf16 parts
+  constexpr int NU = (sizeof(IO) == 2) ? 2 : 3;
   __shared__ float hbuf[32];
   __shared__ float sbuf[2][32][17];           // state before block b, per part and mode
 
@@ -142,75 +154,73 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   }
   __syncthreads();
   // A = T (row i32, slot (s,j) -> token blk_tok): T[i][tok] = h[i - tok] for tok <= i
-  bf16x8 t_hi[2], t_lo[2];
+  bf16x8 tm[3][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int d = i32 - blk_tok(8 * s + j, hf);
       const float val = (d >= 0) ? hbuf[d] : 0.0f;
-      __bf16 hi, lo;
-      split_bf16(val, hi, lo);
-      t_hi[s][j] = hi;
-      t_lo[s][j] = lo;
+      __bf16 a0, a1, a2;
+      split3(val, a0, a1, a2);
+      tm[0][s][j] = a0;
+      tm[1][s][j] = a1;
+      tm[2][s][j] = a2;
     }
   }
   // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1)
-  bf16x8 g_hi, g_lo;
+  bf16x8 gm[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int n = 8 * hf + j;
     const float val = (n < N) ? resc[n] * expf(lamc[n] * static_cast<float>(i32 + 1)) : 0.0f;
-    __bf16 hi, lo;
-    split_bf16(val, hi, lo);
-    g_hi[j] = hi;
-    g_lo[j] = lo;
+    __bf16 a0, a1, a2;
+    split3(val, a0, a1, a2);
+    gm[0][j] = a0;
+    gm[1][j] = a1;
+    gm[2][j] = a2;
   }
-  // scan lane: mode n (hi/lo part) for all 32 blocks; padded modes have p = 1, R = 0
+  // scan lane: mode n (part 0 or 1 of the column pair) for all 32 blocks;
+  // padded modes have p = 1 and R = 0
   const int part = i32 >> 4;
   const int n_sc = i32 & 15;
   const float lam_n = (n_sc < N) ? lamc[n_sc] : 0.0f;
-  bf16x8 p_a[2], p_b[2];
-  build_state_weights(lam_n, part, hf, 31, p_a, p_b);
+  bf16x8 pa[2], pb[2], pc[2];
+  build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
   const float a1 = expf(lam_n * 32.0f), a2 = expf(lam_n * 64.0f);
   const float a3 = expf(lam_n * 96.0f), a4 = expf(lam_n * 128.0f);
   float carry = (part == 0 && n_sc < N && state_in) ? state_in[row * N + n_sc] : 0.0f;
 
 #pragma unroll 1
   for (int t0 = 0; t0 < L; t0 += 1024) {
-    // ---- load u = x1*v and x2 for block i32, tokens blk_tok(r, hf)
-    float u[16], g[16];
+    // ---- u = x1*v for block i32, tokens blk_tok(r, hf), as bf16 parts
     const int64_t base = static_cast<int64_t>(t0) + 32 * i32 + 4 * hf;
+    bf16x8 um[NU][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float a[4], b[4], gg[4];
+      float a[4], b[4];
       ld4<IO, VEC>(x1r, base + 8 * q, L, a);
       ld4<IO, VEC>(vr, base + 8 * q, L, b);
-      ld4<IO, VEC>(x2r, base + 8 * q, L, gg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        u[4 * q + e] = a[e] * b[e];
-        g[4 * q + e] = gg[e];
-      }
-    }
-    bf16x8 u_hi[2], u_lo[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        __bf16 hi, lo;
-        split_bf16(u[8 * s + j], hi, lo);
-        u_hi[s][j] = hi;
-        u_lo[s][j] = lo;
+        const int r = 4 * q + e;
+        __bf16 p0, p1, p2;
+        split3(a[e] * b[e], p0, p1, p2);
+        um[0][r >> 3][r & 7] = p0;
+        um[1][r >> 3][r & 7] = p1;
+        if constexpr (NU == 3) um[NU - 1][r >> 3][r & 7] = p2;
       }
     }
 
     // ---- block-local end states, transposed: lane = mode column, 16 blocks per lane
     f32x16 ce = {};
-    ce = mfma(u_hi[0], p_a[0], ce);
-    ce = mfma(u_hi[1], p_a[1], ce);
-    ce = mfma(u_lo[0], p_b[0], ce);
-    ce = mfma(u_lo[1], p_b[1], ce);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ce = mfma(um[0][s], pa[s], ce);
+      ce = mfma(um[1][s], pa[s], ce);
+      ce = mfma(um[0][s], pb[s], ce);
+      if constexpr (NU == 3) ce = mfma(um[NU - 1][s], pc[s], ce);
+    }
 
     // ---- scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
     float x[16];
@@ -257,35 +267,55 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     }
     __syncthreads();
 
-    // ---- B = state before block i32, modes 8hf + j (hi + lo parts summed)
-    bf16x8 s_hi, s_lo;
+    // ---- B = state before block i32, modes 8hf + j (column pair summed)
+    bf16x8 sm[3];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int n = 8 * hf + j;
-      __bf16 hi, lo;
-      split_bf16(sbuf[0][i32][n] + sbuf[1][i32][n], hi, lo);
-      s_hi[j] = hi;
-      s_lo[j] = lo;
+      __bf16 p0, p1, p2;
+      split3(sbuf[0][i32][n] + sbuf[1][i32][n], p0, p1, p2);
+      sm[0][j] = p0;
+      sm[1][j] = p1;
+      sm[2][j] = p2;
+    }
+    float g[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gg[4];
+      ld4<IO, VEC>(x2r, base + 8 * q, L, gg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[4 * q + e] = gg[e];
     }
 
-    // ---- z = T.U + G.S
+    // ---- z = T.U + G.S, products of order <= 2
     f32x16 cz = {};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      cz = mfma(t_hi[s], u_hi[s], cz);
-      cz = mfma(t_hi[s], u_lo[s], cz);
-      cz = mfma(t_lo[s], u_hi[s], cz);
+      cz = mfma(tm[0][s], um[0][s], cz);
+      cz = mfma(tm[0][s], um[1][s], cz);
+      cz = mfma(tm[1][s], um[0][s], cz);
+      cz = mfma(tm[1][s], um[1][s], cz);
+      cz = mfma(tm[2][s], um[0][s], cz);
+      if constexpr (NU == 3) cz = mfma(tm[0][s], um[NU - 1][s], cz);
     }
-    cz = mfma(g_hi, s_hi, cz);
-    cz = mfma(g_hi, s_lo, cz);
-    cz = mfma(g_lo, s_hi, cz);
+    cz = mfma(gm[0], sm[0], cz);
+    cz = mfma(gm[0], sm[1], cz);
+    cz = mfma(gm[1], sm[0], cz);
+    cz = mfma(gm[1], sm[1], cz);
+    cz = mfma(gm[0], sm[2], cz);
+    cz = mfma(gm[2], sm[0], cz);
 
     // ---- y = x2 * z + skip * u
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = fmaf(g[4 * q + e], cz[4 * q + e], sk * u[4 * q + e]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q + e;
+        float u = static_cast<float>(um[0][r >> 3][r & 7]) + static_cast<float>(um[1][r >> 3][r & 7]);
+        if constexpr (NU == 3) u += static_cast<float>(um[NU - 1][r >> 3][r & 7]);
+        o[e] = fmaf(g[r], cz[r], sk * u);
+      }
       st4<IO, VEC>(yr, base + 8 * q, L, o);
     }
 
@@ -297,13 +327,16 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       } else {
         const int bstar = (rem - 1) >> 5;
         const int estar = (rem - 1) & 31;
-        bf16x8 q_a[2], q_b[2];
-        build_state_weights(lam_n, part, hf, estar, q_a, q_b);
+        bf16x8 qa[2], qb[2], qc[2];
+        build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
         f32x16 cf = {};
-        cf = mfma(u_hi[0], q_a[0], cf);
-        cf = mfma(u_hi[1], q_a[1], cf);
-        cf = mfma(u_lo[0], q_b[0], cf);
-        cf = mfma(u_lo[1], q_b[1], cf);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          cf = mfma(um[0][s], qa[s], cf);
+          cf = mfma(um[1][s], qa[s], cf);
+          cf = mfma(um[0][s], qb[s], cf);
+          if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qc[s], cf);
+        }
         const bool mine = (((bstar >> 2) & 1) == hf);
         const int rs = 4 * (bstar >> 3) + (bstar & 3);
         float ev = 0.0f;

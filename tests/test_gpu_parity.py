@@ -122,13 +122,19 @@ def test_chunked_equals_single_pass_on_gpu():
         for C in (1024, 4096):
             y, _ = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
             gate(y, ref, "bf16", label=f"chunk/{algo} C={C}")
+            # two outputs that each carry one bf16 rounding: twice the gates
             m = oracle.compare(to_f64(y), to_f64(y_full))
             log(f"  chunk/{algo} C={C} vs fftconv: {m}")
-            assert oracle.passes(m)
+            assert oracle.passes(m, 2 * oracle.REL_L2_MAX, 2 * oracle.ELEM_REL_MAX)
 
 
 # ------------------------------------------------------------------ exact special cases
-def test_impulse_is_exactly_causal():
+def test_impulse_is_causal():
+    """x1 = delta at t0, v = x2 = 1, skip = 0: y = h shifted by t0.
+
+    Direct evaluations (MFMA blocks, FIR) give exact zeros before t0; FFT
+    evaluations give rounding noise there, except in chunks that end before
+    t0, whose input is all zero."""
     D, L = 4, 4096
     w = small("bf16", D=D, L=L)
     t0 = 1500
@@ -139,16 +145,17 @@ def test_impulse_is_exactly_causal():
     dv = act_to_dev(one, "bf16")
     lam, res = par_to_dev(w.log_poles), par_to_dev(w.residues)
     h = oracle.modal_filter(w.log_poles, w.residues, L)
-    outs = {
-        "fftconv": G.fftconv_fwd(dx1, dv, dv, lam, res),
-        "chunk/mfma": G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="mfma")[0],
-        "chunk/fft": G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="fft")[0],
+    ref = np.zeros((1, D, L))
+    ref[0, :, t0:] = h[:, :L - t0]
+    outs = {   # name -> (output, first index that must be exactly zero-free of noise)
+        "fftconv": (G.fftconv_fwd(dx1, dv, dv, lam, res), 0),
+        "chunk/mfma": (G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="mfma")[0], t0),
+        "chunk/fft": (G.chunk_fwd(dx1, dv, dv, lam, res, 1024, algo="fft")[0], 1024),
     }
-    for name, y in outs.items():
+    for name, (y, exact_until) in outs.items():
         yy = to_f64(y)
-        assert np.all(yy[..., :t0] == 0.0), name
-        ref = np.zeros((1, D, L))
-        ref[0, :, t0:] = h[:, :L - t0]
+        assert np.all(yy[..., :exact_until] == 0.0), name
+        assert np.max(np.abs(yy[..., :t0])) <= 1e-6 * np.max(np.abs(ref)), name
         gate(y, ref, "bf16", label=f"impulse {name}")
     taps = par_to_dev(W.random_taps(7, D, seed=1, bf16=True))
     yf = to_f64(G.fir_fwd(dx1, dv, dv, taps))
