@@ -77,26 +77,6 @@ __device__ __forceinline__ void ld4(const IO* row, int64_t i, int64_t L, float (
   for (int e = 0; e < 4; ++e) o[e] = (i + e < L) ? Io<IO>::ld(row, i + e) : 0.0f;
 }
 
-template <typename IO, bool VEC>
-__device__ __forceinline__ void st4(IO* row, int64_t i, int64_t L, const float (&o)[4]) {
-  if constexpr (VEC) {
-    if (i + 4 <= L) {
-      if constexpr (sizeof(IO) == 2) {
-        uint2 w;
-        w.x = static_cast<uint32_t>(f32_to_bf16(o[0])) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-        w.y = static_cast<uint32_t>(f32_to_bf16(o[2])) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-        *reinterpret_cast<uint2*>(row + i) = w;
-      } else {
-        *reinterpret_cast<float4*>(row + i) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (i + e < L) Io<IO>::st(row, i + e, o[e]);
-}
-
 // B operands of E^T = U^T . P^T for one lane: column nn (mode nn & 15, part
 // nn >> 4), slots (s, j) -> token blk_tok(8s + j, hf).  The weight of token
 // tok is w = p^(ref - tok) for tok <= ref, else 0, split as w0 + w1 + w2.
@@ -121,6 +101,39 @@ __device__ __forceinline__ void build_state_weights(float lam_n, int part, int h
   }
 }
 
+// Raw storage of 4 consecutive activations (one run of a lane): 8 bytes of
+// bf16 or 16 bytes of fp32, loaded without conversion so that the next tile
+// can be in flight while the current one is computed.
+template <typename IO> struct Raw4;
+template <> struct Raw4<bf16_t> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t x = (e < 2) ? w.x : w.y;
+    return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+template <> struct Raw4<float> {
+  float4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+  }
+};
+
+// The three input runs of one lane for one tile.
+template <typename IO> struct TileIn {
+  Raw4<IO> a[4], b[4], g[4];     // x1, v, x2 at tokens base + 8q .. +3
+  __device__ __forceinline__ void load(const IO* x1r, const IO* vr, const IO* x2r, int64_t base) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q].load(x1r + base + 8 * q);
+      b[q].load(vr + base + 8 * q);
+      g[q].load(x2r + base + 8 * q);
+    }
+  }
+};
+
 template <typename IO, bool VEC>
 __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
@@ -144,6 +157,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   const IO* vr = v + row * L;
   IO* yr = y + row * L;
   const float sk = skip ? skip[c] : 0.0f;
+  const int lane_off = 32 * i32 + 4 * hf;     // token offset of run 0 within a tile
 
   // ---- per-row constants
   // h[d], d < 32
@@ -191,28 +205,23 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   const float a3 = expf(lam_n * 96.0f), a4 = expf(lam_n * 128.0f);
   float carry = (part == 0 && n_sc < N && state_in) ? state_in[row * N + n_sc] : 0.0f;
 
-#pragma unroll 1
-  for (int t0 = 0; t0 < L; t0 += 1024) {
-    // ---- u = x1*v for block i32, tokens blk_tok(r, hf), as bf16 parts
-    const int64_t base = static_cast<int64_t>(t0) + 32 * i32 + 4 * hf;
-    bf16x8 um[NU][2];
+  // One 1024-token tile: inputs in `in` (u = x1 * v, gate x2), output to y.
+  // Returns nothing; updates `carry` (state after the tile, in part-0 lanes)
+  // and leaves sbuf holding the state before each block of the tile.
+  auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float a[4], b[4];
-      ld4<IO, VEC>(x1r, base + 8 * q, L, a);
-      ld4<IO, VEC>(vr, base + 8 * q, L, b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
         __bf16 p0, p1, p2;
-        split3(a[e] * b[e], p0, p1, p2);
+        split3(in.a[q].get(e) * in.b[q].get(e), p0, p1, p2);
         um[0][r >> 3][r & 7] = p0;
         um[1][r >> 3][r & 7] = p1;
         if constexpr (NU == 3) um[NU - 1][r >> 3][r & 7] = p2;
       }
     }
-
-    // ---- block-local end states, transposed: lane = mode column, 16 blocks per lane
+    // block-local end states, transposed: lane = mode column, 16 blocks per lane
     f32x16 ce = {};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -221,8 +230,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       ce = mfma(um[0][s], pb[s], ce);
       if constexpr (NU == 3) ce = mfma(um[NU - 1][s], pc[s], ce);
     }
-
-    // ---- scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
+    // scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = ce[r];
@@ -266,8 +274,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       carry = (part == 0) ? tot : 0.0f;
     }
     __syncthreads();
-
-    // ---- B = state before block i32, modes 8hf + j (column pair summed)
+    // B = state before block i32, modes 8hf + j (column pair summed)
     bf16x8 sm[3];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -278,16 +285,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       sm[1][j] = p1;
       sm[2][j] = p2;
     }
-    float g[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float gg[4];
-      ld4<IO, VEC>(x2r, base + 8 * q, L, gg);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) g[4 * q + e] = gg[e];
-    }
-
-    // ---- z = T.U + G.S, products of order <= 2
+    // z = T.U + G.S, products of order <= 2
     f32x16 cz = {};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -304,49 +302,107 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     cz = mfma(gm[1], sm[1], cz);
     cz = mfma(gm[0], sm[2], cz);
     cz = mfma(gm[2], sm[0], cz);
-
-    // ---- y = x2 * z + skip * u
+    // y = x2 * z + skip * u
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        float u = static_cast<float>(um[0][r >> 3][r & 7]) + static_cast<float>(um[1][r >> 3][r & 7]);
-        if constexpr (NU == 3) u += static_cast<float>(um[NU - 1][r >> 3][r & 7]);
-        o[e] = fmaf(g[r], cz[r], sk * u);
+        const float u = in.a[q].get(e) * in.b[q].get(e);
+        o[e] = fmaf(in.g[q].get(e), cz[r], sk * u);
       }
-      st4<IO, VEC>(yr, base + 8 * q, L, o);
-    }
-
-    // ---- final state when the sequence ends inside this tile
-    const int rem = L - t0;
-    if (rem <= 1024) {
-      if (rem == 1024) {
-        if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
-      } else {
-        const int bstar = (rem - 1) >> 5;
-        const int estar = (rem - 1) & 31;
-        bf16x8 qa[2], qb[2], qc[2];
-        build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
-        f32x16 cf = {};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          cf = mfma(um[0][s], qa[s], cf);
-          cf = mfma(um[1][s], qa[s], cf);
-          cf = mfma(um[0][s], qb[s], cf);
-          if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qc[s], cf);
+      const int64_t pos = t0 + lane_off + 8 * q;
+      if (full) {
+        if constexpr (sizeof(IO) == 2) {
+          uint2 w;
+          w.x = static_cast<uint32_t>(f32_to_bf16(o[0])) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+          w.y = static_cast<uint32_t>(f32_to_bf16(o[2])) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+          *reinterpret_cast<uint2*>(yr + pos) = w;
+        } else {
+          *reinterpret_cast<float4*>(yr + pos) = make_float4(o[0], o[1], o[2], o[3]);
         }
-        const bool mine = (((bstar >> 2) & 1) == hf);
-        const int rs = 4 * (bstar >> 3) + (bstar & 3);
-        float ev = 0.0f;
+      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ev = (r == rs) ? cf[r] : ev;
-        const float fin = mine ? fmaf(expf(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev)
-                               : 0.0f;
-        const float tot = fin + __shfl_xor(fin, 16);
-        if (mine && part == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
+        for (int e = 0; e < 4; ++e)
+          if (pos + e < L) Io<IO>::st(yr, pos + e, o[e]);
       }
+    }
+  };
+
+  // ---- full tiles, the next one in flight while the current one computes
+  const int nfull = VEC ? (L >> 10) : 0;
+  TileIn<IO> nxt;
+  if (nfull > 0) nxt.load(x1r, vr, x2r, lane_off);
+#pragma unroll 1
+  for (int k = 0; k < nfull; ++k) {
+    const TileIn<IO> cur = nxt;
+    const int64_t t0 = static_cast<int64_t>(k) << 10;
+    if (k + 1 < nfull) nxt.load(x1r, vr, x2r, t0 + 1024 + lane_off);
+    bf16x8 um[NU][2];
+    tile(cur, t0, true, um);
+    __syncthreads();                           // sbuf reads done before the next tile writes
+  }
+  if (nfull > 0 && (static_cast<int64_t>(nfull) << 10) == L) {
+    if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
+    return;
+  }
+
+  // ---- remaining tokens: tiles with bounds checks (at most one when VEC)
+#pragma unroll 1
+  for (int64_t t0 = static_cast<int64_t>(nfull) << 10; t0 < L; t0 += 1024) {
+    TileIn<IO> in;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float fa[4], fb[4], fg[4];
+      const int64_t pos = t0 + lane_off + 8 * q;
+      ld4<IO, false>(x1r, pos, L, fa);
+      ld4<IO, false>(vr, pos, L, fb);
+      ld4<IO, false>(x2r, pos, L, fg);
+      if constexpr (sizeof(IO) == 2) {
+        auto pk = [](const float (&f)[4]) {
+          uint2 w;
+          w.x = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+          w.y = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u);
+          return w;
+        };
+        in.a[q].w = pk(fa);
+        in.b[q].w = pk(fb);
+        in.g[q].w = pk(fg);
+      } else {
+        in.a[q].w = make_float4(fa[0], fa[1], fa[2], fa[3]);
+        in.b[q].w = make_float4(fb[0], fb[1], fb[2], fb[3]);
+        in.g[q].w = make_float4(fg[0], fg[1], fg[2], fg[3]);
+      }
+    }
+    bf16x8 um[NU][2];
+    tile(in, t0, false, um);
+    const int64_t rem = L - t0;
+    if (rem == 1024) {
+      if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
+    } else if (rem < 1024) {
+      // the sequence ends inside this tile: state after token L-1
+      const int bstar = static_cast<int>(rem - 1) >> 5;
+      const int estar = static_cast<int>(rem - 1) & 31;
+      bf16x8 qa[2], qb[2], qc[2];
+      build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
+      f32x16 cf = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        cf = mfma(um[0][s], qa[s], cf);
+        cf = mfma(um[1][s], qa[s], cf);
+        cf = mfma(um[0][s], qb[s], cf);
+        if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qc[s], cf);
+      }
+      const bool mine = (((bstar >> 2) & 1) == hf);
+      const int rs = 4 * (bstar >> 3) + (bstar & 3);
+      float ev = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ev = (r == rs) ? cf[r] : ev;
+      const float fin = mine ? fmaf(expf(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev)
+                             : 0.0f;
+      const float tot = fin + __shfl_xor(fin, 16);
+      if (mine && part == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
     }
     __syncthreads();                           // sbuf reads done before the next tile writes
   }
