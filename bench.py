@@ -45,11 +45,26 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--algo", default="mfma", choices=["mfma", "fft", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": steps}), flush=True)
 
 
 def timed(fn, steps, warmup, stream):
@@ -95,6 +110,10 @@ def main():
               "shards over channels with no communication, so N GPUs run N independent copies "
               "of this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import numpy as np
     import torch

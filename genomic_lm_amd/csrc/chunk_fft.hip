@@ -40,7 +40,7 @@ constexpr int CHUNK_NG = 16;             // modes per reduction group
 
 template <int S, int T, typename IO, bool VEC>
 __global__ __launch_bounds__(T) void chunk_fft_kernel(
-    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, const float* state_in,
     float* state_out, IO* __restrict__ y, int D, int L, int C) {

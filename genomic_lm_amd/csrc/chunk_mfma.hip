@@ -39,6 +39,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int MFMA_MAXN = 16;
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row operands are computed once and must stay in registers: the empty
+// asm hides how they were made, so the compiler cannot recompute them (with
+// their exp calls) inside the tile loop to save registers.
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(w));
+  x = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -49,6 +61,27 @@ __device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& 
   const float r1 = x - static_cast<float>(p0);
   p1 = static_cast<__bf16>(r1);
   p2 = static_cast<__bf16>(r1 - static_cast<float>(p1));
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair (one v_cvt_pk_bf16_f32), and back.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// split3 on a pair, each part a packed bf16 pair
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+  p0 = cvt2(a, b);
+  float ra = a - lo_f(p0), rb = b - hi_f(p0);
+  p1 = cvt2(ra, rb);
+  ra -= lo_f(p1);
+  rb -= hi_f(p1);
+  p2 = cvt2(ra, rb);
 }
 
 // token (within a 32-token block) of output register r / operand slot
@@ -134,6 +167,43 @@ template <typename IO> struct TileIn {
   }
 };
 
+// bf16 tiles move between HBM and LDS in 16-byte chunks (8 tokens), one
+// chunk per lane per instruction, which keeps every load and store fully
+// coalesced.  Chunk c = 4m + q holds tokens 32m + 8q .. +7 of block m and
+// lives in LDS slot swz(c) = 4m + ((q + m/4) & 3): the coalesced writes stay
+// conflict-free and so do the reads of a lane's run (block m, half hf),
+// which for a fixed q touch 16 distinct slots per 256 bytes.
+__device__ __forceinline__ int swz(int c) { return (c & ~3) | (((c & 3) + (c >> 4)) & 3); }
+
+__device__ __forceinline__ int unswz(int s) { return (s & ~3) | (((s & 3) - (s >> 4)) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte chunk per lane from global memory straight into LDS (no
+// registers): the wave writes 1 KB at `dst`, lane l at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+}
+
+// The workgroup is a single wave: its LDS operations execute in order, so
+// making LDS writes visible to the other lanes needs only that they have
+// completed and that the compiler keeps program order -- no s_barrier and, in
+// particular, no wait for outstanding global loads (the DMA of the next
+// tile), which a __syncthreads() fence would add.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding.  They retire in issue order, so this waits for everything
+// issued before the last N.  (s_waitcnt simm16 on gfx9: vmcnt[3:0] in bits
+// 3:0, expcnt in bits 6:4, lgkmcnt in bits 11:8, vmcnt[5:4] in bits 15:14;
+// expcnt and lgkmcnt are left free.)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
+}
+
 template <typename IO, bool VEC>
 __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
@@ -143,7 +213,13 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // parts of u: x1*v of two bf16 values is exactly two bf16 parts
   constexpr int NU = (sizeof(IO) == 2) ? 2 : 3;
   __shared__ float hbuf[32];
-  __shared__ float sbuf[2][32][17];           // state before block b, per part and mode
+  // state before block b, per part and mode (row 32: unused); two copies
+  // used by alternate tiles, so a tile's writes never meet the previous
+  // tile's reads
+  __shared__ float sbufs[1][2][33][17];
+  // staged x1, v, x2 tiles (bf16, swizzled chunks), two tiles in turn; the
+  // y tile is staged over the x1 slice of its own tile, already consumed
+  __shared__ uint4 tin_a[3][128], tin_b[3][128];
 
   const int l = threadIdx.x;
   const int hf = l >> 5;                      // half-wave
@@ -166,7 +242,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     for (int n = 0; n < N; ++n) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
     if (hf == 0) hbuf[i32] = hd;
   }
-  __syncthreads();
+  lds_sync();
   // A = T (row i32, slot (s,j) -> token blk_tok): T[i][tok] = h[i - tok] for tok <= i
   bf16x8 tm[3][2];
 #pragma unroll
@@ -201,25 +277,74 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   const float lam_n = (n_sc < N) ? lamc[n_sc] : 0.0f;
   bf16x8 pa[2], pb[2], pc[2];
   build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
-  const float a1 = expf(lam_n * 32.0f), a2 = expf(lam_n * 64.0f);
-  const float a3 = expf(lam_n * 96.0f), a4 = expf(lam_n * 128.0f);
+  float a1 = expf(lam_n * 32.0f), a2 = expf(lam_n * 64.0f);
+  float a3 = expf(lam_n * 96.0f), a4 = expf(lam_n * 128.0f);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    pin(pa[s]);
+    pin(pb[s]);
+    if constexpr (NU == 3) pin(pc[s]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) pin(tm[k][s]);
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) pin(gm[k]);
+  pin(a1);
+  pin(a2);
+  pin(a3);
+  pin(a4);
   float carry = (part == 0 && n_sc < N && state_in) ? state_in[row * N + n_sc] : 0.0f;
 
   // One 1024-token tile: inputs in `in` (u = x1 * v, gate x2), output to y.
   // Returns nothing; updates `carry` (state after the tile, in part-0 lanes)
   // and leaves sbuf holding the state before each block of the tile.
-  auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2]) {
+  // Runs of the tile: from `in` (registers) or, for bf16 tiles staged in
+  // LDS, straight from the staged chunks when they are needed.
+  auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2],
+                  uint4 (*tin)[128], bool staged) {
+    float (*sbuf)[33][17] = sbufs[0];
+    uint4* tout = tin[0];
+    auto run = [&](int arr, int q) {
+      Raw4<IO> r;
+      if constexpr (sizeof(IO) == 2) {
+        if (staged) {
+          r.w = reinterpret_cast<const uint2*>(&tin[arr][swz(4 * i32 + q)])[hf];
+          return r;
+        }
+      }
+      r = arr == 0 ? in.a[q] : arr == 1 ? in.b[q] : in.g[q];
+      return r;
+    };
+    float su[16];                              // skip * u, for the output
+    u32x4 uw[NU][2];                           // parts of u as packed bf16 pairs
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const Raw4<IO> ra = run(0, q), rb = run(1, q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; e += 2) {
         const int r = 4 * q + e;
-        __bf16 p0, p1, p2;
-        split3(in.a[q].get(e) * in.b[q].get(e), p0, p1, p2);
-        um[0][r >> 3][r & 7] = p0;
-        um[1][r >> 3][r & 7] = p1;
-        if constexpr (NU == 3) um[NU - 1][r >> 3][r & 7] = p2;
+        const float u0 = ra.get(e) * rb.get(e);
+        const float u1 = ra.get(e + 1) * rb.get(e + 1);
+        su[r] = sk * u0;
+        su[r + 1] = sk * u1;
+        uint32_t p0, p1, p2;
+        if constexpr (NU == 2) {
+          // exact: the remainder of a product of two bf16 fits one bf16
+          p0 = cvt2(u0, u1);
+          p1 = cvt2(u0 - lo_f(p0), u1 - hi_f(p0));
+          p2 = 0;
+        } else {
+          split3_pair(u0, u1, p0, p1, p2);
+        }
+        uw[0][r >> 3][(r & 7) >> 1] = p0;
+        uw[1][r >> 3][(r & 7) >> 1] = p1;
+        if constexpr (NU == 3) uw[NU - 1][r >> 3][(r & 7) >> 1] = p2;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      um[k][0] = __builtin_bit_cast(bf16x8, uw[k][0]);
+      um[k][1] = __builtin_bit_cast(bf16x8, uw[k][1]);
     }
     // block-local end states, transposed: lane = mode column, 16 blocks per lane
     f32x16 ce = {};
@@ -229,6 +354,18 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       ce = mfma(um[1][s], pa[s], ce);
       ce = mfma(um[0][s], pb[s], ce);
       if constexpr (NU == 3) ce = mfma(um[NU - 1][s], pc[s], ce);
+    }
+    // in-block Toeplitz part of z; independent of the scan, so the matrix
+    // cores work on it while the scan runs on the vector ALUs
+    f32x16 cz = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      cz = mfma(tm[0][s], um[0][s], cz);
+      cz = mfma(tm[0][s], um[1][s], cz);
+      cz = mfma(tm[1][s], um[0][s], cz);
+      cz = mfma(tm[1][s], um[1][s], cz);
+      cz = mfma(tm[2][s], um[0][s], cz);
+      if constexpr (NU == 3) cz = mfma(tm[0][s], um[NU - 1][s], cz);
     }
     // scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
     float x[16];
@@ -255,47 +392,38 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float ci = cin[2 * q + hf];
+      const float ci = hf ? cin[2 * q + 1] : cin[2 * q];
       x[4 * q + 0] = fmaf(a1, ci, x[4 * q + 0]);
       x[4 * q + 1] = fmaf(a2, ci, x[4 * q + 1]);
       x[4 * q + 2] = fmaf(a3, ci, x[4 * q + 2]);
       x[4 * q + 3] = fmaf(a4, ci, x[4 * q + 3]);
     }
-    // state before block b+1 = x for block b; before block 0 = cin[0]
+    // state before block b+1 = x for block b (b = 31 lands in the unused row
+    // 32); before block 0 = cin[0], identical in both half-waves
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int b = blk_tok(r, hf);
-      if (b < 31) sbuf[part][b + 1][n_sc] = x[r];
-    }
-    if (hf == 0) sbuf[part][0][n_sc] = cin[0];
+    for (int r = 0; r < 16; ++r) sbuf[part][blk_tok(r, hf) + 1][n_sc] = x[r];
+    sbuf[part][0][n_sc] = cin[0];
     {
       const float fin = cin[8];
       const float tot = fin + __shfl_xor(fin, 16);
       carry = (part == 0) ? tot : 0.0f;
     }
-    __syncthreads();
+    lds_sync();
     // B = state before block i32, modes 8hf + j (column pair summed)
-    bf16x8 sm[3];
+    u32x4 sw[3];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; j += 2) {
       const int n = 8 * hf + j;
-      __bf16 p0, p1, p2;
-      split3(sbuf[0][i32][n] + sbuf[1][i32][n], p0, p1, p2);
-      sm[0][j] = p0;
-      sm[1][j] = p1;
-      sm[2][j] = p2;
+      uint32_t p0, p1, p2;
+      split3_pair(sbuf[0][i32][n] + sbuf[1][i32][n], sbuf[0][i32][n + 1] + sbuf[1][i32][n + 1],
+                  p0, p1, p2);
+      sw[0][j >> 1] = p0;
+      sw[1][j >> 1] = p1;
+      sw[2][j >> 1] = p2;
     }
-    // z = T.U + G.S, products of order <= 2
-    f32x16 cz = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      cz = mfma(tm[0][s], um[0][s], cz);
-      cz = mfma(tm[0][s], um[1][s], cz);
-      cz = mfma(tm[1][s], um[0][s], cz);
-      cz = mfma(tm[1][s], um[1][s], cz);
-      cz = mfma(tm[2][s], um[0][s], cz);
-      if constexpr (NU == 3) cz = mfma(tm[0][s], um[NU - 1][s], cz);
-    }
+    const bf16x8 sm[3] = {__builtin_bit_cast(bf16x8, sw[0]), __builtin_bit_cast(bf16x8, sw[1]),
+                          __builtin_bit_cast(bf16x8, sw[2])};
+    // z = T.U + G.S, products of order <= 2 (G.S added after the scan)
     cz = mfma(gm[0], sm[0], cz);
     cz = mfma(gm[0], sm[1], cz);
     cz = mfma(gm[1], sm[0], cz);
@@ -306,19 +434,16 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
+      const Raw4<IO> rg = run(2, q);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        const float u = in.a[q].get(e) * in.b[q].get(e);
-        o[e] = fmaf(in.g[q].get(e), cz[r], sk * u);
+        o[e] = fmaf(rg.get(e), cz[r], su[r]);
       }
       const int64_t pos = t0 + lane_off + 8 * q;
       if (full) {
         if constexpr (sizeof(IO) == 2) {
-          uint2 w;
-          w.x = static_cast<uint32_t>(f32_to_bf16(o[0])) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-          w.y = static_cast<uint32_t>(f32_to_bf16(o[2])) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-          *reinterpret_cast<uint2*>(yr + pos) = w;
+          reinterpret_cast<uint2*>(&tout[swz(4 * i32 + q)])[hf] = make_uint2(cvt2(o[0], o[1]), cvt2(o[2], o[3]));
         } else {
           *reinterpret_cast<float4*>(yr + pos) = make_float4(o[0], o[1], o[2], o[3]);
         }
@@ -328,21 +453,90 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
           if (pos + e < L) Io<IO>::st(yr, pos + e, o[e]);
       }
     }
+    if constexpr (sizeof(IO) == 2) {
+      if (full) {
+        lds_sync();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<uint4*>(yr + t0 + 8 * (l + 64 * h)) = tout[swz(l + 64 * h)];
+      }
+    }
   };
 
   // ---- full tiles, the next one in flight while the current one computes
+  // (two buffers used alternately, so nothing is copied between iterations;
+  // past the last tile the prefetch re-reads the last tile instead of
+  // branching)
   const int nfull = VEC ? (L >> 10) : 0;
-  TileIn<IO> nxt;
-  if (nfull > 0) nxt.load(x1r, vr, x2r, lane_off);
+  if constexpr (sizeof(IO) == 2) {
+    // coalesced 16-byte chunks DMA'd into LDS one tile ahead, read from
+    // there in the MFMA run layout
+    auto prefetch = [&](int64_t t0, uint4 (*tin)[128]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = unswz(64 * h + l);
+        dma16(x1r + t0 + 8 * c, &tin[0][64 * h]);
+        dma16(vr + t0 + 8 * c, &tin[1][64 * h]);
+        dma16(x2r + t0 + 8 * c, &tin[2][64 * h]);
+      }
+    };
+    const TileIn<IO> none{};
+    // tiles alternate between the two LDS buffers; each is written by the
+    // DMA while the other one is computed
+    // At the top of every tile after the first, the only operations issued
+    // after that tile's DMA are the previous tile's two 16-byte y stores,
+    // which may stay in flight.
+    if (nfull > 0) prefetch(0, tin_a);
+    int k = 0;
 #pragma unroll 1
-  for (int k = 0; k < nfull; ++k) {
-    const TileIn<IO> cur = nxt;
-    const int64_t t0 = static_cast<int64_t>(k) << 10;
-    if (k + 1 < nfull) nxt.load(x1r, vr, x2r, t0 + 1024 + lane_off);
-    bf16x8 um[NU][2];
-    tile(cur, t0, true, um);
-    __syncthreads();                           // sbuf reads done before the next tile writes
+    for (; k + 1 < nfull; k += 2) {
+      const int64_t t0 = static_cast<int64_t>(k) << 10;
+      if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
+      lds_sync();                         // tile k in tin_a; tin_b free
+      prefetch(t0 + 1024, tin_b);
+      {
+        bf16x8 um[NU][2];
+        tile(none, t0, true, um, tin_a, true);
+      }
+      wait_vmem<2>();
+      lds_sync();                         // tile k+1 in tin_b; tin_a free
+      if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
+      {
+        bf16x8 um[NU][2];
+        tile(none, t0 + 1024, true, um, tin_b, true);
+      }
+    }
+    if (k < nfull) {
+      if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
+      lds_sync();
+      bf16x8 um[NU][2];
+      tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true);
+    }
+  } else {
+    TileIn<IO> ta, tb;
+    if (nfull > 0) ta.load(x1r, vr, x2r, lane_off);
+    int k = 0;
+#pragma unroll 1
+    for (; k + 1 < nfull; k += 2) {
+      const int64_t t0 = static_cast<int64_t>(k) << 10;
+      tb.load(x1r, vr, x2r, t0 + 1024 + lane_off);
+      {
+        bf16x8 um[NU][2];
+        tile(ta, t0, true, um, tin_a, false);
+      }
+      const int64_t nxt = (static_cast<int64_t>(min(k + 2, nfull - 1)) << 10) + lane_off;
+      ta.load(x1r, vr, x2r, nxt);
+      {
+        bf16x8 um[NU][2];
+        tile(tb, t0 + 1024, true, um, tin_a, false);
+      }
+    }
+    if (k < nfull) {
+      bf16x8 um[NU][2];
+      tile(ta, static_cast<int64_t>(k) << 10, true, um, tin_a, false);
+    }
   }
+  lds_sync();
   if (nfull > 0 && (static_cast<int64_t>(nfull) << 10) == L) {
     if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
     return;
@@ -376,7 +570,8 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       }
     }
     bf16x8 um[NU][2];
-    tile(in, t0, false, um);
+    tile(in, t0, false, um, tin_a, false);
+    float (*sbuf)[33][17] = sbufs[0];
     const int64_t rem = L - t0;
     if (rem == 1024) {
       if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
@@ -404,7 +599,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       const float tot = fin + __shfl_xor(fin, 16);
       if (mine && part == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
     }
-    __syncthreads();                           // sbuf reads done before the next tile writes
+    lds_sync();                           // sbuf reads done before the next tile writes
   }
 }
 

@@ -72,7 +72,7 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
 
 template <int S, int T, typename IO, bool VEC>
 __global__ __launch_bounds__(T) void fftconv_kernel(
-    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, IO* __restrict__ y, int D, int L) {
   constexpr int P = S / T;
