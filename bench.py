@@ -10,7 +10,7 @@ Prints ONE JSON line.  Besides the headline it reports the roofline of the
 dominant kernel (HIP-event timing of the same launches), the other entry points
 at the same shape, and the fp64 CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 100] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -44,8 +44,8 @@ def kernel_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--algo", default="mfma", choices=["mfma", "fft", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")

@@ -147,6 +147,8 @@ static hipError_t launch_fir_io(const FirArgs& a, bool vec) {
 }
 
 hipError_t launch_fir(const FirArgs& a) {
+  // bf16 activations and up to 128 taps go to the matrix-core kernel
+  if (a.bf16 && a.K <= 128) return launch_fir_mfma(a);
   const bool vec = (a.L % 8 == 0) && aligned_all(16, a.x1, a.x2, a.v, a.y);
   return a.bf16 ? launch_fir_io<bf16_t>(a, vec) : launch_fir_io<float>(a, vec);
 }

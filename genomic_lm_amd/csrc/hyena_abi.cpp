@@ -97,7 +97,7 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, cons
   if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
   if (empty) return HYENA_OK;
   if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
-  if (B * D > 65535) return HYENA_ERR_UNSUPPORTED;   // grid.y
+  if (B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;   // grid.y
   hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
                    static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
   return from_hip(hyena::launch_fir(a));

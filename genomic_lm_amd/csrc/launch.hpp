@@ -64,7 +64,8 @@ struct ChunkArgs {
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
                                float* h, hipStream_t stream);
 
-hipError_t launch_fir(const FirArgs& a);
+hipError_t launch_fir(const FirArgs& a);        // picks the kernel below or the VALU one
+hipError_t launch_fir_mfma(const FirArgs& a);   // bf16, K <= 128
 
 // Sub-transform size S of the on-chip single-pass kernel for length L, or 0
 // when L is too long for it (L > 32768).

@@ -1,0 +1,156 @@
+// mfma_common.hpp -- pieces shared by the matrix-core kernels (chunk_mfma.hip,
+// fir_mfma.hip): bf16 operand vectors and splits, the 32x32x16 MFMA, the
+// per-lane token layout, and the LDS staging of 1024-token tiles.
+#pragma once
+
+#include "common.hpp"
+
+namespace hyena {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int MFMA_MAXN = 16;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row operands are computed once and must stay in registers: the empty
+// asm hides how they were made, so the compiler cannot recompute them (with
+// their exp calls) inside the tile loop to save registers.
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(w));
+  x = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// x = p0 + p1 + p2 + r with p_k = rne_bf16 of the remainder so far; |r| <= 2^-24 |x|
+__device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& p2) {
+  p0 = static_cast<__bf16>(x);
+  const float r1 = x - static_cast<float>(p0);
+  p1 = static_cast<__bf16>(r1);
+  p2 = static_cast<__bf16>(r1 - static_cast<float>(p1));
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair (one v_cvt_pk_bf16_f32), and back.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// split3 on a pair, each part a packed bf16 pair
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+  p0 = cvt2(a, b);
+  float ra = a - lo_f(p0), rb = b - hi_f(p0);
+  p1 = cvt2(ra, rb);
+  ra -= lo_f(p1);
+  rb -= hi_f(p1);
+  p2 = cvt2(ra, rb);
+}
+
+// token (within a 32-token block) of output register r / operand slot
+// (s, j) = r = 8s + j of a lane in half-wave hf
+__device__ __forceinline__ int blk_tok(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// 4 consecutive elements at [i, i+4) of a row, zero at and beyond L
+template <typename IO, bool VEC>
+__device__ __forceinline__ void ld4(const IO* row, int64_t i, int64_t L, float (&o)[4]) {
+  if constexpr (VEC) {
+    if (i + 4 <= L) {
+      if constexpr (sizeof(IO) == 2) {
+        const uint2 w = *reinterpret_cast<const uint2*>(row + i);
+        o[0] = __uint_as_float(w.x << 16);
+        o[1] = __uint_as_float(w.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(w.y << 16);
+        o[3] = __uint_as_float(w.y & 0xFFFF0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(row + i);
+        o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (i + e < L) ? Io<IO>::ld(row, i + e) : 0.0f;
+}
+
+// Raw storage of 4 consecutive activations (one run of a lane): 8 bytes of
+// bf16 or 16 bytes of fp32, loaded without conversion so that the next tile
+// can be in flight while the current one is computed.
+template <typename IO> struct Raw4;
+template <> struct Raw4<bf16_t> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t x = (e < 2) ? w.x : w.y;
+    return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+template <> struct Raw4<float> {
+  float4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+  }
+};
+
+// The three input runs of one lane for one tile.
+template <typename IO> struct TileIn {
+  Raw4<IO> a[4], b[4], g[4];     // x1, v, x2 at tokens base + 8q .. +3
+  __device__ __forceinline__ void load(const IO* x1r, const IO* vr, const IO* x2r, int64_t base) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q].load(x1r + base + 8 * q);
+      b[q].load(vr + base + 8 * q);
+      g[q].load(x2r + base + 8 * q);
+    }
+  }
+};
+
+// bf16 tiles move between HBM and LDS in 16-byte chunks (8 tokens), one
+// chunk per lane per instruction, which keeps every load and store fully
+// coalesced.  Chunk c = 4m + q holds tokens 32m + 8q .. +7 of block m and
+// lives in LDS slot swz(c) = 4m + ((q + m/4) & 3): the coalesced writes stay
+// conflict-free and so do the reads of a lane's run (block m, half hf),
+// which for a fixed q touch 16 distinct slots per 256 bytes.
+__device__ __forceinline__ int swz(int c) { return (c & ~3) | (((c & 3) + (c >> 4)) & 3); }
+
+__device__ __forceinline__ int unswz(int s) { return (s & ~3) | (((s & 3) - (s >> 4)) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte chunk per lane from global memory straight into LDS (no
+// registers): the wave writes 1 KB at `dst`, lane l at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+}
+
+// The workgroup is a single wave: its LDS operations execute in order, so
+// making LDS writes visible to the other lanes needs only that they have
+// completed and that the compiler keeps program order -- no s_barrier and, in
+// particular, no wait for outstanding global loads (the DMA of the next
+// tile), which a __syncthreads() fence would add.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding.  They retire in issue order, so this waits for everything
+// issued before the last N.  (s_waitcnt simm16 on gfx9: vmcnt[3:0] in bits
+// 3:0, expcnt in bits 6:4, lgkmcnt in bits 11:8, vmcnt[5:4] in bits 15:14;
+// expcnt and lgkmcnt are left free.)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace hyena

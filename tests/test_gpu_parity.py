@@ -69,6 +69,31 @@ def test_fir_small(io, K, L):
     gate(y, oracle_fir(w, K, taps=taps), io, label=f"fir K={K} L={L}")
 
 
+@pytest.mark.parametrize("K", [1, 2, 7, 33, 64, 100, 128])
+@pytest.mark.parametrize("L,B", [(1024, 1), (3000, 2), (4096, 1), (777, 1), (100, 1), (5120, 1)])
+def test_fir_mfma_cases(K, L, B):
+    """bf16 FIR with K <= 128 runs on the matrix cores: every diagonal count
+    (1..5), whole tiles, a ragged last tile, rows shorter than a tile, rows not
+    16-byte aligned (odd L), batch > 1."""
+    w = small("bf16", D=4, L=L, B=B)
+    d = DevWorkload(w)
+    taps = W.random_taps(K, w.D, seed=K + 1000, bf16=True)
+    log(f"fir/mfma K={K} L={L} B={B}")
+    y = G.fir_fwd(d.x1, d.x2, d.v, par_to_dev(taps), d.skip)
+    gate(y, oracle_fir(w, K, taps=taps), "bf16", label=f"fir/mfma K={K} L={L}")
+
+
+@pytest.mark.parametrize("K", [7, 128])
+def test_fir_mfma_fp32_taps(K):
+    """Taps that are not bf16 values take the two-part product path."""
+    w = small("bf16", D=8, L=4096)
+    d = DevWorkload(w)
+    taps = W.random_taps(K, w.D, seed=K + 2000, bf16=False)
+    assert not np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(taps)), taps)
+    y = G.fir_fwd(d.x1, d.x2, d.v, par_to_dev(taps), d.skip)
+    gate(y, oracle_fir(w, K, taps=taps), "bf16", label=f"fir/mfma fp32 taps K={K}")
+
+
 # ------------------------------------------------------------------ chunked
 CHUNK_CASES = [(1, 50), (7, 300), (64, 1000), (128, 1024), (1000, 4096), (1024, 3000),
                (1024, 5000), (4096, 8192), (8192, 8192), (2048, 1500)]
