@@ -23,18 +23,6 @@
 
 namespace hyena {
 
-__device__ __forceinline__ float2 real_spectrum_c(float2 ck, float2 cm, float2 w) {
-  float2 a = make_float2(ck.x + cm.x, ck.y - cm.y);
-  float2 b = make_float2(ck.x - cm.x, ck.y + cm.y);
-  return cscale(cadd(a, cmul_mi(cmul(w, b))), 0.5f);
-}
-
-__device__ __forceinline__ float2 inverse_pack_c(float2 zk, float2 zm, float2 w) {
-  float2 a = make_float2(zk.x + zm.x, zk.y - zm.y);
-  float2 b = make_float2(zk.x - zm.x, zk.y + zm.y);
-  return cscale(cadd(a, cmul_pi(cmul(cconj(w), b))), 0.5f);
-}
-
 constexpr int CHUNK_MAXN = 64;
 constexpr int CHUNK_NG = 16;             // modes per reduction group
 
@@ -104,7 +92,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     for (int i = 0; i < P; ++i) {
       const int k = t + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      hs[q][i] = real_spectrum_c(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+      hs[q][i] = real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
     }
     if (q == 0 && t == 0) h_nyq = a[0].x - a[0].y;
   }
@@ -138,7 +126,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       for (int i = 0; i < P; ++i) {
         const int k = t + T * i;
         const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-        z[i] = cmul(real_spectrum_c(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)), hs[q][i]);
+        z[i] = cmul(real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)), hs[q][i]);
       }
       if (q == 0 && t == 0) zm_nyq = (a[0].x - a[0].y) * h_nyq;
       __syncthreads();
@@ -151,7 +139,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
         float2 zmir = lds[lds_pad(kk)];
         if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
-        a[i] = inverse_pack_c(z[i], zmir, twiddle(2 * k + q, LG_N));
+        a[i] = inverse_pack(z[i], zmir, twiddle(2 * k + q, LG_N));
       }
       fft_inverse<S, T>(a, lds, t);
       if (q == 0) {

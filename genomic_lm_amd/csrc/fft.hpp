@@ -169,12 +169,15 @@ __device__ __forceinline__ void fft_from(float2 (&reg)[S / T], float2* lds, int 
 
 // Forward transform X[k] = sum_m x[m] exp(-2*pi*i*m*k/S), in place in
 // registers (strided natural order), using lds (lds_padded_size(S) complex) as
-// exchange space.  Every thread of the workgroup must call it.  On return lds
-// may still be read by other threads: synchronise before writing to it.
+// exchange space.  t is the thread's index among the T threads of this
+// transform; a workgroup may run several transforms side by side (each group
+// of T threads with its own lds), but every thread of the workgroup must call
+// it, since the passes are separated by workgroup barriers.  On return lds may
+// still be read by other threads: synchronise before writing to it.
 template <int S, int T>
 __device__ __forceinline__ void fft_forward(float2 (&reg)[S / T], float2* lds, int t) {
   static_assert(S % T == 0 && (S & (S - 1)) == 0, "power-of-two size, T | S");
-  static_assert(S / T == 4 || S / T == 8 || S / T == 16, "4, 8 or 16 points per thread");
+  static_assert(S / T == 2 || S / T == 4 || S / T == 8 || S / T == 16, "2, 4, 8 or 16 points per thread");
   fft_from<S, T, 1>(reg, lds, t);
 }
 
@@ -186,6 +189,28 @@ __device__ __forceinline__ void fft_inverse(float2 (&reg)[S / T], float2* lds, i
   fft_forward<S, T>(reg, lds, t);
 #pragma unroll
   for (int i = 0; i < S / T; ++i) reg[i].y = -reg[i].y;
+}
+
+// ------------------------------------------------------------- real signals
+// A real length-Nfft signal x is transformed as the complex length-M signal
+// c[m] = x[2m] + i x[2m+1], M = Nfft / 2.  Its spectrum X[K] (K < M) follows
+// from C[K] and C[M-K]:
+//   X[K] = (C[K] + conj C[M-K]) / 2 - i w (C[K] - conj C[M-K]) / 2,
+//   w = exp(-2 pi i K / Nfft),
+// and the inverse real transform takes the length-M complex input
+//   C_z[K] = ((Z[K] + conj Z[M-K]) + i conj(w) (Z[K] - conj Z[M-K])) / 2,
+// whose unnormalised inverse DFT, divided by M, is z[2m] + i z[2m+1].  At
+// K = 0 the partner Z[M] (the real Nyquist bin) replaces Z[M-0].
+__device__ __forceinline__ float2 real_spectrum(float2 ck, float2 cm, float2 w) {
+  const float2 a = make_float2(ck.x + cm.x, ck.y - cm.y);
+  const float2 b = make_float2(ck.x - cm.x, ck.y + cm.y);
+  return cscale(cadd(a, cmul_mi(cmul(w, b))), 0.5f);
+}
+
+__device__ __forceinline__ float2 inverse_pack(float2 zk, float2 zm, float2 w) {
+  const float2 a = make_float2(zk.x + zm.x, zk.y - zm.y);
+  const float2 b = make_float2(zk.x - zm.x, zk.y + zm.y);
+  return cscale(cadd(a, cmul_pi(cmul(cconj(w), b))), 0.5f);
 }
 
 }  // namespace hyena

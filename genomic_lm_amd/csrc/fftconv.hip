@@ -28,22 +28,6 @@
 
 namespace hyena {
 
-// U[K] = (C[K] + conj C[M-K]) / 2 - i w (C[K] - conj C[M-K]) / 2, w = exp(-2 pi i K / Nfft)
-__device__ __forceinline__ float2 real_spectrum(float2 ck, float2 cm, float2 w) {
-  float2 a = make_float2(ck.x + cm.x, ck.y - cm.y);
-  float2 b = make_float2(ck.x - cm.x, ck.y + cm.y);
-  float2 r = cadd(a, cmul_mi(cmul(w, b)));
-  return cscale(r, 0.5f);
-}
-
-// C_z[K] = ((Z[K] + conj Z[M-K]) + i conj(w) (Z[K] - conj Z[M-K])) / 2
-__device__ __forceinline__ float2 inverse_pack(float2 zk, float2 zm, float2 w) {
-  float2 a = make_float2(zk.x + zm.x, zk.y - zm.y);
-  float2 b = make_float2(zk.x - zm.x, zk.y + zm.y);
-  float2 r = cadd(a, cmul_pi(cmul(cconj(w), b)));
-  return cscale(r, 0.5f);
-}
-
 // a[i] = (h[2m], h[2m+1]) for m = t + T*i, zero at and beyond L.
 template <int P, int T>
 __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, const float* res,

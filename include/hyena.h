@@ -137,8 +137,14 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
  *   log_poles, residues : (D, N) fp32, 1 <= N <= HYENA_MAX_MODES
  *   skip : (D) fp32 or NULL
  *   workspace : device buffer of at least hyena_fftconv_workspace_size(...)
- *               bytes (may be NULL when that size is 0), contents scratch.
- * Nfft > HYENA_MAX_FFT_LEN -> HYENA_ERR_UNSUPPORTED.
+ *               bytes, 16-byte aligned, owned by the caller, contents
+ *               scratch (may be NULL when that size is 0).  Rows with
+ *               L <= 32768 are transformed on chip and need none; longer rows
+ *               go through it in batches of rows, 32 * Nfft / 4 bytes per row,
+ *               at most 256 MiB.  Calls sharing one workspace must be ordered
+ *               (same stream).
+ * Nfft > HYENA_MAX_FFT_LEN -> HYENA_ERR_UNSUPPORTED; workspace NULL, short or
+ * misaligned when one is needed -> HYENA_ERR_WORKSPACE.
  */
 hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  const float* log_poles, const float* residues,
@@ -146,7 +152,8 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
                                  void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes hyena_fftconv_fwd needs for this shape (0 when the FFT runs on chip). */
+/* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when the FFT runs
+ * on chip (L <= 32768) or the shape is empty or unsupported. */
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                     hyena_dtype_t io);
 

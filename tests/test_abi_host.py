@@ -98,8 +98,25 @@ def test_fftconv_validation():
                            (10, 1 << 20, G.ERR_UNSUPPORTED)]:
         a = list(good); a[idx] = val
         assert f(*a) == want, (idx, val)
-    assert G.lib().hyena_fftconv_workspace_size(1, 4, 1024, 16, G.BF16) == 0
-    assert G.lib().hyena_fftconv_workspace_size(0, 4, 1024, 16, G.BF16) == 0
+    ws = G.lib().hyena_fftconv_workspace_size
+    assert ws(1, 4, 1024, 16, G.BF16) == 0                     # on-chip path, no workspace
+    assert ws(1, 4, 32768, 16, G.BF16) == 0
+    assert ws(0, 4, 1024, 16, G.BF16) == 0
+    # four-step path: 32 S bytes per row (u and h, two parity halves, complex
+    # fp32), rows batched up to 256 MiB
+    assert ws(1, 4, 32769, 16, G.BF16) == 4 * 32 * 32768
+    assert ws(2, 3, 65536, 16, G.F32) == 6 * 32 * 32768
+    assert ws(1, 4096, 262144, 16, G.BF16) == 64 * 32 * 131072
+    assert ws(1, 4096, 1 << 19, 16, G.BF16) == 32 * 32 * 262144
+    assert ws(1, 4, (1 << 19) + 1, 16, G.BF16) == 0             # beyond the largest FFT
+    # missing, short or misaligned workspace is refused before any launch
+    big = list(good); big[10] = 40000
+    assert f(*big) == G.ERR_WORKSPACE
+    need = ws(1, 4, 40000, 16, G.BF16)
+    big[12] = FAKE; big[13] = need - 1
+    assert f(*big) == G.ERR_WORKSPACE
+    big[12] = P(0x10008); big[13] = need
+    assert f(*big) == G.ERR_WORKSPACE
 
 
 def test_chunk_validation():

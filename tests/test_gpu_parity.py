@@ -56,6 +56,42 @@ def test_fftconv_small(io, L):
     gate(y, ref, io, label=f"fftconv L={L}")
 
 
+# Rows longer than one CU's LDS holds: the three-kernel four-step path through
+# a workspace.  Lengths cover each row-transform size (S/256 = 128 ... 1024),
+# odd lengths (the pair loads' ragged tail), and B*D above one row batch.
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("L,B,D", [(32769, 1, 3), (40000, 2, 2), (65536, 1, 2), (65001, 1, 2),
+                                   (131072, 1, 2), (262143, 1, 1), (300000, 1, 1)])
+def test_fftconv_large(io, L, B, D):
+    w = small(io, D=D, L=L, B=B)
+    d = DevWorkload(w)
+    ws = G.fftconv_workspace_size(B, D, L, w.N, d.x1.dtype)
+    log(f"fftconv large io={io} B={B} D={D} L={L} workspace={ws}")
+    assert ws > 0
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    ref, _ = oracle_modal(w)
+    gate(y, ref, io, label=f"fftconv L={L}")
+
+
+def test_fftconv_large_row_batches():
+    # 300 rows of S = 32768: two row batches (256 + 44) through one workspace
+    w = small("bf16", D=100, L=33000, B=3)
+    d = DevWorkload(w)
+    log("fftconv large B=3 D=100 L=33000")
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    ref, _ = oracle_modal(w)
+    gate(y, ref, "bf16", label="fftconv 300 rows")
+
+
+def test_fftconv_large_workspace_errors():
+    w = small("bf16", D=1, L=40000)
+    d = DevWorkload(w)
+    need = G.fftconv_workspace_size(1, 1, 40000, w.N, d.x1.dtype)
+    short = torch.empty(need - 16, dtype=torch.uint8, device=d.x1.device)
+    with pytest.raises(G.HyenaError, match="WORKSPACE"):
+        G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip, workspace=short)
+
+
 # ------------------------------------------------------------------ FIR
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("K,L", [(1, 100), (3, 1), (7, 2048), (7, 3001), (8, 4096), (9, 100),
@@ -297,3 +333,12 @@ def test_config_262k_chunked():
         y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 4096, d.skip, algo=algo)
         gate(y, ref, "bf16", rows, label=f"262k chunk/{algo} C=4096")
         state_gate(s, ref_s, rows, label=f"262k chunk/{algo}")
+
+
+def test_config_262k_single_pass():
+    # the whole 262144-token row as one FFT product of length 524288
+    w, d = _full("262k")
+    rows = sample_rows(w.D, k=4)
+    ref, _ = oracle_modal(w, rows)
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    gate(y, ref, "bf16", rows, label="262k fftconv N=524288")
