@@ -72,9 +72,10 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // used by alternate tiles, so a tile's writes never meet the previous
   // tile's reads
   __shared__ float sbufs[1][2][33][17];
-  // staged x1, v, x2 tiles (bf16, swizzled chunks), two tiles in turn; the
-  // y tile is staged over the x1 slice of its own tile, already consumed
+  // staged x1, v, x2 tiles (bf16, swizzled chunks), two tiles in turn, and
+  // the staged y tile
   __shared__ uint4 tin_a[3][128], tin_b[3][128];
+  __shared__ uint4 tout[128];
 
   const int l = threadIdx.x;
   const int hf = l >> 5;                      // half-wave
@@ -149,32 +150,45 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   pin(a3);
   pin(a4);
   float carry = (part == 0 && n_sc < N && state_in) ? state_in[row * N + n_sc] : 0.0f;
+  // consume the load here: a load still pending at the loop would make the
+  // compiler wait for all vector memory (the DMAs in flight included) at its
+  // first use in every iteration
+  asm volatile("" : "+v"(carry));
 
   // One 1024-token tile: inputs in `in` (u = x1 * v, gate x2), output to y.
   // Returns nothing; updates `carry` (state after the tile, in part-0 lanes)
   // and leaves sbuf holding the state before each block of the tile.
   // Runs of the tile: from `in` (registers) or, for bf16 tiles staged in
-  // LDS, straight from the staged chunks when they are needed.
+  // LDS, from the staged chunks.  All inputs are read first; `released` is
+  // called once they are in registers, so the caller may refill `tin`.
   auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2],
-                  uint4 (*tin)[128], bool staged) {
+                  uint4 (*tin)[128], bool staged, auto&& released) {
     float (*sbuf)[33][17] = sbufs[0];
-    uint4* tout = tin[0];
-    auto run = [&](int arr, int q) {
-      Raw4<IO> r;
-      if constexpr (sizeof(IO) == 2) {
-        if (staged) {
-          r.w = reinterpret_cast<const uint2*>(&tin[arr][swz(4 * i32 + q)])[hf];
-          return r;
+    Raw4<IO> rx[4], rv[4], rg[4];              // x1, v, gate x2
+    if constexpr (sizeof(IO) == 2) {
+      if (staged) {
+        read_staged_runs(tin, i32, hf, rx, rv, rg);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          rx[q] = in.a[q];
+          rv[q] = in.b[q];
+          rg[q] = in.g[q];
         }
       }
-      r = arr == 0 ? in.a[q] : arr == 1 ? in.b[q] : in.g[q];
-      return r;
-    };
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rx[q] = in.a[q];
+        rv[q] = in.b[q];
+        rg[q] = in.g[q];
+      }
+    }
     float su[16];                              // skip * u, for the output
     u32x4 uw[NU][2];                           // parts of u as packed bf16 pairs
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const Raw4<IO> ra = run(0, q), rb = run(1, q);
+      const Raw4<IO> ra = rx[q], rb = rv[q];
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
         const int r = 4 * q + e;
@@ -201,6 +215,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       um[k][0] = __builtin_bit_cast(bf16x8, uw[k][0]);
       um[k][1] = __builtin_bit_cast(bf16x8, uw[k][1]);
     }
+    released();
     // block-local end states, transposed: lane = mode column, 16 blocks per lane
     f32x16 ce = {};
 #pragma unroll
@@ -289,11 +304,10 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
-      const Raw4<IO> rg = run(2, q);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        o[e] = fmaf(rg.get(e), cz[r], su[r]);
+        o[e] = fmaf(rg[q].get(e), cz[r], su[r]);
       }
       const int64_t pos = t0 + lane_off + 8 * q;
       if (full) {
@@ -336,36 +350,52 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       }
     };
     const TileIn<IO> none{};
-    // tiles alternate between the two LDS buffers; each is written by the
-    // DMA while the other one is computed
-    // At the top of every tile after the first, the only operations issued
-    // after that tile's DMA are the previous tile's two 16-byte y stores,
-    // which may stay in flight.
+    // Two tiles in flight: tile k is read out of its buffer at the top of
+    // its computation, and the buffer is refilled at once with tile k + 2.
+    // vmcnt retires in issue order, so waiting for tile k means allowing
+    // the operations issued after its DMA to stay in flight: the y stores of
+    // tiles k-2 and k-1 (2 each) and the DMA of tile k+1 (6), where they
+    // exist.
     if (nfull > 0) prefetch(0, tin_a);
+    if (nfull > 1) prefetch(1024, tin_b);
     int k = 0;
 #pragma unroll 1
     for (; k + 1 < nfull; k += 2) {
       const int64_t t0 = static_cast<int64_t>(k) << 10;
-      if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
-      lds_sync();                         // tile k in tin_a; tin_b free
-      prefetch(t0 + 1024, tin_b);
-      {
-        bf16x8 um[NU][2];
-        tile(none, t0, true, um, tin_a, true);
+      if (k == 0) {
+        wait_vmem<6>();                   // nfull > 1 here: DMA(1) may fly
+      } else if (k + 1 < nfull) {
+        wait_vmem<10>();
+      } else {
+        wait_vmem<4>();
       }
-      wait_vmem<2>();
-      lds_sync();                         // tile k+1 in tin_b; tin_a free
-      if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
+      lds_sync();                         // tile k in tin_a
       {
         bf16x8 um[NU][2];
-        tile(none, t0 + 1024, true, um, tin_b, true);
+        tile(none, t0, true, um, tin_a, true, [&] {
+          lds_sync();                     // tin_a read out
+          if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
+        });
+      }
+      if (k + 2 < nfull) {
+        if (k == 0) wait_vmem<8>(); else wait_vmem<10>();
+      } else {
+        if (k == 0) wait_vmem<2>(); else wait_vmem<4>();
+      }
+      lds_sync();                         // tile k+1 in tin_b
+      {
+        bf16x8 um[NU][2];
+        tile(none, t0 + 1024, true, um, tin_b, true, [&] {
+          lds_sync();                     // tin_b read out
+          if (k + 3 < nfull) prefetch(t0 + 3072, tin_b);
+        });
       }
     }
     if (k < nfull) {
-      if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
+      if (k == 0) wait_vmem<0>(); else wait_vmem<4>();
       lds_sync();
       bf16x8 um[NU][2];
-      tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true);
+      tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true, [] {});
     }
   } else {
     TileIn<IO> ta, tb;
@@ -377,18 +407,18 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       tb.load(x1r, vr, x2r, t0 + 1024 + lane_off);
       {
         bf16x8 um[NU][2];
-        tile(ta, t0, true, um, tin_a, false);
+        tile(ta, t0, true, um, tin_a, false, [] {});
       }
       const int64_t nxt = (static_cast<int64_t>(min(k + 2, nfull - 1)) << 10) + lane_off;
       ta.load(x1r, vr, x2r, nxt);
       {
         bf16x8 um[NU][2];
-        tile(tb, t0 + 1024, true, um, tin_a, false);
+        tile(tb, t0 + 1024, true, um, tin_a, false, [] {});
       }
     }
     if (k < nfull) {
       bf16x8 um[NU][2];
-      tile(ta, static_cast<int64_t>(k) << 10, true, um, tin_a, false);
+      tile(ta, static_cast<int64_t>(k) << 10, true, um, tin_a, false, [] {});
     }
   }
   lds_sync();
@@ -425,7 +455,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       }
     }
     bf16x8 um[NU][2];
-    tile(in, t0, false, um, tin_a, false);
+    tile(in, t0, false, um, tin_a, false, [] {});
     float (*sbuf)[33][17] = sbufs[0];
     const int64_t rem = L - t0;
     if (rem == 1024) {
