@@ -59,7 +59,10 @@ __device__ __forceinline__ void build_state_weights(float lam_n, int part, int h
   }
 }
 
-template <typename IO, bool VEC>
+// VEC: rows of whole 16-byte chunks, 16-byte aligned (full tiles take the
+// unchecked path).  PIPE (bf16, VEC, L >= 2048): at least two full tiles, so
+// the first two DMAs are issued without a branch.
+template <typename IO, bool VEC, bool PIPE>
 __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
@@ -90,6 +93,54 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   IO* yr = y + row * L;
   const float sk = skip ? skip[c] : 0.0f;
   const int lane_off = 32 * i32 + 4 * hf;     // token offset of run 0 within a tile
+  const int nfull = VEC ? (L >> 10) : 0;      // full 1024-token tiles
+  // bf16 tiles: coalesced 16-byte chunks DMA'd into LDS, read from there in
+  // the MFMA run layout
+  auto prefetch = [&](int64_t t0, uint4 (*tin)[128]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = unswz(64 * h + l);
+      dma16(x1r + t0 + 8 * ch, &tin[0][64 * h]);
+      dma16(vr + t0 + 8 * ch, &tin[1][64 * h]);
+      dma16(x2r + t0 + 8 * ch, &tin[2][64 * h]);
+    }
+  };
+
+  // ---- per-lane parameters, then the first two tiles in flight while the
+  // per-row constants are set up
+  const int part = i32 >> 4;                  // scan lane: mode n_sc, part 0 or 1
+  const int n_sc = i32 & 15;
+  // Every load is issued unconditionally from an in-bounds address (index
+  // clamped, the value dropped afterwards), so that they are all in flight
+  // together.
+  const float lam_ld = lamc[min(n_sc, N - 1)];
+  float g_lam[8], g_res[8];                   // modes 8 hf + j of G
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = min(8 * hf + j, N - 1);
+    g_lam[j] = lamc[n];
+    g_res[j] = resc[n];
+  }
+  const float* sp = state_in ? state_in + row * N + min(n_sc, N - 1) : lamc;
+  const float st_ld = *sp;
+  // Wait for the parameters before the first DMAs: with only these loads
+  // outstanding the wait costs their latency alone, whereas a wait placed
+  // after the DMAs is compiled as a wait for everything.
+  asm volatile("" ::"v"(lam_ld), "v"(st_ld), "v"(g_lam[0]), "v"(g_lam[1]), "v"(g_lam[2]),
+               "v"(g_lam[3]), "v"(g_lam[4]), "v"(g_lam[5]), "v"(g_lam[6]), "v"(g_lam[7]),
+               "v"(g_res[0]), "v"(g_res[1]), "v"(g_res[2]), "v"(g_res[3]), "v"(g_res[4]),
+               "v"(g_res[5]), "v"(g_res[6]), "v"(g_res[7]) : "memory");
+  if constexpr (sizeof(IO) == 2) {
+    if (PIPE || nfull > 0) prefetch(0, tin_a);
+    if (PIPE || nfull > 1) prefetch(1024, tin_b);
+  }
+
+  const float lam_n = (n_sc < N) ? lam_ld : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (8 * hf + j >= N) g_res[j] = 0.0f;
+  }
+  float carry = (part == 0 && n_sc < N && state_in) ? st_ld : 0.0f;
 
   // ---- per-row constants
   // h[d], d < 32
@@ -118,19 +169,15 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   bf16x8 gm[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int n = 8 * hf + j;
-    const float val = (n < N) ? resc[n] * expf(lamc[n] * static_cast<float>(i32 + 1)) : 0.0f;
+    const float val = g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
     __bf16 a0, a1, a2;
     split3(val, a0, a1, a2);
     gm[0][j] = a0;
     gm[1][j] = a1;
     gm[2][j] = a2;
   }
-  // scan lane: mode n (part 0 or 1 of the column pair) for all 32 blocks;
-  // padded modes have p = 1 and R = 0
-  const int part = i32 >> 4;
-  const int n_sc = i32 & 15;
-  const float lam_n = (n_sc < N) ? lamc[n_sc] : 0.0f;
+  // scan lane: mode n_sc (part 0 or 1 of the column pair) for all 32
+  // blocks; padded modes have p = 1 and R = 0
   bf16x8 pa[2], pb[2], pc[2];
   build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
   float a1 = expf(lam_n * 32.0f), a2 = expf(lam_n * 64.0f);
@@ -149,10 +196,9 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   pin(a2);
   pin(a3);
   pin(a4);
-  float carry = (part == 0 && n_sc < N && state_in) ? state_in[row * N + n_sc] : 0.0f;
-  // consume the load here: a load still pending at the loop would make the
-  // compiler wait for all vector memory (the DMAs in flight included) at its
-  // first use in every iteration
+  // consume the state load here: a load still pending at the loop would make
+  // the compiler wait for all vector memory (the DMAs in flight included) at
+  // its first use in every iteration
   asm volatile("" : "+v"(carry));
 
   // One 1024-token tile: inputs in `in` (u = x1 * v, gate x2), output to y.
@@ -250,7 +296,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       own[q] = x[4 * q + 3];
-      oth[q] = __shfl_xor(own[q], 32);
+      oth[q] = xor32(own[q], hf);
     }
     // run rho = 2q + half covers blocks 4*rho .. 4*rho+3; cin[rho] = state before it
     float cin[9];
@@ -275,7 +321,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     sbuf[part][0][n_sc] = cin[0];
     {
       const float fin = cin[8];
-      const float tot = fin + __shfl_xor(fin, 16);
+      const float tot = fin + xor16(fin, l);
       carry = (part == 0) ? tot : 0.0f;
     }
     lds_sync();
@@ -336,28 +382,14 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // (two buffers used alternately, so nothing is copied between iterations;
   // past the last tile the prefetch re-reads the last tile instead of
   // branching)
-  const int nfull = VEC ? (L >> 10) : 0;
   if constexpr (sizeof(IO) == 2) {
-    // coalesced 16-byte chunks DMA'd into LDS one tile ahead, read from
-    // there in the MFMA run layout
-    auto prefetch = [&](int64_t t0, uint4 (*tin)[128]) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = unswz(64 * h + l);
-        dma16(x1r + t0 + 8 * c, &tin[0][64 * h]);
-        dma16(vr + t0 + 8 * c, &tin[1][64 * h]);
-        dma16(x2r + t0 + 8 * c, &tin[2][64 * h]);
-      }
-    };
     const TileIn<IO> none{};
     // Two tiles in flight: tile k is read out of its buffer at the top of
     // its computation, and the buffer is refilled at once with tile k + 2.
     // vmcnt retires in issue order, so waiting for tile k means allowing
     // the operations issued after its DMA to stay in flight: the y stores of
     // tiles k-2 and k-1 (2 each) and the DMA of tile k+1 (6), where they
-    // exist.
-    if (nfull > 0) prefetch(0, tin_a);
-    if (nfull > 1) prefetch(1024, tin_b);
+    // exist.  Tiles 0 and 1 were issued before the constant setup.
     int k = 0;
 #pragma unroll 1
     for (; k + 1 < nfull; k += 2) {
@@ -488,27 +520,22 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   }
 }
 
-template <typename IO>
-static hipError_t launch_mfma_io(const ChunkArgs& a, bool vec) {
+template <typename IO, bool VEC, bool PIPE>
+static hipError_t launch_mfma_k(const ChunkArgs& a) {
   dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
-  const IO* x1 = static_cast<const IO*>(a.x1);
-  const IO* x2 = static_cast<const IO*>(a.x2);
-  const IO* v = static_cast<const IO*>(a.v);
-  IO* y = static_cast<IO*>(a.y);
-  if (vec)
-    chunk_mfma_kernel<IO, true><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L);
-  else
-    chunk_mfma_kernel<IO, false><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L);
+  chunk_mfma_kernel<IO, VEC, PIPE><<<grid, block, 0, a.stream>>>(
+      static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
+      a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (a.N > MFMA_MAXN) return hipErrorInvalidValue;
-  const size_t esz = a.bf16 ? 2 : 4;
-  const bool vec = (a.L % 4 == 0) && aligned_all(4 * esz, a.x1, a.x2, a.v, a.y);
-  return a.bf16 ? launch_mfma_io<bf16_t>(a, vec) : launch_mfma_io<float>(a, vec);
+  const int esz = a.bf16 ? 2 : 4;
+  const bool vec = (a.L % (16 / esz) == 0) && aligned_all(16, a.x1, a.x2, a.v, a.y);
+  if (!a.bf16) return vec ? launch_mfma_k<float, true, false>(a) : launch_mfma_k<float, false, false>(a);
+  if (!vec) return launch_mfma_k<bf16_t, false, false>(a);
+  return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true>(a) : launch_mfma_k<bf16_t, true, false>(a);
 }
 
 }  // namespace hyena

@@ -126,6 +126,22 @@ __device__ __forceinline__ int swz(int c) { return (c & ~3) | (((c & 3) + (c >> 
 
 __device__ __forceinline__ int unswz(int s) { return (s & ~3) | (((s & 3) - (s >> 4)) & 3); }
 
+// x of lane l ^ 32 (the other half-wave).  v_permlane32_swap exchanges the
+// upper half-wave of its first operand with the lower half-wave of its
+// second; with x in both, the first result holds lanes 0..31 of x in both
+// halves and the second lanes 32..63.  A VALU op, unlike ds_bpermute.
+__device__ __forceinline__ float xor32(float x, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(hf ? r[0] : r[1]);
+}
+
+// x of lane l ^ 16.  v_permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second.
+__device__ __forceinline__ float xor16(float x, int l) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((l & 16) ? r[0] : r[1]);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One 16-byte chunk per lane from global memory straight into LDS (no
