@@ -184,6 +184,20 @@ def main():
             "fir7": lambda: G.fir_fwd(x1, x2, v, taps7, skip, out=y),
             "fir128": lambda: G.fir_fwd(x1, x2, v, taps128, skip, out=y),
         }
+        # the same prefill as 32 calls of one chunk each, the state handed over
+        xs = [(t[..., t0:t0 + CHUNK].contiguous() for t in (x1, x2, v)) for t0 in range(0, L, CHUNK)]
+        xs = [tuple(g) for g in xs]
+        ys = [torch.empty_like(c[0]) for c in xs]
+        sts = [torch.empty_like(st), torch.empty_like(st)]
+
+        def per_chunk_calls():
+            s_in = None
+            for i, (a, b, c) in enumerate(xs):
+                G.chunk_fwd(a, b, c, lam, res, CHUNK, skip, state_in=s_in, algo=args.algo,
+                            out=ys[i], state_out=sts[i & 1])
+                s_in = sts[i & 1]
+
+        runs[f"chunk_{args.algo}_x{len(xs)}_calls"] = per_chunk_calls
         for name, fn in runs.items():
             t = timed(fn, comp_steps, 2, stream)
             comps[name] = {"ms": round(t * 1e3, 4), "Gtc_per_s": round(tc / t / 1e9, 2),

@@ -174,6 +174,25 @@ def test_chunk_resume_matches_single_call(algo):
         assert d_ <= 2e-2 * scale
 
 
+@pytest.mark.parametrize("algo", ["mfma", "fft"])
+def test_chunk_state_in_place(algo):
+    """state_out may be the state_in buffer: per-chunk calls updating one cache."""
+    w = small("bf16", D=8, L=3072)
+    d = DevWorkload(w)
+    C = 1024
+    ref, ref_s = oracle_modal(w)
+    st = torch.zeros((1, w.D, w.N), dtype=torch.float32, device=d.x1.device)
+    ys = []
+    for t0 in range(0, w.L, C):
+        log(f"in-place state algo={algo} t0={t0}")
+        sl = [t[..., t0:t0 + C].contiguous() for t in (d.x1, d.x2, d.v)]
+        yc, s_out = G.chunk_fwd(*sl, d.lam, d.res, C, d.skip, state_in=st, state_out=st, algo=algo)
+        assert s_out.data_ptr() == st.data_ptr()
+        ys.append(yc)
+    gate(torch.cat(ys, -1), ref, "bf16", label=f"in-place state {algo}")
+    state_gate(st, ref_s, label=f"in-place state {algo}")
+
+
 def test_chunked_equals_single_pass_on_gpu():
     w = small("bf16", D=8, L=32768)
     d = DevWorkload(w)
