@@ -35,8 +35,20 @@ What it computes (plain definitions, written out, in fp64):
   model card, §Implementation Notes 'Custom cache', and Evo1-1.5-7B-8K model
   card, §Implementation Notes 'Cache subclass').
 
+* Decode from the per-layer caches.  The hcl cache is the modal state
+  (Evo2-7B-262K model card, §Implementation Notes 'Custom cache': IIR inference
+  params for hcl, FIR inference params for hcm / hcs; Evo1-1.5-7B-8K model
+  card, §Implementation Notes 'Cache subclass': the Hyena params hold the FIR
+  window and the IIR modal state).  One modal step is the state recurrence
+  s_n <- p_n s_n + u followed by z = sum_n R_n s_n (the same z as the
+  convolution, since z[t] = sum_n R_n s_n(t)).  The FIR cache is the window of
+  the last K-1 values of u; a call continuing a sequence convolves over the
+  window followed by its own u, and leaves the last K-1 values of that
+  concatenation as the new window.
+
 Arrays are channel-major: activations (B, D, L), parameters (D, N) / (D,) /
-(D, K), state (B, D, N).  Everything is upcast to fp64 first.
+(D, K), state (B, D, N), FIR window (B, D, K-1) oldest first.  Everything is
+upcast to fp64 first.
 """
 from __future__ import annotations
 
@@ -46,6 +58,7 @@ import scipy.fft
 __all__ = [
     "modal_filter", "conv_direct", "conv_fft", "causal_conv",
     "hyena_fwd", "fir_fwd", "modal_state", "chunk_fwd", "next_pow2",
+    "modal_decode", "fir_fwd_window",
 ]
 
 DIRECT_MAX_L = 4096      # direct O(L^2) sum up to this length, FFT above
@@ -181,3 +194,52 @@ def chunk_fwd(x1, x2, v, log_poles, residues, skip, C: int, state_in=None,
     if return_states:
         return y, s, states
     return y, s
+
+
+def modal_decode(x1, x2, v, log_poles, residues, skip, state_in=None):
+    """One decode step of the modal operator from its cached state, fp64.
+
+    x1, x2, v are the token's three streams, (B, D).  The cache holds
+    s_n = s_n(t-1) (zero for an empty prefix); the step updates it to
+    s_n(t) = p_n s_n(t-1) + u_t, p_n = exp(lam_n), and outputs
+    y_t = x2_t * sum_n R_n s_n(t) + skip * u_t.
+    Returns y (B, D) and the new state (B, D, N).
+    """
+    x1 = np.asarray(x1, dtype=np.float64)
+    x2 = np.asarray(x2, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lam = np.asarray(log_poles, dtype=np.float64)
+    R = np.asarray(residues, dtype=np.float64)
+    B, D = x1.shape
+    s = (np.zeros((B, D, lam.shape[1])) if state_in is None
+         else np.asarray(state_in, dtype=np.float64))
+    u = x1 * v
+    s = np.exp(lam)[None] * s + u[:, :, None]
+    z = np.einsum("dn,bdn->bd", R, s)
+    sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
+    return x2 * z + sk[None, :] * u, s
+
+
+def fir_fwd_window(x1, x2, v, taps, skip, window_in=None):
+    """Explicit-FIR operator continuing a sequence from its cached window, fp64.
+
+    window_in (B, D, K-1) holds u of the K-1 tokens before this call, oldest
+    first (zeros, or None, for a fresh sequence).  With e the window followed
+    by this call's u, z[t] = sum_{k<K} w[c,k] e[K-1+t-k].  Returns y (B, D, L)
+    and the new window: the last K-1 entries of e.
+    """
+    x1 = np.asarray(x1, dtype=np.float64)
+    x2 = np.asarray(x2, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    w = np.asarray(taps, dtype=np.float64)
+    B, D, L = x1.shape
+    K = w.shape[1]
+    win = (np.zeros((B, D, K - 1)) if window_in is None
+           else np.asarray(window_in, dtype=np.float64))
+    u = x1 * v
+    e = np.concatenate([win, u], axis=-1)
+    z = np.zeros_like(u)
+    for k in range(K):
+        z += w[None, :, k:k + 1] * e[..., K - 1 - k:K - 1 - k + L]
+    sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
+    return x2 * z + sk[None, :, None] * u, e[..., e.shape[-1] - (K - 1):]

@@ -309,10 +309,76 @@ def pin_scale_equivariance(O):
     assert np.all(err <= 1e-12), err
 
 
+# ---------------------------------------------------------------- decode / caches
+def pin_decode_after_prefill(O):
+    """Prefill L tokens, then decode T more one at a time from the cached
+    state: equals the single-pass operator over all L + T tokens (computed by
+    the convolution, not the recurrence)."""
+    rng = _rng(30)
+    B, D, N, L, T = 2, 3, 16, 300, 40
+    lam, R = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, B, D, L + T))
+    skip = rng.normal(size=D)
+    y_full = O.hyena_fwd(x1, x2, v, lam, R, skip)
+    y_pre, s = O.chunk_fwd(x1[..., :L], x2[..., :L], v[..., :L], lam, R, skip, 128)
+    ys = [y_pre]
+    for t in range(L, L + T):
+        yt, s = O.modal_decode(x1[..., t], x2[..., t], v[..., t], lam, R, skip, state_in=s)
+        ys.append(yt[..., None])
+    y = np.concatenate(ys, axis=-1)
+    assert np.max(np.abs(y - y_full)) <= 1e-10 * np.max(np.abs(y_full))
+    # decoding from an empty prefix
+    s = None
+    for t in range(T):
+        yt, s = O.modal_decode(x1[..., t], x2[..., t], v[..., t], lam, R, skip, state_in=s)
+        ref = O.hyena_fwd(x1[..., :t + 1], x2[..., :t + 1], v[..., :t + 1], lam, R, skip)[..., t]
+        assert np.max(np.abs(yt - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), t
+
+
+def pin_decode_impulse_rational(O):
+    """A unit impulse decoded step by step gives h[t] = sum_n R_n p_n^t exactly
+    (rational poles and residues, fractions.Fraction)."""
+    poles = [Fraction(1, 2), Fraction(3, 4), Fraction(5, 8)]      # p = exp(lam) > 0
+    res = [Fraction(1), Fraction(-2, 3), Fraction(5, 4)]
+    lam = np.log(np.array([float(p) for p in poles]))[None]
+    R = np.array([float(r) for r in res])[None]
+    s = None
+    for t in range(12):
+        one = np.array([[1.0 if t == 0 else 0.0]])
+        yt, s = O.modal_decode(one, np.ones((1, 1)), np.ones((1, 1)), lam, R, None, state_in=s)
+        exact = sum(r * p ** t for r, p in zip(res, poles))
+        assert abs(yt[0, 0] - float(exact)) <= 1e-14, (t, yt, exact)
+
+
+def pin_fir_window_pieces(O):
+    """An FIR sequence cut into pieces of any length (shorter than K-1 too,
+    single tokens too), the window handed over between calls, equals one call
+    over the whole sequence; the final window is the last K-1 values of u."""
+    rng = _rng(31)
+    B, D, L = 2, 3, 300
+    x1, x2, v = rng.normal(size=(3, B, D, L))
+    skip = rng.normal(size=D)
+    for K in (1, 2, 7, 33):
+        w = rng.normal(size=(D, K))
+        y_full = O.fir_fwd(x1, x2, v, w, skip)
+        for cuts in ([0, 100, L], [0, 1, 2, 3, 5, 40, 41, 200, L], list(range(0, L + 1, 7)) + [L]):
+            cuts = sorted(set(cuts))
+            win, ys = None, []
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                yp, win = O.fir_fwd_window(x1[..., a:b], x2[..., a:b], v[..., a:b], w, skip,
+                                           window_in=win)
+                ys.append(yp)
+            y = np.concatenate(ys, axis=-1)
+            assert np.max(np.abs(y - y_full)) <= 1e-12 * np.max(np.abs(y_full)), (K, cuts[:4])
+            assert win.shape == (B, D, K - 1)
+            assert np.array_equal(win, (x1 * v)[..., L - (K - 1):]), K
+
+
 ALL_PINS = [
     pin_golden, pin_filter_rational, pin_filter_dft, pin_recurrence,
     pin_impulse, pin_linearity_time_invariance, pin_numpy_convolve,
     pin_direct_vs_fft, pin_fraction_bruteforce, pin_gate_special,
     pin_fir_delta, pin_chunk_equals_full, pin_chunk_resume,
     pin_chunk_state_rational, pin_scale_equivariance,
+    pin_decode_after_prefill, pin_decode_impulse_rational, pin_fir_window_pieces,
 ]

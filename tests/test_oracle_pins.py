@@ -117,6 +117,43 @@ def _chunk_variant(carry_off=1, decay_off=1, last_len_full=False):
     return chunk_fwd
 
 
+def _decode_variant(forget_input=False, output_before_update=False):
+    """modal_decode with a planted mistake in the state step."""
+    def modal_decode(x1, x2, v, log_poles, residues, skip, state_in=None):
+        x1, x2, v = (np.asarray(a, float) for a in (x1, x2, v))
+        lam = np.asarray(log_poles, float)
+        R = np.asarray(residues, float)
+        B, D = x1.shape
+        s0 = np.zeros((B, D, lam.shape[1])) if state_in is None else np.asarray(state_in, float)
+        u = x1 * v
+        s = np.exp(lam)[None] * s0 + (0.0 if forget_input else u[:, :, None])
+        z = np.einsum("dn,bdn->bd", R, s0 if output_before_update else s)
+        sk = np.zeros(D) if skip is None else np.asarray(skip, float)
+        return x2 * z + sk[None, :] * u, s
+    return modal_decode
+
+
+def _fir_window_variant(first_values=False, reversed_taps=False):
+    """fir_fwd_window with a planted mistake in the window or the taps."""
+    def fir_fwd_window(x1, x2, v, taps, skip, window_in=None):
+        x1, x2, v = (np.asarray(a, float) for a in (x1, x2, v))
+        w = np.asarray(taps, float)
+        if reversed_taps:
+            w = w[:, ::-1]
+        B, D, L = x1.shape
+        K = w.shape[1]
+        win = np.zeros((B, D, K - 1)) if window_in is None else np.asarray(window_in, float)
+        u = x1 * v
+        e = np.concatenate([win, u], axis=-1)
+        z = np.zeros_like(u)
+        for k in range(K):
+            z += w[None, :, k:k + 1] * e[..., K - 1 - k:K - 1 - k + L]
+        sk = np.zeros(D) if skip is None else np.asarray(skip, float)
+        out_win = e[..., :K - 1] if first_values else e[..., e.shape[-1] - (K - 1):]
+        return x2 * z + sk[None, :, None] * u, out_win
+    return fir_fwd_window
+
+
 MUTANTS = {
     "filter_time_origin": dict(modal_filter=_filter_shifted),
     "filter_dropped_mode": dict(modal_filter=_filter_dropped_mode),
@@ -126,6 +163,10 @@ MUTANTS = {
     "chunk_carry_exponent": dict(chunk_fwd=_chunk_variant(carry_off=0)),
     "chunk_decay_exponent": dict(chunk_fwd=_chunk_variant(decay_off=0)),
     "chunk_last_length": dict(chunk_fwd=_chunk_variant(last_len_full=True)),
+    "decode_forgets_input": dict(modal_decode=_decode_variant(forget_input=True)),
+    "decode_output_before_update": dict(modal_decode=_decode_variant(output_before_update=True)),
+    "fir_window_first_values": dict(fir_fwd_window=_fir_window_variant(first_values=True)),
+    "fir_window_reversed_taps": dict(fir_fwd_window=_fir_window_variant(reversed_taps=True)),
 }
 
 
