@@ -12,6 +12,9 @@ Entry points (names follow the C ABI):
   fftconv_fwd(x1, x2, v, log_poles, residues, skip=None)    -> y
   chunk_fwd(x1, x2, v, log_poles, residues, C, skip=None,
             state_in=None, algo="auto")                      -> (y, state_out)
+  modal_decode(x1, x2, v, log_poles, residues, skip=None,
+               state_in=None)       (x of shape (B, D))       -> (y, state_out)
+  fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None) -> (y, window_out)
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ import torch
 __all__ = [
     "HyenaError", "HyenaNotBuilt", "lib", "LIB_PATH", "abi_version",
     "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
+    "modal_decode", "fir_fwd_window",
     "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_LAUNCH",
     "F32", "BF16", "ALGOS", "EXPORTS",
 ]
@@ -49,6 +53,10 @@ EXPORTS = {
     "hyena_fftconv_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
     "hyena_chunk_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
                                _i64, _int, _int, _p]),
+    "hyena_modal_decode": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _int,
+                                  _p]),
+    "hyena_fir_fwd_window": (_int, [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
+                                    _int, _p]),
 }
 
 
@@ -102,15 +110,16 @@ def _ptr(t):
     return None if t is None else _p(t.data_ptr())
 
 
-def _act(name, t, like=None):
+def _act(name, t, like=None, dims=3):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
     if t.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"{name} must be bfloat16 or float32, got {t.dtype}")
-    if t.dim() != 3:
-        raise ValueError(f"{name} must be (B, D, L), got shape {tuple(t.shape)}")
+    if t.dim() != dims:
+        want = "(B, D, L)" if dims == 3 else "(B, D)"
+        raise ValueError(f"{name} must be {want}, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if like is not None:
@@ -217,3 +226,53 @@ def chunk_fwd(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
         _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, int(C), _io(x1), ALGOS[algo],
         _stream(x1)))
     return y, state_out
+
+
+def modal_decode(x1, x2, v, log_poles, residues, skip=None, state_in=None, out=None,
+                 state_out=None):
+    """One decode step from the modal state: x1, x2, v are (B, D), one token each.
+
+    Returns (y (B, D), state_out (B, D, N)); state_out may be state_in.
+    """
+    _act("x1", x1, dims=2)
+    _act("x2", x2, x1, dims=2)
+    _act("v", v, x1, dims=2)
+    B, D = x1.shape
+    N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
+    _param("log_poles", log_poles, (D, N), x1.device)
+    _param("residues", residues, (D, N), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    _param("state_in", state_in, (B, D, N), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1, dims=2)
+    if state_out is None:
+        state_out = torch.empty((B, D, N), dtype=torch.float32, device=x1.device)
+    else:
+        _param("state_out", state_out, (B, D, N), x1.device)
+    _check("hyena_modal_decode", lib().hyena_modal_decode(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip),
+        _ptr(state_in), _ptr(state_out), _ptr(y), B, D, _io(x1), _stream(x1)))
+    return y, state_out
+
+
+def fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None, out=None, window_out=None):
+    """Gated explicit FIR continuing from the window of the last K-1 inputs.
+
+    Returns (y, window_out (B, D, K-1) fp32); window_out may be window_in.
+    """
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    K = taps.shape[-1] if isinstance(taps, torch.Tensor) and taps.dim() == 2 else -1
+    _param("taps", taps, (D, K), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    _param("window_in", window_in, (B, D, K - 1), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    if window_out is None:
+        window_out = torch.empty((B, D, K - 1), dtype=torch.float32, device=x1.device)
+    else:
+        _param("window_out", window_out, (B, D, K - 1), x1.device)
+    _check("hyena_fir_fwd_window", lib().hyena_fir_fwd_window(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(taps), K, _ptr(skip), _ptr(window_in),
+        _ptr(window_out), _ptr(y), B, D, L, _io(x1), _stream(x1)))
+    return y, window_out

@@ -1,0 +1,126 @@
+// decode.hip -- the operator continued from its per-layer caches.
+//
+// The hcl block's cache is its modal state, the hcm / hcs blocks' cache the
+// window of their last K-1 inputs (Evo2-7B-262K model card, Implementation
+// Notes, 'Custom cache'; Evo1-1.5-7B-8K model card, Implementation Notes,
+// 'Cache subclass': FIR window + IIR modal state).
+//
+// modal_decode_kernel: one token per (b, c) row,
+//     s_n <- p_n s_n + u,   y = x2 * sum_n R_n s_n + skip * u,   u = x1 v,
+// one thread per row, the N modes in a loop (the state row is contiguous).
+//
+// fir_window_kernel: the first min(L, K-1) outputs of an FIR call that
+// continues a sequence, i.e. those that reach back into the window, and the
+// new window.  The rest of the outputs do not depend on the window and come
+// from the ordinary FIR kernels, launched first on the same stream; this
+// kernel then overwrites the outputs they computed with a zero history.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void modal_decode_kernel(
+    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const float* __restrict__ lam, const float* __restrict__ res, int N,
+    const float* __restrict__ skip, const float* state_in, float* state_out,
+    IO* __restrict__ y, int D, int64_t rows) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const int c = static_cast<int>(row % D);
+  const float u = Io<IO>::ld(x1, row) * Io<IO>::ld(v, row);
+  const float* lc = lam + static_cast<int64_t>(c) * N;
+  const float* rc = res + static_cast<int64_t>(c) * N;
+  const float* si = state_in ? state_in + row * N : nullptr;
+  float* so = state_out + row * N;
+  float z = 0.0f;
+  for (int n = 0; n < N; ++n) {
+    // read before write: state_out may be state_in
+    const float s = fmaf(expf(lc[n]), si ? si[n] : 0.0f, u);
+    so[n] = s;
+    z = fmaf(rc[n], s, z);
+  }
+  const float sk = skip ? skip[c] : 0.0f;
+  Io<IO>::st(y, row, fmaf(Io<IO>::ld(x2, row), z, sk * u));
+}
+
+constexpr int FIRW_T = 128;
+
+// One workgroup per row.  LDS: the taps, then e = [window, u[0:T0)],
+// T0 = min(L, K-1).
+template <typename IO>
+__global__ __launch_bounds__(FIRW_T) void fir_window_kernel(
+    const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
+    const float* __restrict__ taps, int K, const float* __restrict__ skip,
+    const float* win_in, float* win_out, IO* __restrict__ y, int D, int L) {
+  extern __shared__ float smf[];
+  const int W = K - 1;
+  const int T0 = L < W ? L : W;
+  float* w = smf;
+  float* e = smf + K;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int c = static_cast<int>(row % D);
+  const IO* x1r = x1 + row * L;
+  const IO* x2r = x2 + row * L;
+  const IO* vr = v + row * L;
+  for (int k = tid; k < K; k += FIRW_T) w[k] = taps[static_cast<int64_t>(c) * K + k];
+  for (int j = tid; j < W; j += FIRW_T) e[j] = win_in ? win_in[row * W + j] : 0.0f;
+  for (int t = tid; t < T0; t += FIRW_T) e[W + t] = Io<IO>::ld(x1r, t) * Io<IO>::ld(vr, t);
+  __syncthreads();                      // every read of win_in is done
+
+  const float sk = skip ? skip[c] : 0.0f;
+  for (int t = tid; t < T0; t += FIRW_T) {
+    float z = 0.0f;
+    for (int k = 0; k < K; ++k) z = fmaf(w[k], e[W + t - k], z);
+    Io<IO>::st(y + row * L, t, fmaf(Io<IO>::ld(x2r, t), z, sk * e[W + t]));
+  }
+  // new window: entries L .. L+W-1 of [window, u]
+  for (int j = tid; j < W; j += FIRW_T) {
+    const int src = L + j;
+    const float val = (src < W) ? e[src] : Io<IO>::ld(x1r, src - W) * Io<IO>::ld(vr, src - W);
+    win_out[row * W + j] = val;
+  }
+}
+
+hipError_t launch_modal_decode(const DecodeArgs& a) {
+  const int64_t rows = static_cast<int64_t>(a.B) * a.D;
+  const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
+  if (a.bf16)
+    modal_decode_kernel<bf16_t><<<blocks, 256, 0, a.stream>>>(
+        static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
+        static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
+        static_cast<bf16_t*>(a.y), a.D, rows);
+  else
+    modal_decode_kernel<float><<<blocks, 256, 0, a.stream>>>(
+        static_cast<const float*>(a.x1), static_cast<const float*>(a.x2),
+        static_cast<const float*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
+        static_cast<float*>(a.y), a.D, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fir_window(const FirArgs& a, const float* win_in, float* win_out) {
+  // outputs that do not reach back into the window: the ordinary kernels
+  if (a.L > a.K - 1) {
+    const hipError_t e = launch_fir(a);
+    if (e != hipSuccess) return e;
+  }
+  if (a.K == 1) return hipSuccess;      // no window
+  const int W = a.K - 1;
+  const int T0 = a.L < W ? a.L : W;
+  const size_t shmem = static_cast<size_t>(a.K + W + T0) * sizeof(float);
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.D);
+  if (a.bf16)
+    fir_window_kernel<bf16_t><<<grid, FIRW_T, shmem, a.stream>>>(
+        static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
+        static_cast<const bf16_t*>(a.v), a.taps, a.K, a.skip, win_in, win_out,
+        static_cast<bf16_t*>(a.y), a.D, a.L);
+  else
+    fir_window_kernel<float><<<grid, FIRW_T, shmem, a.stream>>>(
+        static_cast<const float*>(a.x1), static_cast<const float*>(a.x2),
+        static_cast<const float*>(a.v), a.taps, a.K, a.skip, win_in, win_out,
+        static_cast<float*>(a.y), a.D, a.L);
+  return hipGetLastError();
+}
+
+}  // namespace hyena

@@ -103,6 +103,48 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, cons
   return from_hip(hyena::launch_fir(a));
 }
 
+hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* v,
+                                    const float* taps, int64_t K, const float* skip,
+                                    const float* window_in, float* window_out, void* y,
+                                    int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                    void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  // L = 0 still moves the window over; only B = 0 or D = 0 is a no-op
+  if (st != HYENA_OK) return st;
+  if (K < 1) return HYENA_ERR_INVALID_ARG;
+  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return HYENA_OK;
+  if (empty && K == 1) return HYENA_OK;
+  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
+  if (K > 1 && (!window_out || !aligned_to(window_out, 4) || (window_in && !aligned_to(window_in, 4))))
+    return HYENA_ERR_INVALID_ARG;
+  if (L > K - 1 && B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;
+  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+  return from_hip(hyena::launch_fir_window(a, window_in, window_out));
+}
+
+hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
+                                  const float* log_poles, const float* residues, int64_t N,
+                                  const float* skip, const float* state_in, float* state_out,
+                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                  void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, 1, io, &empty);
+  if (st != HYENA_OK) return st;
+  if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (empty) return HYENA_OK;
+  st = check_modal(log_poles, residues, N, skip);
+  if (st != HYENA_OK) return st;
+  if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
+    return HYENA_ERR_INVALID_ARG;
+  hyena::DecodeArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
+                      state_out, y, static_cast<int>(B), static_cast<int>(D),
+                      io == HYENA_BF16, as_stream(stream)};
+  return from_hip(hyena::launch_modal_decode(a));
+}
+
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {
   (void)N;
   (void)io;

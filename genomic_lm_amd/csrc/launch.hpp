@@ -61,6 +61,22 @@ struct ChunkArgs {
   hipStream_t stream;
 };
 
+struct DecodeArgs {
+  const void* x1;
+  const void* x2;
+  const void* v;
+  const float* lam;
+  const float* res;
+  int N;
+  const float* skip;
+  const float* state_in;
+  float* state_out;
+  void* y;
+  int B, D;
+  bool bf16;
+  hipStream_t stream;
+};
+
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
                                float* h, hipStream_t stream);
 
@@ -78,6 +94,12 @@ hipError_t launch_fftconv_large(const FftconvArgs& a);
 
 hipError_t launch_chunk_fft(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
+
+// One token per row from the modal state (decode.hip).
+hipError_t launch_modal_decode(const DecodeArgs& a);
+// FIR continuing from a window of the last K-1 inputs: launch_fir for the
+// outputs past the window's reach, then the window kernel (decode.hip).
+hipError_t launch_fir_window(const FirArgs& a, const float* win_in, float* win_out);
 
 // state_out <- state_in (or 0 when state_in is null), count floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t count,

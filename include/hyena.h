@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 1
+#define HYENA_ABI_VERSION 2
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -183,6 +183,49 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
                                void* y, int64_t B, int64_t D, int64_t L, int64_t C,
                                hyena_dtype_t io, hyena_chunk_algo_t algo,
                                void* stream);
+
+/*
+ * hyena_modal_decode -- one decode step of the modal operator from its cache.
+ * The hcl block's inference cache is its modal state (Evo2-7B-262K model
+ * card, Implementation Notes, 'Custom cache'; Evo1-1.5-7B-8K model card,
+ * Implementation Notes, 'Cache subclass').  For one token per (b, c):
+ *   s_n <- p_n s_n + u,  u = x1 v,  p_n = exp(log_poles[c, n]),
+ *   y = x2 * sum_n R_n s_n + skip * u,  rounded once to `io`.
+ * Equal to hyena_chunk_fwd with L = 1, without its per-row set-up.
+ *   x1, x2, v : (B, D) `io` (one token);  y : (B, D) `io`, written
+ *   log_poles, residues : (D, N) fp32, 1 <= N <= HYENA_MAX_MODES
+ *   skip : (D) fp32 or NULL
+ *   state_in  : (B, D, N) fp32 or NULL (empty prefix)
+ *   state_out : (B, D, N) fp32, written (may equal state_in)
+ */
+hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
+                                  const float* log_poles, const float* residues,
+                                  int64_t N, const float* skip,
+                                  const float* state_in, float* state_out,
+                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                  void* stream);
+
+/*
+ * hyena_fir_fwd_window -- explicit FIR continuing a sequence from its cache.
+ * The hcm / hcs blocks' inference cache is the window of their last K-1
+ * inputs u (Evo2-7B-262K model card, Implementation Notes, 'Custom cache';
+ * Evo1-1.5-7B-8K model card, Implementation Notes, 'Cache subclass').  With
+ * e = [window_in, u[0:L)]:
+ *   z[t] = sum_{k<K} w[c, k] e[K-1+t-k],  y = x2 * z + skip * u,
+ * and window_out = the last K-1 entries of e.  Any L >= 0 (L = 1 per decode
+ * step, L < K-1 included); successive calls with the window handed over
+ * equal one call over the whole sequence.
+ *   x1, x2, v, taps, K, skip, y, B, D, L, io : as hyena_fir_fwd
+ *   window_in  : (B, D, K-1) fp32, oldest first, or NULL (fresh sequence)
+ *   window_out : (B, D, K-1) fp32, written (may equal window_in); may be
+ *                NULL only when K = 1
+ * L = 0 moves window_in to window_out (zeros when window_in is NULL).
+ */
+hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* v,
+                                    const float* taps, int64_t K, const float* skip,
+                                    const float* window_in, float* window_out,
+                                    void* y, int64_t B, int64_t D, int64_t L,
+                                    hyena_dtype_t io, void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 1
+    assert G.abi_version() == 2
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -87,6 +87,38 @@ def test_fir_validation():
     assert f(*bad) == G.ERR_INVALID_ARG
     empty = list(good); empty[9] = 0; empty[0] = None
     assert f(*empty) == G.OK
+
+
+def test_fir_window_validation():
+    f = G.lib().hyena_fir_fwd_window
+    # x1 x2 v taps K skip win_in win_out y B D L io stream
+    good = [FAKE, FAKE, FAKE, FAKE, 7, None, None, FAKE, FAKE, 1, 4, 64, G.BF16, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (3, None, G.ERR_INVALID_ARG),
+                           (4, 0, G.ERR_INVALID_ARG), (4, 1025, G.ERR_UNSUPPORTED),
+                           (7, None, G.ERR_INVALID_ARG),          # window_out needed when K > 1
+                           (7, MISALIGNED, G.ERR_INVALID_ARG), (6, MISALIGNED, G.ERR_INVALID_ARG),
+                           (11, -1, G.ERR_INVALID_ARG), (12, 5, G.ERR_INVALID_ARG)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[10] = 0; a[0] = None                     # D = 0: nothing to do
+    assert f(*a) == G.OK
+    a = list(good); a[4] = 1; a[7] = None; a[11] = 0; a[0] = None   # K = 1, L = 0: no window
+    assert f(*a) == G.OK
+
+
+def test_modal_decode_validation():
+    f = G.lib().hyena_modal_decode
+    # x1 x2 v lam res N skip s_in s_out y B D io stream
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, None, FAKE, FAKE, 1, 4, G.BF16, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (3, None, G.ERR_INVALID_ARG),
+                           (5, 0, G.ERR_INVALID_ARG), (5, 65, G.ERR_INVALID_ARG),
+                           (8, None, G.ERR_INVALID_ARG), (7, MISALIGNED, G.ERR_INVALID_ARG),
+                           (9, MISALIGNED, G.ERR_INVALID_ARG), (11, -2, G.ERR_INVALID_ARG),
+                           (12, 9, G.ERR_INVALID_ARG)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[10] = 0; a[0] = None
+    assert f(*a) == G.OK
 
 
 def test_fftconv_validation():

@@ -1,0 +1,194 @@
+"""Decode from the per-layer caches on the GPU, through the C ABI, against the
+fp64 oracle: the modal decode step and the FIR window.
+
+The property that matters for inference: a prefill followed by decode steps
+(or any split of an FIR sequence into calls, with the window handed over)
+gives the output of one pass over the whole sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import genomic_lm_amd as G
+import oracle
+import workloads as W
+from tests.gpu_util import DevWorkload, gate, log, oracle_fir, oracle_modal, sample_rows, state_gate, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()
+    yield
+
+
+def _wl(io, D, L, B=1, N=None):
+    return W.make("tiny" if io == "f32" else "7b_layer_set", B=B, D=D, L=L, N=N)
+
+
+def _tok(t, i):
+    return t[..., i].contiguous()
+
+
+# ------------------------------------------------------------------ modal
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1, 16, 64])
+def test_modal_decode_step(io, N):
+    w = _wl(io, D=96, L=4, B=2, N=N)
+    d = DevWorkload(w)
+    rng = np.random.default_rng(5)
+    s0 = rng.normal(size=(2, w.D, N)).astype(np.float32)
+    s_dev = torch.from_numpy(s0).to(d.x1.device)
+    for t in range(w.L):
+        log(f"decode io={io} N={N} t={t}")
+        y, s1 = G.modal_decode(_tok(d.x1, t), _tok(d.x2, t), _tok(d.v, t), d.lam, d.res, d.skip,
+                               state_in=s_dev)
+        ref_y, ref_s = oracle.modal_decode(w.f64("x1")[..., t], w.f64("x2")[..., t],
+                                           w.f64("v")[..., t], w.log_poles, w.residues, w.skip,
+                                           state_in=s_dev.cpu().numpy())
+        gate(y[..., None], ref_y[..., None], io, label=f"decode step t={t}")
+        state_gate(s1, ref_s, label=f"decode t={t}", tol=1e-6)
+        s_dev = s1
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("algo", ["mfma", "fft"])
+def test_decode_after_prefill(io, algo):
+    """Chunked prefill of L tokens, then T decode steps: the single pass over L + T."""
+    L, T = 3000, 24
+    w = _wl(io, D=16, L=L + T, B=2)
+    d = DevWorkload(w)
+    pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
+    y_pre, s = G.chunk_fwd(*pre, d.lam, d.res, 1024, d.skip, algo=algo)
+    ys = [y_pre]
+    for t in range(L, L + T):
+        yt, s = G.modal_decode(_tok(d.x1, t), _tok(d.x2, t), _tok(d.v, t), d.lam, d.res, d.skip,
+                               state_in=s, state_out=s)
+        ys.append(yt[..., None])
+    ref, ref_s = oracle_modal(w)
+    log(f"prefill {L} ({algo}) + decode {T}, io={io}")
+    gate(torch.cat(ys, -1), ref, io, label=f"prefill+decode {algo}")
+    state_gate(s, ref_s, label=f"prefill+decode {algo}")
+
+
+def test_decode_from_empty_state_equals_chunk():
+    w = _wl("bf16", D=32, L=6)
+    d = DevWorkload(w)
+    s = None
+    ys = []
+    for t in range(w.L):
+        yt, s = G.modal_decode(_tok(d.x1, t), _tok(d.x2, t), _tok(d.v, t), d.lam, d.res, d.skip,
+                               state_in=s)
+        ys.append(yt[..., None])
+    y_chunk, s_chunk = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1, d.skip, algo="mfma")
+    ref, ref_s = oracle_modal(w)
+    gate(torch.cat(ys, -1), ref, "bf16", label="decode from empty")
+    state_gate(s, ref_s, label="decode from empty")
+    gate(y_chunk, ref, "bf16", label="chunk C=1")
+
+
+def test_decode_7b_shape():
+    """D = 4096: 8184 prefill tokens through one chunk launch, 8 decode steps."""
+    w = W.make("7b_layer_set")
+    d = DevWorkload(w)
+    L = w.L - 8
+    pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
+    y_pre, s = G.chunk_fwd(*pre, d.lam, d.res, 1024, d.skip, algo="mfma")
+    ys = [y_pre]
+    for t in range(L, w.L):
+        yt, s = G.modal_decode(_tok(d.x1, t), _tok(d.x2, t), _tok(d.v, t), d.lam, d.res, d.skip,
+                               state_in=s, state_out=s)
+        ys.append(yt[..., None])
+    rows = sample_rows(w.D)
+    ref, ref_s = oracle_modal(w, rows)
+    gate(torch.cat(ys, -1), ref, "bf16", rows, label="7b prefill+decode")
+    state_gate(s, ref_s, rows, label="7b prefill+decode")
+
+
+# ------------------------------------------------------------------ FIR window
+CUTS = {
+    "halves": lambda L: [0, L // 2, L],
+    "ragged": lambda L: [0, 1, 2, 3, 5, 40, 41, 1100, 1101, L - 3, L],
+    "steps": lambda L: list(range(0, 70)) + [70, 1500, L],
+}
+
+
+def _u32(w):
+    """u = x1 * v in fp32, as both sides compute it."""
+    return w.f64("x1").astype(np.float32) * w.f64("v").astype(np.float32)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [1, 7, 128, 200])
+@pytest.mark.parametrize("cuts", sorted(CUTS))
+def test_fir_window_pieces(io, K, cuts):
+    L = 3000
+    w = _wl(io, D=8, L=L, B=2)
+    rng = np.random.default_rng(K)
+    taps = rng.normal(0, 1 / np.sqrt(K), (w.D, K)).astype(np.float32)
+    if io == "bf16":
+        taps = W.bf16_bits_to_f32(W.f32_to_bf16_bits(taps))
+    d = DevWorkload(w)
+    tp = torch.from_numpy(taps).to(d.x1.device)
+    pts = sorted(set(CUTS[cuts](L)))
+    win, ys = None, []
+    log(f"fir window io={io} K={K} cuts={cuts} ({len(pts) - 1} calls)")
+    for a, b in zip(pts[:-1], pts[1:]):
+        sl = [t[..., a:b].contiguous() for t in (d.x1, d.x2, d.v)]
+        yp, win = G.fir_fwd_window(*sl, tp, d.skip, window_in=win)
+        ys.append(yp)
+    ref = oracle.fir_fwd(w.f64("x1"), w.f64("x2"), w.f64("v"), taps, w.skip)
+    gate(torch.cat(ys, -1), ref, io, label=f"fir window K={K} {cuts}")
+    # the final window is u of the last K-1 tokens, bit for bit
+    assert win.shape == (2, w.D, K - 1)
+    assert np.array_equal(win.cpu().numpy(), _u32(w)[..., L - (K - 1):])
+
+
+@pytest.mark.parametrize("K", [7, 128])
+def test_fir_window_in_place_and_decode(K):
+    """One window buffer updated in place: a prefill call, then single-token steps."""
+    L, T = 2000, 30
+    w = _wl("bf16", D=8, L=L + T)
+    d = DevWorkload(w)
+    win = torch.zeros((1, w.D, K - 1), dtype=torch.float32, device=d.x1.device)
+    pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
+    y0, wo = G.fir_fwd_window(*pre, d.taps[K], d.skip, window_in=win, window_out=win)
+    assert wo.data_ptr() == win.data_ptr()
+    ys = [y0]
+    for t in range(L, L + T):
+        sl = [x[..., t:t + 1].contiguous() for x in (d.x1, d.x2, d.v)]
+        yt, _ = G.fir_fwd_window(*sl, d.taps[K], d.skip, window_in=win, window_out=win)
+        ys.append(yt)
+    ref = oracle_fir(w, K)
+    gate(torch.cat(ys, -1), ref, "bf16", label=f"fir in-place K={K}")
+    assert np.array_equal(win.cpu().numpy(), _u32(w)[..., L + T - (K - 1):])
+
+
+def test_fir_window_empty_call_moves_window():
+    w = _wl("bf16", D=4, L=1)
+    d = DevWorkload(w)
+    K = 7
+    e = torch.empty((1, w.D, 0), dtype=torch.bfloat16, device=d.x1.device)
+    src = torch.arange(w.D * (K - 1), dtype=torch.float32, device=d.x1.device).reshape(1, w.D, K - 1)
+    y, out = G.fir_fwd_window(e, e, e, d.taps[K], d.skip, window_in=src)
+    assert y.shape == (1, w.D, 0)
+    assert torch.equal(out, src)
+    _, out0 = G.fir_fwd_window(e, e, e, d.taps[K], d.skip)
+    assert torch.count_nonzero(out0).item() == 0
+
+
+def test_fir_window_7b_shape():
+    """D = 4096, L = 8192 in two calls per filter, K = 7 and 128, sampled rows."""
+    w = W.make("7b_layer_set")
+    d = DevWorkload(w)
+    rows = sample_rows(w.D)
+    for K in (7, 128):
+        ya, wa = G.fir_fwd_window(*[t[..., :5000].contiguous() for t in (d.x1, d.x2, d.v)],
+                                  d.taps[K], d.skip)
+        yb, wb = G.fir_fwd_window(*[t[..., 5000:].contiguous() for t in (d.x1, d.x2, d.v)],
+                                  d.taps[K], d.skip, window_in=wa)
+        ref = oracle_fir(w, K, rows)
+        gate(torch.cat([ya, yb], -1), ref, "bf16", rows, label=f"7b fir window K={K}")
