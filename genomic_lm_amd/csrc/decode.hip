@@ -6,8 +6,7 @@
 // 'Cache subclass': FIR window + IIR modal state).
 //
 // modal_decode_kernel: one token per (b, c) row,
-//     s_n <- p_n s_n + u,   y = x2 * sum_n R_n s_n + skip * u,   u = x1 v,
-// one thread per row, the N modes in a loop (the state row is contiguous).
+//     s_n <- p_n s_n + u,   y = x2 * sum_n R_n s_n + skip * u,   u = x1 v.
 //
 // fir_window_kernel: the first min(L, K-1) outputs of an FIR call that
 // continues a sequence, i.e. those that reach back into the window, and the
@@ -19,35 +18,49 @@
 
 namespace hyena {
 
+// One lane per (row, mode): a row's modes sit in a group of G = next power
+// of two >= N lanes of one wave, so every load is coalesced across the group
+// and the sum over modes is a butterfly of log2(G) lane exchanges.
 template <typename IO>
 __global__ __launch_bounds__(256) void modal_decode_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
-    const float* __restrict__ lam, const float* __restrict__ res, int N,
+    const float* __restrict__ lam, const float* __restrict__ res, int N, int lgG,
     const float* __restrict__ skip, const float* state_in, float* state_out,
     IO* __restrict__ y, int D, int64_t rows) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (row >= rows) return;
-  const int c = static_cast<int>(row % D);
-  const float u = Io<IO>::ld(x1, row) * Io<IO>::ld(v, row);
-  const float* lc = lam + static_cast<int64_t>(c) * N;
-  const float* rc = res + static_cast<int64_t>(c) * N;
-  const float* si = state_in ? state_in + row * N : nullptr;
-  float* so = state_out + row * N;
-  float z = 0.0f;
-  for (int n = 0; n < N; ++n) {
-    // read before write: state_out may be state_in
-    const float s = fmaf(expf(lc[n]), si ? si[n] : 0.0f, u);
-    so[n] = s;
-    z = fmaf(rc[n], s, z);
+  const int G = 1 << lgG;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> lgG;
+  const int n = static_cast<int>(gid & (G - 1));
+  const bool live = row < rows && n < N;
+  float part = 0.0f, u = 0.0f;
+  int c = 0;
+  if (row < rows) {
+    c = static_cast<int>(row % D);
+    u = Io<IO>::ld(x1, row) * Io<IO>::ld(v, row);
   }
-  const float sk = skip ? skip[c] : 0.0f;
-  Io<IO>::st(y, row, fmaf(Io<IO>::ld(x2, row), z, sk * u));
+  if (live) {
+    const int64_t pi = static_cast<int64_t>(c) * N + n;
+    const int64_t si = row * N + n;
+    // read before write: state_out may be state_in
+    const float s = fmaf(expf(lam[pi]), state_in ? state_in[si] : 0.0f, u);
+    state_out[si] = s;
+    part = res[pi] * s;
+  }
+  // every lane of the wave takes part in the exchanges (groups never span
+  // waves: G divides 64)
+  for (int o = 1; o < G; o <<= 1) part += __shfl_xor(part, o);
+  if (row < rows && n == 0) {
+    const float sk = skip ? skip[c] : 0.0f;
+    Io<IO>::st(y, row, fmaf(Io<IO>::ld(x2, row), part, sk * u));
+  }
 }
 
 constexpr int FIRW_T = 128;
 
 // One workgroup per row.  LDS: the taps, then e = [window, u[0:T0)],
-// T0 = min(L, K-1).
+// T0 = min(L, K-1).  Each of the T0 outputs is one wave's dot product (taps
+// strided over the lanes, then a butterfly), so a decode step (T0 = 1) does
+// not run K products on one lane.
 template <typename IO>
 __global__ __launch_bounds__(FIRW_T) void fir_window_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
@@ -59,6 +72,7 @@ __global__ __launch_bounds__(FIRW_T) void fir_window_kernel(
   float* w = smf;
   float* e = smf + K;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int c = static_cast<int>(row % D);
   const IO* x1r = x1 + row * L;
@@ -70,10 +84,11 @@ __global__ __launch_bounds__(FIRW_T) void fir_window_kernel(
   __syncthreads();                      // every read of win_in is done
 
   const float sk = skip ? skip[c] : 0.0f;
-  for (int t = tid; t < T0; t += FIRW_T) {
+  for (int t = wave; t < T0; t += FIRW_T / 64) {
     float z = 0.0f;
-    for (int k = 0; k < K; ++k) z = fmaf(w[k], e[W + t - k], z);
-    Io<IO>::st(y + row * L, t, fmaf(Io<IO>::ld(x2r, t), z, sk * e[W + t]));
+    for (int k = lane; k < K; k += 64) z = fmaf(w[k], e[W + t - k], z);
+    for (int o = 1; o < 64; o <<= 1) z += __shfl_xor(z, o);
+    if (lane == 0) Io<IO>::st(y + row * L, t, fmaf(Io<IO>::ld(x2r, t), z, sk * e[W + t]));
   }
   // new window: entries L .. L+W-1 of [window, u]
   for (int j = tid; j < W; j += FIRW_T) {
@@ -85,16 +100,18 @@ __global__ __launch_bounds__(FIRW_T) void fir_window_kernel(
 
 hipError_t launch_modal_decode(const DecodeArgs& a) {
   const int64_t rows = static_cast<int64_t>(a.B) * a.D;
-  const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
+  int lgG = 0;
+  while ((1 << lgG) < a.N) ++lgG;         // N <= 64: G <= 64 lanes
+  const unsigned blocks = static_cast<unsigned>(((rows << lgG) + 255) / 256);
   if (a.bf16)
     modal_decode_kernel<bf16_t><<<blocks, 256, 0, a.stream>>>(
         static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
-        static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
+        static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, lgG, a.skip, a.state_in, a.state_out,
         static_cast<bf16_t*>(a.y), a.D, rows);
   else
     modal_decode_kernel<float><<<blocks, 256, 0, a.stream>>>(
         static_cast<const float*>(a.x1), static_cast<const float*>(a.x2),
-        static_cast<const float*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
+        static_cast<const float*>(a.v), a.lam, a.res, a.N, lgG, a.skip, a.state_in, a.state_out,
         static_cast<float*>(a.y), a.D, rows);
   return hipGetLastError();
 }
