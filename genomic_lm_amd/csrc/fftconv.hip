@@ -78,7 +78,10 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   float2 b0[P];           // inverse transform of the even half, kept for the recombination
   float zm_nyq = 0.0f;    // Z[M] (real), only used by thread 0
 
-#pragma unroll 1
+  // Both parity halves are unrolled: as a loop, the address and twiddle
+  // arithmetic common to the two iterations was hoisted out of it and held
+  // in registers across both transforms.
+#pragma unroll
   for (int q = 0; q < 2; ++q) {
     float2 a[P];
     // ---- u = x1 * v, packed in pairs, parity pre-twiddle
@@ -181,12 +184,14 @@ static hipError_t launch_s(const FftconvArgs& a, bool vec) {
 template <typename IO>
 static hipError_t launch_io(const FftconvArgs& a, int S, bool vec) {
   switch (S) {
+    // 8 points per thread wherever the workgroup size allows: at 16 points
+    // the transforms need more than 256 registers per thread
     case 256: return launch_s<256, 64, IO>(a, vec);
     case 512: return launch_s<512, 64, IO>(a, vec);
-    case 1024: return launch_s<1024, 64, IO>(a, vec);
-    case 2048: return launch_s<2048, 128, IO>(a, vec);
-    case 4096: return launch_s<4096, 256, IO>(a, vec);
-    case 8192: return launch_s<8192, 512, IO>(a, vec);
+    case 1024: return launch_s<1024, 128, IO>(a, vec);
+    case 2048: return launch_s<2048, 256, IO>(a, vec);
+    case 4096: return launch_s<4096, 512, IO>(a, vec);
+    case 8192: return launch_s<8192, 1024, IO>(a, vec);
     case 16384: return launch_s<16384, 1024, IO>(a, vec);
     default: return hipErrorInvalidValue;
   }
