@@ -34,13 +34,15 @@ namespace {
 
 constexpr int LG_S2 = 8;
 constexpr int S2 = 1 << LG_S2;                 // column transform size
-constexpr int CT = 16;                         // threads per column transform
-constexpr int CP = S2 / CT;                    // points per thread
-constexpr int GC = 32;                         // columns per workgroup
+constexpr int CT = 32;                         // threads per column transform
+constexpr int CP = S2 / CT;                    // points per thread (8: at 16 the
+                                               // transforms need too many registers)
+constexpr int GC = 16;                         // columns per workgroup
 constexpr int NTC = CT * GC;                   // threads of the column kernels
 constexpr int CSTRIDE = lds_padded_size(S2) + 1;   // odd stride: columns on distinct banks
 constexpr int MIN_S1 = 128, MAX_S1 = 1024;
-constexpr size_t BATCH_BYTES = size_t(256) << 20;  // workspace of one row batch
+constexpr size_t BATCH_BYTES = size_t(1) << 30;    // workspace of one row batch: larger
+                                                   // launches fill the chip better
 
 // Number of mirror-row units of one row: parity 0 has rows 0 and 128 paired
 // with themselves and 127 pairs (k2, 256 - k2); parity 1 has 128 pairs
@@ -49,8 +51,8 @@ constexpr int ROW_UNITS = 129 + 128;
 
 }  // namespace
 
-// Column pass, forward.  Thread (t, col): t-major so that one wave touches 32
-// consecutive columns of two rows (256-byte segments).
+// Column pass, forward.  Thread (t, col): t-major so that one wave touches 16
+// consecutive columns of four rows (128-byte segments).
 template <typename IO, bool VEC>
 __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
     const IO* x1, const IO* v, const float* __restrict__ lam, const float* __restrict__ res,
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
 
   float2* out = ws + (int64_t(rb) * 4 + sig * 2) * S;
   float2* lc = lds + col * CSTRIDE;
-#pragma unroll 1
+#pragma unroll
   for (int q = 0; q < 2; ++q) {
     float2 a[CP];
 #pragma unroll
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_inv(
   float2* lc = lds + col * CSTRIDE;
 
   float2 b0[CP];
-#pragma unroll 1
+#pragma unroll
   for (int q = 0; q < 2; ++q) {
     float2 a[CP];
 #pragma unroll

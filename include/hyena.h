@@ -141,7 +141,7 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
  *               scratch (may be NULL when that size is 0).  Rows with
  *               L <= 32768 are transformed on chip and need none; longer rows
  *               go through it in batches of rows, 32 * Nfft / 4 bytes per row,
- *               at most 256 MiB.  Calls sharing one workspace must be ordered
+ *               at most 1 GiB.  Calls sharing one workspace must be ordered
  *               (same stream).
  * Nfft > HYENA_MAX_FFT_LEN -> HYENA_ERR_UNSUPPORTED; workspace NULL, short or
  * misaligned when one is needed -> HYENA_ERR_WORKSPACE.

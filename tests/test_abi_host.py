@@ -135,11 +135,11 @@ def test_fftconv_validation():
     assert ws(1, 4, 32768, 16, G.BF16) == 0
     assert ws(0, 4, 1024, 16, G.BF16) == 0
     # four-step path: 32 S bytes per row (u and h, two parity halves, complex
-    # fp32), rows batched up to 256 MiB
+    # fp32), rows batched up to 1 GiB
     assert ws(1, 4, 32769, 16, G.BF16) == 4 * 32 * 32768
     assert ws(2, 3, 65536, 16, G.F32) == 6 * 32 * 32768
-    assert ws(1, 4096, 262144, 16, G.BF16) == 64 * 32 * 131072
-    assert ws(1, 4096, 1 << 19, 16, G.BF16) == 32 * 32 * 262144
+    assert ws(1, 4096, 262144, 16, G.BF16) == 256 * 32 * 131072
+    assert ws(1, 4096, 1 << 19, 16, G.BF16) == 128 * 32 * 262144
     assert ws(1, 4, (1 << 19) + 1, 16, G.BF16) == 0             # beyond the largest FFT
     # missing, short or misaligned workspace is refused before any launch
     big = list(good); big[10] = 40000
