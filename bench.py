@@ -179,10 +179,13 @@ def main():
     if not args.no_components:
         comp_steps = max(3, args.steps // 4)
         taps7, taps128 = par(w.taps[7]), par(w.taps[128])
+        fft_ws = torch.empty(max(G.fftconv_workspace_size(B, D, L, w.N, x1.dtype), 16),
+                             dtype=torch.uint8, device=dev)
         runs = {
             "chunk_fft": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="fft", out=y, state_out=st),
             "chunk_mfma": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="mfma", out=y, state_out=st),
-            "fftconv_single_pass": lambda: G.fftconv_fwd(x1, x2, v, lam, res, skip, out=y),
+            "fftconv_single_pass": lambda: G.fftconv_fwd(x1, x2, v, lam, res, skip, out=y,
+                                                         workspace=fft_ws),
             "fir7": lambda: G.fir_fwd(x1, x2, v, taps7, skip, out=y),
             "fir128": lambda: G.fir_fwd(x1, x2, v, taps128, skip, out=y),
         }

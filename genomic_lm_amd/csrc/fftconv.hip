@@ -192,7 +192,6 @@ static hipError_t launch_io(const FftconvArgs& a, int S, bool vec) {
     case 2048: return launch_s<2048, 256, IO>(a, vec);
     case 4096: return launch_s<4096, 512, IO>(a, vec);
     case 8192: return launch_s<8192, 1024, IO>(a, vec);
-    case 16384: return launch_s<16384, 1024, IO>(a, vec);
     default: return hipErrorInvalidValue;
   }
 }
@@ -201,7 +200,7 @@ int fftconv_onchip_S(int64_t L) {
   int64_t half = (L + 1) / 2;
   int64_t S = 256;
   while (S < half) S <<= 1;
-  return S <= 16384 ? static_cast<int>(S) : 0;
+  return S <= 8192 ? static_cast<int>(S) : 0;
 }
 
 hipError_t launch_fftconv_onchip(const FftconvArgs& a) {

@@ -139,7 +139,7 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
  *   workspace : device buffer of at least hyena_fftconv_workspace_size(...)
  *               bytes, 16-byte aligned, owned by the caller, contents
  *               scratch (may be NULL when that size is 0).  Rows with
- *               L <= 32768 are transformed on chip and need none; longer rows
+ *               L <= 16384 are transformed on chip and need none; longer rows
  *               go through it in batches of rows, 32 * Nfft / 4 bytes per row,
  *               at most 1 GiB.  Calls sharing one workspace must be ordered
  *               (same stream).
@@ -153,7 +153,7 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when the FFT runs
- * on chip (L <= 32768) or the shape is empty or unsupported. */
+ * on chip (L <= 16384) or the shape is empty or unsupported. */
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                     hyena_dtype_t io);
 

@@ -132,7 +132,9 @@ def test_fftconv_validation():
         assert f(*a) == want, (idx, val)
     ws = G.lib().hyena_fftconv_workspace_size
     assert ws(1, 4, 1024, 16, G.BF16) == 0                     # on-chip path, no workspace
-    assert ws(1, 4, 32768, 16, G.BF16) == 0
+    assert ws(1, 4, 16384, 16, G.BF16) == 0
+    assert ws(1, 4, 16385, 16, G.BF16) == 4 * 32 * 16384       # four-step from L > 16384
+    assert ws(1, 4, 32768, 16, G.BF16) == 4 * 32 * 16384
     assert ws(0, 4, 1024, 16, G.BF16) == 0
     # four-step path: 32 S bytes per row (u and h, two parity halves, complex
     # fp32), rows batched up to 1 GiB

@@ -56,11 +56,12 @@ def test_fftconv_small(io, L):
     gate(y, ref, io, label=f"fftconv L={L}")
 
 
-# Rows longer than one CU's LDS holds: the three-kernel four-step path through
-# a workspace.  Lengths cover each row-transform size (S/256 = 128 ... 1024),
+# Rows longer than 16384: the three-kernel four-step path through a
+# workspace.  Lengths cover each row-transform size (S/256 = 64 ... 1024),
 # odd lengths (the pair loads' ragged tail), and B*D above one row batch.
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("L,B,D", [(32769, 1, 3), (40000, 2, 2), (65536, 1, 2), (65001, 1, 2),
+@pytest.mark.parametrize("L,B,D", [(16385, 1, 3), (20001, 2, 2), (32768, 1, 2),
+                                   (32769, 1, 3), (40000, 2, 2), (65536, 1, 2), (65001, 1, 2),
                                    (131072, 1, 2), (262143, 1, 1), (300000, 1, 1)])
 def test_fftconv_large(io, L, B, D):
     w = small(io, D=D, L=L, B=B)
