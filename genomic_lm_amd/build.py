@@ -38,6 +38,15 @@ def flags() -> list[str]:
     ]
 
 
+# Extra flags per source file.  The MFMA kernels keep their accumulators in
+# ordinary VGPRs: they have the registers to spare, and the AGPR form costs a
+# v_accvgpr_read for every result element used by the vector ALUs.
+EXTRA_FLAGS = {
+    "chunk_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fir_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -45,7 +54,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *flags(), "-c", src, "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
