@@ -46,9 +46,20 @@ What it computes (plain definitions, written out, in fp64):
   window followed by its own u, and leaves the last K-1 values of that
   concatenation as the new window.
 
+* Complex-pole modal filters (Evo 1: the Hyena filter is given by modal-form
+  poles / residues with a state size of 8, Evo1-1.5-7B-8K model card,
+  §Architecture).  The pages give no formula; the reading taken here is the
+  real part of a sum of complex exponentials,
+      h[c,t] = Re sum_n R[c,n] * exp(lam[c,n] * t),  lam, R complex,
+  with the poles given in log form like Evo 2's log_poles (p = exp(lam); a
+  pole p enters as lam = log|p| + i arg p).  Real modes are the case
+  Im lam = 0 = Im R.  The modal state is complex, s_n(t) = sum_{k<=t}
+  p_n^(t-k) u[k], and z[t] = Re sum_n R_n s_n(t).
+
 Arrays are channel-major: activations (B, D, L), parameters (D, N) / (D,) /
-(D, K), state (B, D, N), FIR window (B, D, K-1) oldest first.  Everything is
-upcast to fp64 first.
+(D, K), state (B, D, N), FIR window (B, D, K-1) oldest first; complex
+parameters and states are numpy complex arrays.  Everything is upcast to
+fp64 (complex128) first.
 """
 from __future__ import annotations
 
@@ -59,6 +70,7 @@ __all__ = [
     "modal_filter", "conv_direct", "conv_fft", "causal_conv",
     "hyena_fwd", "fir_fwd", "modal_state", "chunk_fwd", "next_pow2",
     "modal_decode", "fir_fwd_window",
+    "modal_filter_cpx", "hyena_fwd_cpx", "modal_state_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
 ]
 
 DIRECT_MAX_L = 4096      # direct O(L^2) sum up to this length, FFT above
@@ -243,3 +255,85 @@ def fir_fwd_window(x1, x2, v, taps, skip, window_in=None):
         z += w[None, :, k:k + 1] * e[..., K - 1 - k:K - 1 - k + L]
     sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
     return x2 * z + sk[None, :, None] * u, e[..., e.shape[-1] - (K - 1):]
+
+
+# ---------------------------------------------------------------- complex poles
+def _cpx(a):
+    return np.asarray(a, dtype=np.complex128)
+
+
+def modal_filter_cpx(log_poles, residues, L: int) -> np.ndarray:
+    """h[c, t] = Re sum_n R[c, n] exp(lam[c, n] t), t in [0, L); fp64 (D, L)."""
+    lam = _cpx(log_poles)
+    R = _cpx(residues)
+    t = np.arange(L, dtype=np.float64)
+    return np.real(np.einsum("dn,dnt->dt", R, np.exp(lam[:, :, None] * t[None, None, :])))
+
+
+def hyena_fwd_cpx(x1, x2, v, log_poles, residues, skip, conv=causal_conv) -> np.ndarray:
+    """The Hyena operator with a complex-pole modal filter, single pass."""
+    L = np.asarray(x1).shape[-1]
+    h = modal_filter_cpx(log_poles, residues, L)
+    return _gate(x1, x2, v, lambda u: conv(u, h[None]), skip)
+
+
+def modal_state_cpx(u, log_poles, state_in=None) -> np.ndarray:
+    """s_n(L-1) = p^L s_in + sum_k p^(L-1-k) u[k], complex (B, D, N)."""
+    u = np.asarray(u, dtype=np.float64)
+    lam = _cpx(log_poles)
+    L = u.shape[-1]
+    k = np.arange(L, dtype=np.float64)
+    w = np.exp(lam[:, :, None] * (L - 1 - k)[None, None, :])
+    s = np.einsum("bdl,dnl->bdn", u, w)
+    if state_in is not None:
+        s = s + np.exp(lam * L)[None] * _cpx(state_in)
+    return s
+
+
+def chunk_fwd_cpx(x1, x2, v, log_poles, residues, skip, C: int, state_in=None):
+    """Chunked prefill with a complex modal state, fp64.
+
+    Within the chunk [t0, t0 + C'): the in-chunk convolution plus
+    Re sum_n R_n p_n^(t-t0+1) s_n; then s_n <- p_n^C' s_n + sum_j
+    p_n^(C'-1-j) u[t0+j].  Returns y (B, D, L) and the state (B, D, N).
+    """
+    x1 = np.asarray(x1, dtype=np.float64)
+    x2 = np.asarray(x2, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lam = _cpx(log_poles)
+    R = _cpx(residues)
+    B, D, L = x1.shape
+    N = lam.shape[1]
+    s = np.zeros((B, D, N), np.complex128) if state_in is None else _cpx(state_in).copy()
+    u = x1 * v
+    z = np.zeros_like(u)
+    h = modal_filter_cpx(lam, R, min(C, L))
+    for t0 in range(0, L, C):
+        Cp = min(C, L - t0)
+        uc = u[..., t0:t0 + Cp]
+        zc = causal_conv(uc, h[None, :, :Cp])
+        j = np.arange(Cp, dtype=np.float64)
+        carry = np.exp(lam[:, :, None] * (j + 1)[None, None, :])
+        zc = zc + np.real(np.einsum("dn,bdn,dnj->bdj", R, s, carry))
+        z[..., t0:t0 + Cp] = zc
+        decay_in = np.exp(lam[:, :, None] * (Cp - 1 - j)[None, None, :])
+        s = np.exp(lam * Cp)[None] * s + np.einsum("bdj,dnj->bdn", uc, decay_in)
+    sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
+    return x2 * z + sk[:, None] * u, s
+
+
+def modal_decode_cpx(x1, x2, v, log_poles, residues, skip, state_in=None):
+    """One decode step with a complex modal state: s <- p s + u,
+    y = x2 Re sum_n R_n s_n + skip u.  Returns y (B, D) and the state."""
+    x1 = np.asarray(x1, dtype=np.float64)
+    x2 = np.asarray(x2, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lam = _cpx(log_poles)
+    R = _cpx(residues)
+    B, D = x1.shape
+    s = np.zeros((B, D, lam.shape[1]), np.complex128) if state_in is None else _cpx(state_in)
+    u = x1 * v
+    s = np.exp(lam)[None] * s + u[:, :, None]
+    z = np.real(np.einsum("dn,bdn->bd", R, s))
+    sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
+    return x2 * z + sk[None, :] * u, s

@@ -374,6 +374,92 @@ def pin_fir_window_pieces(O):
             assert np.array_equal(win, (x1 * v)[..., L - (K - 1):]), K
 
 
+# ---------------------------------------------------------------- complex poles
+def _cparams(rng, D, N, lam_lo=1e-3):
+    a = -np.exp(rng.uniform(math.log(lam_lo), 0.0, (D, N)))
+    b = rng.uniform(-math.pi, math.pi, (D, N))
+    R = rng.normal(0, 0.25, (D, N)) + 1j * rng.normal(0, 0.25, (D, N))
+    return a + 1j * b, R
+
+
+def _gmul(x, y):
+    return (x[0] * y[0] - x[1] * y[1], x[0] * y[1] + x[1] * y[0])
+
+
+def pin_cpx_filter_rational(O):
+    """h[t] = Re sum_n R_n p_n^t with Gaussian-rational poles and residues,
+    computed exactly with fractions.Fraction pairs."""
+    poles = [(Fraction(1, 2), Fraction(1, 3)), (Fraction(-3, 4), Fraction(1, 8)),
+             (Fraction(2, 5), Fraction(-3, 5))]
+    res = [(Fraction(1), Fraction(-1, 2)), (Fraction(2, 3), Fraction(1, 4)),
+           (Fraction(-5, 4), Fraction(3, 2))]
+    lam = np.log(np.array([complex(float(a), float(b)) for a, b in poles]))[None]
+    R = np.array([complex(float(a), float(b)) for a, b in res])[None]
+    h = O.modal_filter_cpx(lam, R, 14)
+    for t in range(14):
+        tot = Fraction(0)
+        for p, r in zip(poles, res):
+            pt = (Fraction(1), Fraction(0))
+            for _ in range(t):
+                pt = _gmul(pt, p)
+            tot += _gmul(r, pt)[0]
+        assert abs(h[0, t] - float(tot)) <= 1e-14 * max(1.0, abs(float(tot))), (t, h[0, t], tot)
+
+
+def pin_cpx_second_order_recurrence(O):
+    """One complex mode p = r e^(i th) gives a real filter obeying
+    h[t] = 2 r cos(th) h[t-1] - r^2 h[t-2]."""
+    rng = _rng(40)
+    lam, R = _cparams(rng, 3, 1)
+    h = O.modal_filter_cpx(lam, R, 300)
+    r = np.exp(lam.real)[:, 0]
+    th = lam.imag[:, 0]
+    pred = 2 * r[:, None] * np.cos(th)[:, None] * h[:, 1:-1] - (r ** 2)[:, None] * h[:, :-2]
+    assert np.max(np.abs(pred - h[:, 2:])) <= 1e-12 * np.max(np.abs(h))
+
+
+def pin_cpx_real_special_case(O):
+    """Complex modes with zero imaginary parts give the real-mode operator,
+    state and decode step."""
+    rng = _rng(41)
+    B, D, N, L = 2, 3, 16, 400
+    lam, R = _params(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, B, D, L))
+    skip = rng.normal(size=D)
+    y_r = O.hyena_fwd(x1, x2, v, lam, R, skip)
+    y_c = O.hyena_fwd_cpx(x1, x2, v, lam + 0j, R + 0j, skip)
+    assert np.max(np.abs(y_c - y_r)) <= 1e-12 * np.max(np.abs(y_r))
+    yc_r, s_r = O.chunk_fwd(x1, x2, v, lam, R, skip, 128)
+    yc_c, s_c = O.chunk_fwd_cpx(x1, x2, v, lam + 0j, R + 0j, skip, 128)
+    assert np.max(np.abs(yc_c - yc_r)) <= 1e-12 * np.max(np.abs(yc_r))
+    assert np.max(np.abs(s_c.imag)) == 0.0
+    assert np.max(np.abs(s_c.real - s_r)) <= 1e-12 * np.max(np.abs(s_r))
+    yd_r, sd_r = O.modal_decode(x1[..., 0], x2[..., 0], v[..., 0], lam, R, skip, state_in=s_r)
+    yd_c, sd_c = O.modal_decode_cpx(x1[..., 0], x2[..., 0], v[..., 0], lam + 0j, R + 0j, skip,
+                                    state_in=s_c)
+    assert np.max(np.abs(yd_c - yd_r)) <= 1e-12 * np.max(np.abs(yd_r))
+
+
+def pin_cpx_chunk_and_decode_equal_full(O):
+    """Complex modes: chunked prefill (any C) and decode steps after it give
+    the single pass over the whole sequence; the state is its definition."""
+    rng = _rng(42)
+    B, D, N, L, T = 2, 3, 8, 500, 12
+    lam, R = _cparams(rng, D, N)
+    x1, x2, v = rng.normal(size=(3, B, D, L + T))
+    skip = rng.normal(size=D)
+    y_full = O.hyena_fwd_cpx(x1, x2, v, lam, R, skip)
+    s_full = O.modal_state_cpx((x1 * v)[..., :L], lam)
+    for C in (1, 64, 100, L):
+        yc, sc = O.chunk_fwd_cpx(x1[..., :L], x2[..., :L], v[..., :L], lam, R, skip, C)
+        assert np.max(np.abs(yc - y_full[..., :L])) <= 1e-10 * np.max(np.abs(y_full)), C
+        assert np.max(np.abs(sc - s_full)) <= 1e-10 * np.max(np.abs(s_full)), C
+    s = sc
+    for t in range(L, L + T):
+        yt, s = O.modal_decode_cpx(x1[..., t], x2[..., t], v[..., t], lam, R, skip, state_in=s)
+        assert np.max(np.abs(yt - y_full[..., t])) <= 1e-10 * np.max(np.abs(y_full)), t
+
+
 ALL_PINS = [
     pin_golden, pin_filter_rational, pin_filter_dft, pin_recurrence,
     pin_impulse, pin_linearity_time_invariance, pin_numpy_convolve,
@@ -381,4 +467,6 @@ ALL_PINS = [
     pin_fir_delta, pin_chunk_equals_full, pin_chunk_resume,
     pin_chunk_state_rational, pin_scale_equivariance,
     pin_decode_after_prefill, pin_decode_impulse_rational, pin_fir_window_pieces,
+    pin_cpx_filter_rational, pin_cpx_second_order_recurrence, pin_cpx_real_special_case,
+    pin_cpx_chunk_and_decode_equal_full,
 ]

@@ -41,8 +41,16 @@ def _mutant(**over):
             return mod.conv_direct(u, h)
         return mod.conv_fft(u, h)
 
+    def hyena_fwd_cpx(x1, x2, v, log_poles, residues, skip, conv=None):
+        L = np.asarray(x1).shape[-1]
+        h = mod.modal_filter_cpx(log_poles, residues, L)
+        cv = conv or mod.causal_conv
+        return mod._gate(x1, x2, v, lambda u: cv(u, h[None]), skip)
+
     if "hyena_fwd" not in over:
         mod.hyena_fwd = hyena_fwd
+    if "hyena_fwd_cpx" not in over:
+        mod.hyena_fwd_cpx = hyena_fwd_cpx
     if "fir_fwd" not in over:
         mod.fir_fwd = fir_fwd
     if "causal_conv" not in over:
@@ -154,6 +162,42 @@ def _fir_window_variant(first_values=False, reversed_taps=False):
     return fir_fwd_window
 
 
+def _filter_cpx_imag(log_poles, residues, L):        # imaginary part taken
+    lam = np.asarray(log_poles, complex)
+    R = np.asarray(residues, complex)
+    t = np.arange(L, dtype=float)
+    return np.imag(np.einsum("dn,dnt->dt", R, np.exp(lam[:, :, None] * t)))
+
+
+def _filter_cpx_conj_pole(log_poles, residues, L):   # pole conjugated
+    lam = np.conj(np.asarray(log_poles, complex))
+    R = np.asarray(residues, complex)
+    t = np.arange(L, dtype=float)
+    return np.real(np.einsum("dn,dnt->dt", R, np.exp(lam[:, :, None] * t)))
+
+
+def _chunk_cpx_carry_conj(x1, x2, v, log_poles, residues, skip, C, state_in=None):
+    """chunk_fwd_cpx with the carried state conjugated."""
+    x1, x2, v = (np.asarray(a, float) for a in (x1, x2, v))
+    lam = np.asarray(log_poles, complex)
+    R = np.asarray(residues, complex)
+    B, D, L = x1.shape
+    s = np.zeros((B, D, lam.shape[1]), complex) if state_in is None else np.array(state_in, complex)
+    u = x1 * v
+    z = np.zeros_like(u)
+    h = HO.modal_filter_cpx(lam, R, min(C, L))
+    for t0 in range(0, L, C):
+        Cp = min(C, L - t0)
+        uc = u[..., t0:t0 + Cp]
+        zc = HO.causal_conv(uc, h[None, :, :Cp])
+        j = np.arange(Cp, dtype=float)
+        zc = zc + np.real(np.einsum("dn,bdn,dnj->bdj", R, np.conj(s), np.exp(lam[:, :, None] * (j + 1))))
+        z[..., t0:t0 + Cp] = zc
+        s = np.exp(lam * Cp)[None] * s + np.einsum("bdj,dnj->bdn", uc, np.exp(lam[:, :, None] * (Cp - 1 - j)))
+    sk = np.zeros(D) if skip is None else np.asarray(skip, float)
+    return x2 * z + sk[:, None] * u, s
+
+
 MUTANTS = {
     "filter_time_origin": dict(modal_filter=_filter_shifted),
     "filter_dropped_mode": dict(modal_filter=_filter_dropped_mode),
@@ -167,6 +211,9 @@ MUTANTS = {
     "decode_output_before_update": dict(modal_decode=_decode_variant(output_before_update=True)),
     "fir_window_first_values": dict(fir_fwd_window=_fir_window_variant(first_values=True)),
     "fir_window_reversed_taps": dict(fir_fwd_window=_fir_window_variant(reversed_taps=True)),
+    "cpx_filter_imag_part": dict(modal_filter_cpx=_filter_cpx_imag),
+    "cpx_filter_conj_pole": dict(modal_filter_cpx=_filter_cpx_conj_pole),
+    "cpx_chunk_carry_conj": dict(chunk_fwd_cpx=_chunk_cpx_carry_conj),
 }
 
 
