@@ -214,6 +214,14 @@ def main():
         win = torch.zeros((B, D, 127), dtype=torch.float32, device=dev)
         runs["fir128_window_step"] = lambda: G.fir_fwd_window(*tok3, taps128, skip, window_in=win,
                                                               out=y3, window_out=win)
+        # complex-pole modes (Evo 1 form, 8 per channel) at the same shape
+        lc, rc = W.complex_modes(D, 8, seed=5)
+        lc_d, rc_d = torch.from_numpy(lc).to(dev), torch.from_numpy(rc).to(dev)
+        stc = torch.empty((B, D, 8), dtype=torch.complex64, device=dev)
+        runs["fftconv_cpx_single_pass"] = lambda: G.fftconv_fwd_cpx(x1, x2, v, lc_d, rc_d, skip,
+                                                                     out=y, workspace=fft_ws)
+        runs["chunk_cpx_fft"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip, out=y,
+                                                        state_out=stc)
         one_token = {"modal_decode_step", "fir128_window_step"}   # B*D token·channels
         for name, fn in runs.items():
             t = timed(fn, comp_steps, 2, stream)

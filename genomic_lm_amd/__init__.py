@@ -15,6 +15,9 @@ Entry points (names follow the C ABI):
   modal_decode(x1, x2, v, log_poles, residues, skip=None,
                state_in=None)       (x of shape (B, D))       -> (y, state_out)
   fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None) -> (y, window_out)
+Complex-pole variants (log_poles / residues complex64 (D, N), states
+complex64 (B, D, N)): modal_filter_cpx, fftconv_fwd_cpx, chunk_fwd_cpx,
+modal_decode_cpx.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ __all__ = [
     "HyenaError", "HyenaNotBuilt", "lib", "LIB_PATH", "abi_version",
     "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
     "modal_decode", "fir_fwd_window",
+    "modal_filter_cpx", "fftconv_fwd_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
     "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_LAUNCH",
     "F32", "BF16", "ALGOS", "EXPORTS",
 ]
@@ -57,6 +61,13 @@ EXPORTS = {
                                   _p]),
     "hyena_fir_fwd_window": (_int, [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
                                     _int, _p]),
+    "hyena_modal_filter_cpx": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
+    "hyena_fftconv_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
+                                     _p, _size, _p]),
+    "hyena_chunk_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
+                                   _i64, _int, _p]),
+    "hyena_modal_decode_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64,
+                                      _int, _p]),
 }
 
 
@@ -276,3 +287,116 @@ def fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None, out=None, window_
         _ptr(x1), _ptr(x2), _ptr(v), _ptr(taps), K, _ptr(skip), _ptr(window_in),
         _ptr(window_out), _ptr(y), B, D, L, _io(x1), _stream(x1)))
     return y, window_out
+
+
+# ------------------------------------------------------------------ complex poles
+def _cparam(name, t, D, dev, optional=False):
+    """A complex (D, N) parameter: complex64, or float32 with a trailing (re, im)
+    axis.  Returns (tensor viewed as float32 pairs, N)."""
+    if t is None:
+        if optional:
+            return None, None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype == torch.complex64:
+        t = torch.view_as_real(t)
+    if t.dtype != torch.float32 or t.dim() != 3 or t.shape[0] != D or t.shape[2] != 2:
+        raise ValueError(f"{name} must be complex64 (D, N) or float32 (D, N, 2)")
+    if t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous on {dev}")
+    return t, t.shape[1]
+
+
+def _cstate(name, t, shape, dev, optional=False):
+    """A complex state (B, D, N): complex64 or float32 (B, D, N, 2)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype == torch.complex64:
+        t = torch.view_as_real(t)
+    _param(name, t, tuple(shape) + (2,), dev)
+    return t
+
+
+def modal_filter_cpx(log_poles, residues, L: int) -> torch.Tensor:
+    """h[c, t] = Re sum_n residues[c, n] exp(log_poles[c, n] t), fp32 (D, L)."""
+    D = log_poles.shape[0]
+    lp, N = _cparam("log_poles", log_poles, D, log_poles.device)
+    rs, N2 = _cparam("residues", residues, D, log_poles.device)
+    if N2 != N:
+        raise ValueError("log_poles and residues must have the same number of modes")
+    h = torch.empty((D, L), dtype=torch.float32, device=lp.device)
+    _check("hyena_modal_filter_cpx", lib().hyena_modal_filter_cpx(
+        _ptr(lp), _ptr(rs), D, N, L, _ptr(h), _stream(h)))
+    return h
+
+
+def _cmodal(x1, log_poles, residues):
+    B, D = x1.shape[0], x1.shape[1]
+    lp, N = _cparam("log_poles", log_poles, D, x1.device)
+    rs, N2 = _cparam("residues", residues, D, x1.device)
+    if N2 != N:
+        raise ValueError("log_poles and residues must have the same number of modes")
+    return lp, rs, N
+
+
+def fftconv_fwd_cpx(x1, x2, v, log_poles, residues, skip=None, out=None,
+                    workspace=None) -> torch.Tensor:
+    """Single pass with a complex-pole modal filter."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    lp, rs, N = _cmodal(x1, log_poles, residues)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    need = fftconv_workspace_size(B, D, L, N, x1.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x1.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hyena_fftconv_fwd_cpx", lib().hyena_fftconv_fwd_cpx(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(y),
+        B, D, L, _io(x1), _ptr(workspace), ws_bytes, _stream(x1)))
+    return y
+
+
+def chunk_fwd_cpx(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
+                  out=None, state_out=None):
+    """Chunked prefill with a complex modal state; returns (y, state_out complex64)."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    lp, rs, N = _cmodal(x1, log_poles, residues)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    si = _cstate("state_in", state_in, (B, D, N), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    if state_out is None:
+        state_out = torch.empty((B, D, N), dtype=torch.complex64, device=x1.device)
+    so = _cstate("state_out", state_out, (B, D, N), x1.device)
+    _check("hyena_chunk_fwd_cpx", lib().hyena_chunk_fwd_cpx(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
+        _ptr(y), B, D, L, int(C), _io(x1), _stream(x1)))
+    return y, state_out
+
+
+def modal_decode_cpx(x1, x2, v, log_poles, residues, skip=None, state_in=None, out=None,
+                     state_out=None):
+    """One decode step from a complex modal state: x1, x2, v are (B, D)."""
+    _act("x1", x1, dims=2)
+    _act("x2", x2, x1, dims=2)
+    _act("v", v, x1, dims=2)
+    B, D = x1.shape
+    lp, rs, N = _cmodal(x1, log_poles, residues)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    si = _cstate("state_in", state_in, (B, D, N), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1, dims=2)
+    if state_out is None:
+        state_out = torch.empty((B, D, N), dtype=torch.complex64, device=x1.device)
+    so = _cstate("state_out", state_out, (B, D, N), x1.device)
+    _check("hyena_modal_decode_cpx", lib().hyena_modal_decode_cpx(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
+        _ptr(y), B, D, _io(x1), _stream(x1)))
+    return y, state_out

@@ -26,7 +26,10 @@ namespace hyena {
 constexpr int CHUNK_MAXN = 64;
 constexpr int CHUNK_NG = 16;             // modes per reduction group
 
-template <int S, int T, typename IO, bool VEC>
+// CPX: complex modes, lam and res as (re, im) pairs, complex state (B, D, N)
+// as (re, im) pairs; h = Re sum_n R_n exp(lam_n t) and the carried term is
+// Re sum_n R_n p_n^(t-t0+1) s_n.
+template <int S, int T, typename IO, bool VEC, bool CPX>
 __global__ __launch_bounds__(T) void chunk_fft_kernel(
     const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
@@ -37,7 +40,9 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   constexpr int LG_M = ilog2(M);
   constexpr int LG_N = LG_M + 1;
   __shared__ float2 lds[lds_padded_size(S)];
-  __shared__ float s_lam[CHUNK_MAXN], s_res[CHUNK_MAXN], s_st[CHUNK_MAXN];
+  constexpr int W = CPX ? 2 : 1;                 // floats per mode parameter / state
+  __shared__ float s_lam[W * CHUNK_MAXN], s_res[W * CHUNK_MAXN], s_st[W * CHUNK_MAXN];
+  __shared__ float s_tot[W * CHUNK_MAXN];
   __shared__ float red[T * (CHUNK_NG + 1)];      // partial sums of one mode group
 
   const int t = threadIdx.x;
@@ -49,10 +54,11 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   IO* yr = y + row * L;
   const float sk = skip ? skip[c] : 0.0f;
 
-  for (int n = t; n < N; n += T) {
-    s_lam[n] = lam[static_cast<int64_t>(c) * N + n];
-    s_res[n] = res[static_cast<int64_t>(c) * N + n];
-    s_st[n] = state_in ? state_in[row * N + n] : 0.0f;
+  const int NR = W * N;                          // real slots of the modes
+  for (int n = t; n < NR; n += T) {
+    s_lam[n] = lam[static_cast<int64_t>(c) * NR + n];
+    s_res[n] = res[static_cast<int64_t>(c) * NR + n];
+    s_st[n] = state_in ? state_in[row * NR + n] : 0.0f;
   }
   __syncthreads();
 
@@ -65,15 +71,29 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
 #pragma unroll
     for (int i = 0; i < P; ++i) a[i] = make_float2(0.0f, 0.0f);
     for (int n = 0; n < N; ++n) {
-      const float l = s_lam[n];
-      const float p = expf(l);
-      const float step = expf(l * static_cast<float>(2 * T));
-      float e = s_res[n] * expf(l * static_cast<float>(2 * t));
+      if constexpr (CPX) {
+        const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
+        const float2 p = cexp_at(md, 1.0f);
+        const float2 step = cexp_at(md, static_cast<float>(2 * T));
+        float2 e = cmul(make_float2(s_res[2 * n], s_res[2 * n + 1]),
+                        cexp_at(md, static_cast<float>(2 * t)));
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        a[i].x += e;
-        a[i].y = fmaf(e, p, a[i].y);
-        e *= step;
+        for (int i = 0; i < P; ++i) {
+          a[i].x += e.x;
+          a[i].y += fmaf(e.x, p.x, -e.y * p.y);   // Re(e p)
+          e = cmul(e, step);
+        }
+      } else {
+        const float l = s_lam[n];
+        const float p = expf(l);
+        const float step = expf(l * static_cast<float>(2 * T));
+        float e = s_res[n] * expf(l * static_cast<float>(2 * t));
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          a[i].x += e;
+          a[i].y = fmaf(e, p, a[i].y);
+          e *= step;
+        }
       }
     }
 #pragma unroll
@@ -156,49 +176,105 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     // carried term sum_n R_n p_n^(tau+1) s_n (old state), and the state
     // partials, reduced over the workgroup 16 modes at a time
     const bool full = (Cp == 2 * S);       // ladder only when the chunk fills the frame
-    for (int n0 = 0; n0 < N; n0 += CHUNK_NG) {
-      const int ng = min(CHUNK_NG, N - n0);
-      for (int g = 0; g < ng; ++g) {
-        const int n = n0 + g;
-        const float l = s_lam[n];
-        const float p = expf(l);
-        const float step = expf(l * static_cast<float>(2 * T));
-        float e = s_res[n] * s_st[n] * expf(l * static_cast<float>(2 * t + 1));
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-          zz[i].x += e;
-          zz[i].y = fmaf(e, p, zz[i].y);
-          e *= step;
-        }
-        // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
-        float part = 0.0f;
-        if (full) {
-          float w = expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
-#pragma unroll
-          for (int i = P - 1; i >= 0; --i) {
-            part = fmaf(u[i].x, w * p, part);
-            part = fmaf(u[i].y, w, part);
-            w *= step;
-          }
-        } else {
+    // groups of CHUNK_NG real slots (a complex mode takes two: re, im)
+    for (int n0 = 0; n0 < NR; n0 += CHUNK_NG) {
+      const int ng = min(CHUNK_NG, NR - n0);
+      if constexpr (CPX) {
+        for (int g = 0; g < ng; g += 2) {
+          const int n = (n0 + g) >> 1;
+          const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
+          const float2 p = cexp_at(md, 1.0f);
+          const float2 step = cexp_at(md, static_cast<float>(2 * T));
+          float2 e = cmul(cmul(make_float2(s_res[2 * n], s_res[2 * n + 1]),
+                               make_float2(s_st[2 * n], s_st[2 * n + 1])),
+                          cexp_at(md, static_cast<float>(2 * t + 1)));
 #pragma unroll
           for (int i = 0; i < P; ++i) {
-            const int m2 = 2 * (t + T * i);
-            const float w = expf(l * static_cast<float>(max(Cp - 2 - m2, 0)));
-            part = fmaf(u[i].x, (m2 + 1 < Cp) ? w * p : w, part);   // m2 = Cp-1: weight p^0
-            part = fmaf(u[i].y, w, part);                              // zero beyond Cp anyway
+            zz[i].x += e.x;
+            zz[i].y += fmaf(e.x, p.x, -e.y * p.y);   // Re(e p)
+            e = cmul(e, step);
           }
+          // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
+          float2 part = make_float2(0.0f, 0.0f);
+          if (full) {
+            float2 w = cexp_at(md, static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+#pragma unroll
+            for (int i = P - 1; i >= 0; --i) {
+              const float2 wp = cmul(w, p);
+              part = make_float2(fmaf(u[i].x, wp.x, fmaf(u[i].y, w.x, part.x)),
+                                 fmaf(u[i].x, wp.y, fmaf(u[i].y, w.y, part.y)));
+              w = cmul(w, step);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+              const int m2 = 2 * (t + T * i);
+              const float2 w = cexp_at(md, static_cast<float>(max(Cp - 2 - m2, 0)));
+              const float2 w0 = (m2 + 1 < Cp) ? cmul(w, p) : w;   // m2 = Cp-1: weight p^0
+              part = make_float2(fmaf(u[i].x, w0.x, fmaf(u[i].y, w.x, part.x)),
+                                 fmaf(u[i].x, w0.y, fmaf(u[i].y, w.y, part.y)));
+            }
+          }
+          red[t * (CHUNK_NG + 1) + g] = part.x;
+          red[t * (CHUNK_NG + 1) + g + 1] = part.y;
         }
-        red[t * (CHUNK_NG + 1) + g] = part;
+      } else {
+        for (int g = 0; g < ng; ++g) {
+          const int n = n0 + g;
+          const float l = s_lam[n];
+          const float p = expf(l);
+          const float step = expf(l * static_cast<float>(2 * T));
+          float e = s_res[n] * s_st[n] * expf(l * static_cast<float>(2 * t + 1));
+#pragma unroll
+          for (int i = 0; i < P; ++i) {
+            zz[i].x += e;
+            zz[i].y = fmaf(e, p, zz[i].y);
+            e *= step;
+          }
+          // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
+          float part = 0.0f;
+          if (full) {
+            float w = expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+#pragma unroll
+            for (int i = P - 1; i >= 0; --i) {
+              part = fmaf(u[i].x, w * p, part);
+              part = fmaf(u[i].y, w, part);
+              w *= step;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+              const int m2 = 2 * (t + T * i);
+              const float w = expf(l * static_cast<float>(max(Cp - 2 - m2, 0)));
+              part = fmaf(u[i].x, (m2 + 1 < Cp) ? w * p : w, part);   // m2 = Cp-1: weight p^0
+              part = fmaf(u[i].y, w, part);                              // zero beyond Cp anyway
+            }
+          }
+          red[t * (CHUNK_NG + 1) + g] = part;
+        }
       }
       __syncthreads();                     // partials written; old state no longer read
       for (int g = t; g < ng; g += T) {
         float tot = 0.0f;
         for (int j = 0; j < T; ++j) tot += red[j * (CHUNK_NG + 1) + g];
         const int n = n0 + g;
-        s_st[n] = fmaf(expf(s_lam[n] * static_cast<float>(Cp)), s_st[n], tot);
+        if constexpr (CPX) {
+          s_tot[n] = tot;                  // the complex update needs both slots
+        } else {
+          s_st[n] = fmaf(expf(s_lam[n] * static_cast<float>(Cp)), s_st[n], tot);
+        }
       }
       __syncthreads();                     // red reusable
+    }
+    if constexpr (CPX) {
+      for (int n = t; n < N; n += T) {
+        const float2 pc = cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
+        const float2 sn = cadd(cmul(pc, make_float2(s_st[2 * n], s_st[2 * n + 1])),
+                               make_float2(s_tot[2 * n], s_tot[2 * n + 1]));
+        s_st[2 * n] = sn.x;
+        s_st[2 * n + 1] = sn.y;
+      }
+      __syncthreads();
     }
     // gate and store
 #pragma unroll
@@ -210,7 +286,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       st_pair<IO, VEC>(yr, pos, lim, out);
     }
   }
-  for (int n = t; n < N; n += T) state_out[row * N + n] = s_st[n];
+  for (int n = t; n < NR; n += T) state_out[row * NR + n] = s_st[n];
 }
 
 int chunk_fft_S(int64_t C) {
@@ -220,19 +296,19 @@ int chunk_fft_S(int64_t C) {
   return S <= 4096 ? static_cast<int>(S) : 0;
 }
 
+template <int S, int T, typename IO, bool VEC, bool CPX>
+static void launch_chunk_k(const ChunkArgs& a, int C) {
+  chunk_fft_kernel<S, T, IO, VEC, CPX><<<dim3(static_cast<unsigned>(a.B * a.D)), dim3(T), 0, a.stream>>>(
+      static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
+      a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L, C);
+}
+
 template <int S, int T, typename IO>
 static hipError_t launch_chunk_s(const ChunkArgs& a, int C, bool vec) {
-  dim3 grid(static_cast<unsigned>(a.B * a.D)), block(T);
-  const IO* x1 = static_cast<const IO*>(a.x1);
-  const IO* x2 = static_cast<const IO*>(a.x2);
-  const IO* v = static_cast<const IO*>(a.v);
-  IO* y = static_cast<IO*>(a.y);
-  if (vec)
-    chunk_fft_kernel<S, T, IO, true><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L, C);
+  if (a.cpx)
+    vec ? launch_chunk_k<S, T, IO, true, true>(a, C) : launch_chunk_k<S, T, IO, false, true>(a, C);
   else
-    chunk_fft_kernel<S, T, IO, false><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L, C);
+    vec ? launch_chunk_k<S, T, IO, true, false>(a, C) : launch_chunk_k<S, T, IO, false, false>(a, C);
   return hipGetLastError();
 }
 

@@ -96,4 +96,35 @@ __device__ __forceinline__ float2 twiddle(int num, int lg) {
   return make_float2(__builtin_amdgcn_cosf(x), __builtin_amdgcn_sinf(x));
 }
 
+// ------------------------------------------------------------------ complex modes
+// A complex mode exp(lam x), lam = a + i b, evaluated for real x >= 0 (up to
+// 2^20).  The phase b x is reduced in revolutions at double-float precision:
+// b / (2 pi) = fhi + flo, fhi x is split exactly by an fma, and only the
+// fractional part reaches v_cos / v_sin (which take revolutions); a plain
+// fp32 b * x would lose ~1e-3 revolutions at x = 2^15.
+struct CpxMode {
+  float a, fhi, flo;
+};
+
+__device__ __forceinline__ CpxMode cpx_mode(float a, float b) {
+  constexpr float c_hi = 0.15915494f;   // 1 / (2 pi), high part
+  constexpr float c_lo = static_cast<float>(0.15915494309189535 - static_cast<double>(c_hi));
+  CpxMode m;
+  m.a = a;
+  m.fhi = b * c_hi;
+  m.flo = fmaf(b, c_hi, -m.fhi) + b * c_lo;
+  return m;
+}
+
+__device__ __forceinline__ float2 cexp_at(const CpxMode& m, float x) {
+  // no contraction here: fused into p - rint(p), the product fhi x would be
+  // taken exactly there and its rounding error e then added a second time
+#pragma clang fp contract(off)
+  const float p = m.fhi * x;
+  const float e = fmaf(m.fhi, x, -p);              // exact: fhi x = p + e
+  const float r = (p - rintf(p)) + fmaf(m.flo, x, e);
+  const float mag = expf(m.a * x);
+  return make_float2(mag * __builtin_amdgcn_cosf(r), mag * __builtin_amdgcn_sinf(r));
+}
+
 }  // namespace hyena

@@ -13,6 +13,8 @@
 // new window.  The rest of the outputs do not depend on the window and come
 // from the ordinary FIR kernels, launched first on the same stream; this
 // kernel then overwrites the outputs they computed with a zero history.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,7 +23,8 @@ namespace hyena {
 // One lane per (row, mode): a row's modes sit in a group of G = next power
 // of two >= N lanes of one wave, so every load is coalesced across the group
 // and the sum over modes is a butterfly of log2(G) lane exchanges.
-template <typename IO>
+// CPX: complex modes and state as (re, im) pairs; y = x2 Re sum_n R_n s_n + skip u.
+template <typename IO, bool CPX>
 __global__ __launch_bounds__(256) void modal_decode_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
     const float* __restrict__ lam, const float* __restrict__ res, int N, int lgG,
@@ -42,9 +45,19 @@ __global__ __launch_bounds__(256) void modal_decode_kernel(
     const int64_t pi = static_cast<int64_t>(c) * N + n;
     const int64_t si = row * N + n;
     // read before write: state_out may be state_in
-    const float s = fmaf(expf(lam[pi]), state_in ? state_in[si] : 0.0f, u);
-    state_out[si] = s;
-    part = res[pi] * s;
+    if constexpr (CPX) {
+      const float2 p = cexp_at(cpx_mode(lam[2 * pi], lam[2 * pi + 1]), 1.0f);
+      const float2 s0 = state_in ? make_float2(state_in[2 * si], state_in[2 * si + 1])
+                                 : make_float2(0.0f, 0.0f);
+      const float2 s = make_float2(cmul(p, s0).x + u, cmul(p, s0).y);
+      state_out[2 * si] = s.x;
+      state_out[2 * si + 1] = s.y;
+      part = fmaf(res[2 * pi], s.x, -res[2 * pi + 1] * s.y);
+    } else {
+      const float s = fmaf(expf(lam[pi]), state_in ? state_in[si] : 0.0f, u);
+      state_out[si] = s;
+      part = res[pi] * s;
+    }
   }
   // every lane of the wave takes part in the exchanges (groups never span
   // waves: G divides 64)
@@ -103,16 +116,17 @@ hipError_t launch_modal_decode(const DecodeArgs& a) {
   int lgG = 0;
   while ((1 << lgG) < a.N) ++lgG;         // N <= 64: G <= 64 lanes
   const unsigned blocks = static_cast<unsigned>(((rows << lgG) + 255) / 256);
-  if (a.bf16)
-    modal_decode_kernel<bf16_t><<<blocks, 256, 0, a.stream>>>(
-        static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
-        static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, lgG, a.skip, a.state_in, a.state_out,
-        static_cast<bf16_t*>(a.y), a.D, rows);
-  else
-    modal_decode_kernel<float><<<blocks, 256, 0, a.stream>>>(
-        static_cast<const float*>(a.x1), static_cast<const float*>(a.x2),
-        static_cast<const float*>(a.v), a.lam, a.res, a.N, lgG, a.skip, a.state_in, a.state_out,
-        static_cast<float*>(a.y), a.D, rows);
+  auto go = [&](auto io_tag, auto cpx_tag) {
+    using IO = decltype(io_tag);
+    modal_decode_kernel<IO, decltype(cpx_tag)::value><<<blocks, 256, 0, a.stream>>>(
+        static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
+        a.lam, a.res, a.N, lgG, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, rows);
+  };
+  if (a.bf16) {
+    if (a.cpx) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
+  } else {
+    if (a.cpx) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

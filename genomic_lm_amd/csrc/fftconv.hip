@@ -54,7 +54,35 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
   }
 }
 
-template <int S, int T, typename IO, bool VEC>
+// The same pairs for complex modes (lam, res as (re, im) pairs):
+// (Re sum_n R_n p_n^(2m), Re sum_n R_n p_n^(2m+1)), a ladder of P steps of
+// p^(2T) from an exact anchor per mode.
+template <int P, int T>
+__device__ __forceinline__ void modal_pairs_cpx(float2 (&a)[P], const float* lam, const float* res,
+                                                int N, int t, int L) {
+#pragma unroll
+  for (int i = 0; i < P; ++i) a[i] = make_float2(0.0f, 0.0f);
+  for (int n = 0; n < N; ++n) {
+    const CpxMode md = cpx_mode(lam[2 * n], lam[2 * n + 1]);
+    const float2 p = cexp_at(md, 1.0f);
+    const float2 step = cexp_at(md, static_cast<float>(2 * T));
+    float2 e = cmul(make_float2(res[2 * n], res[2 * n + 1]), cexp_at(md, static_cast<float>(2 * t)));
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      a[i].x += e.x;
+      a[i].y += fmaf(e.x, p.x, -e.y * p.y);      // Re(e p)
+      e = cmul(e, step);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int m2 = 2 * (t + T * i);
+    if (m2 >= L) a[i].x = 0.0f;
+    if (m2 + 1 >= L) a[i].y = 0.0f;
+  }
+}
+
+template <int S, int T, typename IO, bool VEC, bool CPX>
 __global__ __launch_bounds__(T) void fftconv_kernel(
     const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
@@ -72,8 +100,9 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   const IO* x2r = x2 + row * L;
   const IO* vr = v + row * L;
   IO* yr = y + row * L;
-  const float* lamc = lam + static_cast<int64_t>(c) * N;
-  const float* resc = res + static_cast<int64_t>(c) * N;
+  constexpr int W = CPX ? 2 : 1;               // floats per mode parameter
+  const float* lamc = lam + static_cast<int64_t>(c) * N * W;
+  const float* resc = res + static_cast<int64_t>(c) * N * W;
 
   float2 b0[P];           // inverse transform of the even half, kept for the recombination
   float zm_nyq = 0.0f;    // Z[M] (real), only used by thread 0
@@ -109,7 +138,10 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
     if (q == 0 && t == 0) um_nyq = a[0].x - a[0].y;
 
     // ---- h, generated on chip, same packing
-    modal_pairs<P, T>(a, lamc, resc, N, t, L);
+    if constexpr (CPX)
+      modal_pairs_cpx<P, T>(a, lamc, resc, N, t, L);
+    else
+      modal_pairs<P, T>(a, lamc, resc, N, t, L);
     if (q) {
 #pragma unroll
       for (int i = 0; i < P; ++i) a[i] = cmul(a[i], twiddle(t + T * i, LG_M));
@@ -165,19 +197,19 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   }
 }
 
+template <int S, int T, typename IO, bool VEC, bool CPX>
+static void launch_k(const FftconvArgs& a) {
+  fftconv_kernel<S, T, IO, VEC, CPX><<<dim3(static_cast<unsigned>(a.B * a.D)), dim3(T), 0, a.stream>>>(
+      static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
+      a.lam, a.res, a.N, a.skip, static_cast<IO*>(a.y), a.D, a.L);
+}
+
 template <int S, int T, typename IO>
 static hipError_t launch_s(const FftconvArgs& a, bool vec) {
-  dim3 grid(static_cast<unsigned>(a.B * a.D)), block(T);
-  const IO* x1 = static_cast<const IO*>(a.x1);
-  const IO* x2 = static_cast<const IO*>(a.x2);
-  const IO* v = static_cast<const IO*>(a.v);
-  IO* y = static_cast<IO*>(a.y);
-  if (vec)
-    fftconv_kernel<S, T, IO, true><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, y, a.D, a.L);
+  if (a.cpx)
+    vec ? launch_k<S, T, IO, true, true>(a) : launch_k<S, T, IO, false, true>(a);
   else
-    fftconv_kernel<S, T, IO, false><<<grid, block, 0, a.stream>>>(
-        x1, x2, v, a.lam, a.res, a.N, a.skip, y, a.D, a.L);
+    vec ? launch_k<S, T, IO, true, false>(a) : launch_k<S, T, IO, false, false>(a);
   return hipGetLastError();
 }
 

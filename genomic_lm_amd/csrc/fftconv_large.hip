@@ -55,7 +55,7 @@ constexpr int ROW_UNITS = 129 + 128;
 
 // Column pass, forward.  Thread (t, col): t-major so that one wave touches 16
 // consecutive columns of four rows (128-byte segments).
-template <typename IO, bool VEC>
+template <typename IO, bool VEC, bool CPX>
 __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
     const IO* x1, const IO* v, const float* __restrict__ lam, const float* __restrict__ res,
     int N, float2* __restrict__ ws, int row0, int D, int L, int lgS1) {
@@ -82,23 +82,38 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
       d[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
     }
   } else {
-    // (h[2m], h[2m+1]), h[t] = sum_n R_n exp(lam_n t); a ladder of CP steps
-    // of exp(2 lam S1 CT) from an exact anchor per mode
+    // (h[2m], h[2m+1]), h[t] = (Re) sum_n R_n exp(lam_n t); a ladder of CP
+    // steps of exp(2 lam S1 CT) from an exact anchor per mode
     const int c = static_cast<int>(row % D);
-    const float* lamc = lam + int64_t(c) * N;
-    const float* resc = res + int64_t(c) * N;
+    constexpr int W = CPX ? 2 : 1;
+    const float* lamc = lam + int64_t(c) * N * W;
+    const float* resc = res + int64_t(c) * N * W;
 #pragma unroll
     for (int i = 0; i < CP; ++i) d[i] = make_float2(0.0f, 0.0f);
     for (int n = 0; n < N; ++n) {
-      const float l = lamc[n];
-      const float p = expf(l);
-      const float step = expf(l * static_cast<float>(2 * S1 * CT));
-      float e = resc[n] * expf(l * static_cast<float>(2 * (m1 + S1 * t)));
+      if constexpr (CPX) {
+        const CpxMode md = cpx_mode(lamc[2 * n], lamc[2 * n + 1]);
+        const float2 p = cexp_at(md, 1.0f);
+        const float2 step = cexp_at(md, static_cast<float>(2 * S1 * CT));
+        float2 e = cmul(make_float2(resc[2 * n], resc[2 * n + 1]),
+                        cexp_at(md, static_cast<float>(2 * (m1 + S1 * t))));
 #pragma unroll
-      for (int i = 0; i < CP; ++i) {
-        d[i].x += e;
-        d[i].y = fmaf(e, p, d[i].y);
-        e *= step;
+        for (int i = 0; i < CP; ++i) {
+          d[i].x += e.x;
+          d[i].y += fmaf(e.x, p.x, -e.y * p.y);   // Re(e p)
+          e = cmul(e, step);
+        }
+      } else {
+        const float l = lamc[n];
+        const float p = expf(l);
+        const float step = expf(l * static_cast<float>(2 * S1 * CT));
+        float e = resc[n] * expf(l * static_cast<float>(2 * (m1 + S1 * t)));
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+          d[i].x += e;
+          d[i].y = fmaf(e, p, d[i].y);
+          e *= step;
+        }
       }
     }
 #pragma unroll
@@ -281,7 +296,7 @@ hipError_t launch_rows(float2* ws, int nr, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename IO, bool VEC>
+template <typename IO, bool VEC, bool CPX>
 hipError_t launch_large_io(const FftconvArgs& a, int64_t S) {
   const int S1 = static_cast<int>(S / S2);
   const int lgS1 = ilog2(S1);
@@ -294,7 +309,7 @@ hipError_t launch_large_io(const FftconvArgs& a, int64_t S) {
   float2* ws = static_cast<float2*>(a.workspace);
   for (int64_t r0 = 0; r0 < rows; r0 += nb) {
     const int nr = static_cast<int>(rows - r0 < nb ? rows - r0 : nb);
-    fftconv_cols_fwd<IO, VEC><<<dim3(S1 / GC, 2, nr), NTC, 0, a.stream>>>(
+    fftconv_cols_fwd<IO, VEC, CPX><<<dim3(S1 / GC, 2, nr), NTC, 0, a.stream>>>(
         x1, v, a.lam, a.res, a.N, ws, static_cast<int>(r0), a.D, a.L, lgS1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -329,9 +344,14 @@ hipError_t launch_fftconv_large(const FftconvArgs& a) {
   if (S == 0) return hipErrorInvalidValue;
   const size_t esz = a.bf16 ? 2 : 4;
   const bool vec = (a.L % 2 == 0) && aligned_all(2 * esz, a.x1, a.x2, a.v, a.y);
+  if (a.cpx) {
+    if (a.bf16)
+      return vec ? launch_large_io<bf16_t, true, true>(a, S) : launch_large_io<bf16_t, false, true>(a, S);
+    return vec ? launch_large_io<float, true, true>(a, S) : launch_large_io<float, false, true>(a, S);
+  }
   if (a.bf16)
-    return vec ? launch_large_io<bf16_t, true>(a, S) : launch_large_io<bf16_t, false>(a, S);
-  return vec ? launch_large_io<float, true>(a, S) : launch_large_io<float, false>(a, S);
+    return vec ? launch_large_io<bf16_t, true, false>(a, S) : launch_large_io<bf16_t, false, false>(a, S);
+  return vec ? launch_large_io<float, true, false>(a, S) : launch_large_io<float, false, false>(a, S);
 }
 
 }  // namespace hyena

@@ -10,24 +10,39 @@
 
 namespace hyena {
 
+// CPX: lam and R are complex, (re, im) pairs, and h = Re sum_n R_n exp(lam_n t)
+// (the complex-pole form of Evo 1's poles / residues, Evo1-1.5-7B-8K model
+// card, Architecture).
+template <bool CPX>
 __global__ __launch_bounds__(256) void modal_filter_kernel(
     const float* __restrict__ lam, const float* __restrict__ res, int N, int L,
     float* __restrict__ h) {
   const int c = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= L) return;
-  const float* lc = lam + static_cast<int64_t>(c) * N;
-  const float* rc = res + static_cast<int64_t>(c) * N;
+  constexpr int W = CPX ? 2 : 1;
+  const float* lc = lam + static_cast<int64_t>(c) * N * W;
+  const float* rc = res + static_cast<int64_t>(c) * N * W;
   const float tf = static_cast<float>(t);
   float acc = 0.0f;
-  for (int n = 0; n < N; ++n) acc = fmaf(rc[n], expf(lc[n] * tf), acc);
+  for (int n = 0; n < N; ++n) {
+    if constexpr (CPX) {
+      const float2 e = cexp_at(cpx_mode(lc[2 * n], lc[2 * n + 1]), tf);
+      acc = fmaf(rc[2 * n], e.x, fmaf(-rc[2 * n + 1], e.y, acc));
+    } else {
+      acc = fmaf(rc[n], expf(lc[n] * tf), acc);
+    }
+  }
   h[static_cast<int64_t>(c) * L + t] = acc;
 }
 
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
-                               float* h, hipStream_t stream) {
+                               float* h, bool cpx, hipStream_t stream) {
   dim3 grid((L + 255) / 256, D);
-  modal_filter_kernel<<<grid, 256, 0, stream>>>(lam, res, N, L, h);
+  if (cpx)
+    modal_filter_kernel<true><<<grid, 256, 0, stream>>>(lam, res, N, L, h);
+  else
+    modal_filter_kernel<false><<<grid, 256, 0, stream>>>(lam, res, N, L, h);
   return hipGetLastError();
 }
 

@@ -72,8 +72,12 @@ const char* hyena_status_string(hyena_status_t status) {
   return "HYENA_ERR_UNKNOWN";
 }
 
-hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
-                                  int64_t N, int64_t L, float* h, void* stream) {
+}  // extern "C"
+
+namespace {
+
+hyena_status_t modal_filter_impl(const float* log_poles, const float* residues, int64_t D,
+                                 int64_t N, int64_t L, float* h, bool cpx, void* stream) {
   if (D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
   if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
   if (D == 0 || L == 0) return HYENA_OK;
@@ -84,7 +88,21 @@ hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues,
     return HYENA_ERR_UNSUPPORTED;
   return from_hip(hyena::launch_modal_filter(log_poles, residues, static_cast<int>(D),
                                              static_cast<int>(N), static_cast<int>(L), h,
-                                             as_stream(stream)));
+                                             cpx, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
+                                  int64_t N, int64_t L, float* h, void* stream) {
+  return modal_filter_impl(log_poles, residues, D, N, L, h, false, stream);
+}
+
+hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues, int64_t D,
+                                      int64_t N, int64_t L, float* h, void* stream) {
+  return modal_filter_impl(log_poles, residues, D, N, L, h, true, stream);
 }
 
 hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, const float* taps,
@@ -125,11 +143,15 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
   return from_hip(hyena::launch_fir_window(a, window_in, window_out));
 }
 
-hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
-                                  const float* log_poles, const float* residues, int64_t N,
-                                  const float* skip, const float* state_in, float* state_out,
-                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
+                           const float* log_poles, const float* residues, int64_t N,
+                           const float* skip, const float* state_in, float* state_out,
+                           void* y, int64_t B, int64_t D, hyena_dtype_t io, bool cpx,
+                           void* stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, 1, io, &empty);
   if (st != HYENA_OK) return st;
@@ -141,8 +163,30 @@ hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
     return HYENA_ERR_INVALID_ARG;
   hyena::DecodeArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                       state_out, y, static_cast<int>(B), static_cast<int>(D),
-                      io == HYENA_BF16, as_stream(stream)};
+                      io == HYENA_BF16, as_stream(stream), cpx};
   return from_hip(hyena::launch_modal_decode(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
+                                  const float* log_poles, const float* residues, int64_t N,
+                                  const float* skip, const float* state_in, float* state_out,
+                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                  void* stream) {
+  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
+                     false, stream);
+}
+
+hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void* v,
+                                      const float* log_poles, const float* residues, int64_t N,
+                                      const float* skip, const float* state_in, float* state_out,
+                                      void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                      void* stream) {
+  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
+                     true, stream);
 }
 
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {
@@ -154,11 +198,15 @@ size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, 
   return hyena::fftconv_large_workspace(B, D, L);
 }
 
-hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
-                                 const float* log_poles, const float* residues, int64_t N,
-                                 const float* skip, void* y, int64_t B, int64_t D, int64_t L,
-                                 hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
+                            const float* log_poles, const float* residues, int64_t N,
+                            const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                            hyena_dtype_t io, void* workspace, size_t ws_bytes, bool cpx,
+                            void* stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
   if (st != HYENA_OK) return st;
@@ -169,7 +217,7 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
   if (st != HYENA_OK) return st;
   hyena::FftconvArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, y,
                        static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
-                       io == HYENA_BF16, workspace, ws_bytes, as_stream(stream)};
+                       io == HYENA_BF16, workspace, ws_bytes, as_stream(stream), cpx};
   if (hyena::fftconv_onchip_S(L) != 0) return from_hip(hyena::launch_fftconv_onchip(a));
   const size_t need = hyena::fftconv_large_workspace(B, D, L);
   if (need == 0) return HYENA_ERR_UNSUPPORTED;
@@ -177,11 +225,37 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
   return from_hip(hyena::launch_fftconv_large(a));
 }
 
-hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
-                               const float* log_poles, const float* residues, int64_t N,
-                               const float* skip, const float* state_in, float* state_out,
-                               void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                               hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
+}  // namespace
+
+extern "C" {
+
+hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
+                                 const float* log_poles, const float* residues, int64_t N,
+                                 const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                                 hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
+                      ws_bytes, false, stream);
+}
+
+hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void* v,
+                                     const float* log_poles, const float* residues, int64_t N,
+                                     const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                                     hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
+                      ws_bytes, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
+                          const float* log_poles, const float* residues, int64_t N,
+                          const float* skip, const float* state_in, float* state_out,
+                          void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                          hyena_dtype_t io, hyena_chunk_algo_t algo, bool cpx, void* stream) {
   if (algo != HYENA_CHUNK_AUTO && algo != HYENA_CHUNK_FFT && algo != HYENA_CHUNK_MFMA)
     return HYENA_ERR_INVALID_ARG;
   bool empty = false;
@@ -193,7 +267,8 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
     if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
       return HYENA_ERR_INVALID_ARG;
     if (B * D > kMaxInt) return HYENA_ERR_UNSUPPORTED;
-    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N, as_stream(stream)));
+    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N * (cpx ? 2 : 1),
+                                             as_stream(stream)));
   }
   if (st != HYENA_OK) return st;
   if (C < 1) return HYENA_ERR_INVALID_ARG;
@@ -205,14 +280,36 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
     return HYENA_ERR_INVALID_ARG;
   const int64_t Ceff = C < L ? C : L;
   hyena_chunk_algo_t use = algo;
-  if (use == HYENA_CHUNK_AUTO) use = (N <= 16) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
-  if (use == HYENA_CHUNK_MFMA && N > 16) return HYENA_ERR_UNSUPPORTED;
+  if (use == HYENA_CHUNK_AUTO) use = (N <= 16 && !cpx) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
+  if (use == HYENA_CHUNK_MFMA && (N > 16 || cpx)) return HYENA_ERR_UNSUPPORTED;
   if (use == HYENA_CHUNK_FFT && Ceff > HYENA_MAX_FFT_CHUNK) return HYENA_ERR_UNSUPPORTED;
   hyena::ChunkArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                      state_out, y, static_cast<int>(B), static_cast<int>(D),
                      static_cast<int>(L), static_cast<int>(Ceff), io == HYENA_BF16,
-                     as_stream(stream)};
+                     as_stream(stream), cpx};
   return from_hip(use == HYENA_CHUNK_MFMA ? hyena::launch_chunk_mfma(a) : hyena::launch_chunk_fft(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
+                               const float* log_poles, const float* residues, int64_t N,
+                               const float* skip, const float* state_in, float* state_out,
+                               void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                               hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
+  return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
+                    C, io, algo, false, stream);
+}
+
+hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
+                                   const float* log_poles, const float* residues, int64_t N,
+                                   const float* skip, const float* state_in, float* state_out,
+                                   void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                                   hyena_dtype_t io, void* stream) {
+  return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
+                    C, io, HYENA_CHUNK_FFT, true, stream);
 }
 
 }  // extern "C"

@@ -30,6 +30,7 @@ struct FftconvArgs {
   void* workspace;
   size_t ws_bytes;
   hipStream_t stream;
+  bool cpx = false;
 };
 
 struct FirArgs {
@@ -59,6 +60,7 @@ struct ChunkArgs {
   int B, D, L, C;
   bool bf16;
   hipStream_t stream;
+  bool cpx = false;
 };
 
 struct DecodeArgs {
@@ -75,10 +77,12 @@ struct DecodeArgs {
   int B, D;
   bool bf16;
   hipStream_t stream;
+  bool cpx = false;
 };
 
+// cpx: complex modes, lam and res as (re, im) pairs (also in the structs below)
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
-                               float* h, hipStream_t stream);
+                               float* h, bool cpx, hipStream_t stream);
 
 hipError_t launch_fir(const FirArgs& a);        // picks the kernel below or the VALU one
 hipError_t launch_fir_mfma(const FirArgs& a);   // bf16, K <= 128

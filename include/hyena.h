@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 2
+#define HYENA_ABI_VERSION 3
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -226,6 +226,53 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
                                     const float* window_in, float* window_out,
                                     void* y, int64_t B, int64_t D, int64_t L,
                                     hyena_dtype_t io, void* stream);
+
+/*
+ * Complex-pole modal filters.  Evo 1's Hyena filter is given by modal-form
+ * poles / residues with a Hyena state size of 8, kept in fp32 (Evo1-1.5-7B-8K
+ * model card, Architecture).  The entry points below take the poles in log
+ * form like Evo 2's log_poles, as complex numbers:
+ *   h[c, t] = Re sum_{n<N} R[c, n] exp(lam[c, n] t),   p = exp(lam),
+ * where log_poles and residues are (D, N) complex, stored as (D, N, 2) fp32
+ * (re, im) pairs; a pole p enters as lam = log|p| + i arg(p).  Modes with zero
+ * imaginary parts give exactly the real-mode operator.  States are (B, D, N)
+ * complex, stored as (B, D, N, 2) fp32 pairs.  Everything else -- layouts,
+ * ownership, errors, workspace -- is as for the real-mode entry point of the
+ * same name.
+ */
+
+/* h (D, L) fp32, as hyena_modal_filter. */
+hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues,
+                                      int64_t D, int64_t N, int64_t L, float* h,
+                                      void* stream);
+
+/* Single pass, as hyena_fftconv_fwd (same workspace size). */
+hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void* v,
+                                     const float* log_poles, const float* residues,
+                                     int64_t N, const float* skip, void* y,
+                                     int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Chunked prefill with the complex modal state carried in and out, as
+ * hyena_chunk_fwd with the FFT algorithm:
+ *   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + Re sum_n R_n p_n^(t-t0+1) s_n,
+ *   s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j];
+ * C' <= HYENA_MAX_FFT_CHUNK. */
+hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
+                                   const float* log_poles, const float* residues,
+                                   int64_t N, const float* skip,
+                                   const float* state_in, float* state_out,
+                                   void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                                   hyena_dtype_t io, void* stream);
+
+/* One decode step, as hyena_modal_decode: s_n <- p_n s_n + u,
+ * y = x2 * Re sum_n R_n s_n + skip * u. */
+hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void* v,
+                                      const float* log_poles, const float* residues,
+                                      int64_t N, const float* skip,
+                                      const float* state_in, float* state_out,
+                                      void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                      void* stream);
 
 #ifdef __cplusplus
 }

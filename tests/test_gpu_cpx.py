@@ -1,0 +1,134 @@
+"""Complex-pole modal filters (Evo 1's poles / residues, in log form) on the
+GPU, through the C ABI, against the fp64 oracle: the filter, the single pass
+(on chip and four-step), chunked prefill with a complex state, and decode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import genomic_lm_amd as G
+import oracle
+import workloads as W
+from tests.gpu_util import DevWorkload, gate, log, sample_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()
+    yield
+
+
+def _setup(io, D, L, B=1, N=8, seed=21, lam_lo=1e-3):
+    w = W.make("tiny" if io == "f32" else "7b_layer_set", B=B, D=D, L=L)
+    lam, R = W.complex_modes(D, N, seed, lam_lo)
+    d = DevWorkload(w)
+    dev = d.x1.device
+    return w, d, lam, R, torch.from_numpy(lam).to(dev), torch.from_numpy(R).to(dev)
+
+
+def _ref(w, lam, R, rows=None, C=None, state_in=None):
+    rows = np.arange(w.D) if rows is None else np.asarray(rows)
+    x1, x2, v = (w.f64(k, rows) for k in ("x1", "x2", "v"))
+    s0 = None if state_in is None else state_in[:, rows]
+    if C is None and s0 is None:
+        y = oracle.hyena_fwd_cpx(x1, x2, v, lam[rows], R[rows], w.skip[rows])
+        return y, oracle.modal_state_cpx(x1 * v, lam[rows])
+    return oracle.chunk_fwd_cpx(x1, x2, v, lam[rows], R[rows], w.skip[rows], C or w.L, state_in=s0)
+
+
+def _state_err(s_dev, ref):
+    s = s_dev.cpu().numpy().astype(np.complex128)
+    num = np.sqrt(np.sum(np.abs(s - ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(np.abs(ref) ** 2, axis=-1))
+    return float(np.sqrt(np.mean((num / np.where(den > 0, den, 1)) ** 2)))
+
+
+@pytest.mark.parametrize("L", [1, 777, 8192, 40000])
+def test_modal_filter_cpx(L):
+    w, d, lam, R, lam_d, R_d = _setup("f32", D=16, L=8)
+    log(f"modal_filter_cpx L={L}")
+    h = to_f64(G.modal_filter_cpx(lam_d, R_d, L))
+    ref = oracle.modal_filter_cpx(lam, R, L)
+    err = np.sqrt(np.sum((h - ref) ** 2, -1) / np.sum(ref ** 2, -1))
+    assert np.max(err) < 2e-5, err
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [100, 1024, 3001, 16384, 20001, 40000])
+def test_fftconv_cpx(io, L):
+    w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2 if L < 5000 else 1)
+    log(f"fftconv_cpx io={io} L={L}")
+    y = G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, d.skip)
+    ref, _ = _ref(w, lam, R)
+    gate(y, ref, io, label=f"fftconv_cpx L={L}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("C,L", [(64, 1000), (1024, 3000), (1000, 4096), (4096, 9000), (8192, 8192)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_chunk_cpx(io, C, L, with_state):
+    w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2)
+    s0 = W.random_complex_state(2, w.D, 8, seed=C) if with_state else None
+    s0_d = None if s0 is None else torch.from_numpy(s0).to(d.x1.device)
+    log(f"chunk_cpx io={io} C={C} L={L} state={with_state}")
+    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, C, d.skip, state_in=s0_d)
+    ref, ref_s = _ref(w, lam, R, C=C, state_in=s0)
+    gate(y, ref, io, label=f"chunk_cpx C={C}")
+    err = _state_err(s, ref_s)
+    log(f"  state rel_l2_ch={err:.3e}")
+    assert err < 1e-4
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_cpx_after_prefill(io):
+    L, T = 3000, 16
+    w, d, lam, R, lam_d, R_d = _setup(io, D=16, L=L + T, B=2)
+    pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
+    y_pre, s = G.chunk_fwd_cpx(*pre, lam_d, R_d, 1024, d.skip)
+    ys = [y_pre]
+    for t in range(L, L + T):
+        yt, s = G.modal_decode_cpx(d.x1[..., t].contiguous(), d.x2[..., t].contiguous(),
+                                   d.v[..., t].contiguous(), lam_d, R_d, d.skip,
+                                   state_in=s, state_out=s)
+        ys.append(yt[..., None])
+    ref, ref_s = _ref(w, lam, R)
+    gate(torch.cat(ys, -1), ref, io, label="cpx prefill+decode")
+    assert _state_err(s, ref_s) < 1e-4
+
+
+def test_cpx_with_real_modes_matches_real_entries():
+    """Zero imaginary parts: the complex entry points equal the real ones."""
+    w = W.make("7b_layer_set", D=8, L=5000)
+    d = DevWorkload(w)
+    lam_c = torch.complex(d.lam, torch.zeros_like(d.lam))
+    R_c = torch.complex(d.res, torch.zeros_like(d.res))
+    ref, ref_s = oracle.hyena_fwd(w.f64("x1"), w.f64("x2"), w.f64("v"), w.log_poles, w.residues,
+                                  w.skip), None
+    for name, y in (
+        ("fftconv", G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, d.skip)),
+        ("chunk", G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, 1024, d.skip)[0]),
+    ):
+        gate(y, ref, "bf16", label=f"real modes via {name}_cpx")
+        y_real = (G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip) if name == "fftconv"
+                  else G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="fft")[0])
+        diff = (y.float() - y_real.float()).abs().max().item()
+        assert diff <= 2e-2 * y_real.float().abs().max().item(), (name, diff)
+
+
+def test_cpx_7b_shape():
+    """D = 4096, L = 8192, N = 8 complex modes: single pass and chunked, sampled rows."""
+    w = W.make("7b_layer_set")
+    lam, R = W.complex_modes(w.D, 8, seed=77)
+    d = DevWorkload(w)
+    lam_d, R_d = torch.from_numpy(lam).to(d.x1.device), torch.from_numpy(R).to(d.x1.device)
+    rows = sample_rows(w.D)
+    ref, ref_s = _ref(w, lam, R, rows)
+    gate(G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, d.skip), ref, "bf16", rows,
+         label="7b cpx fftconv")
+    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip)
+    gate(y, ref, "bf16", rows, label="7b cpx chunk")
+    assert _state_err(s[:, torch.as_tensor(rows, device=s.device)], ref_s) < 1e-4

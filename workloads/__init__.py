@@ -233,3 +233,22 @@ def random_state(B: int, D: int, N: int, seed: int) -> np.ndarray:
     """A (B, D, N) fp32 modal state ~ N(0, 1) for resume tests."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
     return g.normal(0.0, 1.0, (B, D, N)).astype(np.float32)
+
+
+def complex_modes(D: int, N: int, seed: int, lam_lo: float = 1e-3):
+    """Complex log-poles and residues (D, N) complex64, the parameters of a
+    complex-pole modal filter (Evo 1: state size 8):
+    Re lam = -exp(U(ln lam_lo, 0)) (decay as the real log_poles),
+    Im lam ~ U(-pi, pi) (oscillation per token),
+    R ~ N(0, 1/16) + i N(0, 1/16)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 11])))
+    a = -np.exp(g.uniform(np.log(lam_lo), 0.0, (D, N)))
+    b = g.uniform(-np.pi, np.pi, (D, N))
+    R = g.normal(0.0, 0.25, (D, N)) + 1j * g.normal(0.0, 0.25, (D, N))
+    return (a + 1j * b).astype(np.complex64), R.astype(np.complex64)
+
+
+def random_complex_state(B: int, D: int, N: int, seed: int) -> np.ndarray:
+    """A (B, D, N) complex64 modal state ~ N(0, 1) + i N(0, 1) for resume tests."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 13])))
+    return (g.normal(0.0, 1.0, (B, D, N)) + 1j * g.normal(0.0, 1.0, (B, D, N))).astype(np.complex64)
