@@ -154,6 +154,24 @@ def test_chunk_small(algo, io, C, L):
         state_gate(s, ref_s, label=f"chunk/{algo} C={C} L={L}")
 
 
+@pytest.mark.parametrize("N", [1, 3, 17, 64])
+def test_mode_counts(N):
+    """From one mode to the maximum of 64: single pass, chunked with AUTO (the
+    matrix-core path up to 16 modes, FFT beyond), and each algorithm it has."""
+    w = W.make("7b_layer_set", B=2, D=4, L=3000, N=N)
+    d = DevWorkload(w)
+    log(f"modes N={N}")
+    ref, ref_s = oracle_modal(w)
+    gate(G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip), ref, "bf16", label=f"fftconv N={N}")
+    for algo in (["auto", "fft", "mfma"] if N <= 16 else ["auto", "fft"]):
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo=algo)
+        gate(y, ref, "bf16", label=f"chunk/{algo} N={N}")
+        state_gate(s, ref_s, label=f"chunk/{algo} N={N}")
+    if N > 16:
+        with pytest.raises(G.HyenaError, match="UNSUPPORTED"):
+            G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="mfma")
+
+
 @pytest.mark.parametrize("algo", ["mfma", "fft"])
 def test_chunk_resume_matches_single_call(algo):
     """Split anywhere, carry the state through the host, continue."""
