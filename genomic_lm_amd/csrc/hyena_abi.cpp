@@ -55,26 +55,8 @@ int64_t next_pow2(int64_t x) {
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-int hyena_abi_version(void) { return HYENA_ABI_VERSION; }
-
-const char* hyena_status_string(hyena_status_t status) {
-  switch (status) {
-    case HYENA_OK: return "HYENA_OK";
-    case HYENA_ERR_INVALID_ARG: return "HYENA_ERR_INVALID_ARG: null, negative, misaligned or out-of-range argument";
-    case HYENA_ERR_UNSUPPORTED: return "HYENA_ERR_UNSUPPORTED: shape beyond the limits of this build";
-    case HYENA_ERR_WORKSPACE: return "HYENA_ERR_WORKSPACE: workspace missing or too small";
-    case HYENA_ERR_LAUNCH: return "HYENA_ERR_LAUNCH: a HIP launch or runtime call failed";
-  }
-  return "HYENA_ERR_UNKNOWN";
-}
-
-}  // extern "C"
-
-namespace {
+// ---- validated implementations; the real- and complex-mode entry points
+// share them (cpx: parameters and states as (re, im) pairs)
 
 hyena_status_t modal_filter_impl(const float* log_poles, const float* residues, int64_t D,
                                  int64_t N, int64_t L, float* h, bool cpx, void* stream) {
@@ -90,62 +72,6 @@ hyena_status_t modal_filter_impl(const float* log_poles, const float* residues, 
                                              static_cast<int>(N), static_cast<int>(L), h,
                                              cpx, as_stream(stream)));
 }
-
-}  // namespace
-
-extern "C" {
-
-hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
-                                  int64_t N, int64_t L, float* h, void* stream) {
-  return modal_filter_impl(log_poles, residues, D, N, L, h, false, stream);
-}
-
-hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues, int64_t D,
-                                      int64_t N, int64_t L, float* h, void* stream) {
-  return modal_filter_impl(log_poles, residues, D, N, L, h, true, stream);
-}
-
-hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, const float* taps,
-                             int64_t K, const float* skip, void* y, int64_t B, int64_t D,
-                             int64_t L, hyena_dtype_t io, void* stream) {
-  bool empty = false;
-  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
-  if (st != HYENA_OK) return st;
-  if (K < 1) return HYENA_ERR_INVALID_ARG;
-  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
-  if (empty) return HYENA_OK;
-  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
-  if (B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;   // grid.y
-  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
-                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
-  return from_hip(hyena::launch_fir(a));
-}
-
-hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* v,
-                                    const float* taps, int64_t K, const float* skip,
-                                    const float* window_in, float* window_out, void* y,
-                                    int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                    void* stream) {
-  bool empty = false;
-  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
-  // L = 0 still moves the window over; only B = 0 or D = 0 is a no-op
-  if (st != HYENA_OK) return st;
-  if (K < 1) return HYENA_ERR_INVALID_ARG;
-  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
-  if (B == 0 || D == 0) return HYENA_OK;
-  if (empty && K == 1) return HYENA_OK;
-  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
-  if (K > 1 && (!window_out || !aligned_to(window_out, 4) || (window_in && !aligned_to(window_in, 4))))
-    return HYENA_ERR_INVALID_ARG;
-  if (L > K - 1 && B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;
-  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
-                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
-  return from_hip(hyena::launch_fir_window(a, window_in, window_out));
-}
-
-}  // extern "C"
-
-namespace {
 
 hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
                            const float* log_poles, const float* residues, int64_t N,
@@ -166,41 +92,6 @@ hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
                       io == HYENA_BF16, as_stream(stream), cpx};
   return from_hip(hyena::launch_modal_decode(a));
 }
-
-}  // namespace
-
-extern "C" {
-
-hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
-                                  const float* log_poles, const float* residues, int64_t N,
-                                  const float* skip, const float* state_in, float* state_out,
-                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                  void* stream) {
-  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
-                     false, stream);
-}
-
-hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void* v,
-                                      const float* log_poles, const float* residues, int64_t N,
-                                      const float* skip, const float* state_in, float* state_out,
-                                      void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                      void* stream) {
-  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
-                     true, stream);
-}
-
-size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {
-  (void)N;
-  (void)io;
-  if (B <= 0 || D <= 0 || L <= 0) return 0;
-  if (hyena::fftconv_onchip_S(L) != 0) return 0;
-  if (next_pow2(2 * L) > HYENA_MAX_FFT_LEN) return 0;
-  return hyena::fftconv_large_workspace(B, D, L);
-}
-
-}  // extern "C"
-
-namespace {
 
 hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
                             const float* log_poles, const float* residues, int64_t N,
@@ -224,32 +115,6 @@ hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
   if (!workspace || ws_bytes < need || !aligned_to(workspace, 16)) return HYENA_ERR_WORKSPACE;
   return from_hip(hyena::launch_fftconv_large(a));
 }
-
-}  // namespace
-
-extern "C" {
-
-hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
-                                 const float* log_poles, const float* residues, int64_t N,
-                                 const float* skip, void* y, int64_t B, int64_t D, int64_t L,
-                                 hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                 void* stream) {
-  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
-                      ws_bytes, false, stream);
-}
-
-hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void* v,
-                                     const float* log_poles, const float* residues, int64_t N,
-                                     const float* skip, void* y, int64_t B, int64_t D, int64_t L,
-                                     hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                     void* stream) {
-  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
-                      ws_bytes, true, stream);
-}
-
-}  // extern "C"
-
-namespace {
 
 hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
                           const float* log_poles, const float* residues, int64_t N,
@@ -294,6 +159,58 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
 
 extern "C" {
 
+int hyena_abi_version(void) { return HYENA_ABI_VERSION; }
+
+const char* hyena_status_string(hyena_status_t status) {
+  switch (status) {
+    case HYENA_OK: return "HYENA_OK";
+    case HYENA_ERR_INVALID_ARG: return "HYENA_ERR_INVALID_ARG: null, negative, misaligned or out-of-range argument";
+    case HYENA_ERR_UNSUPPORTED: return "HYENA_ERR_UNSUPPORTED: shape beyond the limits of this build";
+    case HYENA_ERR_WORKSPACE: return "HYENA_ERR_WORKSPACE: workspace missing or too small";
+    case HYENA_ERR_LAUNCH: return "HYENA_ERR_LAUNCH: a HIP launch or runtime call failed";
+  }
+  return "HYENA_ERR_UNKNOWN";
+}
+
+hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
+                                  int64_t N, int64_t L, float* h, void* stream) {
+  return modal_filter_impl(log_poles, residues, D, N, L, h, false, stream);
+}
+
+hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, const float* taps,
+                             int64_t K, const float* skip, void* y, int64_t B, int64_t D,
+                             int64_t L, hyena_dtype_t io, void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  if (st != HYENA_OK) return st;
+  if (K < 1) return HYENA_ERR_INVALID_ARG;
+  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
+  if (empty) return HYENA_OK;
+  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
+  if (B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;   // grid.y
+  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+  return from_hip(hyena::launch_fir(a));
+}
+
+hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
+                                 const float* log_poles, const float* residues, int64_t N,
+                                 const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                                 hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
+                      ws_bytes, false, stream);
+}
+
+size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {
+  (void)N;
+  (void)io;
+  if (B <= 0 || D <= 0 || L <= 0) return 0;
+  if (hyena::fftconv_onchip_S(L) != 0) return 0;
+  if (next_pow2(2 * L) > HYENA_MAX_FFT_LEN) return 0;
+  return hyena::fftconv_large_workspace(B, D, L);
+}
+
 hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
                                const float* log_poles, const float* residues, int64_t N,
                                const float* skip, const float* state_in, float* state_out,
@@ -303,6 +220,51 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
                     C, io, algo, false, stream);
 }
 
+hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
+                                  const float* log_poles, const float* residues, int64_t N,
+                                  const float* skip, const float* state_in, float* state_out,
+                                  void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                  void* stream) {
+  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
+                     false, stream);
+}
+
+hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* v,
+                                    const float* taps, int64_t K, const float* skip,
+                                    const float* window_in, float* window_out, void* y,
+                                    int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                    void* stream) {
+  bool empty = false;
+  hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
+  // L = 0 still moves the window over; only B = 0 or D = 0 is a no-op
+  if (st != HYENA_OK) return st;
+  if (K < 1) return HYENA_ERR_INVALID_ARG;
+  if (K > HYENA_MAX_FIR_TAPS) return HYENA_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return HYENA_OK;
+  if (empty && K == 1) return HYENA_OK;
+  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
+  if (K > 1 && (!window_out || !aligned_to(window_out, 4) || (window_in && !aligned_to(window_in, 4))))
+    return HYENA_ERR_INVALID_ARG;
+  if (L > K - 1 && B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;
+  hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+  return from_hip(hyena::launch_fir_window(a, window_in, window_out));
+}
+
+hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues, int64_t D,
+                                      int64_t N, int64_t L, float* h, void* stream) {
+  return modal_filter_impl(log_poles, residues, D, N, L, h, true, stream);
+}
+
+hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void* v,
+                                     const float* log_poles, const float* residues, int64_t N,
+                                     const float* skip, void* y, int64_t B, int64_t D, int64_t L,
+                                     hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
+                      ws_bytes, true, stream);
+}
+
 hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
                                    const float* log_poles, const float* residues, int64_t N,
                                    const float* skip, const float* state_in, float* state_out,
@@ -310,6 +272,15 @@ hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v
                                    hyena_dtype_t io, void* stream) {
   return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
                     C, io, HYENA_CHUNK_FFT, true, stream);
+}
+
+hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void* v,
+                                      const float* log_poles, const float* residues, int64_t N,
+                                      const float* skip, const float* state_in, float* state_out,
+                                      void* y, int64_t B, int64_t D, hyena_dtype_t io,
+                                      void* stream) {
+  return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
+                     true, stream);
 }
 
 }  // extern "C"
