@@ -117,6 +117,48 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     if (q == 0 && t == 0) h_nyq = a[0].x - a[0].y;
   }
 
+  // ---- chunk-invariant mode factors, once per row: p, p^(2T) and the full
+  // chunk's p^(2S) per mode, and (one wave per row, up to 16 real slots) each
+  // thread's anchors of the carried-term ladder p^(2t+1) and of the
+  // state-weight ladder p^(2T-2-2t).  Partial chunks recompute theirs.
+  __shared__ float s_p[W * CHUNK_MAXN], s_step[W * CHUNK_MAXN], s_pf[W * CHUNK_MAXN];
+  constexpr bool TAB = (T == 64);
+  __shared__ float t_ea[TAB ? CHUNK_NG * T : 1], t_wa[TAB ? CHUNK_NG * T : 1];
+  const bool use_tab = TAB && NR <= CHUNK_NG;
+  for (int n = t; n < N; n += T) {
+    if constexpr (CPX) {
+      const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
+      const float2 p = cexp_at(md, 1.0f), st = cexp_at(md, static_cast<float>(2 * T)),
+                   pf = cexp_at(md, static_cast<float>(2 * S));
+      s_p[2 * n] = p.x;     s_p[2 * n + 1] = p.y;
+      s_step[2 * n] = st.x; s_step[2 * n + 1] = st.y;
+      s_pf[2 * n] = pf.x;   s_pf[2 * n + 1] = pf.y;
+    } else {
+      const float l = s_lam[n];
+      s_p[n] = expf(l);
+      s_step[n] = expf(l * static_cast<float>(2 * T));
+      s_pf[n] = expf(l * static_cast<float>(2 * S));
+    }
+  }
+  if (use_tab) {
+    for (int n = 0; n < N; ++n) {
+      if constexpr (CPX) {
+        const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
+        const float2 ea = cexp_at(md, static_cast<float>(2 * t + 1));
+        const float2 wa = cexp_at(md, static_cast<float>(2 * T - 2 - 2 * t));
+        t_ea[(2 * n) * T + t] = ea.x;
+        t_ea[(2 * n + 1) * T + t] = ea.y;
+        t_wa[(2 * n) * T + t] = wa.x;
+        t_wa[(2 * n + 1) * T + t] = wa.y;
+      } else {
+        const float l = s_lam[n];
+        t_ea[n * T + t] = expf(l * static_cast<float>(2 * t + 1));
+        t_wa[n * T + t] = expf(l * static_cast<float>(2 * T - 2 - 2 * t));
+      }
+    }
+  }
+  __syncthreads();
+
   const float inv_m = 1.0f / static_cast<float>(M);
 #pragma unroll 1
   for (int t0 = 0; t0 < L; t0 += C) {
@@ -183,11 +225,12 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         for (int g = 0; g < ng; g += 2) {
           const int n = (n0 + g) >> 1;
           const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
-          const float2 p = cexp_at(md, 1.0f);
-          const float2 step = cexp_at(md, static_cast<float>(2 * T));
+          const float2 p = make_float2(s_p[2 * n], s_p[2 * n + 1]);
+          const float2 step = make_float2(s_step[2 * n], s_step[2 * n + 1]);
+          const float2 ea = use_tab ? make_float2(t_ea[(2 * n) * T + t], t_ea[(2 * n + 1) * T + t])
+                                    : cexp_at(md, static_cast<float>(2 * t + 1));
           float2 e = cmul(cmul(make_float2(s_res[2 * n], s_res[2 * n + 1]),
-                               make_float2(s_st[2 * n], s_st[2 * n + 1])),
-                          cexp_at(md, static_cast<float>(2 * t + 1)));
+                               make_float2(s_st[2 * n], s_st[2 * n + 1])), ea);
 #pragma unroll
           for (int i = 0; i < P; ++i) {
             zz[i].x += e.x;
@@ -197,7 +240,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
           // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
           float2 part = make_float2(0.0f, 0.0f);
           if (full) {
-            float2 w = cexp_at(md, static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+            float2 w = use_tab ? make_float2(t_wa[(2 * n) * T + t], t_wa[(2 * n + 1) * T + t])
+                               : cexp_at(md, static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
 #pragma unroll
             for (int i = P - 1; i >= 0; --i) {
               const float2 wp = cmul(w, p);
@@ -222,9 +266,10 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         for (int g = 0; g < ng; ++g) {
           const int n = n0 + g;
           const float l = s_lam[n];
-          const float p = expf(l);
-          const float step = expf(l * static_cast<float>(2 * T));
-          float e = s_res[n] * s_st[n] * expf(l * static_cast<float>(2 * t + 1));
+          const float p = s_p[n];
+          const float step = s_step[n];
+          float e = s_res[n] * s_st[n] *
+                    (use_tab ? t_ea[n * T + t] : expf(l * static_cast<float>(2 * t + 1)));
 #pragma unroll
           for (int i = 0; i < P; ++i) {
             zz[i].x += e;
@@ -234,7 +279,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
           // weight of position 2m+1 is p^(Cp-2-2m), of 2m it is p^(Cp-1-2m)
           float part = 0.0f;
           if (full) {
-            float w = expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+            float w = use_tab ? t_wa[n * T + t]
+                              : expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
 #pragma unroll
             for (int i = P - 1; i >= 0; --i) {
               part = fmaf(u[i].x, w * p, part);
@@ -261,14 +307,16 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         if constexpr (CPX) {
           s_tot[n] = tot;                  // the complex update needs both slots
         } else {
-          s_st[n] = fmaf(expf(s_lam[n] * static_cast<float>(Cp)), s_st[n], tot);
+          const float pc = full ? s_pf[n] : expf(s_lam[n] * static_cast<float>(Cp));
+          s_st[n] = fmaf(pc, s_st[n], tot);
         }
       }
       __syncthreads();                     // red reusable
     }
     if constexpr (CPX) {
       for (int n = t; n < N; n += T) {
-        const float2 pc = cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
+        const float2 pc = full ? make_float2(s_pf[2 * n], s_pf[2 * n + 1])
+                               : cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
         const float2 sn = cadd(cmul(pc, make_float2(s_st[2 * n], s_st[2 * n + 1])),
                                make_float2(s_tot[2 * n], s_tot[2 * n + 1]));
         s_st[2 * n] = sn.x;
