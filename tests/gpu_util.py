@@ -37,6 +37,15 @@ def par_to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
 
 
+def offset_copy(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous copy of t whose data starts one element into its buffer
+    (2 or 4 bytes: no 16-byte alignment), for the kernels' unaligned paths."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    out = buf[1:].view(t.shape)
+    out.copy_(t)
+    return out
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 

@@ -9,7 +9,7 @@ import torch
 import genomic_lm_amd as G
 import oracle
 import workloads as W
-from tests.gpu_util import DevWorkload, gate, log, sample_rows, to_f64
+from tests.gpu_util import DevWorkload, gate, log, offset_copy, sample_rows, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +98,28 @@ def test_decode_cpx_after_prefill(io):
     ref, ref_s = _ref(w, lam, R)
     gate(torch.cat(ys, -1), ref, io, label="cpx prefill+decode")
     assert _state_err(s, ref_s) < 1e-4
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_cpx_misaligned_rows(io):
+    """Complex entry points with activations one element off 16-byte alignment,
+    on chip and four-step, then a decode step from offset single tokens."""
+    for L in (4096, 20000):
+        w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2 if L < 5000 else 1)
+        x1, x2, v = (offset_copy(t) for t in (d.x1, d.x2, d.v))
+        assert x1.data_ptr() % 16 != 0
+        ref, ref_s = _ref(w, lam, R)
+        log(f"cpx misaligned io={io} L={L}")
+        gate(G.fftconv_fwd_cpx(x1, x2, v, lam_d, R_d, d.skip), ref, io, label="fftconv_cpx misaligned")
+        if L > 8192:
+            continue
+        n = L - 1
+        pre = [offset_copy(t[..., :n].contiguous()) for t in (d.x1, d.x2, d.v)]
+        y, s = G.chunk_fwd_cpx(*pre, lam_d, R_d, 1024, d.skip)
+        tok = [offset_copy(t[..., n].contiguous()) for t in (d.x1, d.x2, d.v)]
+        yt, s = G.modal_decode_cpx(*tok, lam_d, R_d, d.skip, state_in=s)
+        gate(torch.cat([y, yt[..., None]], -1), ref, io, label="chunk_cpx + decode_cpx misaligned")
+        assert _state_err(s, ref_s) < 1e-4
 
 
 def test_cpx_with_real_modes_matches_real_entries():

@@ -12,7 +12,8 @@ import torch
 import genomic_lm_amd as G
 import oracle
 import workloads as W
-from tests.gpu_util import DevWorkload, gate, log, oracle_fir, oracle_modal, sample_rows, state_gate, to_f64
+from tests.gpu_util import (DevWorkload, gate, log, offset_copy, oracle_fir, oracle_modal,
+                            sample_rows, state_gate, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +89,36 @@ def test_decode_from_empty_state_equals_chunk():
     gate(torch.cat(ys, -1), ref, "bf16", label="decode from empty")
     state_gate(s, ref_s, label="decode from empty")
     gate(y_chunk, ref, "bf16", label="chunk C=1")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_misaligned(io):
+    """Decode steps and FIR window steps from single tokens that sit one element
+    off alignment, with the state and window buffers offset too."""
+    L, T = 1000, 6
+    w = _wl(io, D=16, L=L + T, B=2)
+    d = DevWorkload(w)
+    pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
+    _, s0 = G.chunk_fwd(*pre, d.lam, d.res, 1024, d.skip, algo="fft")
+    s = offset_copy(s0)
+    ys = []
+    for t in range(L, L + T):
+        yt, s = G.modal_decode(*(offset_copy(_tok(x, t)) for x in (d.x1, d.x2, d.v)), d.lam, d.res,
+                               d.skip, state_in=s, state_out=s)
+        ys.append(yt[..., None])
+    ref, ref_s = oracle_modal(w)
+    log(f"decode misaligned io={io}")
+    gate(torch.cat(ys, -1), ref[..., L:], io, label="decode misaligned")
+    state_gate(s, ref_s, label="decode misaligned")
+    for K in (7, 128):
+        _, win0 = G.fir_fwd_window(*pre, d.taps[K], d.skip)
+        win = offset_copy(win0)
+        ys = []
+        for t in range(L, L + T):
+            sl = [offset_copy(x[..., t:t + 1].contiguous()) for x in (d.x1, d.x2, d.v)]
+            yt, _ = G.fir_fwd_window(*sl, d.taps[K], d.skip, window_in=win, window_out=win)
+            ys.append(yt)
+        gate(torch.cat(ys, -1), oracle_fir(w, K)[..., L:], io, label=f"fir{K} window misaligned")
 
 
 def test_decode_7b_shape():

@@ -13,7 +13,7 @@ import genomic_lm_amd as G
 import oracle
 import workloads as W
 from tests.gpu_util import (DevWorkload, act_to_dev, gate, log, oracle_fir, oracle_modal,
-                            par_to_dev, sample_rows, state_gate, to_f64)
+                            offset_copy, par_to_dev, sample_rows, state_gate, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -382,3 +382,34 @@ def test_config_262k_single_pass():
     ref, _ = oracle_modal(w, rows)
     y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
     gate(y, ref, "bf16", rows, label="262k fftconv N=524288")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_misaligned_rows(io):
+    """Every entry point with activations one element off 16-byte alignment
+    (and L a multiple of 8, so only the alignment disables the vector paths)."""
+    w = small(io, D=4, L=4096, B=2)
+    d = DevWorkload(w)
+    x1, x2, v = (offset_copy(t) for t in (d.x1, d.x2, d.v))
+    y = offset_copy(torch.zeros_like(d.x1))
+    assert x1.data_ptr() % 16 != 0 and y.data_ptr() % 16 != 0
+    ref, ref_s = oracle_modal(w)
+    log(f"misaligned io={io}")
+    gate(G.fftconv_fwd(x1, x2, v, d.lam, d.res, d.skip, out=y), ref, io, label="fftconv misaligned")
+    for algo in ("mfma", "fft"):
+        yy, s = G.chunk_fwd(x1, x2, v, d.lam, d.res, 1024, d.skip, algo=algo, out=y)
+        gate(yy, ref, io, label=f"chunk/{algo} misaligned")
+        state_gate(s, ref_s, label=f"chunk/{algo} misaligned")
+    for K in (7, 128, 200):
+        taps = d.taps[K] if K in d.taps else par_to_dev(
+            W.random_taps(K, w.D, seed=K, bf16=(io == "bf16")))
+        tp_np = w.taps[K] if K in w.taps else taps.cpu().numpy()
+        ref_f = oracle_fir(w, K, taps=tp_np)
+        gate(G.fir_fwd(x1, x2, v, taps, d.skip, out=y), ref_f, io, label=f"fir{K} misaligned")
+        yw, _ = G.fir_fwd_window(x1, x2, v, taps, d.skip, out=y)
+        gate(yw, ref_f, io, label=f"fir{K} window misaligned")
+    # the single pass through the four-step path
+    wl = small(io, D=2, L=20000)
+    dl = DevWorkload(wl)
+    yl = G.fftconv_fwd(*(offset_copy(t) for t in (dl.x1, dl.x2, dl.v)), dl.lam, dl.res, dl.skip)
+    gate(yl, oracle_modal(wl)[0], io, label="fftconv four-step misaligned")
