@@ -56,7 +56,17 @@ What it computes (plain definitions, written out, in fp64):
   Im lam = 0 = Im R.  The modal state is complex, s_n(t) = sum_{k<=t}
   p_n^(t-k) u[k], and z[t] = Re sum_n R_n s_n(t).
 
-Arrays are channel-major: activations (B, D, L), parameters (D, N) / (D,) /
+* Token-major layout of the mixer's projections.  in_proj's 3H output holds
+  every channel's three streams side by side (Hyena channels are interleaved
+  per triple: evo2_flash README, §Limitations), one row per token, and the
+  gated output feeds out_proj token by token (evo2_flash README, layer_names
+  table).  The reading taken here: xin is (B, L, 3D) with channel c's x1, x2,
+  v at columns 3c + pos[0], 3c + pos[1], 3c + pos[2] -- the order inside a
+  triple is not given on the pages, so it is a parameter -- and y is
+  (B, L, D).  The operator itself is unchanged: the streams are split out and
+  the chunked oracle above runs on them as one chunk.
+
+Arrays are channel-major unless named token-major: activations (B, D, L), parameters (D, N) / (D,) /
 (D, K), state (B, D, N), FIR window (B, D, K-1) oldest first; complex
 parameters and states are numpy complex arrays.  Everything is upcast to
 fp64 (complex128) first.
@@ -71,6 +81,7 @@ __all__ = [
     "hyena_fwd", "fir_fwd", "modal_state", "chunk_fwd", "next_pow2",
     "modal_decode", "fir_fwd_window",
     "modal_filter_cpx", "hyena_fwd_cpx", "modal_state_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
+    "tokmajor_streams", "chunk_fwd_tokmajor",
 ]
 
 DIRECT_MAX_L = 4096      # direct O(L^2) sum up to this length, FFT above
@@ -337,3 +348,29 @@ def modal_decode_cpx(x1, x2, v, log_poles, residues, skip, state_in=None):
     z = np.real(np.einsum("dn,bdn->bd", R, s))
     sk = np.zeros(D) if skip is None else np.asarray(skip, dtype=np.float64)
     return x2 * z + sk[None, :] * u, s
+
+
+# ---------------------------------------------------------------- token-major layout
+def tokmajor_streams(xin, pos=(0, 1, 2)):
+    """Split in_proj's token-major output into the three channel-major streams.
+
+    xin (B, L, 3D): channel c's x1, x2, v at columns 3c + pos[0], 3c + pos[1],
+    3c + pos[2] (channels interleaved per triple: evo2_flash README,
+    §Limitations).  Returns x1, x2, v as (B, D, L) arrays.
+    """
+    xin = np.asarray(xin)
+    B, L, D3 = xin.shape
+    per_channel = xin.reshape(B, L, D3 // 3, 3)          # [b, t, c, position in triple]
+    return tuple(np.ascontiguousarray(np.moveaxis(per_channel[..., p], 1, 2)) for p in pos)
+
+
+def chunk_fwd_tokmajor(xin, log_poles, residues, skip, pos=(0, 1, 2), state_in=None):
+    """The modal operator on the token-major layout, fp64: the streams of xin
+    (see tokmajor_streams), the sequence continued from state_in (zero state
+    when None) as one chunk of chunk_fwd.  Returns y as (B, L, D), the layout
+    out_proj reads (evo2_flash README, layer_names table: 'blocks.N.filter'),
+    and the final state (B, D, N)."""
+    x1, x2, v = tokmajor_streams(xin, pos)
+    L = x1.shape[-1]
+    y, s = chunk_fwd(x1, x2, v, log_poles, residues, skip, max(L, 1), state_in=state_in)
+    return np.ascontiguousarray(np.moveaxis(y, 1, 2)), s

@@ -460,6 +460,42 @@ def pin_cpx_chunk_and_decode_equal_full(O):
         assert np.max(np.abs(yt - y_full[..., t])) <= 1e-10 * np.max(np.abs(y_full)), t
 
 
+# ---------------------------------------------------------------- token-major layout
+def pin_tokmajor_layout_literal(O):
+    """in_proj's token-major layout written out by hand: B = 1, L = 2, D = 2,
+    element (t, 3c + j) = 100 t + 10 c + j, with x1, x2, v at triple
+    positions 2, 0, 1."""
+    xin = np.array([[[0, 1, 2, 10, 11, 12],
+                     [100, 101, 102, 110, 111, 112]]], dtype=np.float64)
+    x1, x2, v = O.tokmajor_streams(xin, (2, 0, 1))
+    assert np.array_equal(x1, [[[2, 102], [12, 112]]]), x1
+    assert np.array_equal(x2, [[[0, 100], [10, 110]]]), x2
+    assert np.array_equal(v, [[[1, 101], [11, 111]]]), v
+
+
+def pin_tokmajor_impulse(O):
+    """An impulse in x1 of channel c0 at token t0, v = x2 = 1, skip = 0: y
+    (B, L, D) holds channel c0's filter from t0 on in column c0 and zeros
+    elsewhere; poles 1/2 and 1/4 make every value exact."""
+    D, L, t0, c0 = 3, 12, 4, 1
+    pos = (1, 2, 0)
+    lam = np.log(np.array([[0.5, 0.25]] * D))
+    R = np.array([[1.0, -2.0], [3.0, 0.5], [-1.0, 1.0]])
+    xin = np.zeros((1, L, 3 * D))
+    xin[0, :, 3 * np.arange(D) + pos[1]] = 1.0          # x2
+    xin[0, :, 3 * np.arange(D) + pos[2]] = 1.0          # v
+    xin[0, t0, 3 * c0 + pos[0]] = 1.0                   # x1
+    y, s = O.chunk_fwd_tokmajor(xin, lam, R, np.zeros(D), pos)
+    want = np.zeros((1, L, D))
+    for t in range(t0, L):
+        k = t - t0
+        want[0, t, c0] = R[c0, 0] * 0.5 ** k + R[c0, 1] * 0.25 ** k
+    assert y.shape == (1, L, D) and np.allclose(y, want, rtol=0, atol=1e-15), (y, want)
+    want_s = np.zeros((1, D, 2))
+    want_s[0, c0] = [0.5 ** (L - 1 - t0), 0.25 ** (L - 1 - t0)]
+    assert np.allclose(s, want_s, rtol=0, atol=1e-15), s
+
+
 ALL_PINS = [
     pin_golden, pin_filter_rational, pin_filter_dft, pin_recurrence,
     pin_impulse, pin_linearity_time_invariance, pin_numpy_convolve,
@@ -469,4 +505,5 @@ ALL_PINS = [
     pin_decode_after_prefill, pin_decode_impulse_rational, pin_fir_window_pieces,
     pin_cpx_filter_rational, pin_cpx_second_order_recurrence, pin_cpx_real_special_case,
     pin_cpx_chunk_and_decode_equal_full,
+    pin_tokmajor_layout_literal, pin_tokmajor_impulse,
 ]

@@ -47,6 +47,15 @@ def _mutant(**over):
         cv = conv or mod.causal_conv
         return mod._gate(x1, x2, v, lambda u: cv(u, h[None]), skip)
 
+    def chunk_fwd_tokmajor(xin, log_poles, residues, skip, pos=(0, 1, 2), state_in=None):
+        x1, x2, v = mod.tokmajor_streams(xin, pos)
+        L = x1.shape[-1]
+        y, s = mod.chunk_fwd(x1, x2, v, log_poles, residues, skip, max(L, 1), state_in=state_in)
+        return mod.tokmajor_out(y), s
+
+    mod.tokmajor_out = over.get("tokmajor_out", lambda y: np.moveaxis(y, 1, 2))
+    if "chunk_fwd_tokmajor" not in over:
+        mod.chunk_fwd_tokmajor = chunk_fwd_tokmajor
     if "hyena_fwd" not in over:
         mod.hyena_fwd = hyena_fwd
     if "hyena_fwd_cpx" not in over:
@@ -198,6 +207,22 @@ def _chunk_cpx_carry_conj(x1, x2, v, log_poles, residues, skip, C, state_in=None
     return x2 * z + sk[:, None] * u, s
 
 
+def _streams_fixed_order(xin, pos=(0, 1, 2)):         # triple order ignored
+    return HO.tokmajor_streams(xin, (0, 1, 2))
+
+
+def _streams_blocked(xin, pos=(0, 1, 2)):             # [x1 | x2 | v] blocks, not triples
+    xin = np.asarray(xin)
+    B, L, D3 = xin.shape
+    D = D3 // 3
+    return tuple(np.ascontiguousarray(np.moveaxis(xin[..., p * D:(p + 1) * D], 1, 2)) for p in pos)
+
+
+def _out_reshaped(y):                                 # y reshaped instead of transposed
+    B, D, L = y.shape
+    return y.reshape(B, L, D)
+
+
 MUTANTS = {
     "filter_time_origin": dict(modal_filter=_filter_shifted),
     "filter_dropped_mode": dict(modal_filter=_filter_dropped_mode),
@@ -214,6 +239,9 @@ MUTANTS = {
     "cpx_filter_imag_part": dict(modal_filter_cpx=_filter_cpx_imag),
     "cpx_filter_conj_pole": dict(modal_filter_cpx=_filter_cpx_conj_pole),
     "cpx_chunk_carry_conj": dict(chunk_fwd_cpx=_chunk_cpx_carry_conj),
+    "tokmajor_order_ignored": dict(tokmajor_streams=_streams_fixed_order),
+    "tokmajor_blocked_streams": dict(tokmajor_streams=_streams_blocked),
+    "tokmajor_output_reshaped": dict(tokmajor_out=_out_reshaped),
 }
 
 

@@ -252,3 +252,15 @@ def random_complex_state(B: int, D: int, N: int, seed: int) -> np.ndarray:
     """A (B, D, N) complex64 modal state ~ N(0, 1) + i N(0, 1) for resume tests."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 13])))
     return (g.normal(0.0, 1.0, (B, D, N)) + 1j * g.normal(0.0, 1.0, (B, D, N))).astype(np.complex64)
+
+
+def interleave_triples(x1, x2, v, pos=(0, 1, 2)) -> np.ndarray:
+    """The same streams in in_proj's token-major layout: (B, D, L) arrays
+    (stored bf16 bits or fp32) -> (B, L, 3D) with channel c's x1, x2, v at
+    columns 3c + pos[0], 3c + pos[1], 3c + pos[2].  Layout only: elements are
+    copied bit for bit."""
+    B, D, L = x1.shape
+    out = np.empty((B, L, D, 3), dtype=x1.dtype)
+    for a, p in zip((x1, x2, v), pos):
+        out[..., p] = np.moveaxis(a, 1, 2)
+    return out.reshape(B, L, 3 * D)
