@@ -222,6 +222,14 @@ def main():
                                                                      out=y, workspace=fft_ws)
         runs["chunk_cpx_fft"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip, out=y,
                                                         state_out=stc)
+        # the same prefill read straight from in_proj's token-major layout
+        # (B, L, 3D), channels interleaved per triple, y written (B, L, D)
+        xin = torch.stack((x1, x2, v), -1).permute(0, 2, 1, 3).contiguous().view(B, L, 3 * D)
+        y_tm = torch.empty((B, L, D), dtype=torch.bfloat16, device=dev)
+        tm_ws = torch.empty(max(G.chunk_tokmajor_workspace_size(B, D, L, w.N), 16),
+                            dtype=torch.uint8, device=dev)
+        runs["chunk_tokmajor"] = lambda: G.chunk_fwd_tokmajor(xin, lam, res, skip, out=y_tm,
+                                                              state_out=st, workspace=tm_ws)
         one_token = {"modal_decode_step", "fir128_window_step"}   # B*D token·channels
         for name, fn in runs.items():
             t = timed(fn, comp_steps, 2, stream)

@@ -15,6 +15,8 @@ Entry points (names follow the C ABI):
   modal_decode(x1, x2, v, log_poles, residues, skip=None,
                state_in=None)       (x of shape (B, D))       -> (y, state_out)
   fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None) -> (y, window_out)
+  chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None,
+                     pos=(0, 1, 2))  (xin (B, L, 3D))   -> (y (B, L, D), state_out)
 Complex-pole variants (log_poles / residues complex64 (D, N), states
 complex64 (B, D, N)): modal_filter_cpx, fftconv_fwd_cpx, chunk_fwd_cpx,
 modal_decode_cpx.
@@ -31,6 +33,7 @@ __all__ = [
     "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
     "modal_decode", "fir_fwd_window",
     "modal_filter_cpx", "fftconv_fwd_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
+    "chunk_fwd_tokmajor", "chunk_tokmajor_workspace_size",
     "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_LAUNCH",
     "F32", "BF16", "ALGOS", "EXPORTS",
 ]
@@ -68,6 +71,10 @@ EXPORTS = {
                                    _i64, _int, _p]),
     "hyena_modal_decode_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64,
                                       _int, _p]),
+    "hyena_chunk_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
+                                        _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int, _p,
+                                        _size, _p]),
+    "hyena_chunk_tokmajor_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
 }
 
 
@@ -399,4 +406,47 @@ def modal_decode_cpx(x1, x2, v, log_poles, residues, skip=None, state_in=None, o
     _check("hyena_modal_decode_cpx", lib().hyena_modal_decode_cpx(
         _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
         _ptr(y), B, D, _io(x1), _stream(x1)))
+    return y, state_out
+
+
+def chunk_tokmajor_workspace_size(B: int, D: int, L: int, N: int, dtype=torch.bfloat16) -> int:
+    return int(lib().hyena_chunk_tokmajor_workspace_size(
+        B, D, L, N, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None, pos=(0, 1, 2),
+                       out=None, state_out=None, workspace=None):
+    """The modal operator on in_proj's token-major layout: xin (B, L, 3D) with
+    channel c's x1, x2, v at columns 3c + pos[0], 3c + pos[1], 3c + pos[2];
+    returns (y (B, L, D), state_out (B, D, N))."""
+    _act("xin", xin)
+    B, L, D3 = xin.shape
+    if D3 % 3:
+        raise ValueError(f"xin must be (B, L, 3D), got shape {tuple(xin.shape)}")
+    D = D3 // 3
+    if sorted(int(p) for p in pos) != [0, 1, 2]:
+        raise ValueError("pos must be a permutation of (0, 1, 2)")
+    N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
+    _param("log_poles", log_poles, (D, N), xin.device)
+    _param("residues", residues, (D, N), xin.device)
+    _param("skip", skip, (D,), xin.device, optional=True)
+    _param("state_in", state_in, (B, D, N), xin.device, optional=True)
+    if out is None:
+        y = torch.empty((B, L, D), dtype=xin.dtype, device=xin.device)
+    else:
+        y = _act("out", out)
+        if tuple(y.shape) != (B, L, D) or y.dtype != xin.dtype or y.device != xin.device:
+            raise ValueError("out must be (B, L, D) with the dtype and device of xin")
+    if state_out is None:
+        state_out = torch.empty((B, D, N), dtype=torch.float32, device=xin.device)
+    else:
+        _param("state_out", state_out, (B, D, N), xin.device)
+    need = chunk_tokmajor_workspace_size(B, D, L, N, xin.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xin.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hyena_chunk_fwd_tokmajor", lib().hyena_chunk_fwd_tokmajor(
+        _ptr(xin), int(pos[0]), int(pos[1]), int(pos[2]), _ptr(log_poles), _ptr(residues), N,
+        _ptr(skip), _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, _io(xin),
+        _ptr(workspace), ws_bytes, _stream(xin)))
     return y, state_out

@@ -155,6 +155,38 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
   return from_hip(use == HYENA_CHUNK_MFMA ? hyena::launch_chunk_mfma(a) : hyena::launch_chunk_fft(a));
 }
 
+hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                   int32_t pos_v, const float* log_poles, const float* residues,
+                                   int64_t N, const float* skip, const float* state_in,
+                                   float* state_out, void* y, int64_t B, int64_t D, int64_t L,
+                                   hyena_dtype_t io, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  if (!valid_io(io) || B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
+  const bool perm = pos_x1 >= 0 && pos_x2 >= 0 && pos_v >= 0 && pos_x1 < 3 && pos_x2 < 3 &&
+                    pos_v < 3 && pos_x1 != pos_x2 && pos_x1 != pos_v && pos_x2 != pos_v;
+  if (!perm || N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
+  if (B == 0 || D == 0) return HYENA_OK;
+  if (B > 65535 || D > kMaxInt / 3 || L > kMaxInt - 1024 || B * D > kMaxInt)
+    return HYENA_ERR_UNSUPPORTED;
+  if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
+    return HYENA_ERR_INVALID_ARG;
+  if (L == 0)   // no token: the state passes through unchanged
+    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N, as_stream(stream)));
+  if (B * D > std::numeric_limits<int64_t>::max() / (3 * L)) return HYENA_ERR_UNSUPPORTED;
+  const size_t a = io_size(io);
+  if (!xin || !y || !aligned_to(xin, a) || !aligned_to(y, a)) return HYENA_ERR_INVALID_ARG;
+  hyena_status_t st = check_modal(log_poles, residues, N, skip);
+  if (st != HYENA_OK) return st;
+  const size_t need = hyena::tokmajor_workspace(B, D, L, N, io == HYENA_BF16);
+  if (need && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
+    return HYENA_ERR_WORKSPACE;
+  hyena::TokmajorArgs args{xin, pos_x1, pos_x2, pos_v, log_poles, residues,
+                           static_cast<int>(N), skip, state_in, state_out, y,
+                           static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
+                           io == HYENA_BF16, workspace, as_stream(stream)};
+  return from_hip(hyena::launch_tokmajor(args));
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +313,23 @@ hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void
                                       void* stream) {
   return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
                      true, stream);
+}
+
+hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                        int32_t pos_v, const float* log_poles,
+                                        const float* residues, int64_t N, const float* skip,
+                                        const float* state_in, float* state_out, void* y,
+                                        int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, log_poles, residues, N, skip, state_in,
+                             state_out, y, B, D, L, io, workspace, ws_bytes, stream);
+}
+
+size_t hyena_chunk_tokmajor_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                           hyena_dtype_t io) {
+  if (!valid_io(io) || N < 1 || N > HYENA_MAX_MODES) return 0;
+  if (B > 65535 || D > kMaxInt / 3 || L > kMaxInt - 1024 || B * D > kMaxInt) return 0;
+  return hyena::tokmajor_workspace(B, D, L, N, io == HYENA_BF16);
 }
 
 }  // extern "C"

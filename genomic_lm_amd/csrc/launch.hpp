@@ -80,6 +80,24 @@ struct DecodeArgs {
   bool cpx = false;
 };
 
+// Token-major input (B, L, 3D), channel c's x1, x2, v at columns 3c + pos_*;
+// y (B, L, D).
+struct TokmajorArgs {
+  const void* xin;
+  int pos_x1, pos_x2, pos_v;
+  const float* lam;
+  const float* res;
+  int N;
+  const float* skip;
+  const float* state_in;
+  float* state_out;
+  void* y;
+  int B, D, L;
+  bool bf16;
+  void* workspace;
+  hipStream_t stream;
+};
+
 // cpx: complex modes, lam and res as (re, im) pairs (also in the structs below)
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
                                float* h, bool cpx, hipStream_t stream);
@@ -104,6 +122,12 @@ hipError_t launch_modal_decode(const DecodeArgs& a);
 // FIR continuing from a window of the last K-1 inputs: launch_fir for the
 // outputs past the window's reach, then the window kernel (decode.hip).
 hipError_t launch_fir_window(const FirArgs& a, const float* win_in, float* win_out);
+
+// Token-major modal operator (tokmajor.hip): segment length TS and count P
+// for the shape, the workspace it needs (0 when P = 1), and the launcher.
+void tokmajor_segments(int64_t B, int64_t D, int64_t L, bool bf16, int* TS, int* P);
+size_t tokmajor_workspace(int64_t B, int64_t D, int64_t L, int64_t N, bool bf16);
+hipError_t launch_tokmajor(const TokmajorArgs& a);
 
 // state_out <- state_in (or 0 when state_in is null), count floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t count,

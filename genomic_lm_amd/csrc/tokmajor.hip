@@ -1,0 +1,361 @@
+// tokmajor.hip -- the modal operator on the token-major layout that in_proj
+// produces: (B, L, 3D) with each channel's three streams side by side
+// (Hyena channels interleaved per triple: evo2_flash README, Limitations),
+// writing y as (B, L, D), the layout out_proj consumes (evo2_flash README,
+// layer_names table: 'blocks.N.projections', 'blocks.N.filter').
+//
+// For G consecutive channels one token's streams are one contiguous span of
+// 3G elements, so a workgroup of G lanes (one lane per channel) stages tiles
+// of TT token rows through LDS with coalesced 16-byte loads, and each lane
+// walks its channel's tokens with the decode step's recurrence
+//     s_n <- p_n s_n + u_t,   z_t = sum_n R_n s_n,   y_t = x2_t z_t + skip u_t,
+// i.e. the modal state form of the causal convolution (the IIR modal state
+// of the inference cache: Evo2-7B-262K model card, Implementation Notes,
+// 'Custom cache').  One lane per channel alone gives D / G workgroups, far
+// too few for the chip, so the sequence is also cut into P segments of TS
+// tokens:
+//   1. tm_states:  segment r < P-1 from a zero state; its end state e_r goes
+//                  to slot r+1 of the workspace;
+//   2. tm_scan:    slot 0 = state_in, slot r = p^TS slot(r-1) + e_(r-1), the
+//                  true state entering segment r;
+//   3. tm_outputs: every segment from its slot, emitting y; the last one's
+//                  end state is state_out.
+// Passes 1 and 3 both read the input: 14 bytes per token-channel at bf16
+// against the 8 of the channel-major kernels, the price of the parallelism.
+//
+// Accuracy of the recurrence.  The step uses p_f, the pole rounded to fp32,
+// and by itself would weight lag j by p_f^j = p^j (1 + j d), |d| <= 2^-24:
+// over the ~1/(1 - p) tokens a slow mode remembers, that drift reaches ~1e-5
+// of the output, far above the rest of the error.  So at the start of every
+// full tile of K tokens the state is scaled by p^K / p_f^K, as s += g s with
+// g = p^K / p_f^K - 1 from fp64 (tiny, so the fma keeps the correction exact
+// to ~1e-14): the state then carries the exact decay across tiles and each
+// input is off by at most K d.  What remains is the rounding of s itself,
+// which decays with p_n (about sqrt(1/(1 - p_n)) ulps of the state).
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TM_G = 256;                      // channels (lanes) per workgroup
+constexpr int TM_TILE_BYTES = 12 * 1024;       // input bytes per tile (two buffers)
+
+template <typename IO>
+struct TmShape {
+  static constexpr int ESZ = sizeof(IO);
+  static constexpr int SPAN = 3 * TM_G;                 // elements of one token row's span
+  static constexpr int TT = TM_TILE_BYTES / (SPAN * ESZ);   // tokens per tile: 8 (bf16), 4 (f32)
+  static constexpr int EPC = 16 / ESZ;                  // elements per 16-byte chunk
+  static constexpr int CW = SPAN / EPC;                 // chunks per token row
+  static constexpr int PER = TT * CW / TM_G;            // chunks per lane per tile
+  static constexpr int PER_E = TT * SPAN / TM_G;        // elements per lane per tile (scalar path)
+  static_assert(TT * CW % TM_G == 0, "tile");
+};
+
+// One tile of token rows [t0, t0 + TT) of the span [col0, col0 + cols) of
+// the input, rows past t_end and columns past cols left as zeros.  VEC: 16-byte
+// chunks (needs a 16-byte aligned input and rows of a multiple of 16 bytes);
+// otherwise single elements.
+template <typename IO, bool VEC>
+struct TmLoader {
+  using S = TmShape<IO>;
+  static constexpr int NREG = VEC ? S::PER : S::PER_E;
+  using Reg = typename std::conditional<VEC, u32x4, IO>::type;
+  Reg r[NREG];
+
+  __device__ __forceinline__ void load(const IO* __restrict__ xb, int64_t ld, int col0, int cols,
+                                       int t0, int t_end, int tid) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int k = tid + TM_G * i;
+        const int tt = k / S::CW, pc = k % S::CW;
+        if (t0 + tt < t_end && pc * S::EPC < cols) {
+          const u32x4* src =
+              reinterpret_cast<const u32x4*>(xb + int64_t(t0 + tt) * ld + col0) + pc;
+          r[i] = __builtin_nontemporal_load(src);
+        } else {
+          r[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int k = tid + TM_G * i;
+        const int tt = k / S::SPAN, e = k % S::SPAN;
+        r[i] = (t0 + tt < t_end && e < cols) ? xb[int64_t(t0 + tt) * ld + col0 + e] : IO(0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(IO* tile, int tid) const {
+    if constexpr (VEC) {
+      u32x4* t4 = reinterpret_cast<u32x4*>(tile);
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) t4[tid + TM_G * i] = r[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) tile[tid + TM_G * i] = r[i];
+    }
+  }
+};
+
+// Per-lane poles for n < N: pf[n] = exp(lam_n) rounded to fp32 and the tile
+// correction g[n] = p^TT / pf^TT - 1 (0 where pf is so small that the mode
+// is gone within a token); zeros in the NM - N padding slots and for lanes
+// past the last channel.
+template <int NM, int TT>
+__device__ __forceinline__ void tm_poles(const float* __restrict__ lam, int N, int c, bool live,
+                                         float (&pf)[NM], float (&g)[NM]) {
+#pragma unroll
+  for (int n = 0; n < NM; ++n) {
+    pf[n] = 0.0f;
+    g[n] = 0.0f;
+    if (live && n < N) {
+      const double l = static_cast<double>(lam[int64_t(c) * N + n]);
+      pf[n] = static_cast<float>(exp(l));
+      double pk = 1.0;
+#pragma unroll
+      for (int k = 0; k < TT; ++k) pk *= static_cast<double>(pf[n]);
+      if (pf[n] > 1e-30f && pk > 0.0) g[n] = static_cast<float>(exp(l * TT) / pk - 1.0);
+    }
+  }
+}
+
+// Pass 1: end state of segment r < P-1 from a zero state, to slot r+1.
+// Grid (ceil(D / G), P - 1, B).
+template <typename IO, bool VEC, int NM>
+__global__ __launch_bounds__(TM_G) void tm_states(
+    const IO* __restrict__ xin, int pos1, int posv, const float* __restrict__ lam, int N,
+    float* __restrict__ ws, int D, int L, int TS, int P) {
+  using S = TmShape<IO>;
+  __shared__ IO tile[2][S::TT * S::SPAN];
+  const int tid = threadIdx.x;
+  const int col0 = 3 * TM_G * blockIdx.x;
+  const int c = TM_G * blockIdx.x + tid;
+  const bool live = c < D;
+  const int r = blockIdx.y;
+  const int b = blockIdx.z;
+  const int cols = min(S::SPAN, 3 * D - col0);
+  const int64_t ld = 3 * int64_t(D);
+  const IO* xb = xin + int64_t(b) * L * ld;
+
+  float pf[NM], g[NM], s[NM];
+  tm_poles<NM, S::TT>(lam, N, c, live, pf, g);
+#pragma unroll
+  for (int n = 0; n < NM; ++n) s[n] = 0.0f;
+
+  const int t_begin = r * TS, t_end = t_begin + TS;   // full: r < P-1
+  const int o1 = 3 * tid + pos1, ov = 3 * tid + posv;
+  TmLoader<IO, VEC> ldr;
+  ldr.load(xb, ld, col0, cols, t_begin, t_end, tid);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += S::TT) {
+    ldr.store(tile[buf], tid);
+    __syncthreads();
+    if (t0 + S::TT < t_end) ldr.load(xb, ld, col0, cols, t0 + S::TT, t_end, tid);
+    const IO* tb = tile[buf];
+    float u[S::TT];                     // the tile's inputs first: one LDS wait per tile
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt)
+      u[tt] = Io<IO>::ld(tb, tt * S::SPAN + o1) * Io<IO>::ld(tb, tt * S::SPAN + ov);
+#pragma unroll
+    for (int n = 0; n < NM; ++n) s[n] = fmaf(g[n], s[n], s[n]);   // every tile is full
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt) {
+#pragma unroll
+      for (int n = 0; n < NM; ++n) s[n] = fmaf(pf[n], s[n], u[tt]);
+    }
+    buf ^= 1;
+  }
+  if (live) {
+    float* dst = ws + ((int64_t(b) * P + r + 1) * D + c) * N;
+#pragma unroll
+    for (int n = 0; n < NM; ++n)
+      if (n < N) dst[n] = s[n];
+  }
+}
+
+// Pass 2: the scan over segments, one thread per (b, c, n).
+__global__ __launch_bounds__(256) void tm_scan(const float* __restrict__ lam, int N,
+                                               const float* state_in, float* __restrict__ ws,
+                                               int D, int TS, int P, int64_t total) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t dn = int64_t(D) * N;
+  const int64_t b = i / dn, cn = i % dn;        // cn = c N + n
+  const float q = static_cast<float>(exp(static_cast<double>(lam[cn]) * TS));
+  float s = state_in ? state_in[i] : 0.0f;
+  float* w = ws + b * P * dn + cn;
+  w[0] = s;
+  // slots in groups of 16 independent loads, so the chain waits on memory
+  // once per group instead of once per segment
+  constexpr int GRP = 16;
+  for (int r0 = 1; r0 < P; r0 += GRP) {
+    float e[GRP];
+#pragma unroll
+    for (int k = 0; k < GRP; ++k) e[k] = (r0 + k < P) ? w[(r0 + k) * dn] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < GRP; ++k) {
+      if (r0 + k < P) {
+        s = fmaf(q, s, e[k]);
+        w[(r0 + k) * dn] = s;
+      }
+    }
+  }
+}
+
+// Pass 3: every segment from its entering state, emitting y.  Grid
+// (ceil(D / G), P, B).  With P = 1 the entering state is state_in itself
+// (each lane reads its own channel's state before writing it).
+template <typename IO, bool VEC, int NM>
+__global__ __launch_bounds__(TM_G) void tm_outputs(
+    const IO* __restrict__ xin, int pos1, int pos2, int posv, const float* __restrict__ lam,
+    const float* __restrict__ res, int N, const float* __restrict__ skip, const float* state_in,
+    const float* __restrict__ ws, float* state_out, IO* __restrict__ y, int D, int L, int TS,
+    int P) {
+  using S = TmShape<IO>;
+  __shared__ IO tile[2][S::TT * S::SPAN];
+  const int tid = threadIdx.x;
+  const int col0 = 3 * TM_G * blockIdx.x;
+  const int c = TM_G * blockIdx.x + tid;
+  const bool live = c < D;
+  const int r = blockIdx.y;
+  const int b = blockIdx.z;
+  const int cols = min(S::SPAN, 3 * D - col0);
+  const int64_t ld = 3 * int64_t(D);
+  const IO* xb = xin + int64_t(b) * L * ld;
+  IO* yb = y + int64_t(b) * L * D + c;
+
+  float pf[NM], g[NM], R[NM], s[NM];
+  tm_poles<NM, S::TT>(lam, N, c, live, pf, g);
+#pragma unroll
+  for (int n = 0; n < NM; ++n) R[n] = (live && n < N) ? res[int64_t(c) * N + n] : 0.0f;
+  const float* s0 = (P > 1) ? ws + ((int64_t(b) * P + r) * D + c) * N
+                            : (state_in ? state_in + (int64_t(b) * D + c) * N : nullptr);
+#pragma unroll
+  for (int n = 0; n < NM; ++n) s[n] = (live && n < N && s0) ? s0[n] : 0.0f;
+  const float sk = (live && skip) ? skip[c] : 0.0f;
+
+  const int t_begin = r * TS, t_end = min(L, t_begin + TS);
+  const int o1 = 3 * tid + pos1, o2 = 3 * tid + pos2, ov = 3 * tid + posv;
+  TmLoader<IO, VEC> ldr;
+  ldr.load(xb, ld, col0, cols, t_begin, t_end, tid);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += S::TT) {
+    ldr.store(tile[buf], tid);
+    __syncthreads();
+    if (t0 + S::TT < t_end) ldr.load(xb, ld, col0, cols, t0 + S::TT, t_end, tid);
+    const IO* tb = tile[buf];
+    const int nt = min(S::TT, t_end - t0);
+    if (nt == S::TT) {
+      // a partial last tile goes uncorrected: its drift is at most nt d
+#pragma unroll
+      for (int n = 0; n < NM; ++n) s[n] = fmaf(g[n], s[n], s[n]);
+    }
+    float u[S::TT], x2[S::TT];          // the tile's inputs first: one LDS wait per tile
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt) {
+      u[tt] = Io<IO>::ld(tb, tt * S::SPAN + o1) * Io<IO>::ld(tb, tt * S::SPAN + ov);
+      x2[tt] = Io<IO>::ld(tb, tt * S::SPAN + o2);
+    }
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt) {
+      if (tt < nt) {
+        float z0 = 0.0f, z1 = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NM; n += 2) {
+          s[n] = fmaf(pf[n], s[n], u[tt]);
+          z0 = fmaf(R[n], s[n], z0);
+          s[n + 1] = fmaf(pf[n + 1], s[n + 1], u[tt]);
+          z1 = fmaf(R[n + 1], s[n + 1], z1);
+        }
+        if (live) Io<IO>::st(yb, int64_t(t0 + tt) * D, fmaf(x2[tt], z0 + z1, sk * u[tt]));
+      }
+    }
+    buf ^= 1;
+  }
+  if (r == P - 1 && live) {
+    float* dst = state_out + (int64_t(b) * D + c) * N;
+#pragma unroll
+    for (int n = 0; n < NM; ++n)
+      if (n < N) dst[n] = s[n];
+  }
+}
+
+int tm_tile_tokens(bool bf16) { return bf16 ? TmShape<bf16_t>::TT : TmShape<float>::TT; }
+
+template <typename IO, bool VEC, int NM>
+hipError_t launch_tm(const TokmajorArgs& a, int TS, int P) {
+  const IO* xin = static_cast<const IO*>(a.xin);
+  const unsigned gx = static_cast<unsigned>((a.D + TM_G - 1) / TM_G);
+  float* ws = static_cast<float*>(a.workspace);
+  if (P > 1) {
+    tm_states<IO, VEC, NM><<<dim3(gx, P - 1, a.B), TM_G, 0, a.stream>>>(
+        xin, a.pos_x1, a.pos_v, a.lam, a.N, ws, a.D, a.L, TS, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = int64_t(a.B) * a.D * a.N;
+    tm_scan<<<static_cast<unsigned>((total + 255) / 256), 256, 0, a.stream>>>(
+        a.lam, a.N, a.state_in, ws, a.D, TS, P, total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  tm_outputs<IO, VEC, NM><<<dim3(gx, P, a.B), TM_G, 0, a.stream>>>(
+      xin, a.pos_x1, a.pos_x2, a.pos_v, a.lam, a.res, a.N, a.skip, a.state_in, ws, a.state_out,
+      static_cast<IO*>(a.y), a.D, a.L, TS, P);
+  return hipGetLastError();
+}
+
+template <typename IO, bool VEC>
+hipError_t launch_tm_modes(const TokmajorArgs& a, int TS, int P) {
+  if (a.N <= 8) return launch_tm<IO, VEC, 8>(a, TS, P);
+  if (a.N <= 16) return launch_tm<IO, VEC, 16>(a, TS, P);
+  if (a.N <= 32) return launch_tm<IO, VEC, 32>(a, TS, P);
+  return launch_tm<IO, VEC, 64>(a, TS, P);
+}
+
+}  // namespace
+
+// Segment length: a multiple of the tile, chosen so that about TM_TARGET
+// workgroups run per pass (about four per CU) when the shape allows it, and
+// at least TM_MIN_SEG tokens, so that the per-segment state traffic (4 N
+// floats per channel through the workspace) stays small next to the input.
+void tokmajor_segments(int64_t B, int64_t D, int64_t L, bool bf16, int* TS, int* P) {
+  constexpr int64_t TM_TARGET = 1024;
+  constexpr int64_t TM_MIN_SEG = 64;
+  const int64_t tt = tm_tile_tokens(bf16);
+  const int64_t groups = B * ((D + TM_G - 1) / TM_G);
+  int64_t want = (TM_TARGET + groups - 1) / groups;
+  if (want < 1) want = 1;
+  int64_t ts = (L + want - 1) / want;
+  if (ts < TM_MIN_SEG) ts = TM_MIN_SEG;
+  ts = (ts + tt - 1) / tt * tt;
+  *TS = static_cast<int>(ts);
+  *P = static_cast<int>((L + ts - 1) / ts);
+}
+
+size_t tokmajor_workspace(int64_t B, int64_t D, int64_t L, int64_t N, bool bf16) {
+  if (B <= 0 || D <= 0 || L <= 0 || N <= 0) return 0;
+  int TS = 0, P = 0;
+  tokmajor_segments(B, D, L, bf16, &TS, &P);
+  return P > 1 ? static_cast<size_t>(B * P * D * N) * sizeof(float) : 0;
+}
+
+hipError_t launch_tokmajor(const TokmajorArgs& a) {
+  int TS = 0, P = 0;
+  tokmajor_segments(a.B, a.D, a.L, a.bf16, &TS, &P);
+  const size_t esz = a.bf16 ? 2 : 4;
+  const bool vec = aligned_to(a.xin, 16) && (3 * static_cast<size_t>(a.D) * esz) % 16 == 0;
+  if (a.bf16)
+    return vec ? launch_tm_modes<bf16_t, true>(a, TS, P) : launch_tm_modes<bf16_t, false>(a, TS, P);
+  return vec ? launch_tm_modes<float, true>(a, TS, P) : launch_tm_modes<float, false>(a, TS, P);
+}
+
+}  // namespace hyena

@@ -64,13 +64,13 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 3
+#define HYENA_ABI_VERSION 4
 
 typedef enum hyena_status {
     HYENA_OK = 0,
     HYENA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad enum, misalignment, N out of [1, 64] */
     HYENA_ERR_UNSUPPORTED = 2,   /* valid but beyond what this build implements (limits below) */
-    HYENA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than hyena_fftconv_workspace_size() */
+    HYENA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the entry point's *_workspace_size() */
     HYENA_ERR_LAUNCH = 4,        /* a HIP launch or runtime call failed (hipGetLastError) */
 } hyena_status_t;
 
@@ -273,6 +273,48 @@ hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void
                                       const float* state_in, float* state_out,
                                       void* y, int64_t B, int64_t D, hyena_dtype_t io,
                                       void* stream);
+
+/*
+ * hyena_chunk_fwd_tokmajor -- the modal operator on the token-major layout
+ * of the mixer's projections, with the state carried in and out.
+ * in_proj's 3H output holds every channel's three streams side by side
+ * (Hyena channels are interleaved per triple: evo2_flash README,
+ * Limitations), and y feeds out_proj token by token (evo2_flash README,
+ * layer_names table: 'blocks.N.projections', 'blocks.N.filter').  This entry
+ * reads and writes those layouts directly, with no transposing pass:
+ *   xin : (B, L, 3D) `io`; channel c's x1, x2 and v at columns
+ *         3c + pos_x1, 3c + pos_x2 and 3c + pos_v, where (pos_x1, pos_x2,
+ *         pos_v) is a permutation of (0, 1, 2) (the pages do not give the
+ *         order within a triple, so the caller states it)
+ *   y   : (B, L, D) `io`, written
+ *   log_poles, residues : (D, N) fp32, 1 <= N <= HYENA_MAX_MODES
+ *   skip : (D) fp32 or NULL
+ *   state_in  : (B, D, N) fp32 or NULL (zero state)
+ *   state_out : (B, D, N) fp32, written (may equal state_in)
+ *   workspace : device buffer of at least hyena_chunk_tokmajor_workspace_size()
+ *               bytes, 16-byte aligned, contents scratch (NULL when that size
+ *               is 0); calls sharing one workspace must be ordered.
+ * The result is that of hyena_chunk_fwd on the same streams, for any C:
+ *   y[b, t, c] = x2 * (sum_{k<=t} h[c, t-k] u[k] + sum_n R_n p_n^(t+1) s_in_n)
+ *                + skip[c] * u[t],  u = x1 * v,
+ * evaluated per token with the decode step's recurrence s_n <- p_n s_n + u,
+ * over segments of the sequence that run in parallel: each segment's end
+ * state from zero, a scan of those over the segments, then every segment from
+ * its true entering state.  B <= 65535.  L = 0 copies state_in to state_out.
+ * Workspace NULL, short or misaligned when one is needed -> HYENA_ERR_WORKSPACE.
+ */
+hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                        int32_t pos_v, const float* log_poles,
+                                        const float* residues, int64_t N, const float* skip,
+                                        const float* state_in, float* state_out, void* y,
+                                        int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes hyena_chunk_fwd_tokmajor needs for this shape: B * P * D * N
+ * floats for its P segments, 0 when the sequence is one segment or the shape
+ * is empty or unsupported. */
+size_t hyena_chunk_tokmajor_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                           hyena_dtype_t io);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 3
+    assert G.abi_version() == 4
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -168,6 +168,42 @@ def test_chunk_validation():
     assert f(*a) == G.ERR_UNSUPPORTED                          # FFT chunk > 8192
     a = list(good); a[10] = 0                                  # empty batch
     assert f(*a) == G.OK
+
+
+def test_chunk_tokmajor_validation():
+    f = G.lib().hyena_chunk_fwd_tokmajor
+    # xin, pos x3, lam, res, N, skip, state_in, state_out, y, B, D, L, io, ws, ws_bytes, stream
+    good = [FAKE, 0, 1, 2, FAKE, FAKE, 16, None, None, FAKE, FAKE, 1, 4, 64, G.BF16, None, 0,
+            None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (10, None, G.ERR_INVALID_ARG),
+                           (9, None, G.ERR_INVALID_ARG), (4, None, G.ERR_INVALID_ARG),
+                           (1, 1, G.ERR_INVALID_ARG), (3, 3, G.ERR_INVALID_ARG),
+                           (2, -1, G.ERR_INVALID_ARG), (6, 0, G.ERR_INVALID_ARG),
+                           (6, 65, G.ERR_INVALID_ARG), (0, MISALIGNED, G.ERR_INVALID_ARG),
+                           (14, 2, G.ERR_INVALID_ARG), (11, 65536, G.ERR_UNSUPPORTED),
+                           (13, -1, G.ERR_INVALID_ARG)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[11] = 0                                  # empty batch
+    assert f(*a) == G.OK
+    ws = G.lib().hyena_chunk_tokmajor_workspace_size
+    # one workgroup of 256 channels per channel group and segment; segments
+    # of at least 64 tokens (a multiple of the tile) are cut so that about
+    # 1024 workgroups run; B * P * D * N fp32 slots, none for one segment
+    assert ws(1, 4, 64, 16, G.BF16) == 0                        # one segment
+    assert ws(1, 4, 65, 16, G.BF16) == 1 * 2 * 4 * 16 * 4       # P = 2 segments of 64
+    assert ws(1, 4, 4096, 16, G.BF16) == 64 * 4 * 16 * 4
+    assert ws(1, 4096, 32768, 16, G.BF16) == 64 * 4096 * 16 * 4  # 16 groups x 64 segments of 512
+    assert ws(1, 8192, 32768, 16, G.BF16) == 32 * 8192 * 16 * 4
+    assert ws(2, 300, 1000, 3, G.F32) == 2 * 16 * 300 * 3 * 4
+    assert ws(1, 4, 64, 0, G.BF16) == 0
+    big = list(good); big[13] = 4096                           # needs a workspace
+    assert f(*big) == G.ERR_WORKSPACE
+    need = ws(1, 4, 4096, 16, G.BF16)
+    big[15] = FAKE; big[16] = need - 1
+    assert f(*big) == G.ERR_WORKSPACE
+    big[15] = P(0x10008); big[16] = need
+    assert f(*big) == G.ERR_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors_before_any_call():

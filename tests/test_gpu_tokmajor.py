@@ -1,0 +1,163 @@
+"""The modal operator on in_proj's token-major layout, on the GPU, through the
+C ABI, against the fp64 oracle.
+
+xin (B, L, 3D) holds each channel's x1, x2, v side by side (triple order
+`pos`), y is (B, L, D).  The cases cover both element types, both load paths
+(16-byte chunks; single elements when rows are not a multiple of 16 bytes or
+the input is misaligned), partial channel groups, ragged tails, every mode
+count variant, carried and aliased states, and the 32 kb shape sampled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import genomic_lm_amd as G
+import oracle
+import workloads as W
+from tests.gpu_util import (DevWorkload, act_to_dev, gate, log, offset_copy, par_to_dev,
+                            sample_rows, state_gate)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()
+    yield
+
+
+def _setup(io, B, D, L, N=None, pos=(0, 1, 2)):
+    w = W.make("tiny" if io == "f32" else "7b_layer_set", B=B, D=D, L=L, N=N)
+    xin = W.interleave_triples(w.x1, w.x2, w.v, pos)
+    return w, xin, act_to_dev(xin, w.io)
+
+
+def _ref(w, xin, pos, rows=None, state_in=None):
+    """Oracle on channel subset `rows`: y (B, L, len(rows)) and state."""
+    rows = np.arange(w.D) if rows is None else np.asarray(rows)
+    cols = (3 * rows[:, None] + np.arange(3)[None, :]).ravel()
+    x = W.to_f64(xin[..., cols], w.io)
+    s0 = None if state_in is None else np.asarray(state_in, np.float64)[:, rows]
+    return oracle.chunk_fwd_tokmajor(x, w.log_poles[rows].astype(np.float64),
+                                     w.residues[rows].astype(np.float64),
+                                     w.skip[rows].astype(np.float64), pos, state_in=s0)
+
+
+def _gate_tm(y_dev, ref, io, rows=None, label=""):
+    """Gate a token-major output per channel: compare as (B, D, L)."""
+    return gate(y_dev.transpose(1, 2), np.moveaxis(ref, 1, 2), io, rows, label=label)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("D,L", [(256, 1000), (300, 777), (64, 2048), (520, 67), (8, 5)])
+@pytest.mark.parametrize("pos", [(0, 1, 2), (2, 0, 1)])
+def test_tokmajor_small(io, D, L, pos):
+    w, xin, xd = _setup(io, B=2, D=D, L=L, pos=pos)
+    d = DevWorkload(w)
+    log(f"tokmajor io={io} D={D} L={L} pos={pos}")
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=pos)
+    ref, ref_s = _ref(w, xin, pos)
+    assert y.shape == (2, L, D)
+    _gate_tm(y, ref, io, label=f"tokmajor D={D} L={L}")
+    state_gate(s, ref_s, label=f"tokmajor D={D} L={L}")
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 17, 33, 64])
+def test_tokmajor_mode_counts(N):
+    """Every per-lane mode array size (8, 16, 32, 64), with padding."""
+    w, xin, xd = _setup("bf16", B=1, D=260, L=2000, N=N)
+    d = DevWorkload(w)
+    log(f"tokmajor N={N}")
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip)
+    ref, ref_s = _ref(w, xin, (0, 1, 2))
+    _gate_tm(y, ref, "bf16", label=f"tokmajor N={N}")
+    state_gate(s, ref_s, label=f"tokmajor N={N}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_tokmajor_state_in_and_in_place(io):
+    """A carried state in, updated in place (state_out is state_in)."""
+    B, D, L = 2, 384, 1200
+    w, xin, xd = _setup(io, B=B, D=D, L=L)
+    d = DevWorkload(w)
+    s0 = W.random_state(B, D, w.N, seed=3)
+    s_dev = torch.from_numpy(s0).to(xd.device)
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, state_in=s_dev, state_out=s_dev)
+    assert s.data_ptr() == s_dev.data_ptr()
+    ref, ref_s = _ref(w, xin, (0, 1, 2), state_in=s0)
+    _gate_tm(y, ref, io, label="tokmajor state in place")
+    state_gate(s, ref_s, label="tokmajor state in place")
+
+
+def test_tokmajor_split_equals_whole_and_channel_major():
+    """Two token-major calls with the state handed over equal one call, and
+    both equal the channel-major chunk kernels on the same streams."""
+    B, D, L, cut = 1, 512, 6000, 2345
+    w, xin, xd = _setup("bf16", B=B, D=D, L=L, pos=(1, 2, 0))
+    d = DevWorkload(w)
+    ya, sa = G.chunk_fwd_tokmajor(xd[:, :cut].contiguous(), d.lam, d.res, d.skip, pos=(1, 2, 0))
+    yb, sb = G.chunk_fwd_tokmajor(xd[:, cut:].contiguous(), d.lam, d.res, d.skip, pos=(1, 2, 0),
+                                  state_in=sa)
+    ref, ref_s = _ref(w, xin, (1, 2, 0))
+    _gate_tm(torch.cat([ya, yb], 1), ref, "bf16", label="tokmajor split")
+    state_gate(sb, ref_s, label="tokmajor split")
+    yc, sc = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="mfma")
+    yt, st = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=(1, 2, 0))
+    diff = (yc.float().transpose(1, 2) - yt.float()).abs().max().item()
+    assert diff <= 2e-2 * yc.float().abs().max().item(), diff
+    state_gate(st, ref_s, label="tokmajor whole")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_tokmajor_prefill_then_decode(io):
+    """Token-major prefill, then decode steps on the token's (B, D) slices."""
+    B, D, L, T = 2, 256, 1500, 6
+    pos = (2, 1, 0)
+    w, xin, xd = _setup(io, B=B, D=D, L=L + T, pos=pos)
+    d = DevWorkload(w)
+    y, s = G.chunk_fwd_tokmajor(xd[:, :L].contiguous(), d.lam, d.res, d.skip, pos=pos)
+    ys = [y]
+    for t in range(L, L + T):
+        x1, x2, v = (xd[:, t, p::3].contiguous() for p in pos)
+        yt, s = G.modal_decode(x1, x2, v, d.lam, d.res, d.skip, state_in=s, state_out=s)
+        ys.append(yt[:, None, :])
+    ref, ref_s = _ref(w, xin, pos)
+    _gate_tm(torch.cat(ys, 1), ref, io, label="tokmajor prefill + decode")
+    state_gate(s, ref_s, label="tokmajor prefill + decode")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_tokmajor_misaligned_and_tiny(io):
+    """Input one element off 16-byte alignment (single-element loads), and
+    L = 1 and L = 0 (the state passes through)."""
+    w, xin, xd = _setup(io, B=2, D=264, L=700)
+    d = DevWorkload(w)
+    xm = offset_copy(xd)
+    assert xm.data_ptr() % 16 != 0
+    y, s = G.chunk_fwd_tokmajor(xm, d.lam, d.res, d.skip)
+    ref, ref_s = _ref(w, xin, (0, 1, 2))
+    _gate_tm(y, ref, io, label="tokmajor misaligned")
+    state_gate(s, ref_s, label="tokmajor misaligned")
+    y1, s1 = G.chunk_fwd_tokmajor(xd[:, :1].contiguous(), d.lam, d.res, d.skip, state_in=s)
+    r1, rs1 = _ref(w, xin[:, :1], (0, 1, 2), state_in=s.cpu().numpy())
+    _gate_tm(y1, r1, io, label="tokmajor L=1")
+    state_gate(s1, rs1, label="tokmajor L=1", tol=1e-6)
+    e = torch.empty((2, 0, 3 * 264), dtype=xd.dtype, device=xd.device)
+    y0, s0 = G.chunk_fwd_tokmajor(e, d.lam, d.res, d.skip, state_in=s1)
+    assert y0.shape == (2, 0, 264) and torch.equal(s0, s1)
+
+
+def test_tokmajor_32k_shape():
+    """B = 1, D = 4096, L = 32768, bf16, N = 16: the 32 kb shape the benchmark
+    times, in its launch configuration, on sampled channels."""
+    w = W.make("32k_chunked")
+    xin = W.interleave_triples(w.x1, w.x2, w.v)
+    xd = act_to_dev(xin, "bf16")
+    lam, res, skip = par_to_dev(w.log_poles), par_to_dev(w.residues), par_to_dev(w.skip)
+    y, s = G.chunk_fwd_tokmajor(xd, lam, res, skip)
+    rows = sample_rows(w.D)
+    ref, ref_s = _ref(w, xin, (0, 1, 2), rows)
+    _gate_tm(y, ref, "bf16", rows, label="32k tokmajor")
+    state_gate(s, ref_s, rows, label="32k tokmajor")
