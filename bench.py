@@ -220,8 +220,10 @@ def main():
         stc = torch.empty((B, D, 8), dtype=torch.complex64, device=dev)
         runs["fftconv_cpx_single_pass"] = lambda: G.fftconv_fwd_cpx(x1, x2, v, lc_d, rc_d, skip,
                                                                      out=y, workspace=fft_ws)
-        runs["chunk_cpx_fft"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip, out=y,
-                                                        state_out=stc)
+        runs["chunk_cpx_fft"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip,
+                                                        algo="fft", out=y, state_out=stc)
+        runs["chunk_cpx_mfma"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip,
+                                                         algo="mfma", out=y, state_out=stc)
         # the same prefill read straight from in_proj's token-major layout
         # (B, L, 3D), channels interleaved per triple, y written (B, L, D)
         xin = torch.stack((x1, x2, v), -1).permute(0, 2, 1, 3).contiguous().view(B, L, 3 * D)

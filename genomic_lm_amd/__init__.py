@@ -68,7 +68,7 @@ EXPORTS = {
     "hyena_fftconv_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
                                      _p, _size, _p]),
     "hyena_chunk_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
-                                   _i64, _int, _p]),
+                                   _i64, _int, _int, _p]),
     "hyena_modal_decode_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64,
                                       _int, _p]),
     "hyena_chunk_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
@@ -370,8 +370,10 @@ def fftconv_fwd_cpx(x1, x2, v, log_poles, residues, skip=None, out=None,
 
 
 def chunk_fwd_cpx(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
-                  out=None, state_out=None):
+                  algo: str = "auto", out=None, state_out=None):
     """Chunked prefill with a complex modal state; returns (y, state_out complex64)."""
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}")
     _act("x1", x1)
     _act("x2", x2, x1)
     _act("v", v, x1)
@@ -385,7 +387,7 @@ def chunk_fwd_cpx(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=No
     so = _cstate("state_out", state_out, (B, D, N), x1.device)
     _check("hyena_chunk_fwd_cpx", lib().hyena_chunk_fwd_cpx(
         _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
-        _ptr(y), B, D, L, int(C), _io(x1), _stream(x1)))
+        _ptr(y), B, D, L, int(C), _io(x1), ALGOS[algo], _stream(x1)))
     return y, state_out
 
 

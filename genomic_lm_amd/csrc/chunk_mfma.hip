@@ -29,6 +29,15 @@
 // part) per lane: 4 runs of 4 blocks in registers, 8 run carries exchanged
 // with the partner half-wave.  The state before each block goes through 4 KB
 // of LDS to become the B operand of G.S.
+//
+// Complex modes (CPX; the complex-pole form of Evo 1's poles / residues,
+// Evo1-1.5-7B-8K model card, Architecture): N <= 8 complex modes occupy the
+// 16 slots as (Re, Im) pairs, slot 2m + k -- the order of the (D, N, 2)
+// parameter and (B, D, N, 2) state arrays.  Every product stays real:
+// Re(R p^(i+1) s) = Re(R p^(i+1)) Re s - Im(R p^(i+1)) Im s gives G's two
+// columns of a mode, the end-state weights are Re and Im of p^(31-j), and h is
+// real.  Only the scan mixes a slot pair (multiplying by p^32 is a complex
+// product): each step takes the partner slot's value from lane l ^ 1.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -59,10 +68,36 @@ __device__ __forceinline__ void build_state_weights(float lam_n, int part, int h
   }
 }
 
+// The same weights for complex mode `md`: slot component k takes Re (k = 0)
+// or Im (k = 1) of p^(ref - tok).
+__device__ __forceinline__ void build_state_weights_cpx(const CpxMode& md, int k, int part,
+                                                        int hf, int ref, bf16x8 (&pa)[2],
+                                                        bf16x8 (&pb)[2], bf16x8 (&pc)[2]) {
+  const __bf16 zero = static_cast<__bf16>(0.0f);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = blk_tok(8 * s + j, hf);
+      float w = 0.0f;
+      if (tok <= ref) {
+        const float2 e = cexp_at(md, static_cast<float>(ref - tok));
+        w = k ? e.y : e.x;
+      }
+      __bf16 w0, w1, w2;
+      split3(w, w0, w1, w2);
+      pa[s][j] = part ? w1 : w0;
+      pb[s][j] = part ? zero : w2;
+      pc[s][j] = part ? zero : w0;
+    }
+  }
+}
+
 // VEC: rows of whole 16-byte chunks, 16-byte aligned (full tiles take the
 // unchecked path).  PIPE (bf16, VEC, L >= 2048): at least two full tiles, so
-// the first two DMAs are issued without a branch.
-template <typename IO, bool VEC, bool PIPE>
+// the first two DMAs are issued without a branch.  CPX: N complex modes as
+// 2N slots (above).
+template <typename IO, bool VEC, bool PIPE, bool CPX>
 __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
@@ -85,8 +120,9 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   const int i32 = l & 31;                     // row of A / column of B and C
   const int64_t row = blockIdx.x;
   const int c = static_cast<int>(row % D);
-  const float* lamc = lam + static_cast<int64_t>(c) * N;
-  const float* resc = res + static_cast<int64_t>(c) * N;
+  const int NS = CPX ? 2 * N : N;             // slots: floats per channel of lam, res, state
+  const float* lamc = lam + static_cast<int64_t>(c) * NS;
+  const float* resc = res + static_cast<int64_t>(c) * NS;
   const IO* x1r = x1 + row * L;
   const IO* x2r = x2 + row * L;
   const IO* vr = v + row * L;
@@ -113,20 +149,24 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // Every load is issued unconditionally from an in-bounds address (index
   // clamped, the value dropped afterwards), so that they are all in flight
   // together.
-  const float lam_ld = lamc[min(n_sc, N - 1)];
-  float g_lam[8], g_res[8];                   // modes 8 hf + j of G
+  // the scan lane's pole: real lam, or (Re, Im) of its complex mode
+  const int m_sc = CPX ? (n_sc >> 1) : n_sc;
+  const int lam_i = CPX ? 2 * min(m_sc, N - 1) : min(n_sc, N - 1);
+  const float lam_ld = lamc[lam_i];
+  const float lam_ld_im = CPX ? lamc[lam_i + 1] : 0.0f;
+  float g_lam[8], g_res[8];                   // slots 8 hf + j of G
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int n = min(8 * hf + j, N - 1);
+    const int n = min(8 * hf + j, NS - 1);
     g_lam[j] = lamc[n];
     g_res[j] = resc[n];
   }
-  const float* sp = state_in ? state_in + row * N + min(n_sc, N - 1) : lamc;
+  const float* sp = state_in ? state_in + row * NS + min(n_sc, NS - 1) : lamc;
   const float st_ld = *sp;
   // Wait for the parameters before the first DMAs: with only these loads
   // outstanding the wait costs their latency alone, whereas a wait placed
   // after the DMAs is compiled as a wait for everything.
-  asm volatile("" ::"v"(lam_ld), "v"(st_ld), "v"(g_lam[0]), "v"(g_lam[1]), "v"(g_lam[2]),
+  asm volatile("" ::"v"(lam_ld), "v"(lam_ld_im), "v"(st_ld), "v"(g_lam[0]), "v"(g_lam[1]), "v"(g_lam[2]),
                "v"(g_lam[3]), "v"(g_lam[4]), "v"(g_lam[5]), "v"(g_lam[6]), "v"(g_lam[7]),
                "v"(g_res[0]), "v"(g_res[1]), "v"(g_res[2]), "v"(g_res[3]), "v"(g_res[4]),
                "v"(g_res[5]), "v"(g_res[6]), "v"(g_res[7]) : "memory");
@@ -135,18 +175,28 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     if (PIPE || nfull > 1) prefetch(1024, tin_b);
   }
 
-  const float lam_n = (n_sc < N) ? lam_ld : 0.0f;
+  const float lam_n = (n_sc < NS) ? lam_ld : 0.0f;
+  // CPX: the slot's mode (padding slots: p = 1) and its component
+  const CpxMode md = cpx_mode(n_sc < NS ? lam_ld : 0.0f, n_sc < NS ? lam_ld_im : 0.0f);
+  const int kc = n_sc & 1;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (8 * hf + j >= N) g_res[j] = 0.0f;
+    if (8 * hf + j >= NS) g_res[j] = 0.0f;
   }
-  float carry = (part == 0 && n_sc < N && state_in) ? st_ld : 0.0f;
+  float carry = (part == 0 && n_sc < NS && state_in) ? st_ld : 0.0f;
 
   // ---- per-row constants
   // h[d], d < 32
   {
     float hd = 0.0f;
-    for (int n = 0; n < N; ++n) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
+    if constexpr (CPX) {
+      for (int n = 0; n < N; ++n) {
+        const float2 e = cexp_at(cpx_mode(lamc[2 * n], lamc[2 * n + 1]), static_cast<float>(i32));
+        hd = fmaf(resc[2 * n], e.x, fmaf(-resc[2 * n + 1], e.y, hd));
+      }
+    } else {
+      for (int n = 0; n < N; ++n) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
+    }
     if (hf == 0) hbuf[i32] = hd;
   }
   lds_sync();
@@ -165,11 +215,21 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       tm[2][s][j] = a2;
     }
   }
-  // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1)
+  // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1);
+  // CPX: slot 2m holds Re(R_m p_m^(i+1)), slot 2m + 1 holds -Im(R_m p_m^(i+1))
   bf16x8 gm[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float val = g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
+    float val;
+    if constexpr (CPX) {
+      const int j0 = j & ~1;
+      const float2 e = cexp_at(cpx_mode(g_lam[j0], g_lam[j0 + 1]), static_cast<float>(i32 + 1));
+      const float2 rp = cmul(make_float2(g_res[j0], g_res[j0 + 1]), e);
+      val = (j & 1) ? -rp.y : rp.x;
+      if (8 * hf + j0 >= NS) val = 0.0f;
+    } else {
+      val = g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
+    }
     __bf16 a0, a1, a2;
     split3(val, a0, a1, a2);
     gm[0][j] = a0;
@@ -179,9 +239,24 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // scan lane: mode n_sc (part 0 or 1 of the column pair) for all 32
   // blocks; padded modes have p = 1 and R = 0
   bf16x8 pa[2], pb[2], pc[2];
-  build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
-  float a1 = expf(lam_n * 32.0f), a2 = expf(lam_n * 64.0f);
-  float a3 = expf(lam_n * 96.0f), a4 = expf(lam_n * 128.0f);
+  if constexpr (CPX) {
+    build_state_weights_cpx(md, kc, part, hf, 31, pa, pb, pc);
+  } else {
+    build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
+  }
+  // p^32, p^64, p^96, p^128: real part (CPX: and the imaginary part times
+  // the sign of the partner term, -1 for a Re slot, +1 for an Im slot)
+  float a1, a2, a3, a4, b1 = 0.0f, b2 = 0.0f, b3 = 0.0f, b4 = 0.0f;
+  if constexpr (CPX) {
+    const float sg = kc ? 1.0f : -1.0f;
+    const float2 e1 = cexp_at(md, 32.0f), e2 = cexp_at(md, 64.0f);
+    const float2 e3 = cexp_at(md, 96.0f), e4 = cexp_at(md, 128.0f);
+    a1 = e1.x; a2 = e2.x; a3 = e3.x; a4 = e4.x;
+    b1 = sg * e1.y; b2 = sg * e2.y; b3 = sg * e3.y; b4 = sg * e4.y;
+  } else {
+    a1 = expf(lam_n * 32.0f); a2 = expf(lam_n * 64.0f);
+    a3 = expf(lam_n * 96.0f); a4 = expf(lam_n * 128.0f);
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     pin(pa[s]);
@@ -196,6 +271,12 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   pin(a2);
   pin(a3);
   pin(a4);
+  if constexpr (CPX) {
+    pin(b1);
+    pin(b2);
+    pin(b3);
+    pin(b4);
+  }
   // consume the state load here: a load still pending at the loop would make
   // the compiler wait for all vector memory (the DMAs in flight included) at
   // its first use in every iteration
@@ -287,10 +368,15 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = ce[r];
+    // x <- a x (+ b x_partner for CPX: a complex product with p^32k)
+    auto step = [&](float a, float b, float xin, float xadd) {
+      if constexpr (CPX) return fmaf(a, xin, fmaf(b, xor1(xin), xadd));
+      return fmaf(a, xin, xadd);
+    };
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int e = 1; e < 4; ++e) x[4 * q + e] = fmaf(a1, x[4 * q + e - 1], x[4 * q + e]);
+      for (int e = 1; e < 4; ++e) x[4 * q + e] = step(a1, b1, x[4 * q + e - 1], x[4 * q + e]);
     }
     float own[4], oth[4];
 #pragma unroll
@@ -304,15 +390,15 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll
     for (int rho = 0; rho < 8; ++rho) {
       const float end = ((rho & 1) == hf) ? own[rho >> 1] : oth[rho >> 1];
-      cin[rho + 1] = fmaf(a4, cin[rho], end);
+      cin[rho + 1] = step(a4, b4, cin[rho], end);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float ci = hf ? cin[2 * q + 1] : cin[2 * q];
-      x[4 * q + 0] = fmaf(a1, ci, x[4 * q + 0]);
-      x[4 * q + 1] = fmaf(a2, ci, x[4 * q + 1]);
-      x[4 * q + 2] = fmaf(a3, ci, x[4 * q + 2]);
-      x[4 * q + 3] = fmaf(a4, ci, x[4 * q + 3]);
+      x[4 * q + 0] = step(a1, b1, ci, x[4 * q + 0]);
+      x[4 * q + 1] = step(a2, b2, ci, x[4 * q + 1]);
+      x[4 * q + 2] = step(a3, b3, ci, x[4 * q + 2]);
+      x[4 * q + 3] = step(a4, b4, ci, x[4 * q + 3]);
     }
     // state before block b+1 = x for block b (b = 31 lands in the unused row
     // 32); before block 0 = cin[0], identical in both half-waves
@@ -455,7 +541,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   }
   lds_sync();
   if (nfull > 0 && (static_cast<int64_t>(nfull) << 10) == L) {
-    if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
+    if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry;
     return;
   }
 
@@ -491,13 +577,17 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     float (*sbuf)[33][17] = sbufs[0];
     const int64_t rem = L - t0;
     if (rem == 1024) {
-      if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = carry;
+      if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry;
     } else if (rem < 1024) {
       // the sequence ends inside this tile: state after token L-1
       const int bstar = static_cast<int>(rem - 1) >> 5;
       const int estar = static_cast<int>(rem - 1) & 31;
       bf16x8 qa[2], qb[2], qc[2];
-      build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
+      if constexpr (CPX) {
+        build_state_weights_cpx(md, kc, part, hf, estar, qa, qb, qc);
+      } else {
+        build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
+      }
       f32x16 cf = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -511,31 +601,47 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       float ev = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) ev = (r == rs) ? cf[r] : ev;
-      const float fin = mine ? fmaf(expf(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev)
-                             : 0.0f;
+      float fin = 0.0f;
+      if (mine) {
+        if constexpr (CPX) {
+          // p^(estar+1) s, component kc: Re = pr sr - pi si, Im = pr si + pi sr
+          const float2 pe = cexp_at(md, static_cast<float>(estar + 1));
+          const float sg = kc ? 1.0f : -1.0f;
+          fin = fmaf(pe.x, sbuf[part][bstar][n_sc], fmaf(sg * pe.y, sbuf[part][bstar][n_sc ^ 1], ev));
+        } else {
+          fin = fmaf(expf(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev);
+        }
+      }
       const float tot = fin + __shfl_xor(fin, 16);
-      if (mine && part == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
+      if (mine && part == 0 && n_sc < NS) state_out[row * NS + n_sc] = tot;
     }
     lds_sync();                           // sbuf reads done before the next tile writes
   }
 }
 
-template <typename IO, bool VEC, bool PIPE>
+template <typename IO, bool VEC, bool PIPE, bool CPX>
 static hipError_t launch_mfma_k(const ChunkArgs& a) {
   dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
-  chunk_mfma_kernel<IO, VEC, PIPE><<<grid, block, 0, a.stream>>>(
+  chunk_mfma_kernel<IO, VEC, PIPE, CPX><<<grid, block, 0, a.stream>>>(
       static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
       a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a) {
-  if (a.N > MFMA_MAXN) return hipErrorInvalidValue;
+template <bool CPX>
+static hipError_t launch_mfma_modes(const ChunkArgs& a) {
   const int esz = a.bf16 ? 2 : 4;
   const bool vec = (a.L % (16 / esz) == 0) && aligned_all(16, a.x1, a.x2, a.v, a.y);
-  if (!a.bf16) return vec ? launch_mfma_k<float, true, false>(a) : launch_mfma_k<float, false, false>(a);
-  if (!vec) return launch_mfma_k<bf16_t, false, false>(a);
-  return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true>(a) : launch_mfma_k<bf16_t, true, false>(a);
+  if (!a.bf16)
+    return vec ? launch_mfma_k<float, true, false, CPX>(a) : launch_mfma_k<float, false, false, CPX>(a);
+  if (!vec) return launch_mfma_k<bf16_t, false, false, CPX>(a);
+  return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true, CPX>(a)
+                     : launch_mfma_k<bf16_t, true, false, CPX>(a);
+}
+
+hipError_t launch_chunk_mfma(const ChunkArgs& a) {
+  if ((a.cpx ? 2 * a.N : a.N) > MFMA_MAXN) return hipErrorInvalidValue;
+  return a.cpx ? launch_mfma_modes<true>(a) : launch_mfma_modes<false>(a);
 }
 
 }  // namespace hyena

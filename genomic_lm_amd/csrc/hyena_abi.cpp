@@ -144,9 +144,10 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
   if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
     return HYENA_ERR_INVALID_ARG;
   const int64_t Ceff = C < L ? C : L;
+  const int64_t slots = cpx ? 2 * N : N;      // real lanes of the MFMA kernel's scan
   hyena_chunk_algo_t use = algo;
-  if (use == HYENA_CHUNK_AUTO) use = (N <= 16 && !cpx) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
-  if (use == HYENA_CHUNK_MFMA && (N > 16 || cpx)) return HYENA_ERR_UNSUPPORTED;
+  if (use == HYENA_CHUNK_AUTO) use = (slots <= 16) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
+  if (use == HYENA_CHUNK_MFMA && slots > 16) return HYENA_ERR_UNSUPPORTED;
   if (use == HYENA_CHUNK_FFT && Ceff > HYENA_MAX_FFT_CHUNK) return HYENA_ERR_UNSUPPORTED;
   hyena::ChunkArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                      state_out, y, static_cast<int>(B), static_cast<int>(D),
@@ -301,9 +302,9 @@ hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v
                                    const float* log_poles, const float* residues, int64_t N,
                                    const float* skip, const float* state_in, float* state_out,
                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                                   hyena_dtype_t io, void* stream) {
+                                   hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
   return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
-                    C, io, HYENA_CHUNK_FFT, true, stream);
+                    C, io, algo, true, stream);
 }
 
 hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void* v,

@@ -142,6 +142,11 @@ __device__ __forceinline__ float xor16(float x, int l) {
   return __uint_as_float((l & 16) ? r[0] : r[1]);
 }
 
+// x of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2; a VALU op).
+__device__ __forceinline__ float xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One 16-byte chunk per lane from global memory straight into LDS (no

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 4
+#define HYENA_ABI_VERSION 5
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -79,11 +79,13 @@ typedef enum hyena_dtype {
     HYENA_BF16 = 1,
 } hyena_dtype_t;
 
-/* Algorithm for hyena_chunk_fwd.  Both compute the same function. */
+/* Algorithm for hyena_chunk_fwd and hyena_chunk_fwd_cpx.  Both compute the
+ * same function. */
 typedef enum hyena_chunk_algo {
-    HYENA_CHUNK_AUTO = 0,        /* the faster of the two for the shape */
+    HYENA_CHUNK_AUTO = 0,        /* MFMA when the modes fit it (below), else FFT */
     HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms */
-    HYENA_CHUNK_MFMA = 2,        /* blocked Toeplitz on bf16x3 MFMA + modal state scan */
+    HYENA_CHUNK_MFMA = 2,        /* blocked Toeplitz on bf16x3 MFMA + modal state scan;
+                                    N <= 16 real or N <= 8 complex modes */
 } hyena_chunk_algo_t;
 
 /* Limits of this build. */
@@ -254,16 +256,18 @@ hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void*
                                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Chunked prefill with the complex modal state carried in and out, as
- * hyena_chunk_fwd with the FFT algorithm:
+ * hyena_chunk_fwd:
  *   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + Re sum_n R_n p_n^(t-t0+1) s_n,
- *   s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j];
- * C' <= HYENA_MAX_FFT_CHUNK. */
+ *   s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j].
+ * HYENA_CHUNK_MFMA takes N <= 8 complex modes (each a pair of real lanes of
+ * its scan), HYENA_CHUNK_FFT any N with C' <= HYENA_MAX_FFT_CHUNK; AUTO picks
+ * MFMA for N <= 8. */
 hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
                                    const float* log_poles, const float* residues,
                                    int64_t N, const float* skip,
                                    const float* state_in, float* state_out,
                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                                   hyena_dtype_t io, void* stream);
+                                   hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream);
 
 /* One decode step, as hyena_modal_decode: s_n <- p_n s_n + u,
  * y = x2 * Re sum_n R_n s_n + skip * u. */

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 4
+    assert G.abi_version() == 5
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -166,6 +166,20 @@ def test_chunk_validation():
     assert f(*a) == G.ERR_UNSUPPORTED
     a = list(good); a[13] = 16384; a[15] = G.ALGOS["fft"]; a[12] = 16384
     assert f(*a) == G.ERR_UNSUPPORTED                          # FFT chunk > 8192
+    a = list(good); a[10] = 0                                  # empty batch
+    assert f(*a) == G.OK
+
+
+def test_chunk_cpx_validation():
+    f = G.lib().hyena_chunk_fwd_cpx
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, None, FAKE, FAKE, 1, 4, 1024, 1024,
+            G.BF16, 0, None]
+    a = list(good); a[5] = 9; a[15] = G.ALGOS["mfma"]         # 9 complex modes: 18 real lanes
+    assert f(*a) == G.ERR_UNSUPPORTED
+    a = list(good); a[15] = 3
+    assert f(*a) == G.ERR_INVALID_ARG
+    a = list(good); a[5] = 0
+    assert f(*a) == G.ERR_INVALID_ARG
     a = list(good); a[10] = 0                                  # empty batch
     assert f(*a) == G.OK
 

@@ -67,28 +67,50 @@ def test_fftconv_cpx(io, L):
     gate(y, ref, io, label=f"fftconv_cpx L={L}")
 
 
+@pytest.mark.parametrize("algo", ["fft", "mfma"])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("C,L", [(64, 1000), (1024, 3000), (1000, 4096), (4096, 9000), (8192, 8192)])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_chunk_cpx(io, C, L, with_state):
+def test_chunk_cpx(algo, io, C, L, with_state):
     w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2)
     s0 = W.random_complex_state(2, w.D, 8, seed=C) if with_state else None
     s0_d = None if s0 is None else torch.from_numpy(s0).to(d.x1.device)
-    log(f"chunk_cpx io={io} C={C} L={L} state={with_state}")
-    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, C, d.skip, state_in=s0_d)
+    log(f"chunk_cpx {algo} io={io} C={C} L={L} state={with_state}")
+    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, C, d.skip, state_in=s0_d, algo=algo)
     ref, ref_s = _ref(w, lam, R, C=C, state_in=s0)
-    gate(y, ref, io, label=f"chunk_cpx C={C}")
+    gate(y, ref, io, label=f"chunk_cpx {algo} C={C}")
     err = _state_err(s, ref_s)
     log(f"  state rel_l2_ch={err:.3e}")
     assert err < 1e-4
 
 
+@pytest.mark.parametrize("N", [1, 3, 5, 8, 9])
+def test_chunk_cpx_mode_counts(N):
+    """Complex mode counts through AUTO: N <= 8 on the matrix cores (padding
+    slots included), N = 9 on the FFT algorithm; and the unaligned path."""
+    w, d, lam, R, lam_d, R_d = _setup("bf16", D=6, L=2500, B=1, N=N, seed=30 + N)
+    log(f"chunk_cpx auto N={N}")
+    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip)
+    ref, ref_s = _ref(w, lam, R)
+    gate(y, ref, "bf16", label=f"chunk_cpx auto N={N}")
+    assert _state_err(s, ref_s) < 1e-4
+    if N <= 8:
+        y2, s2 = G.chunk_fwd_cpx(*(offset_copy(t) for t in (d.x1, d.x2, d.v)), lam_d, R_d, 1000,
+                                 d.skip, algo="mfma")
+        gate(y2, ref, "bf16", label=f"chunk_cpx mfma unaligned N={N}")
+        assert _state_err(s2, ref_s) < 1e-4
+    else:
+        with pytest.raises(G.HyenaError):
+            G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip, algo="mfma")
+
+
+@pytest.mark.parametrize("algo", ["fft", "mfma"])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_decode_cpx_after_prefill(io):
+def test_decode_cpx_after_prefill(algo, io):
     L, T = 3000, 16
     w, d, lam, R, lam_d, R_d = _setup(io, D=16, L=L + T, B=2)
     pre = [t[..., :L].contiguous() for t in (d.x1, d.x2, d.v)]
-    y_pre, s = G.chunk_fwd_cpx(*pre, lam_d, R_d, 1024, d.skip)
+    y_pre, s = G.chunk_fwd_cpx(*pre, lam_d, R_d, 1024, d.skip, algo=algo)
     ys = [y_pre]
     for t in range(L, L + T):
         yt, s = G.modal_decode_cpx(d.x1[..., t].contiguous(), d.x2[..., t].contiguous(),
@@ -128,15 +150,20 @@ def test_cpx_with_real_modes_matches_real_entries():
     d = DevWorkload(w)
     lam_c = torch.complex(d.lam, torch.zeros_like(d.lam))
     R_c = torch.complex(d.res, torch.zeros_like(d.res))
-    ref, ref_s = oracle.hyena_fwd(w.f64("x1"), w.f64("x2"), w.f64("v"), w.log_poles, w.residues,
-                                  w.skip), None
+    lam_c, R_c = lam_c[:, :8].contiguous(), R_c[:, :8].contiguous()   # MFMA: <= 8 complex
+    lam8, res8 = d.lam[:, :8].contiguous(), d.res[:, :8].contiguous()
+    ref = oracle.hyena_fwd(w.f64("x1"), w.f64("x2"), w.f64("v"), w.log_poles[:, :8],
+                           w.residues[:, :8], w.skip)
     for name, y in (
         ("fftconv", G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, d.skip)),
-        ("chunk", G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, 1024, d.skip)[0]),
+        ("chunk", G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, 1024, d.skip, algo="fft")[0]),
+        ("chunk_mfma", G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_c, R_c, 1024, d.skip,
+                                       algo="mfma")[0]),
     ):
         gate(y, ref, "bf16", label=f"real modes via {name}_cpx")
-        y_real = (G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip) if name == "fftconv"
-                  else G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="fft")[0])
+        y_real = (G.fftconv_fwd(d.x1, d.x2, d.v, lam8, res8, d.skip) if name == "fftconv"
+                  else G.chunk_fwd(d.x1, d.x2, d.v, lam8, res8, 1024, d.skip,
+                                   algo="mfma" if name == "chunk_mfma" else "fft")[0])
         diff = (y.float() - y_real.float()).abs().max().item()
         assert diff <= 2e-2 * y_real.float().abs().max().item(), (name, diff)
 
@@ -151,6 +178,7 @@ def test_cpx_7b_shape():
     ref, ref_s = _ref(w, lam, R, rows)
     gate(G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, d.skip), ref, "bf16", rows,
          label="7b cpx fftconv")
-    y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip)
-    gate(y, ref, "bf16", rows, label="7b cpx chunk")
-    assert _state_err(s[:, torch.as_tensor(rows, device=s.device)], ref_s) < 1e-4
+    for algo in ("fft", "mfma"):
+        y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip, algo=algo)
+        gate(y, ref, "bf16", rows, label=f"7b cpx chunk {algo}")
+        assert _state_err(s[:, torch.as_tensor(rows, device=s.device)], ref_s) < 1e-4
