@@ -7,8 +7,11 @@ skip, and the carried modal state -- all in one launch of hyena_chunk_fwd.
 Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  Besides the headline it reports the roofline of the
-dominant kernel (HIP-event timing of the same launches), the other entry points
-at the same shape, and the fp64 CPU oracle timed on a bounded sample.
+dominant kernel (HIP-event timing of the same launches; HBM bytes and the
+fp32 vector / bf16 matrix-core flops per launch from rocprofv3 counters kept
+in profiles/traffic.json, while the kernel sources are unchanged), the other
+entry points at the same shape, and the fp64 CPU oracle timed on a bounded
+sample.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 100] [--no-cpu-baseline]
 """
@@ -26,6 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Hyena op Gtoken·channels/s at D=4096 L=32768 bf16; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3                     # MI355X fp32 vector (packed FP32)
+BF16_MFMA_PEAK_TFLOPS = 2500.0               # MI355X dense bf16 matrix cores
 WORKLOAD = "32k_chunked"
 CHUNK = 1024
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -169,11 +174,23 @@ def main():
     alg_bytes = 8 * tc                       # x1, x2, v read + y written, bf16
     achieved = alg_bytes / t_step / 1e9
     traffic = None
+    compute = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash() and tr.get("algo") == args.algo:
             traffic = tr.get("bytes_per_launch")
+            fl = tr.get("compute")
+            if fl:
+                # flops per launch from the SQ counters (fp32 VALU: 64 lanes x
+                # (add + mul + transcendental + 2 fma) instructions; bf16 MFMA:
+                # 512 x MFMA_MOPS_BF16) over this run's launch time
+                compute = {}
+                for key, n, peak in (("valu_fp32", fl["valu_fp32_flops"], FP32_PEAK_TFLOPS),
+                                     ("mfma_bf16", fl["mfma_bf16_flops"], BF16_MFMA_PEAK_TFLOPS)):
+                    a = n / t_step / 1e12
+                    compute[key] = {"achieved": round(a, 2), "peak": peak, "unit": "TFLOP/s",
+                                    "frac": round(a / peak, 4), "flops": n}
 
     comps = {}
     if not args.no_components:
@@ -258,6 +275,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        "compute": compute,
         "wall_s_timed": round(t_wall, 3),
         "components": comps,
     }
