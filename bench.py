@@ -249,6 +249,12 @@ def main():
                             dtype=torch.uint8, device=dev)
         runs["chunk_tokmajor"] = lambda: G.chunk_fwd_tokmajor(xin, lam, res, skip, out=y_tm,
                                                               state_out=st, workspace=tm_ws)
+        win6 = torch.empty((B, D, 6), dtype=torch.float32, device=dev)
+        win127 = torch.empty((B, D, 127), dtype=torch.float32, device=dev)
+        runs["fir7_tokmajor"] = lambda: G.fir_fwd_tokmajor(xin, taps7, skip, out=y_tm,
+                                                           window_out=win6)
+        runs["fir128_tokmajor"] = lambda: G.fir_fwd_tokmajor(xin, taps128, skip, out=y_tm,
+                                                             window_out=win127)
         one_token = {"modal_decode_step", "fir128_window_step"}   # B*D token·channels
         for name, fn in runs.items():
             t = timed(fn, comp_steps, 2, stream)

@@ -17,6 +17,8 @@ Entry points (names follow the C ABI):
   fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None) -> (y, window_out)
   chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None,
                      pos=(0, 1, 2))  (xin (B, L, 3D))   -> (y (B, L, D), state_out)
+  fir_fwd_tokmajor(xin, taps, skip=None, window_in=None, pos=(0, 1, 2))
+                                                         -> (y (B, L, D), window_out)
 Complex-pole variants (log_poles / residues complex64 (D, N), states
 complex64 (B, D, N)): modal_filter_cpx, fftconv_fwd_cpx, chunk_fwd_cpx,
 modal_decode_cpx.
@@ -33,7 +35,7 @@ __all__ = [
     "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
     "modal_decode", "fir_fwd_window",
     "modal_filter_cpx", "fftconv_fwd_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
-    "chunk_fwd_tokmajor", "chunk_tokmajor_workspace_size",
+    "chunk_fwd_tokmajor", "chunk_tokmajor_workspace_size", "fir_fwd_tokmajor",
     "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_LAUNCH",
     "F32", "BF16", "ALGOS", "EXPORTS",
 ]
@@ -75,6 +77,8 @@ EXPORTS = {
                                         _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int, _p,
                                         _size, _p]),
     "hyena_chunk_tokmajor_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
+    "hyena_fir_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
+                                      _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
 }
 
 
@@ -452,3 +456,35 @@ def chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None, pos=(
         _ptr(skip), _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, _io(xin),
         _ptr(workspace), ws_bytes, _stream(xin)))
     return y, state_out
+
+
+def fir_fwd_tokmajor(xin, taps, skip=None, window_in=None, pos=(0, 1, 2), out=None,
+                     window_out=None):
+    """Explicit FIR on in_proj's token-major layout, continuing from a window:
+    xin (B, L, 3D) as chunk_fwd_tokmajor; returns (y (B, L, D), window_out
+    (B, D, K-1), None when K = 1)."""
+    _act("xin", xin)
+    B, L, D3 = xin.shape
+    if D3 % 3:
+        raise ValueError(f"xin must be (B, L, 3D), got shape {tuple(xin.shape)}")
+    D = D3 // 3
+    if sorted(int(p) for p in pos) != [0, 1, 2]:
+        raise ValueError("pos must be a permutation of (0, 1, 2)")
+    K = taps.shape[-1] if isinstance(taps, torch.Tensor) and taps.dim() == 2 else -1
+    _param("taps", taps, (D, K), xin.device)
+    _param("skip", skip, (D,), xin.device, optional=True)
+    _param("window_in", window_in, (B, D, K - 1), xin.device, optional=True)
+    if out is None:
+        y = torch.empty((B, L, D), dtype=xin.dtype, device=xin.device)
+    else:
+        y = _act("out", out)
+        if tuple(y.shape) != (B, L, D) or y.dtype != xin.dtype or y.device != xin.device:
+            raise ValueError("out must be (B, L, D) with the dtype and device of xin")
+    if K > 1 and window_out is None:
+        window_out = torch.empty((B, D, K - 1), dtype=torch.float32, device=xin.device)
+    elif window_out is not None:
+        _param("window_out", window_out, (B, D, K - 1), xin.device)
+    _check("hyena_fir_fwd_tokmajor", lib().hyena_fir_fwd_tokmajor(
+        _ptr(xin), int(pos[0]), int(pos[1]), int(pos[2]), _ptr(taps), K, _ptr(skip),
+        _ptr(window_in), _ptr(window_out), _ptr(y), B, D, L, _io(xin), _stream(xin)))
+    return y, window_out

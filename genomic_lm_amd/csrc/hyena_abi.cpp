@@ -188,6 +188,32 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
   return from_hip(hyena::launch_tokmajor(args));
 }
 
+hyena_status_t fir_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_x2, int32_t pos_v,
+                                 const float* taps, int64_t K, const float* skip,
+                                 const float* window_in, float* window_out, void* y, int64_t B,
+                                 int64_t D, int64_t L, hyena_dtype_t io, void* stream) {
+  if (!valid_io(io) || B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
+  const bool perm = pos_x1 >= 0 && pos_x2 >= 0 && pos_v >= 0 && pos_x1 < 3 && pos_x2 < 3 &&
+                    pos_v < 3 && pos_x1 != pos_x2 && pos_x1 != pos_v && pos_x2 != pos_v;
+  if (!perm || K < 1) return HYENA_ERR_INVALID_ARG;
+  if (K > HYENA_MAX_FIR_TAPS_TOKMAJOR) return HYENA_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return HYENA_OK;
+  if (B > 65535 || D > kMaxInt / 3 || L > kMaxInt - 1024 || B * D > kMaxInt)
+    return HYENA_ERR_UNSUPPORTED;
+  if (L > 0 && B * D > std::numeric_limits<int64_t>::max() / (3 * L)) return HYENA_ERR_UNSUPPORTED;
+  if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
+  if ((window_in && !aligned_to(window_in, 4)) || (window_out && !aligned_to(window_out, 4)))
+    return HYENA_ERR_INVALID_ARG;
+  const size_t a = io_size(io);
+  if (L > 0 && (!xin || !y || !aligned_to(xin, a) || !aligned_to(y, a))) return HYENA_ERR_INVALID_ARG;
+  if (L == 0 && (K == 1 || !window_out)) return HYENA_OK;
+  hyena::TokmajorFirArgs args{xin, pos_x1, pos_x2, pos_v, taps, static_cast<int>(K), skip,
+                              window_in, window_out, y, static_cast<int>(B),
+                              static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16,
+                              as_stream(stream)};
+  return from_hip(hyena::launch_tokmajor_fir(args));
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +350,15 @@ hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t
                                         void* workspace, size_t ws_bytes, void* stream) {
   return chunk_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, log_poles, residues, N, skip, state_in,
                              state_out, y, B, D, L, io, workspace, ws_bytes, stream);
+}
+
+hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                      int32_t pos_v, const float* taps, int64_t K,
+                                      const float* skip, const float* window_in,
+                                      float* window_out, void* y, int64_t B, int64_t D, int64_t L,
+                                      hyena_dtype_t io, void* stream) {
+  return fir_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, taps, K, skip, window_in, window_out, y,
+                           B, D, L, io, stream);
 }
 
 size_t hyena_chunk_tokmajor_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,

@@ -98,6 +98,21 @@ struct TokmajorArgs {
   hipStream_t stream;
 };
 
+// Token-major explicit FIR: xin as above, taps (D, K), windows (B, D, K-1).
+struct TokmajorFirArgs {
+  const void* xin;
+  int pos_x1, pos_x2, pos_v;
+  const float* taps;
+  int K;
+  const float* skip;
+  const float* win_in;
+  float* win_out;
+  void* y;
+  int B, D, L;
+  bool bf16;
+  hipStream_t stream;
+};
+
 // cpx: complex modes, lam and res as (re, im) pairs (also in the structs below)
 hipError_t launch_modal_filter(const float* lam, const float* res, int D, int N, int L,
                                float* h, bool cpx, hipStream_t stream);
@@ -128,6 +143,9 @@ hipError_t launch_fir_window(const FirArgs& a, const float* win_in, float* win_o
 void tokmajor_segments(int64_t B, int64_t D, int64_t L, bool bf16, int* TS, int* P);
 size_t tokmajor_workspace(int64_t B, int64_t D, int64_t L, int64_t N, bool bf16);
 hipError_t launch_tokmajor(const TokmajorArgs& a);
+// Token-major explicit FIR (K <= 128), then window_out when requested.
+void tokmajor_fir_segments(int64_t B, int64_t D, int64_t L, int K, int* TS, int* P);
+hipError_t launch_tokmajor_fir(const TokmajorFirArgs& a);
 
 // state_out <- state_in (or 0 when state_in is null), count floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t count,

@@ -43,65 +43,72 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM_G = 256;                      // channels (lanes) per workgroup
-constexpr int TM_TILE_BYTES = 12 * 1024;       // input bytes per tile (two buffers)
+constexpr int TM_THREADS = 256;                // threads per workgroup
+constexpr int TM_G = 256;                      // modal kernels: channels (lanes) per workgroup
+constexpr int TM_TILE_BYTES = 12 * 1024;       // modal kernels: input bytes per tile
 
-template <typename IO>
+// Staging of tiles of TT token rows of a span of G channels (3G elements)
+// by TM_THREADS threads.
+template <typename IO, int G, int TTOK>
 struct TmShape {
+  static constexpr int TT = TTOK;                       // tokens per tile
   static constexpr int ESZ = sizeof(IO);
-  static constexpr int SPAN = 3 * TM_G;                 // elements of one token row's span
-  static constexpr int TT = TM_TILE_BYTES / (SPAN * ESZ);   // tokens per tile: 8 (bf16), 4 (f32)
+  static constexpr int SPAN = 3 * G;                    // elements of one token row's span
   static constexpr int EPC = 16 / ESZ;                  // elements per 16-byte chunk
   static constexpr int CW = SPAN / EPC;                 // chunks per token row
-  static constexpr int PER = TT * CW / TM_G;            // chunks per lane per tile
-  static constexpr int PER_E = TT * SPAN / TM_G;        // elements per lane per tile (scalar path)
-  static_assert(TT * CW % TM_G == 0, "tile");
+  static constexpr int NCH = TT * CW;                   // chunks per tile
+  static constexpr int PER = (NCH + TM_THREADS - 1) / TM_THREADS;        // per thread
+  static constexpr int PER_E = (TT * SPAN + TM_THREADS - 1) / TM_THREADS;  // scalar path
+  static_assert(SPAN % EPC == 0, "span");
 };
 
+// The modal kernels' tile: 12 KB of rows, 8 tokens (bf16) or 4 (f32).
+template <typename IO>
+using TmModal = TmShape<IO, TM_G, TM_TILE_BYTES / (3 * TM_G * int(sizeof(IO)))>;
+
 // One tile of token rows [t0, t0 + TT) of the span [col0, col0 + cols) of
-// the input, rows past t_end and columns past cols left as zeros.  VEC: 16-byte
+// the input, rows outside [t_lo, t_end) and columns past cols left as zeros.  VEC: 16-byte
 // chunks (needs a 16-byte aligned input and rows of a multiple of 16 bytes);
 // otherwise single elements.
-template <typename IO, bool VEC>
+template <typename IO, bool VEC, int G, int TT>
 struct TmLoader {
-  using S = TmShape<IO>;
+  using S = TmShape<IO, G, TT>;
   static constexpr int NREG = VEC ? S::PER : S::PER_E;
+  static constexpr int NITEM = VEC ? S::NCH : TT * S::SPAN;   // chunks or elements per tile
   using Reg = typename std::conditional<VEC, u32x4, IO>::type;
   Reg r[NREG];
 
   __device__ __forceinline__ void load(const IO* __restrict__ xb, int64_t ld, int col0, int cols,
-                                       int t0, int t_end, int tid) {
-    if constexpr (VEC) {
+                                       int t0, int t_end, int tid, int t_lo = 0) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int k = tid + TM_G * i;
+    for (int i = 0; i < NREG; ++i) {
+      const int k = tid + TM_THREADS * i;
+      if constexpr (VEC) {
         const int tt = k / S::CW, pc = k % S::CW;
-        if (t0 + tt < t_end && pc * S::EPC < cols) {
+        if (k < NITEM && t0 + tt >= t_lo && t0 + tt < t_end && pc * S::EPC < cols) {
           const u32x4* src =
               reinterpret_cast<const u32x4*>(xb + int64_t(t0 + tt) * ld + col0) + pc;
           r[i] = __builtin_nontemporal_load(src);
         } else {
           r[i] = u32x4{0u, 0u, 0u, 0u};
         }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int k = tid + TM_G * i;
+      } else {
         const int tt = k / S::SPAN, e = k % S::SPAN;
-        r[i] = (t0 + tt < t_end && e < cols) ? xb[int64_t(t0 + tt) * ld + col0 + e] : IO(0);
+        r[i] = (k < NITEM && t0 + tt >= t_lo && t0 + tt < t_end && e < cols)
+                   ? xb[int64_t(t0 + tt) * ld + col0 + e]
+                   : IO(0);
       }
     }
   }
 
   __device__ __forceinline__ void store(IO* tile, int tid) const {
-    if constexpr (VEC) {
-      u32x4* t4 = reinterpret_cast<u32x4*>(tile);
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) t4[tid + TM_G * i] = r[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NREG; ++i) tile[tid + TM_G * i] = r[i];
+    for (int i = 0; i < NREG; ++i) {
+      const int k = tid + TM_THREADS * i;
+      if (NITEM % TM_THREADS == 0 || k < NITEM) {
+        if constexpr (VEC) reinterpret_cast<u32x4*>(tile)[k] = r[i];
+        else tile[k] = r[i];
+      }
     }
   }
 };
@@ -134,7 +141,7 @@ template <typename IO, bool VEC, int NM>
 __global__ __launch_bounds__(TM_G) void tm_states(
     const IO* __restrict__ xin, int pos1, int posv, const float* __restrict__ lam, int N,
     float* __restrict__ ws, int D, int L, int TS, int P) {
-  using S = TmShape<IO>;
+  using S = TmModal<IO>;
   __shared__ IO tile[2][S::TT * S::SPAN];
   const int tid = threadIdx.x;
   const int col0 = 3 * TM_G * blockIdx.x;
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(TM_G) void tm_states(
 
   const int t_begin = r * TS, t_end = t_begin + TS;   // full: r < P-1
   const int o1 = 3 * tid + pos1, ov = 3 * tid + posv;
-  TmLoader<IO, VEC> ldr;
+  TmLoader<IO, VEC, TM_G, S::TT> ldr;
   ldr.load(xb, ld, col0, cols, t_begin, t_end, tid);
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += S::TT) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(TM_G) void tm_outputs(
     const float* __restrict__ res, int N, const float* __restrict__ skip, const float* state_in,
     const float* __restrict__ ws, float* state_out, IO* __restrict__ y, int D, int L, int TS,
     int P) {
-  using S = TmShape<IO>;
+  using S = TmModal<IO>;
   __shared__ IO tile[2][S::TT * S::SPAN];
   const int tid = threadIdx.x;
   const int col0 = 3 * TM_G * blockIdx.x;
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(TM_G) void tm_outputs(
 
   const int t_begin = r * TS, t_end = min(L, t_begin + TS);
   const int o1 = 3 * tid + pos1, o2 = 3 * tid + pos2, ov = 3 * tid + posv;
-  TmLoader<IO, VEC> ldr;
+  TmLoader<IO, VEC, TM_G, S::TT> ldr;
   ldr.load(xb, ld, col0, cols, t_begin, t_end, tid);
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += S::TT) {
@@ -289,7 +296,236 @@ __global__ __launch_bounds__(TM_G) void tm_outputs(
   }
 }
 
-int tm_tile_tokens(bool bf16) { return bf16 ? TmShape<bf16_t>::TT : TmShape<float>::TT; }
+// ---------------------------------------------------------------- FIR
+// The explicit-FIR operator (hcm / hcs blocks) on the same layout:
+//   z[t] = sum_{k<K} w[c, k] u[t-k],  y = x2 z + skip u,
+// u[t < 0] from the caller's window of the K-1 inputs before the call (or 0).
+// A workgroup of 256 threads covers G = 256 / LPC channels and LPC blocks of
+// TPL taps: thread (j, ch) = (tid / G, tid % G) holds taps [j TPL, (j+1) TPL)
+// of channel ch, so each wave (64 consecutive channels, one tap block) touches
+// LDS only across consecutive channels, free of bank conflicts.  Tiles of
+// FT = 8 token rows are staged through LDS; the tile's u goes into a ring of
+// RD = LPC TPL + FT token slots x G channels, from which thread (j, ch) reads
+// the window u[t0 - (j+1) TPL, t0 - j TPL + FT) and forms its partial sums for
+// the tile's 8 outputs; the LPC partials meet in LDS.  No state crosses
+// segments: segments of TS tokens run in parallel, each starting with LPC TPL
+// tokens of halo that only fill the ring.  fp32 vector work, 2K flops per
+// token and channel.
+
+// Grid (ceil(D / G), P, B); segment r covers [r TS, min(L, (r+1) TS)).
+// win_out, when not null, is written by the last segment from its ring (the
+// caller passes it only when no other segment still reads win_in there).
+template <typename IO, bool VEC, int TPL, int LPC, int FT>
+__global__ __launch_bounds__(TM_THREADS) void tm_fir(
+    const IO* __restrict__ xin, int pos1, int pos2, int posv, const float* __restrict__ taps,
+    int K, const float* __restrict__ skip, const float* win_in, float* win_out,
+    IO* __restrict__ y, int D, int L, int TS) {
+  constexpr int G = TM_THREADS / LPC;
+  constexpr int TAPS = LPC * TPL;              // >= K
+  constexpr int RD = TAPS + FT;                // ring slots, a multiple of FT
+  constexpr int EPT = FT * G / TM_THREADS;     // (token, channel) elements per thread
+  static_assert(TPL % FT == 0 && G % 64 == 0 && FT * G % TM_THREADS == 0, "shape");
+  using S = TmShape<IO, G, FT>;
+  __shared__ IO tile[2][FT * S::SPAN];
+  __shared__ float ring[RD][G];
+  __shared__ float zpart[LPC > 1 ? LPC * FT * G : 1];    // [j][i][ch]
+
+  const int tid = threadIdx.x;
+  const int j = tid / G, ch = tid % G;         // this thread's taps and channel
+  const int gbase = G * static_cast<int>(blockIdx.x);
+  const int r = blockIdx.y;
+  const int b = blockIdx.z;
+  const int col0 = 3 * gbase;
+  const int cols = min(S::SPAN, 3 * D - col0);
+  const int64_t ld = 3 * int64_t(D);
+  const IO* xb = xin + int64_t(b) * L * ld;
+  const int W = K - 1;
+
+  float w[TPL];
+  {
+    const int c = gbase + ch;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int kk = j * TPL + k;
+      w[k] = (c < D && kk < K) ? taps[int64_t(c) * K + kk] : 0.0f;
+    }
+  }
+  // elements (token i, channel ce) this thread gates: e = tid + 256 q
+  float ske[EPT];
+  const float* wrow[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int ce = (tid + TM_THREADS * q) % G, c = gbase + ce;
+    ske[q] = (c < D && skip) ? skip[c] : 0.0f;
+    wrow[q] = (c < D && win_in) ? win_in + (int64_t(b) * D + c) * W : nullptr;
+  }
+
+  const int t_begin = r * TS, t_end = min(L, t_begin + TS);
+  const int t_first = t_begin - TAPS;          // halo start, a multiple of FT
+  TmLoader<IO, VEC, G, FT> ldr;
+  ldr.load(xb, ld, col0, cols, t_first, t_end, tid);
+  int buf = 0;
+  for (int t0 = t_first; t0 < t_end; t0 += FT) {
+    ldr.store(tile[buf], tid);
+    __syncthreads();                           // tile visible; the last tile's LDS reads done
+    if (t0 + FT < t_end) ldr.load(xb, ld, col0, cols, t0 + FT, t_end, tid);
+    const IO* tb = tile[buf];
+    const int slot0 = (t0 - t_first) % RD;
+    // u of this thread's elements into the ring; x2 kept for the gate
+    float ue[EPT], x2e[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + TM_THREADS * q, i = e / G, ce = e % G, t = t0 + i;
+      float u = 0.0f;
+      if (t >= 0) {
+        u = Io<IO>::ld(tb, i * S::SPAN + 3 * ce + pos1) * Io<IO>::ld(tb, i * S::SPAN + 3 * ce + posv);
+      } else if (wrow[q] && t >= -W) {
+        u = wrow[q][W + t];
+      }
+      ue[q] = u;
+      x2e[q] = Io<IO>::ld(tb, i * S::SPAN + 3 * ce + pos2);
+      ring[slot0 + i][ce] = u;
+    }
+    __syncthreads();                           // the tile's u in the ring
+    if (t0 < t_begin) {                        // uniform: halo tiles only fill the ring
+      buf ^= 1;
+      continue;
+    }
+    // window: tokens [t0 - (j+1) TPL, t0 - j TPL + FT), slot order kept by
+    // whole groups of FT (the ring never splits one)
+    float win[TPL + FT];
+    const int tw = t0 - (j + 1) * TPL;
+#pragma unroll
+    for (int gq = 0; gq < TPL / FT + 1; ++gq) {
+      const int s0 = (tw + FT * gq - t_first) % RD;
+#pragma unroll
+      for (int m = 0; m < FT; ++m) win[FT * gq + m] = ring[s0 + m][ch];
+    }
+    // partial sums: token t0 + i, tap j TPL + k reads u[t0 + i - j TPL - k]
+    // = win[TPL + i - k]
+    float z[FT];
+#pragma unroll
+    for (int i = 0; i < FT; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) acc = fmaf(w[k], win[TPL + i - k], acc);
+      z[i] = acc;
+    }
+    if constexpr (LPC > 1) {
+#pragma unroll
+      for (int i = 0; i < FT; ++i) zpart[(j * FT + i) * G + ch] = z[i];
+      __syncthreads();                         // every tap block's partials in
+    }
+    const int nt = min(FT, t_end - t0);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + TM_THREADS * q, i = e / G, ce = e % G;
+      float zz;
+      if constexpr (LPC > 1) {
+        zz = zpart[i * G + ce];
+#pragma unroll
+        for (int jj = 1; jj < LPC; ++jj) zz += zpart[(jj * FT + i) * G + ce];
+      } else {
+        zz = z[q];                             // LPC = 1: element q is token q of this channel
+      }
+      if (i < nt && gbase + ce < D)
+        Io<IO>::st(y, (int64_t(b) * L + t0 + i) * D + gbase + ce, fmaf(x2e[q], zz, ske[q] * ue[q]));
+    }
+    buf ^= 1;
+  }
+  // the new window, u of tokens [L - W, L), is in the ring of the last
+  // segment (its halo reaches back at least K tokens before L - 1); read
+  // across consecutive channels (conflict-free), written once per call
+  if (win_out && r == static_cast<int>(gridDim.y) - 1) {
+    for (int e = tid; e < G * W; e += TM_THREADS) {
+      const int k = e / G, cc = e % G;
+      if (gbase + cc < D)
+        win_out[(int64_t(b) * D + gbase + cc) * W + k] = ring[(L - W + k - t_first) % RD][cc];
+    }
+  }
+}
+
+// window_out[j] = e[L + j] for e = [window_in, u[0:L)], one thread per row
+// (L = 0, or several segments with window_out overlapping window_in); ascending
+// j reads index L + j >= j before writing j, so window_out may be window_in.
+template <typename IO>
+__global__ __launch_bounds__(256) void tm_fir_window(const IO* __restrict__ xin, int pos1,
+                                                     int posv, const float* win_in,
+                                                     float* win_out, int W, int D, int L,
+                                                     int64_t rows) {
+  const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const int64_t b = row / D;
+  const int c = static_cast<int>(row % D);
+  const int64_t ld = 3 * int64_t(D);
+  const IO* xc = xin + b * L * ld + 3 * c;
+  const float* wi = win_in ? win_in + row * W : nullptr;
+  float* wo = win_out + row * W;
+  for (int k = 0; k < W; ++k) {
+    const int64_t src = int64_t(L) + k;
+    float val;
+    if (src < W) {
+      val = wi ? wi[src] : 0.0f;
+    } else {
+      const int64_t t = src - W;
+      val = Io<IO>::ld(xc, t * ld + pos1) * Io<IO>::ld(xc, t * ld + posv);
+    }
+    wo[k] = val;
+  }
+}
+
+// Tap blocks and tile lengths: K <= 8 -> one block of 8 taps, K <= 32 -> one
+// block of 32 (tiles of 8 tokens); K <= 64 -> two blocks, K <= 128 -> four
+// (tiles of TM_FIR_FT_WIDE tokens: longer tiles amortise the window reads
+// and barriers over more fmas, measured 0.89 against 1.09 ms for K = 128 at
+// D = 4096, L = 32768).
+constexpr int TM_FIR_FT_WIDE = 16;
+struct TmFirShape {
+  int TPL, LPC, FT;
+};
+TmFirShape tm_fir_shape(int K) {
+  if (K <= 8) return {8, 1, 8};
+  if (K <= 32) return {32, 1, 8};
+  if (K <= 64) return {32, 2, TM_FIR_FT_WIDE};
+  return {32, 4, TM_FIR_FT_WIDE};
+}
+
+template <typename IO, bool VEC, int TPL, int LPC, int FT>
+hipError_t launch_tm_fir_k(const TokmajorFirArgs& a, int TS, int P) {
+  constexpr int G = TM_THREADS / LPC;
+  // the FIR kernel writes the window itself unless another segment may still
+  // read a window_in that window_out overlaps
+  const bool want_win = a.win_out && a.K > 1;
+  const size_t wbytes = size_t(a.B) * a.D * (a.K - 1) * sizeof(float);
+  const auto* wi = reinterpret_cast<const char*>(a.win_in);
+  const auto* wo = reinterpret_cast<const char*>(a.win_out);
+  const bool overlap = wi && wo && wi < wo + wbytes && wo < wi + wbytes;
+  const bool in_kernel = want_win && a.L > 0 && (!overlap || P == 1);
+  if (a.L > 0) {
+    tm_fir<IO, VEC, TPL, LPC, FT><<<dim3((a.D + G - 1) / G, P, a.B), TM_THREADS, 0, a.stream>>>(
+        static_cast<const IO*>(a.xin), a.pos_x1, a.pos_x2, a.pos_v, a.taps, a.K, a.skip,
+        a.win_in, in_kernel ? a.win_out : nullptr, static_cast<IO*>(a.y), a.D, a.L, TS);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (want_win && !in_kernel) {
+    const int64_t rows = int64_t(a.B) * a.D;
+    tm_fir_window<IO><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, a.stream>>>(
+        static_cast<const IO*>(a.xin), a.pos_x1, a.pos_v, a.win_in, a.win_out, a.K - 1, a.D,
+        a.L, rows);
+  }
+  return hipGetLastError();
+}
+
+template <typename IO, bool VEC>
+hipError_t launch_tm_fir_io(const TokmajorFirArgs& a, int TS, int P) {
+  if (a.K <= 8) return launch_tm_fir_k<IO, VEC, 8, 1, 8>(a, TS, P);
+  if (a.K <= 32) return launch_tm_fir_k<IO, VEC, 32, 1, 8>(a, TS, P);
+  if (a.K <= 64) return launch_tm_fir_k<IO, VEC, 32, 2, TM_FIR_FT_WIDE>(a, TS, P);
+  return launch_tm_fir_k<IO, VEC, 32, 4, TM_FIR_FT_WIDE>(a, TS, P);
+}
+
+int tm_tile_tokens(bool bf16) { return bf16 ? TmModal<bf16_t>::TT : TmModal<float>::TT; }
 
 template <typename IO, bool VEC, int NM>
 hipError_t launch_tm(const TokmajorArgs& a, int TS, int P) {
@@ -346,6 +582,34 @@ size_t tokmajor_workspace(int64_t B, int64_t D, int64_t L, int64_t N, bool bf16)
   int TS = 0, P = 0;
   tokmajor_segments(B, D, L, bf16, &TS, &P);
   return P > 1 ? static_cast<size_t>(B * P * D * N) * sizeof(float) : 0;
+}
+
+// FIR: G = 256 / LPC channels per workgroup; segments a multiple of the tile,
+// at least 8 times the halo (LPC TPL tokens), cut for about TM_TARGET
+// workgroups.
+void tokmajor_fir_segments(int64_t B, int64_t D, int64_t L, int K, int* TS, int* P) {
+  constexpr int64_t TM_TARGET = 1024;
+  const TmFirShape sh = tm_fir_shape(K);
+  const int64_t G = TM_THREADS / sh.LPC;
+  const int64_t groups = B * ((D + G - 1) / G);
+  int64_t want = (TM_TARGET + groups - 1) / groups;
+  if (want < 1) want = 1;
+  int64_t ts = (L + want - 1) / want;
+  const int64_t lo = 8 * sh.LPC * sh.TPL > 64 ? 8 * sh.LPC * sh.TPL : 64;
+  if (ts < lo) ts = lo;
+  ts = (ts + sh.FT - 1) / sh.FT * sh.FT;
+  *TS = static_cast<int>(ts);
+  *P = static_cast<int>(L > 0 ? (L + ts - 1) / ts : 0);
+}
+
+hipError_t launch_tokmajor_fir(const TokmajorFirArgs& a) {
+  int TS = 0, P = 0;
+  tokmajor_fir_segments(a.B, a.D, a.L, a.K, &TS, &P);
+  const size_t esz = a.bf16 ? 2 : 4;
+  const bool vec = aligned_to(a.xin, 16) && (3 * static_cast<size_t>(a.D) * esz) % 16 == 0;
+  if (a.bf16)
+    return vec ? launch_tm_fir_io<bf16_t, true>(a, TS, P) : launch_tm_fir_io<bf16_t, false>(a, TS, P);
+  return vec ? launch_tm_fir_io<float, true>(a, TS, P) : launch_tm_fir_io<float, false>(a, TS, P);
 }
 
 hipError_t launch_tokmajor(const TokmajorArgs& a) {

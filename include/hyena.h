@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 5
+#define HYENA_ABI_VERSION 6
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -91,6 +91,7 @@ typedef enum hyena_chunk_algo {
 /* Limits of this build. */
 #define HYENA_MAX_MODES 64               /* N */
 #define HYENA_MAX_FIR_TAPS 1024          /* K */
+#define HYENA_MAX_FIR_TAPS_TOKMAJOR 128  /* K of hyena_fir_fwd_tokmajor */
 #define HYENA_MAX_FFT_LEN (1 << 20)      /* single-pass FFT length, next pow2 >= 2L */
 #define HYENA_MAX_FFT_CHUNK 8192         /* C for HYENA_CHUNK_FFT (FFT length 2C <= 16384) */
 
@@ -313,6 +314,28 @@ hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t
                                         const float* state_in, float* state_out, void* y,
                                         int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
                                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hyena_fir_fwd_tokmajor -- the explicit-FIR operator (hcm K = 128, hcs
+ * K = 7: Evo2-7B-262K model card, Implementation Notes, 'Block dispatch') on
+ * the same token-major layout, continuing from a window like
+ * hyena_fir_fwd_window.  With e = [window_in, u[0:L)], u = x1 * v:
+ *   y[b, t, c] = x2 * sum_{k<K} taps[c, k] e[K-1+t-k] + skip[c] * u[t],
+ * and window_out = the last K-1 entries of e (the FIR part of the inference
+ * cache: Evo2-7B-262K model card, Implementation Notes, 'Custom cache').
+ *   xin, pos_x1, pos_x2, pos_v, y, B, D, L, io : as hyena_chunk_fwd_tokmajor
+ *   taps : (D, K) fp32, 1 <= K <= HYENA_MAX_FIR_TAPS_TOKMAJOR;  skip : (D) or NULL
+ *   window_in  : (B, D, K-1) fp32, oldest first, or NULL (fresh sequence)
+ *   window_out : (B, D, K-1) fp32, written (may equal window_in), or NULL
+ *                (not kept)
+ * Any L >= 0 (L = 1 per decode step); L = 0 moves the window.  Segments of
+ * the sequence run in parallel, each reading K-1 tokens before it again.
+ */
+hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                      int32_t pos_v, const float* taps, int64_t K,
+                                      const float* skip, const float* window_in,
+                                      float* window_out, void* y, int64_t B, int64_t D, int64_t L,
+                                      hyena_dtype_t io, void* stream);
 
 /* Workspace bytes hyena_chunk_fwd_tokmajor needs for this shape: B * P * D * N
  * floats for its P segments, 0 when the sequence is one segment or the shape

@@ -7,6 +7,6 @@ from .hyena_oracle import (  # noqa: F401
     modal_filter, conv_direct, conv_fft, causal_conv, hyena_fwd, fir_fwd,
     modal_state, chunk_fwd, next_pow2, modal_decode, fir_fwd_window,
     modal_filter_cpx, hyena_fwd_cpx, modal_state_cpx, chunk_fwd_cpx, modal_decode_cpx,
-    tokmajor_streams, chunk_fwd_tokmajor,
+    tokmajor_streams, chunk_fwd_tokmajor, fir_fwd_tokmajor,
 )
 from .metrics import compare, passes, REL_L2_MAX, ELEM_REL_MAX, TAU  # noqa: F401

@@ -81,7 +81,7 @@ __all__ = [
     "hyena_fwd", "fir_fwd", "modal_state", "chunk_fwd", "next_pow2",
     "modal_decode", "fir_fwd_window",
     "modal_filter_cpx", "hyena_fwd_cpx", "modal_state_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
-    "tokmajor_streams", "chunk_fwd_tokmajor",
+    "tokmajor_streams", "chunk_fwd_tokmajor", "fir_fwd_tokmajor",
 ]
 
 DIRECT_MAX_L = 4096      # direct O(L^2) sum up to this length, FFT above
@@ -374,3 +374,12 @@ def chunk_fwd_tokmajor(xin, log_poles, residues, skip, pos=(0, 1, 2), state_in=N
     L = x1.shape[-1]
     y, s = chunk_fwd(x1, x2, v, log_poles, residues, skip, max(L, 1), state_in=state_in)
     return np.ascontiguousarray(np.moveaxis(y, 1, 2)), s
+
+
+def fir_fwd_tokmajor(xin, taps, skip, pos=(0, 1, 2), window_in=None):
+    """The explicit-FIR operator on the token-major layout, fp64: the streams
+    of xin (see tokmajor_streams) through fir_fwd_window.  Returns y as
+    (B, L, D) and the new window (B, D, K-1)."""
+    x1, x2, v = tokmajor_streams(xin, pos)
+    y, win = fir_fwd_window(x1, x2, v, taps, skip, window_in=window_in)
+    return np.ascontiguousarray(np.moveaxis(y, 1, 2)), win

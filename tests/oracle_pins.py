@@ -496,6 +496,27 @@ def pin_tokmajor_impulse(O):
     assert np.allclose(s, want_s, rtol=0, atol=1e-15), s
 
 
+def pin_tokmajor_fir_impulse(O):
+    """FIR on the token-major layout: an impulse in x1 of channel c0 at token
+    t0 gives that channel's taps, lag by lag, in column c0 from t0 on; the
+    window handed out holds u of the last K-1 tokens, here [0, 1, 0] in c0."""
+    D, L, K, t0, c0 = 3, 10, 4, 8, 2
+    pos = (2, 0, 1)
+    taps = np.array([[0.5, -1.0, 2.0, 0.25], [1.0, 0.0, 0.0, 3.0], [-2.0, 0.75, 1.5, -0.125]])
+    xin = np.zeros((1, L, 3 * D))
+    xin[0, :, 3 * np.arange(D) + pos[1]] = 1.0          # x2
+    xin[0, :, 3 * np.arange(D) + pos[2]] = 1.0          # v
+    xin[0, t0, 3 * c0 + pos[0]] = 1.0                   # x1
+    y, win = O.fir_fwd_tokmajor(xin, taps, np.zeros(D), pos)
+    want = np.zeros((1, L, D))
+    want[0, 8, c0] = taps[c0, 0]
+    want[0, 9, c0] = taps[c0, 1]
+    assert y.shape == (1, L, D) and np.array_equal(y, want), (y, want)
+    want_w = np.zeros((1, D, K - 1))
+    want_w[0, c0] = [0.0, 1.0, 0.0]                     # tokens 7, 8, 9
+    assert np.array_equal(win, want_w), win
+
+
 ALL_PINS = [
     pin_golden, pin_filter_rational, pin_filter_dft, pin_recurrence,
     pin_impulse, pin_linearity_time_invariance, pin_numpy_convolve,
@@ -505,5 +526,5 @@ ALL_PINS = [
     pin_decode_after_prefill, pin_decode_impulse_rational, pin_fir_window_pieces,
     pin_cpx_filter_rational, pin_cpx_second_order_recurrence, pin_cpx_real_special_case,
     pin_cpx_chunk_and_decode_equal_full,
-    pin_tokmajor_layout_literal, pin_tokmajor_impulse,
+    pin_tokmajor_layout_literal, pin_tokmajor_impulse, pin_tokmajor_fir_impulse,
 ]

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 5
+    assert G.abi_version() == 6
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -218,6 +218,25 @@ def test_chunk_tokmajor_validation():
     assert f(*big) == G.ERR_WORKSPACE
     big[15] = P(0x10008); big[16] = need
     assert f(*big) == G.ERR_WORKSPACE
+
+
+def test_fir_tokmajor_validation():
+    f = G.lib().hyena_fir_fwd_tokmajor
+    # xin, pos x3, taps, K, skip, window_in, window_out, y, B, D, L, io, stream
+    good = [FAKE, 0, 1, 2, FAKE, 7, None, None, None, FAKE, 1, 4, 64, G.BF16, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (4, None, G.ERR_INVALID_ARG),
+                           (9, None, G.ERR_INVALID_ARG), (5, 0, G.ERR_INVALID_ARG),
+                           (5, 129, G.ERR_UNSUPPORTED), (1, 1, G.ERR_INVALID_ARG),
+                           (3, 5, G.ERR_INVALID_ARG), (10, 65536, G.ERR_UNSUPPORTED),
+                           (13, 2, G.ERR_INVALID_ARG), (0, MISALIGNED, G.ERR_INVALID_ARG),
+                           (7, MISALIGNED, G.ERR_INVALID_ARG), (8, MISALIGNED, G.ERR_INVALID_ARG),
+                           (12, -1, G.ERR_INVALID_ARG)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[10] = 0                                  # empty batch
+    assert f(*a) == G.OK
+    a = list(good); a[12] = 0                                  # no token, no window kept
+    assert f(*a) == G.OK
 
 
 def test_binding_rejects_cpu_tensors_before_any_call():

@@ -5,7 +5,8 @@ xin (B, L, 3D) holds each channel's x1, x2, v side by side (triple order
 `pos`), y is (B, L, D).  The cases cover both element types, both load paths
 (16-byte chunks; single elements when rows are not a multiple of 16 bytes or
 the input is misaligned), partial channel groups, ragged tails, every mode
-count variant, carried and aliased states, and the 32 kb shape sampled.
+count variant, carried and aliased states, and the 32 kb shape sampled; the
+explicit FIR on the same layout, with its window carried between calls.
 """
 import numpy as np
 import pytest
@@ -161,3 +162,89 @@ def test_tokmajor_32k_shape():
     ref, ref_s = _ref(w, xin, (0, 1, 2), rows)
     _gate_tm(y, ref, "bf16", rows, label="32k tokmajor")
     state_gate(s, ref_s, rows, label="32k tokmajor")
+
+
+# ------------------------------------------------------------------ FIR
+def _taps(w, K, seed=None):
+    if K in w.taps and seed is None:
+        return w.taps[K]
+    return W.random_taps(K, w.D, seed=K if seed is None else seed, bf16=(w.io == "bf16"))
+
+
+def _ref_fir(w, xin, pos, taps, rows=None, window_in=None):
+    rows = np.arange(w.D) if rows is None else np.asarray(rows)
+    cols = (3 * rows[:, None] + np.arange(3)[None, :]).ravel()
+    x = W.to_f64(xin[..., cols], w.io)
+    wi = None if window_in is None else np.asarray(window_in, np.float64)[:, rows]
+    return oracle.fir_fwd_tokmajor(x, np.asarray(taps, np.float64)[rows],
+                                   w.skip[rows].astype(np.float64), pos, window_in=wi)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [1, 7, 20, 50, 128])
+@pytest.mark.parametrize("D,L", [(256, 1000), (300, 777), (72, 3000), (40, 5)])
+def test_tokmajor_fir(io, K, D, L):
+    pos = (1, 0, 2)
+    w, xin, xd = _setup(io, B=2, D=D, L=L, pos=pos)
+    d = DevWorkload(w)
+    taps = _taps(w, K)
+    log(f"tokmajor fir io={io} K={K} D={D} L={L}")
+    y, win = G.fir_fwd_tokmajor(xd, par_to_dev(taps), d.skip, pos=pos)
+    ref, ref_w = _ref_fir(w, xin, pos, taps)
+    assert y.shape == (2, L, D)
+    _gate_tm(y, ref, io, label=f"tokmajor fir K={K} D={D} L={L}")
+    if K > 1:
+        assert np.array_equal(win.cpu().numpy(), ref_w.astype(np.float32))
+    else:
+        assert win is None
+
+
+@pytest.mark.parametrize("K", [7, 128])
+def test_tokmajor_fir_pieces_and_decode(K):
+    """A prefill call, calls of assorted lengths and single-token steps with
+    the window handed over (in place) equal one call over the sequence."""
+    L = 2600
+    w, xin, xd = _setup("bf16", B=1, D=264, L=L, pos=(2, 0, 1))
+    d = DevWorkload(w)
+    taps = par_to_dev(_taps(w, K))
+    win = torch.zeros((1, w.D, K - 1), dtype=torch.float32, device=xd.device)
+    # the first call spans several segments with the window updated in place
+    # (written after the FIR kernel); later ones fit one segment (written by it)
+    pts = [0, 2100, 2101, 2103, 2200, 2327, 2500] + list(range(2501, L + 1))
+    ys = []
+    for a, b in zip(pts[:-1], pts[1:]):
+        yp, wo = G.fir_fwd_tokmajor(xd[:, a:b].contiguous(), taps, d.skip, pos=(2, 0, 1),
+                                    window_in=win, window_out=win)
+        assert wo.data_ptr() == win.data_ptr()
+        ys.append(yp)
+    ref, ref_w = _ref_fir(w, xin, (2, 0, 1), _taps(w, K))
+    log(f"tokmajor fir pieces K={K} ({len(pts) - 1} calls)")
+    _gate_tm(torch.cat(ys, 1), ref, "bf16", label=f"tokmajor fir pieces K={K}")
+    assert np.array_equal(win.cpu().numpy(), ref_w.astype(np.float32))
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_tokmajor_fir_misaligned(io):
+    w, xin, xd = _setup(io, B=2, D=256, L=900)
+    d = DevWorkload(w)
+    xm = offset_copy(xd)
+    for K in (7, 128):
+        y, _ = G.fir_fwd_tokmajor(xm, par_to_dev(_taps(w, K)), d.skip)
+        ref, _ = _ref_fir(w, xin, (0, 1, 2), _taps(w, K))
+        _gate_tm(y, ref, io, label=f"tokmajor fir misaligned K={K}")
+    with pytest.raises(G.HyenaError):
+        G.fir_fwd_tokmajor(xd, par_to_dev(_taps(w, 129)), d.skip)
+
+
+def test_tokmajor_fir_7b_shape():
+    """D = 4096, L = 8192 (the 7B layer set), K = 7 and 128, sampled channels."""
+    w = W.make("7b_layer_set")
+    xin = W.interleave_triples(w.x1, w.x2, w.v)
+    xd = act_to_dev(xin, "bf16")
+    skip = par_to_dev(w.skip)
+    rows = sample_rows(w.D)
+    for K in (7, 128):
+        y, win = G.fir_fwd_tokmajor(xd, par_to_dev(w.taps[K]), skip)
+        ref, ref_w = _ref_fir(w, xin, (0, 1, 2), w.taps[K], rows)
+        _gate_tm(y, ref, "bf16", rows, label=f"7b tokmajor fir K={K}")
+        assert np.array_equal(win.cpu().numpy()[:, rows], ref_w.astype(np.float32))

@@ -53,7 +53,14 @@ def _mutant(**over):
         y, s = mod.chunk_fwd(x1, x2, v, log_poles, residues, skip, max(L, 1), state_in=state_in)
         return mod.tokmajor_out(y), s
 
+    def fir_fwd_tokmajor(xin, taps, skip, pos=(0, 1, 2), window_in=None):
+        x1, x2, v = mod.tokmajor_streams(xin, pos)
+        y, win = mod.fir_fwd_window(x1, x2, v, taps, skip, window_in=window_in)
+        return mod.tokmajor_out(y), win
+
     mod.tokmajor_out = over.get("tokmajor_out", lambda y: np.moveaxis(y, 1, 2))
+    if "fir_fwd_tokmajor" not in over:
+        mod.fir_fwd_tokmajor = fir_fwd_tokmajor
     if "chunk_fwd_tokmajor" not in over:
         mod.chunk_fwd_tokmajor = chunk_fwd_tokmajor
     if "hyena_fwd" not in over:
