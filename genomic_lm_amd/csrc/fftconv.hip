@@ -92,6 +92,12 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   constexpr int LG_M = ilog2(M);
   constexpr int LG_N = LG_M + 1;
   __shared__ float2 lds[lds_padded_size(S)];
+  // From S = 1024 on, the even half's inverse transform waits for the odd
+  // half in LDS rather than in 2P registers: there the register budget, not
+  // LDS, limits the workgroups per CU (measured at D = 4096: L = 8192 612 ->
+  // 377 us, L = 4096 201 -> 175 us; at S = 8192 it also ends a spill).
+  constexpr bool B0_LDS = S >= 1024;
+  __shared__ float2 b0s[B0_LDS ? S : 1];
 
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   const float* lamc = lam + static_cast<int64_t>(c) * N * W;
   const float* resc = res + static_cast<int64_t>(c) * N * W;
 
-  float2 b0[P];           // inverse transform of the even half, kept for the recombination
+  float2 b0[B0_LDS ? 1 : P];   // inverse transform of the even half, kept for the recombination
   float zm_nyq = 0.0f;    // Z[M] (real), only used by thread 0
 
   // Both parity halves are unrolled: as a loop, the address and twiddle
@@ -176,7 +182,10 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
 
     if (q == 0) {
 #pragma unroll
-      for (int i = 0; i < P; ++i) b0[i] = a[i];
+      for (int i = 0; i < P; ++i) {
+        if constexpr (B0_LDS) b0s[t + T * i] = a[i];
+        else b0[i] = a[i];
+      }
     } else {
       // ---- recombine, gate, store
       const float sk = skip ? skip[c] : 0.0f;
@@ -185,7 +194,8 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       for (int i = 0; i < P; ++i) {
         const int m = t + T * i;
         if (2 * m >= L) continue;
-        const float2 zz = cscale(cadd(b0[i], cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
+        const float2 e0 = B0_LDS ? b0s[t + T * i] : b0[B0_LDS ? 0 : i];
+        const float2 zz = cscale(cadd(e0, cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
         const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
         const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
         const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
