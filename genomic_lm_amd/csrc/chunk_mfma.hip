@@ -44,28 +44,61 @@
 
 namespace hyena {
 
+// The three bf16 parts (split3) of the 16 operand slots (s, j) of one lane,
+// val(s, j) -> parts[k][s][j], formed two slots at a time (one packed
+// conversion per pair; the same bits as split3 value by value).
+template <typename F>
+__device__ __forceinline__ void split3_slots(F&& val, bf16x8 (&parts)[3][2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 w0, w1, w2;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t a, b, c;
+      split3_pair(val(s, 2 * jj), val(s, 2 * jj + 1), a, b, c);
+      w0[jj] = a;
+      w1[jj] = b;
+      w2[jj] = c;
+    }
+    parts[0][s] = __builtin_bit_cast(bf16x8, w0);
+    parts[1][s] = __builtin_bit_cast(bf16x8, w1);
+    parts[2][s] = __builtin_bit_cast(bf16x8, w2);
+  }
+}
+
 // B operands of E^T = U^T . P^T for one lane: column nn (mode nn & 15, part
-// nn >> 4), slots (s, j) -> token blk_tok(8s + j, hf).  The weight of token
-// tok is w = p^(ref - tok) for tok <= ref, else 0, split as w0 + w1 + w2.
+// nn >> 4), slots (s, j) -> token blk_tok(8s + j, hf), from the weights
+// w(tok) = p^(ref - tok) for tok <= ref, else 0, split as w0 + w1 + w2.
 // Summing columns n and n + 16 of  U0.A + U1.A + U0.B (+ U2.C)  gives every
 // product of order <= 2:  A = [w0 | w1], B = [w2 | 0], C = [w0 | 0].
+template <typename F>
+__device__ __forceinline__ void state_weight_operands(F&& w, int part, int hf, int ref,
+                                                      bf16x8 (&pa)[2], bf16x8 (&pb)[2],
+                                                      bf16x8 (&pc)[2]) {
+  bf16x8 parts[3][2];
+  split3_slots(
+      [&](int s, int j) {
+        const int tok = blk_tok(8 * s + j, hf);
+        return (tok <= ref) ? w(ref - tok) : 0.0f;
+      },
+      parts);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const u32x4 q0 = __builtin_bit_cast(u32x4, parts[0][s]);
+    const u32x4 q1 = __builtin_bit_cast(u32x4, parts[1][s]);
+    const u32x4 q2 = __builtin_bit_cast(u32x4, parts[2][s]);
+    pa[s] = __builtin_bit_cast(bf16x8, part ? q1 : q0);
+    pb[s] = __builtin_bit_cast(bf16x8, part ? zero : q2);
+    pc[s] = __builtin_bit_cast(bf16x8, part ? zero : q0);
+  }
+}
+
 __device__ __forceinline__ void build_state_weights(float lam_n, int part, int hf, int ref,
                                                     bf16x8 (&pa)[2], bf16x8 (&pb)[2],
                                                     bf16x8 (&pc)[2]) {
-  const __bf16 zero = static_cast<__bf16>(0.0f);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = blk_tok(8 * s + j, hf);
-      const float w = (tok <= ref) ? expf(lam_n * static_cast<float>(ref - tok)) : 0.0f;
-      __bf16 w0, w1, w2;
-      split3(w, w0, w1, w2);
-      pa[s][j] = part ? w1 : w0;
-      pb[s][j] = part ? zero : w2;
-      pc[s][j] = part ? zero : w0;
-    }
-  }
+  state_weight_operands([&](int d) { return expf(lam_n * static_cast<float>(d)); }, part, hf,
+                        ref, pa, pb, pc);
 }
 
 // The same weights for complex mode `md`: slot component k takes Re (k = 0)
@@ -73,24 +106,12 @@ __device__ __forceinline__ void build_state_weights(float lam_n, int part, int h
 __device__ __forceinline__ void build_state_weights_cpx(const CpxMode& md, int k, int part,
                                                         int hf, int ref, bf16x8 (&pa)[2],
                                                         bf16x8 (&pb)[2], bf16x8 (&pc)[2]) {
-  const __bf16 zero = static_cast<__bf16>(0.0f);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = blk_tok(8 * s + j, hf);
-      float w = 0.0f;
-      if (tok <= ref) {
-        const float2 e = cexp_at(md, static_cast<float>(ref - tok));
-        w = k ? e.y : e.x;
-      }
-      __bf16 w0, w1, w2;
-      split3(w, w0, w1, w2);
-      pa[s][j] = part ? w1 : w0;
-      pb[s][j] = part ? zero : w2;
-      pc[s][j] = part ? zero : w0;
-    }
-  }
+  state_weight_operands(
+      [&](int d) {
+        const float2 e = cexp_at(md, static_cast<float>(d));
+        return k ? e.y : e.x;
+      },
+      part, hf, ref, pa, pb, pc);
 }
 
 // VEC: rows of whole 16-byte chunks, 16-byte aligned (full tiles take the
@@ -186,55 +207,62 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   float carry = (part == 0 && n_sc < NS && state_in) ? st_ld : 0.0f;
 
   // ---- per-row constants
-  // h[d], d < 32
+  // h[d], d < 32.  The mode loop has its fixed maximum trip count so that
+  // all parameter loads are issued together (a loop over the runtime N
+  // waited on one load per mode, the bulk of a one-tile call's set-up).
   {
     float hd = 0.0f;
     if constexpr (CPX) {
-      for (int n = 0; n < N; ++n) {
-        const float2 e = cexp_at(cpx_mode(lamc[2 * n], lamc[2 * n + 1]), static_cast<float>(i32));
-        hd = fmaf(resc[2 * n], e.x, fmaf(-resc[2 * n + 1], e.y, hd));
+#pragma unroll
+      for (int n = 0; n < MFMA_MAXN / 2; ++n) {
+        if (n < N) {
+          const float2 e = cexp_at(cpx_mode(lamc[2 * n], lamc[2 * n + 1]), static_cast<float>(i32));
+          hd = fmaf(resc[2 * n], e.x, fmaf(-resc[2 * n + 1], e.y, hd));
+        }
       }
     } else {
-      for (int n = 0; n < N; ++n) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
+#pragma unroll
+      for (int n = 0; n < MFMA_MAXN; ++n) {
+        if (n < N) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
+      }
     }
     if (hf == 0) hbuf[i32] = hd;
   }
   lds_sync();
   // A = T (row i32, slot (s,j) -> token blk_tok): T[i][tok] = h[i - tok] for tok <= i
   bf16x8 tm[3][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = i32 - blk_tok(8 * s + j, hf);
-      const float val = (d >= 0) ? hbuf[d] : 0.0f;
-      __bf16 a0, a1, a2;
-      split3(val, a0, a1, a2);
-      tm[0][s][j] = a0;
-      tm[1][s][j] = a1;
-      tm[2][s][j] = a2;
-    }
-  }
+  split3_slots(
+      [&](int s, int j) {
+        const int d = i32 - blk_tok(8 * s + j, hf);
+        return (d >= 0) ? hbuf[d] : 0.0f;
+      },
+      tm);
   // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1);
   // CPX: slot 2m holds Re(R_m p_m^(i+1)), slot 2m + 1 holds -Im(R_m p_m^(i+1))
-  bf16x8 gm[3];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float val;
+  auto gval = [&](int j) {
     if constexpr (CPX) {
       const int j0 = j & ~1;
       const float2 e = cexp_at(cpx_mode(g_lam[j0], g_lam[j0 + 1]), static_cast<float>(i32 + 1));
       const float2 rp = cmul(make_float2(g_res[j0], g_res[j0 + 1]), e);
-      val = (j & 1) ? -rp.y : rp.x;
-      if (8 * hf + j0 >= NS) val = 0.0f;
+      return (j & 1) ? -rp.y : rp.x;          // padding slots: g_res = 0
     } else {
-      val = g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
+      return g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
     }
-    __bf16 a0, a1, a2;
-    split3(val, a0, a1, a2);
-    gm[0][j] = a0;
-    gm[1][j] = a1;
-    gm[2][j] = a2;
+  };
+  bf16x8 gm[3];
+  {
+    u32x4 w0, w1, w2;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t a, b, c;
+      split3_pair(gval(2 * jj), gval(2 * jj + 1), a, b, c);
+      w0[jj] = a;
+      w1[jj] = b;
+      w2[jj] = c;
+    }
+    gm[0] = __builtin_bit_cast(bf16x8, w0);
+    gm[1] = __builtin_bit_cast(bf16x8, w1);
+    gm[2] = __builtin_bit_cast(bf16x8, w2);
   }
   // scan lane: mode n_sc (part 0 or 1 of the column pair) for all 32
   // blocks; padded modes have p = 1 and R = 0
