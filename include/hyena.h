@@ -52,7 +52,9 @@
  *    propagate to the outputs; they are not an error.
  *  - The library keeps no global or per-device state and allocates nothing;
  *    all entry points are reentrant and may be called from several host
- *    threads.
+ *    threads.  No entry point allocates, clears memory with a memset or
+ *    synchronises, so every one may be captured into a HIP graph and
+ *    replayed (the pointers it was captured with stay in use).
  */
 #ifndef HYENA_H_
 #define HYENA_H_

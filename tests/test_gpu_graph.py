@@ -1,0 +1,113 @@
+"""Entry points inside a HIP graph: a chunked prefill, decode steps and FIR
+window steps (channel- and token-major) captured once and replayed several
+times, with the program's own eager work in between; every replay must give
+the eager results bit for bit (every kernel here is deterministic).  Nothing
+in these calls allocates, clears memory with a memset or synchronises, which
+is what capture needs."""
+import numpy as np
+import pytest
+import torch
+
+import genomic_lm_amd as G
+import workloads as W
+from tests.gpu_util import DevWorkload, act_to_dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()
+    yield
+
+
+def _program(d, xin, bufs, n_pre, steps):
+    """Prefill n_pre tokens, then `steps` single-token steps, into bufs."""
+    x1, x2, v = d.x1, d.x2, d.v
+    G.chunk_fwd(*(t[..., :n_pre] for t in bufs["pre"]), d.lam, d.res, 1024, d.skip,
+                out=bufs["y_pre"], state_out=bufs["s"])
+    G.fir_fwd_window(*(t[..., :n_pre] for t in bufs["pre"]), d.taps[128], d.skip,
+                     out=bufs["yf_pre"], window_out=bufs["win"])
+    G.chunk_fwd_tokmajor(bufs["xin_pre"], d.lam, d.res, d.skip, out=bufs["yt_pre"],
+                         state_out=bufs["st"], workspace=bufs["ws"])
+    for i in range(steps):
+        tok = bufs["tok"][i]
+        G.modal_decode(*tok, d.lam, d.res, d.skip, state_in=bufs["s"], out=bufs["y_dec"][i],
+                       state_out=bufs["s"])
+        G.fir_fwd_window(*(t[..., None] for t in tok), d.taps[128], d.skip,
+                         window_in=bufs["win"], out=bufs["yf_dec"][i][..., None],
+                         window_out=bufs["win"])
+        G.fir_fwd_tokmajor(bufs["xin_tok"][i], d.taps[7], d.skip, window_in=bufs["wt"],
+                           out=bufs["yt_dec"][i], window_out=bufs["wt"])
+
+
+def test_graph_capture_and_replay():
+    n_pre, steps = 3000, 4
+    w = W.make("7b_layer_set", D=256, L=n_pre + steps)
+    d = DevWorkload(w)
+    dev = d.x1.device
+    xin = act_to_dev(W.interleave_triples(w.x1, w.x2, w.v), "bf16")
+    B, D = 1, w.D
+    pre = [t[..., :n_pre].contiguous() for t in (d.x1, d.x2, d.v)]
+    ws_bytes = max(16, G.chunk_tokmajor_workspace_size(B, D, n_pre, w.N))
+
+    def fresh():
+        return {
+            "pre": pre,
+            "xin_pre": xin[:, :n_pre].contiguous(),
+            "tok": [[t[..., n_pre + i].contiguous() for t in (d.x1, d.x2, d.v)] for i in range(steps)],
+            "xin_tok": [xin[:, n_pre + i:n_pre + i + 1].contiguous() for i in range(steps)],
+            "y_pre": torch.empty_like(pre[0]), "yf_pre": torch.empty_like(pre[0]),
+            "yt_pre": torch.empty((B, n_pre, D), dtype=torch.bfloat16, device=dev),
+            "s": torch.empty((B, D, w.N), device=dev), "st": torch.empty((B, D, w.N), device=dev),
+            "win": torch.empty((B, D, 127), device=dev), "wt": torch.zeros((B, D, 6), device=dev),
+            "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+            "y_dec": [torch.empty((B, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
+            "yf_dec": [torch.empty((B, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
+            "yt_dec": [torch.empty((B, 1, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
+        }
+
+    outs = ("y_pre", "yf_pre", "yt_pre", "s", "st", "win", "wt")
+    lists = ("y_dec", "yf_dec", "yt_dec")
+
+    def snapshot(b):
+        snap = {k: b[k].clone() for k in outs}
+        for k in lists:
+            snap[k] = [t.clone() for t in b[k]]
+        return snap
+
+    eager = fresh()
+    _program(d, xin, eager, n_pre, steps)
+    torch.cuda.synchronize()
+    ref = snapshot(eager)
+
+    cap = fresh()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        _program(d, xin, cap, n_pre, steps)           # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            _program(d, xin, cap, n_pre, steps)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        cap["wt"].zero_()                             # the token-major FIR window starts empty
+        for k in outs + lists:                        # poison the outputs between replays
+            for t in (cap[k] if k in lists else [cap[k]]):
+                if k != "wt":
+                    t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _program(d, xin, fresh(), n_pre, 1)          # eager work between the replays
+        torch.cuda.synchronize()
+        log(f"graph replay {rep}")
+        for k in outs:
+            assert torch.equal(cap[k], ref[k]), (rep, k)
+        for k in lists:
+            for a, b in zip(cap[k], ref[k]):
+                assert torch.equal(a, b), (rep, k)
