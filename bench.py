@@ -75,6 +75,20 @@ def copy_calibration(steps):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": steps}), flush=True)
 
 
+def copy_bandwidth(stream):
+    """Bytes moved per second (1 GiB read + 1 GiB written) by a plain
+    device-to-device copy on this GPU: the streaming rate the box delivers,
+    beside the published peak."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    t = timed(lambda: dst.copy_(src), 10, 3, stream)
+    del src, dst
+    return 2 * n / t / 1e9
+
+
 def timed(fn, steps, warmup, stream):
     """Average per-call time (s) over `steps` calls, HIP events on `stream`."""
     import torch
@@ -192,6 +206,7 @@ def main():
                     compute[key] = {"achieved": round(a, 2), "peak": peak, "unit": "TFLOP/s",
                                     "frac": round(a / peak, 4), "flops": n}
 
+    copy_gbs = copy_bandwidth(stream)
     comps = {}
     if not args.no_components:
         comp_steps = max(3, args.steps // 4)
@@ -282,6 +297,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "compute": compute,
+        "hbm_copy": {"measured_GBps": round(copy_gbs, 1),
+                     "frac": round(achieved / copy_gbs, 4)},
         "wall_s_timed": round(t_wall, 3),
         "components": comps,
     }
