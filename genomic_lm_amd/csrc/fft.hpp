@@ -97,9 +97,11 @@ template <> struct Dft<16> {
 __host__ __device__ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 
 // ------------------------------------------------------------- passes
+// Radix of the pass with span NS: all of a thread's points (at most 16) in
+// one butterfly, or what is left of S.
 template <int S, int T, int NS>
 struct PassRadix {
-  static constexpr int P = S / T;
+  static constexpr int P = S / T < 16 ? S / T : 16;
   static constexpr int value = (S / NS >= P) ? P : S / NS;
 };
 
@@ -120,7 +122,13 @@ __device__ __forceinline__ void pass_compute(float2 (&reg)[S / T], int t) {
 #pragma unroll
       for (int r = 1; r < R; ++r) {
         v[r] = cmul(v[r], wr);
-        if (r + 1 < R) wr = cmul(wr, w);
+        // the empty asms keep each power of w next to its use: computed all
+        // ahead, the powers hold 2(R-1) more registers through the butterfly
+        asm volatile("" : "+v"(v[r].x), "+v"(v[r].y));
+        if (r + 1 < R) {
+          wr = cmul(wr, w);
+          asm volatile("" : "+v"(wr.x), "+v"(wr.y));
+        }
       }
     }
     Dft<R>::run(v);
@@ -129,9 +137,14 @@ __device__ __forceinline__ void pass_compute(float2 (&reg)[S / T], int t) {
   }
 }
 
+// The LDS addresses of a pass depend only on t and are the same in every
+// transform of a kernel; t passes through an empty asm so that the compiler
+// recomputes them per pass (a few integer ops) instead of keeping every pass's
+// addresses live across whole kernels, which costs registers.
 template <int S, int T, int R, int NS>
 __device__ __forceinline__ void pass_store(const float2 (&reg)[S / T], float2* lds, int t) {
   constexpr int P = S / T;
+  asm volatile("" : "+v"(t));
   constexpr int NB = P / R;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -145,6 +158,7 @@ __device__ __forceinline__ void pass_store(const float2 (&reg)[S / T], float2* l
 template <int S, int T, int R>
 __device__ __forceinline__ void pass_load(float2 (&reg)[S / T], const float2* lds, int t) {
   constexpr int P = S / T;
+  asm volatile("" : "+v"(t));
   constexpr int NB = P / R;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -177,7 +191,8 @@ __device__ __forceinline__ void fft_from(float2 (&reg)[S / T], float2* lds, int 
 template <int S, int T>
 __device__ __forceinline__ void fft_forward(float2 (&reg)[S / T], float2* lds, int t) {
   static_assert(S % T == 0 && (S & (S - 1)) == 0, "power-of-two size, T | S");
-  static_assert(S / T == 2 || S / T == 4 || S / T == 8 || S / T == 16, "2, 4, 8 or 16 points per thread");
+  static_assert(S / T == 2 || S / T == 4 || S / T == 8 || S / T == 16 || S / T == 32,
+                "2 to 32 points per thread");
   fft_from<S, T, 1>(reg, lds, t);
 }
 
@@ -190,6 +205,20 @@ __device__ __forceinline__ void fft_inverse(float2 (&reg)[S / T], float2* lds, i
 #pragma unroll
   for (int i = 0; i < S / T; ++i) reg[i].y = -reg[i].y;
 }
+
+// Sequencing of the per-element loops between transforms (real-spectrum
+// formation, repacking, recombination).  Issued freely, the compiler starts
+// every element's LDS read and twiddle at once (4P registers on top of the 4P
+// of the operands).  Each group of 4 elements
+// takes its thread index through an empty asm and keeps its results with
+// another; volatile asms stay in order, so group g + 1 cannot start before
+// group g is done.
+__device__ __forceinline__ int seq_idx(int t) {
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ void seq_keep(float2& x) { asm volatile("" : "+v"(x.x), "+v"(x.y)); }
+constexpr int SEQ = 4;
 
 // ------------------------------------------------------------- real signals
 // A real length-Nfft signal x is transformed as the complex length-M signal

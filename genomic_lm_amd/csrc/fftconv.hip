@@ -18,10 +18,14 @@
 //  * Z = U * H, repacked for the inverse real transform, inverse size-S DFT
 //    per parity, and the two halves are recombined with one twiddle:
 //    c_z[m] = (B_0[m] + exp(2*pi*i*m/M) B_1[m]) / M.
-// Only one size-S transform lives in LDS at a time, so S = 16384 (L = 32768)
-// still fits in one CU's 160 KB of LDS.  h is generated per thread with short
-// exp ladders (<= 16 multiplications from an exact anchor) and never touches
-// memory.
+// Only one size-S transform lives in LDS at a time.  Up to S = 4096 one
+// workgroup takes both halves.  From S = 8192 (L > 8192) the two halves are
+// two launches with one workgroup per (row, half): the even half writes its
+// inverse transform B_0 (S complex, fp32) to a caller workspace and the odd
+// half reads it back for the recombination -- 4 bytes per token each way,
+// against the 48 of the four-step path that rows longer than 32768 take.  h is
+// generated per thread with short exp ladders (<= 16 multiplications from an
+// exact anchor) and never touches memory.
 #include "common.hpp"
 #include "fft.hpp"
 #include "launch.hpp"
@@ -82,25 +86,33 @@ __device__ __forceinline__ void modal_pairs_cpx(float2 (&a)[P], const float* lam
   }
 }
 
-template <int S, int T, typename IO, bool VEC, bool CPX>
+// PART 0: both parity halves in one workgroup.  PART 1: the even half, its
+// inverse transform stored to ws (S complex per row of the launch, in the
+// order m = t + T*i).  PART 2: the odd half, recombined with ws, gated and
+// stored.  A launch covers rows row0 .. row0 + gridDim.x - 1.
+template <int S, int T, typename IO, bool VEC, bool CPX, int PART>
 __global__ __launch_bounds__(T) void fftconv_kernel(
     const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
-    const float* __restrict__ skip, IO* __restrict__ y, int D, int L) {
+    const float* __restrict__ skip, IO* __restrict__ y, int D, int L,
+    float2* __restrict__ ws, int64_t row0) {
   constexpr int P = S / T;
   constexpr int M = 2 * S;
   constexpr int LG_M = ilog2(M);
   constexpr int LG_N = LG_M + 1;
+  constexpr int Q0 = PART == 2 ? 1 : 0;
+  constexpr int Q1 = PART == 1 ? 0 : 1;
   __shared__ float2 lds[lds_padded_size(S)];
   // From S = 1024 on, the even half's inverse transform waits for the odd
   // half in LDS rather than in 2P registers: there the register budget, not
   // LDS, limits the workgroups per CU (measured at D = 4096: L = 8192 612 ->
   // 377 us, L = 4096 201 -> 175 us; at S = 8192 it also ends a spill).
-  constexpr bool B0_LDS = S >= 1024;
+  constexpr bool B0_LDS = PART == 0 && S >= 1024;
   __shared__ float2 b0s[B0_LDS ? S : 1];
 
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int64_t row = row0 + blockIdx.x;
+  float2* wsr = ws + static_cast<int64_t>(blockIdx.x) * S;
   const int c = static_cast<int>(row % D);
   const IO* x1r = x1 + row * L;
   const IO* x2r = x2 + row * L;
@@ -110,14 +122,14 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   const float* lamc = lam + static_cast<int64_t>(c) * N * W;
   const float* resc = res + static_cast<int64_t>(c) * N * W;
 
-  float2 b0[B0_LDS ? 1 : P];   // inverse transform of the even half, kept for the recombination
+  float2 b0[PART == 0 && !B0_LDS ? P : 1];   // inverse transform of the even half, kept for the recombination
   float zm_nyq = 0.0f;    // Z[M] (real), only used by thread 0
 
   // Both parity halves are unrolled: as a loop, the address and twiddle
   // arithmetic common to the two iterations was hoisted out of it and held
   // in registers across both transforms.
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = Q0; q <= Q1; ++q) {
     float2 a[P];
     // ---- u = x1 * v, packed in pairs, parity pre-twiddle
 #pragma unroll
@@ -135,11 +147,14 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
     __syncthreads();
     float2 z[P];
     float um_nyq = 0.0f;
+    int ts = t;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int k = t + T * i;
+      if (i % SEQ == 0) ts = seq_idx(t);
+      const int k = ts + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
       z[i] = real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+      seq_keep(z[i]);
     }
     if (q == 0 && t == 0) um_nyq = a[0].x - a[0].y;
 
@@ -159,9 +174,11 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int k = t + T * i;
+      if (i % SEQ == 0) ts = seq_idx(t);
+      const int k = ts + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
       z[i] = cmul(z[i], real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)));
+      seq_keep(z[i]);
     }
     if (q == 0 && t == 0) zm_nyq = um_nyq * (a[0].x - a[0].y);
 
@@ -172,18 +189,21 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int k = t + T * i;
+      if (i % SEQ == 0) ts = seq_idx(t);
+      const int k = ts + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
       float2 zmir = lds[lds_pad(kk)];
       if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
       a[i] = inverse_pack(z[i], zmir, twiddle(2 * k + q, LG_N));
+      seq_keep(a[i]);
     }
     fft_inverse<S, T>(a, lds, t);
 
     if (q == 0) {
 #pragma unroll
       for (int i = 0; i < P; ++i) {
-        if constexpr (B0_LDS) b0s[t + T * i] = a[i];
+        if constexpr (PART == 1) (wsr + T * i)[t] = a[i];   // uniform base per i, one offset
+        else if constexpr (B0_LDS) b0s[t + T * i] = a[i];
         else b0[i] = a[i];
       }
     } else {
@@ -192,9 +212,13 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       const float inv_m = 1.0f / static_cast<float>(M);
 #pragma unroll
       for (int i = 0; i < P; ++i) {
-        const int m = t + T * i;
+        if (i % SEQ == 0) ts = seq_idx(t);
+        const int m = ts + T * i;
         if (2 * m >= L) continue;
-        const float2 e0 = B0_LDS ? b0s[t + T * i] : b0[B0_LDS ? 0 : i];
+        float2 e0;
+        if constexpr (PART == 2) e0 = (wsr + T * i)[ts];
+        else if constexpr (B0_LDS) e0 = b0s[t + T * i];
+        else e0 = b0[i];
         const float2 zz = cscale(cadd(e0, cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
         const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
         const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
@@ -207,11 +231,34 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   }
 }
 
+template <int S, int T, typename IO, bool VEC, bool CPX, int PART>
+static void launch_part(const FftconvArgs& a, int64_t row0, int64_t rows) {
+  fftconv_kernel<S, T, IO, VEC, CPX, PART><<<dim3(static_cast<unsigned>(rows)), dim3(T), 0, a.stream>>>(
+      static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
+      a.lam, a.res, a.N, a.skip, static_cast<IO*>(a.y), a.D, a.L,
+      static_cast<float2*>(a.workspace), row0);
+}
+
+// Rows of the split form per pass through the workspace (8 S bytes each, at
+// most 1 GiB).
+static int64_t split_batch_rows(int64_t rows, int S) {
+  const int64_t cap = (int64_t(1) << 30) / (8 * static_cast<int64_t>(S));
+  return rows < cap ? rows : cap;
+}
+
 template <int S, int T, typename IO, bool VEC, bool CPX>
 static void launch_k(const FftconvArgs& a) {
-  fftconv_kernel<S, T, IO, VEC, CPX><<<dim3(static_cast<unsigned>(a.B * a.D)), dim3(T), 0, a.stream>>>(
-      static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
-      a.lam, a.res, a.N, a.skip, static_cast<IO*>(a.y), a.D, a.L);
+  const int64_t rows = static_cast<int64_t>(a.B) * a.D;
+  if constexpr (S <= 4096) {
+    launch_part<S, T, IO, VEC, CPX, 0>(a, 0, rows);
+  } else {
+    const int64_t nb = split_batch_rows(rows, S);
+    for (int64_t r0 = 0; r0 < rows; r0 += nb) {
+      const int64_t n = rows - r0 < nb ? rows - r0 : nb;
+      launch_part<S, T, IO, VEC, CPX, 1>(a, r0, n);
+      launch_part<S, T, IO, VEC, CPX, 2>(a, r0, n);
+    }
+  }
 }
 
 template <int S, int T, typename IO>
@@ -226,14 +273,22 @@ static hipError_t launch_s(const FftconvArgs& a, bool vec) {
 template <typename IO>
 static hipError_t launch_io(const FftconvArgs& a, int S, bool vec) {
   switch (S) {
-    // 8 points per thread wherever the workgroup size allows: at 16 points
-    // the transforms need more than 256 registers per thread
+    // One workgroup for both halves up to S = 4096, 8 points per thread
+    // wherever the workgroup size allows (at 16 points the two-half kernel
+    // needs more than 256 registers per thread).  From S = 8192 on, one
+    // workgroup per half, 16 points per thread: at S = 8192 that is two
+    // 512-thread workgroups per CU instead of one of 1024 threads, and
+    // L = 16384 took 1.14 -> 0.89 ms at D = 4096 (at S = 4096 the split gained
+    // 4 %, at S = 2048 it lost 4 %).  S = 16384 needs 132 KB of LDS, one
+    // workgroup per CU either way, and runs about as fast as the four-step
+    // path (2.29 ms at L = 32768) with a quarter of its workspace.
     case 256: return launch_s<256, 64, IO>(a, vec);
     case 512: return launch_s<512, 64, IO>(a, vec);
     case 1024: return launch_s<1024, 128, IO>(a, vec);
     case 2048: return launch_s<2048, 256, IO>(a, vec);
     case 4096: return launch_s<4096, 512, IO>(a, vec);
-    case 8192: return launch_s<8192, 1024, IO>(a, vec);
+    case 8192: return launch_s<8192, 512, IO>(a, vec);
+    case 16384: return launch_s<16384, 1024, IO>(a, vec);
     default: return hipErrorInvalidValue;
   }
 }
@@ -242,7 +297,13 @@ int fftconv_onchip_S(int64_t L) {
   int64_t half = (L + 1) / 2;
   int64_t S = 256;
   while (S < half) S <<= 1;
-  return S <= 8192 ? static_cast<int>(S) : 0;
+  return S <= 16384 ? static_cast<int>(S) : 0;
+}
+
+size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L) {
+  const int S = fftconv_onchip_S(L);
+  if (S <= 4096 || B <= 0 || D <= 0) return 0;
+  return static_cast<size_t>(split_batch_rows(B * D, S) * 8 * S);
 }
 
 hipError_t launch_fftconv_onchip(const FftconvArgs& a) {

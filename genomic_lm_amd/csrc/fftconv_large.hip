@@ -1,11 +1,11 @@
-// fftconv_large.hip -- single-pass modal Hyena operator for L > 16384.
+// fftconv_large.hip -- single-pass modal Hyena operator for L > 32768.
 //
 // Same operation as fftconv.hip (y = x2 * (h causal-conv u) + skip * u, the
 // convolution as one zero-padded FFT product of length Nfft = 4S >= 2L:
 // 'modal-form IIR via FFT', Evo2-7B-262K model card, Implementation Notes,
-// 'Block dispatch'), for rows too long for one CU: beyond L = 16384 the
-// on-chip kernel would need 16 points per thread and spill, and this path
-// measured faster from L = 32768 on (2.3 against 4.2 ms at D = 4096).  The packing is the
+// 'Block dispatch'), for rows too long for one CU: beyond L = 32768 one
+// parity half (S >= 32768 complex, 256 KB) no longer fits in a CU's LDS.
+// The packing is the
 // one of fftconv.hip: real signals as complex c[m] = x[2m] + i x[2m+1], and the
 // size-M complex DFT (M = 2S) split into its two parity halves, each a size-S
 // DFT of c[m] exp(-2 pi i q m / M), m < S.
@@ -42,7 +42,7 @@ constexpr int CP = S2 / CT;                    // points per thread (8: at 16 th
 constexpr int GC = 16;                         // columns per workgroup
 constexpr int NTC = CT * GC;                   // threads of the column kernels
 constexpr int CSTRIDE = lds_padded_size(S2) + 1;   // odd stride: columns on distinct banks
-constexpr int MIN_S1 = 64, MAX_S1 = 1024;
+constexpr int MIN_S1 = 128, MAX_S1 = 1024;
 constexpr size_t BATCH_BYTES = size_t(1) << 30;    // workspace of one row batch: larger
                                                    // launches fill the chip better
 
@@ -314,7 +314,6 @@ hipError_t launch_large_io(const FftconvArgs& a, int64_t S) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (S1) {
-      case 64: e = launch_rows<64>(ws, nr, a.stream); break;
       case 128: e = launch_rows<128>(ws, nr, a.stream); break;
       case 256: e = launch_rows<256>(ws, nr, a.stream); break;
       case 512: e = launch_rows<512>(ws, nr, a.stream); break;

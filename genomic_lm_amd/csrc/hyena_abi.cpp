@@ -109,7 +109,12 @@ hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
   hyena::FftconvArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, y,
                        static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
                        io == HYENA_BF16, workspace, ws_bytes, as_stream(stream), cpx};
-  if (hyena::fftconv_onchip_S(L) != 0) return from_hip(hyena::launch_fftconv_onchip(a));
+  if (hyena::fftconv_onchip_S(L) != 0) {
+    const size_t need = hyena::fftconv_onchip_workspace(B, D, L);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
+      return HYENA_ERR_WORKSPACE;
+    return from_hip(hyena::launch_fftconv_onchip(a));
+  }
   const size_t need = hyena::fftconv_large_workspace(B, D, L);
   if (need == 0) return HYENA_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < need || !aligned_to(workspace, 16)) return HYENA_ERR_WORKSPACE;
@@ -265,7 +270,7 @@ size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, 
   (void)N;
   (void)io;
   if (B <= 0 || D <= 0 || L <= 0) return 0;
-  if (hyena::fftconv_onchip_S(L) != 0) return 0;
+  if (hyena::fftconv_onchip_S(L) != 0) return hyena::fftconv_onchip_workspace(B, D, L);
   if (next_pow2(2 * L) > HYENA_MAX_FFT_LEN) return 0;
   return hyena::fftconv_large_workspace(B, D, L);
 }

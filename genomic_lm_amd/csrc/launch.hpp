@@ -121,11 +121,14 @@ hipError_t launch_fir(const FirArgs& a);        // picks the kernel below or the
 hipError_t launch_fir_mfma(const FirArgs& a);   // bf16, K <= 128
 
 // Sub-transform size S of the on-chip single-pass kernel for length L, or 0
-// when L is too long for it (L > 16384).
+// when L is too long for it (L > 32768).  From S = 8192 on (L > 8192) the
+// parity halves are two launches that pass the even half's result through a
+// workspace of fftconv_onchip_workspace bytes (0 below).
 int fftconv_onchip_S(int64_t L);
+size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L);
 hipError_t launch_fftconv_onchip(const FftconvArgs& a);
 
-// Multi-kernel single pass for L > 16384 through a caller workspace.
+// Multi-kernel single pass for L > 32768 through a caller workspace.
 size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L);
 hipError_t launch_fftconv_large(const FftconvArgs& a);
 

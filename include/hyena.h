@@ -144,9 +144,12 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
  *   workspace : device buffer of at least hyena_fftconv_workspace_size(...)
  *               bytes, 16-byte aligned, owned by the caller, contents
  *               scratch (may be NULL when that size is 0).  Rows with
- *               L <= 16384 are transformed on chip and need none; longer rows
- *               go through it in batches of rows, 32 * Nfft / 4 bytes per row,
- *               at most 1 GiB.  Calls sharing one workspace must be ordered
+ *               L <= 8192 are transformed on chip and need none; rows with
+ *               8192 < L <= 32768 hand one half-transform between two
+ *               launches through it (2 * Nfft bytes per row); longer rows go
+ *               through the four-step path (8 * Nfft bytes per row).  Either
+ *               way rows are processed in batches of at most 1 GiB of
+ *               workspace.  Calls sharing one workspace must be ordered
  *               (same stream).
  * Nfft > HYENA_MAX_FFT_LEN -> HYENA_ERR_UNSUPPORTED; workspace NULL, short or
  * misaligned when one is needed -> HYENA_ERR_WORKSPACE.
@@ -157,8 +160,9 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
                                  void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when the FFT runs
- * on chip (L <= 16384) or the shape is empty or unsupported. */
+/* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when one launch
+ * transforms the rows on chip (L <= 8192) or the shape is empty or
+ * unsupported. */
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                     hyena_dtype_t io);
 

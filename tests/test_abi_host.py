@@ -132,12 +132,19 @@ def test_fftconv_validation():
         assert f(*a) == want, (idx, val)
     ws = G.lib().hyena_fftconv_workspace_size
     assert ws(1, 4, 1024, 16, G.BF16) == 0                     # on-chip path, no workspace
-    assert ws(1, 4, 16384, 16, G.BF16) == 0
-    assert ws(1, 4, 16385, 16, G.BF16) == 4 * 32 * 16384       # four-step from L > 16384
-    assert ws(1, 4, 32768, 16, G.BF16) == 4 * 32 * 16384
+    assert ws(1, 4, 8192, 16, G.BF16) == 0
+    # 8192 < L <= 32768: two on-chip launches, the even half's result
+    # (S = 4096 ... 16384 complex fp32 per row) through the workspace, up to
+    # 1 GiB of rows
+    assert ws(1, 4, 8193, 16, G.BF16) == 4 * 8 * 8192
+    assert ws(1, 4, 16384, 16, G.BF16) == 4 * 8 * 8192
+    assert ws(1, 4, 16385, 16, G.BF16) == 4 * 8 * 16384
+    assert ws(1, 4, 32768, 16, G.F32) == 4 * 8 * 16384
+    assert ws(1, 4096, 32768, 16, G.BF16) == 4096 * 8 * 16384
+    assert ws(4, 4096, 32768, 16, G.BF16) == 8192 * 8 * 16384
     assert ws(0, 4, 1024, 16, G.BF16) == 0
-    # four-step path: 32 S bytes per row (u and h, two parity halves, complex
-    # fp32), rows batched up to 1 GiB
+    # four-step path from L > 32768: 32 S bytes per row (u and h, two parity
+    # halves, complex fp32), rows batched up to 1 GiB
     assert ws(1, 4, 32769, 16, G.BF16) == 4 * 32 * 32768
     assert ws(2, 3, 65536, 16, G.F32) == 6 * 32 * 32768
     assert ws(1, 4096, 262144, 16, G.BF16) == 256 * 32 * 131072
@@ -151,6 +158,11 @@ def test_fftconv_validation():
     assert f(*big) == G.ERR_WORKSPACE
     big[12] = P(0x10008); big[13] = need
     assert f(*big) == G.ERR_WORKSPACE
+    # the same for the two-launch on-chip range
+    mid = list(good); mid[10] = 20000
+    assert f(*mid) == G.ERR_WORKSPACE
+    mid[12] = FAKE; mid[13] = ws(1, 4, 20000, 16, G.BF16) - 1
+    assert f(*mid) == G.ERR_WORKSPACE
 
 
 def test_chunk_validation():

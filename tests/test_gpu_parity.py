@@ -45,7 +45,8 @@ def test_modal_filter(L):
 
 # ------------------------------------------------------------------ fftconv
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("L", [1, 2, 7, 100, 512, 777, 1000, 1024, 2049, 4096, 8192, 16384, 32768])
+@pytest.mark.parametrize("L", [1, 2, 7, 100, 512, 777, 1000, 1024, 2049, 4096, 8192, 8193, 12000,
+                               16384, 32768])
 def test_fftconv_small(io, L):
     B = 2 if L in (777, 4096) else 1
     w = small(io, D=4, L=L, B=B)
@@ -56,9 +57,11 @@ def test_fftconv_small(io, L):
     gate(y, ref, io, label=f"fftconv L={L}")
 
 
-# Rows longer than 16384: the three-kernel four-step path through a
-# workspace.  Lengths cover each row-transform size (S/256 = 64 ... 1024),
-# odd lengths (the pair loads' ragged tail), and B*D above one row batch.
+# Rows longer than 8192 go through a workspace: up to L = 32768 one launch
+# per parity half, beyond it the three-kernel four-step path.  Lengths cover
+# the two-launch sizes (S = 16384 here; 8192 in test_fftconv_small), each
+# row-transform size of the four-step (S/256 = 128 ... 1024), odd lengths
+# (the pair loads' ragged tail), and B*D above one row batch.
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("L,B,D", [(16385, 1, 3), (20001, 2, 2), (32768, 1, 2),
                                    (32769, 1, 3), (40000, 2, 2), (65536, 1, 2), (65001, 1, 2),
@@ -84,6 +87,20 @@ def test_fftconv_large_row_batches():
     rows = sample_rows(w.D, k=12)
     ref, _ = oracle_modal(w, rows)
     gate(y, ref, "bf16", rows, label="fftconv 1200 rows")
+
+
+def test_fftconv_split_row_batches():
+    # 8200 rows of S = 16384 (128 KiB of workspace each): two row batches
+    # (8192 + 8) of the two-launch form through one workspace; the sampled
+    # channels include the last, whose rows lie in the second batch
+    w = small("bf16", D=4100, L=16385, B=2)
+    d = DevWorkload(w)
+    log("fftconv split B=2 D=4100 L=16385")
+    assert G.fftconv_workspace_size(2, 4100, 16385, w.N) == 8192 * 8 * 16384
+    y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
+    rows = sample_rows(w.D, k=6)
+    ref, _ = oracle_modal(w, rows)
+    gate(y, ref, "bf16", rows, label="fftconv 8200 rows")
 
 
 def test_fftconv_large_workspace_errors():
