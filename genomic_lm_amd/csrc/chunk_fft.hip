@@ -168,8 +168,21 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int m = t + T * i;
-      const float2 p1 = ld_pair<IO, VEC>(x1r, t0 + 2 * m, lim);
-      const float2 p2 = ld_pair<IO, VEC>(vr, t0 + 2 * m, lim);
+      float2 p1, p2;
+      if constexpr (VEC) {
+        // L and C even: the chunk holds whole pairs; clamped pair index,
+        // zero beyond its end, no branch between the loads
+        const int e = min(t0 + 2 * m, lim - 2);
+        Raw2<IO> r1, r2;
+        r1.load(x1r + e);
+        r2.load(vr + e);
+        const bool in = t0 + 2 * m < lim;
+        p1 = in ? r1.get() : make_float2(0.0f, 0.0f);
+        p2 = in ? r2.get() : make_float2(0.0f, 0.0f);
+      } else {
+        p1 = ld_pair<IO, VEC>(x1r, t0 + 2 * m, lim);
+        p2 = ld_pair<IO, VEC>(vr, t0 + 2 * m, lim);
+      }
       u[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
     }
     float2 b0[P], a[P];
@@ -325,13 +338,27 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       __syncthreads();
     }
     // gate and store
+    if constexpr (VEC) {
+      // every x2 pair loaded (clamped into the chunk) before the first store
+      Raw2<IO> rg[P];
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int pos = t0 + 2 * (t + T * i);
-      if (pos >= lim) continue;
-      const float2 g = ld_pair<IO, VEC>(x2r, pos, lim);
-      const float2 out = make_float2(fmaf(g.x, zz[i].x, sk * u[i].x), fmaf(g.y, zz[i].y, sk * u[i].y));
-      st_pair<IO, VEC>(yr, pos, lim, out);
+      for (int i = 0; i < P; ++i) rg[i].load(x2r + min(t0 + 2 * (t + T * i), lim - 2));
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int pos = t0 + 2 * (t + T * i);
+        const float2 g = rg[i].get();
+        const float2 out = make_float2(fmaf(g.x, zz[i].x, sk * u[i].x), fmaf(g.y, zz[i].y, sk * u[i].y));
+        if (pos < lim) Io<IO>::st2(yr, pos, out);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int pos = t0 + 2 * (t + T * i);
+        if (pos >= lim) continue;
+        const float2 g = ld_pair<IO, VEC>(x2r, pos, lim);
+        const float2 out = make_float2(fmaf(g.x, zz[i].x, sk * u[i].x), fmaf(g.y, zz[i].y, sk * u[i].y));
+        st_pair<IO, VEC>(yr, pos, lim, out);
+      }
     }
   }
   for (int n = t; n < NR; n += T) state_out[row * NR + n] = s_st[n];

@@ -22,6 +22,23 @@
 
 namespace hyena {
 
+// Raw storage of one element pair [i, i+1] (4 bytes of bf16 or 8 of fp32),
+// loaded without conversion so that many can be in flight in few registers;
+// p must be aligned to the pair.
+template <typename T> struct Raw2;
+template <> struct Raw2<bf16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ float2 get() const {
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+  }
+};
+template <> struct Raw2<float> {
+  float2 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ float2 get() const { return w; }
+};
+
 __device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
 __host__ __device__ constexpr int lds_padded_size(int S) { return S + (S >> 5); }
 

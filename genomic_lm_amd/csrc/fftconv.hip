@@ -135,8 +135,20 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int m = t + T * i;
-      const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
-      const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+      float2 p1, p2;
+      if constexpr (VEC) {
+        // L even: clamped pair index, zero beyond L without a branch
+        const int64_t e = min(2 * m, L - 2);
+        Raw2<IO> r1, r2;
+        r1.load(x1r + e);
+        r2.load(vr + e);
+        const bool in = 2 * m < L;
+        p1 = in ? r1.get() : make_float2(0.0f, 0.0f);
+        p2 = in ? r2.get() : make_float2(0.0f, 0.0f);
+      } else {
+        p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+        p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+      }
       a[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
       if (q) a[i] = cmul(a[i], twiddle(m, LG_M));
     }
@@ -210,22 +222,57 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       // ---- recombine, gate, store
       const float sk = skip ? skip[c] : 0.0f;
       const float inv_m = 1.0f / static_cast<float>(M);
+      if constexpr (VEC) {
+        // L is even: pair m is whole for 2m < L and absent beyond.  The
+        // operands of a group of 8 elements (B_0, x1, v, x2) are loaded
+        // together from pair indices clamped into the row, so no branch
+        // separates the loads and none waits for an earlier element's store;
+        // pairs beyond L are not stored.
+        constexpr int GG = P < 8 ? P : 8;
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        if (i % SEQ == 0) ts = seq_idx(t);
-        const int m = ts + T * i;
-        if (2 * m >= L) continue;
-        float2 e0;
-        if constexpr (PART == 2) e0 = (wsr + T * i)[ts];
-        else if constexpr (B0_LDS) e0 = b0s[t + T * i];
-        else e0 = b0[i];
-        const float2 zz = cscale(cadd(e0, cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
-        const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
-        const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
-        const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
-        const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
-                                       fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
-        st_pair<IO, VEC>(yr, 2 * m, L, out);
+        for (int g0 = 0; g0 < P; g0 += GG) {
+          ts = seq_idx(t);
+          Raw2<IO> r1[GG], r2[GG], rg[GG];
+          float2 e0[GG];
+#pragma unroll
+          for (int j = 0; j < GG; ++j) {
+            const int i = g0 + j;
+            const int64_t e = min(2 * (ts + T * i), L - 2);
+            if constexpr (PART == 2) e0[j] = (wsr + T * i)[ts];
+            else if constexpr (B0_LDS) e0[j] = b0s[ts + T * i];
+            else e0[j] = b0[i];
+            r1[j].load(x1r + e);
+            r2[j].load(vr + e);
+            rg[j].load(x2r + e);
+          }
+#pragma unroll
+          for (int j = 0; j < GG; ++j) {
+            const int m = ts + T * (g0 + j);
+            const float2 zz = cscale(cadd(e0[j], cmul(cconj(twiddle(m, LG_M)), a[g0 + j])), inv_m);
+            const float2 p1 = r1[j].get(), p2 = r2[j].get(), g = rg[j].get();
+            const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
+                                           fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
+            if (2 * m < L) Io<IO>::st2(yr, 2 * m, out);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          if (i % SEQ == 0) ts = seq_idx(t);
+          const int m = ts + T * i;
+          if (2 * m >= L) continue;
+          float2 e0;
+          if constexpr (PART == 2) e0 = (wsr + T * i)[ts];
+          else if constexpr (B0_LDS) e0 = b0s[ts + T * i];
+          else e0 = b0[i];
+          const float2 zz = cscale(cadd(e0, cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
+          const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+          const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+          const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
+          const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
+                                         fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
+          st_pair<IO, VEC>(yr, 2 * m, L, out);
+        }
       }
     }
   }

@@ -77,8 +77,20 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
 #pragma unroll
     for (int i = 0; i < CP; ++i) {
       const int64_t m = m1 + int64_t(S1) * (t + CT * i);
-      const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
-      const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+      float2 p1, p2;
+      if constexpr (VEC) {
+        // L even: clamped pair index, zero beyond L, no branch between loads
+        const int64_t e = min(2 * m, int64_t(L) - 2);
+        Raw2<IO> r1, r2;
+        r1.load(x1r + e);
+        r2.load(vr + e);
+        const bool in = 2 * m < L;
+        p1 = in ? r1.get() : make_float2(0.0f, 0.0f);
+        p2 = in ? r2.get() : make_float2(0.0f, 0.0f);
+      } else {
+        p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+        p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+      }
       d[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
     }
   } else {
@@ -257,17 +269,39 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_inv(
       IO* yr = y + row * L;
       const float sk = skip ? skip[row % D] : 0.0f;
       const float inv_m = ldexpf(1.0f, -lgM);
+      if constexpr (VEC) {
+        // gate operands loaded together from clamped pair indices (L even),
+        // so no branch separates the loads; pairs beyond L are not stored
+        Raw2<IO> r1[CP], r2[CP], rg[CP];
 #pragma unroll
-      for (int i = 0; i < CP; ++i) {
-        const int m = m1 + S1 * (t + CT * i);
-        if (2 * int64_t(m) >= L) continue;
-        const float2 zz = cscale(cadd(b0[i], cmul(cconj(twiddle(m, lgM)), a[i])), inv_m);
-        const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
-        const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
-        const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
-        st_pair<IO, VEC>(yr, 2 * m, L,
-                         make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
-                                     fmaf(g.y, zz.y, sk * (p1.y * p2.y))));
+        for (int i = 0; i < CP; ++i) {
+          const int64_t e = min(2 * int64_t(m1 + S1 * (t + CT * i)), int64_t(L) - 2);
+          r1[i].load(x1r + e);
+          r2[i].load(vr + e);
+          rg[i].load(x2r + e);
+        }
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+          const int m = m1 + S1 * (t + CT * i);
+          const float2 zz = cscale(cadd(b0[i], cmul(cconj(twiddle(m, lgM)), a[i])), inv_m);
+          const float2 p1 = r1[i].get(), p2 = r2[i].get(), g = rg[i].get();
+          const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
+                                         fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
+          if (2 * int64_t(m) < L) Io<IO>::st2(yr, 2 * int64_t(m), out);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+          const int m = m1 + S1 * (t + CT * i);
+          if (2 * int64_t(m) >= L) continue;
+          const float2 zz = cscale(cadd(b0[i], cmul(cconj(twiddle(m, lgM)), a[i])), inv_m);
+          const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+          const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+          const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);
+          st_pair<IO, VEC>(yr, 2 * m, L,
+                           make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
+                                       fmaf(g.y, zz.y, sk * (p1.y * p2.y))));
+        }
       }
     }
   }
