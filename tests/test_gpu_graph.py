@@ -1,6 +1,6 @@
-"""Entry points inside a HIP graph: a chunked prefill, decode steps and FIR
-window steps (channel- and token-major) captured once and replayed several
-times, with the program's own eager work in between; every replay must give
+"""Entry points inside a HIP graph: a chunked prefill, single passes (on
+chip, and in two launches through a workspace), decode steps and FIR window
+steps (channel- and token-major) captured once and replayed several times, with the program's own eager work in between; every replay must give
 the eager results bit for bit (every kernel here is deterministic).  Nothing
 in these calls allocates, clears memory with a memset or synchronises, which
 is what capture needs."""
@@ -32,6 +32,9 @@ def _program(d, xin, bufs, n_pre, steps):
                      out=bufs["yf_pre"], window_out=bufs["win"])
     G.chunk_fwd_tokmajor(bufs["xin_pre"], d.lam, d.res, d.skip, out=bufs["yt_pre"],
                          state_out=bufs["st"], workspace=bufs["ws"])
+    G.fftconv_fwd(*bufs["pre"], d.lam, d.res, d.skip, out=bufs["yc_pre"])
+    G.fftconv_fwd(*bufs["long"], d.lam, d.res, d.skip, out=bufs["yc_long"],
+                  workspace=bufs["fws"])
     for i in range(steps):
         tok = bufs["tok"][i]
         G.modal_decode(*tok, d.lam, d.res, d.skip, state_in=bufs["s"], out=bufs["y_dec"][i],
@@ -52,6 +55,11 @@ def test_graph_capture_and_replay():
     B, D = 1, w.D
     pre = [t[..., :n_pre].contiguous() for t in (d.x1, d.x2, d.v)]
     ws_bytes = max(16, G.chunk_tokmajor_workspace_size(B, D, n_pre, w.N))
+    n_long = 12000                                   # single pass in two launches
+    wl = W.make("7b_layer_set", D=256, L=n_long)
+    long = [act_to_dev(a, "bf16") for a in (wl.x1, wl.x2, wl.v)]
+    fws_bytes = G.fftconv_workspace_size(B, D, n_long, w.N)
+    assert fws_bytes > 0
 
     def fresh():
         return {
@@ -64,12 +72,15 @@ def test_graph_capture_and_replay():
             "s": torch.empty((B, D, w.N), device=dev), "st": torch.empty((B, D, w.N), device=dev),
             "win": torch.empty((B, D, 127), device=dev), "wt": torch.zeros((B, D, 6), device=dev),
             "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+            "long": long, "yc_pre": torch.empty_like(pre[0]),
+            "yc_long": torch.empty_like(long[0]),
+            "fws": torch.empty(fws_bytes, dtype=torch.uint8, device=dev),
             "y_dec": [torch.empty((B, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
             "yf_dec": [torch.empty((B, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
             "yt_dec": [torch.empty((B, 1, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)],
         }
 
-    outs = ("y_pre", "yf_pre", "yt_pre", "s", "st", "win", "wt")
+    outs = ("y_pre", "yf_pre", "yt_pre", "yc_pre", "yc_long", "s", "st", "win", "wt")
     lists = ("y_dec", "yf_dec", "yt_dec")
 
     def snapshot(b):
