@@ -156,8 +156,14 @@ __device__ __forceinline__ void pass_compute(float2 (&reg)[S / T], int t) {
 
 // The LDS addresses of a pass depend only on t and are the same in every
 // transform of a kernel; t passes through an empty asm so that the compiler
-// recomputes them per pass (a few integer ops) instead of keeping every pass's
-// addresses live across whole kernels, which costs registers.
+// recomputes them per pass instead of keeping every pass's addresses live
+// across whole kernels, which costs registers.  Within a butterfly the
+// padded address is affine in r: for the index sets of these passes (a base
+// whose offset within its 32-element row leaves room for r*NS, or a stride
+// that is a multiple of 32) lds_pad(base + r*NS) = lds_pad(base) + r*NS +
+// (r*NS >> 5), checked exhaustively for every pass shape of S <= 16384.  So
+// one padded base is computed per butterfly and the rest are immediate
+// offsets.
 template <int S, int T, int R, int NS>
 __device__ __forceinline__ void pass_store(const float2 (&reg)[S / T], float2* lds, int t) {
   constexpr int P = S / T;
@@ -166,21 +172,23 @@ __device__ __forceinline__ void pass_store(const float2 (&reg)[S / T], float2* l
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int j = t + T * b;
-    const int base = (j / NS) * NS * R + (j & (NS - 1));
+    float2* row = lds + lds_pad((j / NS) * NS * R + (j & (NS - 1)));
 #pragma unroll
-    for (int r = 0; r < R; ++r) lds[lds_pad(base + r * NS)] = reg[b + r * NB];
+    for (int r = 0; r < R; ++r) row[r * NS + ((r * NS) >> 5)] = reg[b + r * NB];
   }
 }
 
 template <int S, int T, int R>
 __device__ __forceinline__ void pass_load(float2 (&reg)[S / T], const float2* lds, int t) {
   constexpr int P = S / T;
+  constexpr int Q = S / R;
   asm volatile("" : "+v"(t));
   constexpr int NB = P / R;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
+    const float2* row = lds + lds_pad(t + T * b);
 #pragma unroll
-    for (int r = 0; r < R; ++r) reg[b + r * NB] = lds[lds_pad(t + T * b + r * (S / R))];
+    for (int r = 0; r < R; ++r) reg[b + r * NB] = row[r * Q + ((r * Q) >> 5)];
   }
 }
 
