@@ -161,7 +161,8 @@ __device__ __forceinline__ void pass_compute(float2 (&reg)[S / T], int t) {
 // padded address is affine in r: for the index sets of these passes (a base
 // whose offset within its 32-element row leaves room for r*NS, or a stride
 // that is a multiple of 32) lds_pad(base + r*NS) = lds_pad(base) + r*NS +
-// (r*NS >> 5), checked exhaustively for every pass shape of S <= 16384.  So
+// (r*NS >> 5); tests/test_fft_layout.py checks it for every thread of every
+// instantiated shape.  So
 // one padded base is computed per butterfly and the rest are immediate
 // offsets.
 template <int S, int T, int R, int NS>
