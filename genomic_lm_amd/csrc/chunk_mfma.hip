@@ -162,6 +162,20 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       dma16(x2r + t0 + 8 * ch, &tin[2][64 * h]);
     }
   };
+  // The same for the partial last tile of a VEC row (L a multiple of 8, so
+  // its 8-token chunks are whole or absent): chunks at or past L re-read the
+  // tile's first chunk, an in-bounds address, and their runs are zeroed after
+  // they are read out.
+  auto prefetch_part = [&](int64_t t0, uint4 (*tin)[128]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = unswz(64 * h + l);
+      const int64_t src = (t0 + 8 * ch < L) ? t0 + 8 * ch : t0;
+      dma16(x1r + src, &tin[0][64 * h]);
+      dma16(vr + src, &tin[1][64 * h]);
+      dma16(x2r + src, &tin[2][64 * h]);
+    }
+  };
 
   // ---- per-lane parameters, then the first two tiles in flight while the
   // per-row constants are set up
@@ -194,6 +208,9 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   if constexpr (sizeof(IO) == 2) {
     if (PIPE || nfull > 0) prefetch(0, tin_a);
     if (PIPE || nfull > 1) prefetch(1024, tin_b);
+    if constexpr (VEC && !PIPE) {
+      if (nfull == 0) prefetch_part(0, tin_a);   // a row shorter than one tile
+    }
   }
 
   const float lam_n = (n_sc < NS) ? lam_ld : 0.0f;
@@ -323,6 +340,16 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     if constexpr (sizeof(IO) == 2) {
       if (staged) {
         read_staged_runs(tin, i32, hf, rx, rv, rg);
+        if (!full) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (t0 + lane_off + 8 * q >= L) {   // a run is whole or past L
+              rx[q].w = make_uint2(0u, 0u);
+              rv[q].w = make_uint2(0u, 0u);
+              rg[q].w = make_uint2(0u, 0u);
+            }
+          }
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -470,7 +497,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
         o[e] = fmaf(rg[q].get(e), cz[r], su[r]);
       }
       const int64_t pos = t0 + lane_off + 8 * q;
-      if (full) {
+      if (full || staged) {
         if constexpr (sizeof(IO) == 2) {
           reinterpret_cast<uint2*>(&tout[swz(4 * i32 + q)])[hf] = make_uint2(cvt2(o[0], o[1]), cvt2(o[2], o[3]));
         } else {
@@ -488,6 +515,12 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           *reinterpret_cast<uint4*>(yr + t0 + 8 * (l + 64 * h)) = tout[swz(l + 64 * h)];
+      } else if (staged) {
+        lds_sync();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (t0 + 8 * (l + 64 * h) < L)
+            *reinterpret_cast<uint4*>(yr + t0 + 8 * (l + 64 * h)) = tout[swz(l + 64 * h)];
       }
     }
   };
@@ -577,6 +610,16 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 #pragma unroll 1
   for (int64_t t0 = static_cast<int64_t>(nfull) << 10; t0 < L; t0 += 1024) {
     TileIn<IO> in;
+    bool staged = false;
+    if constexpr (sizeof(IO) == 2 && VEC) {
+      if (t0 > 0) {                       // (a row shorter than one tile issued it on entry)
+        wait_vmem<0>();                   // no DMA of the full tiles left in flight
+        prefetch_part(t0, tin_a);
+      }
+      wait_vmem<0>();
+      lds_sync();
+      staged = true;
+    } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float fa[4], fb[4], fg[4];
@@ -600,8 +643,9 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
         in.g[q].w = make_float4(fg[0], fg[1], fg[2], fg[3]);
       }
     }
+    }
     bf16x8 um[NU][2];
-    tile(in, t0, false, um, tin_a, false, [] {});
+    tile(in, t0, false, um, tin_a, staged, [] {});
     float (*sbuf)[33][17] = sbufs[0];
     const int64_t rem = L - t0;
     if (rem == 1024) {

@@ -171,6 +171,25 @@ def test_chunk_small(algo, io, C, L):
         state_gate(s, ref_s, label=f"chunk/{algo} C={C} L={L}")
 
 
+# bf16 rows whose length is a multiple of 8 but not of 1024: the matrix-core
+# kernel stages the partial last tile like a full one (chunks past L re-read
+# an in-bounds chunk and are zeroed); lengths below one tile, one chunk past
+# a tile, one chunk short of one, and a 32-tile row with a partial 33rd.
+@pytest.mark.parametrize("L", [8, 512, 1016, 1032, 2056, 32768 + 744])
+def test_chunk_mfma_partial_tile(L):
+    w = small("bf16", D=5, L=L, B=2)
+    d = DevWorkload(w)
+    s0 = W.random_state(w.B, w.D, w.N, seed=L)
+    log(f"chunk/mfma partial tile L={L}")
+    rows = np.arange(w.D) if L <= 4096 else sample_rows(w.D, k=3)
+    for state in (None, s0):
+        sin = None if state is None else par_to_dev(state)
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, state_in=sin, algo="mfma")
+        ref_y, ref_s = oracle_modal(w, rows, C=1024, state_in=state)
+        gate(y, ref_y, "bf16", rows, label=f"chunk/mfma L={L} state={'yes' if state is not None else 'no'}")
+        state_gate(s, ref_s, rows, label=f"chunk/mfma L={L}")
+
+
 @pytest.mark.parametrize("N", [1, 3, 17, 64])
 def test_mode_counts(N):
     """From one mode to the maximum of 64: single pass, chunked with AUTO (the
