@@ -4,7 +4,10 @@ One step = one pass of the operator over the 32 kb chunked-prefill workload
 (B=1, D=4096, L=32768, bf16 I/O, N=16 modes, chunk 1024 with carried state):
 modal filter generation, input gate, causal long convolution, output gate and
 skip, and the carried modal state -- all in one launch of hyena_chunk_fwd.
-Inputs are resident in HBM before timing starts.
+Inputs are resident in HBM before timing starts; consecutive steps take four
+different input sets in turn (and write four outputs), so no step reads data
+an earlier step left in the last-level cache.  The same step repeated on one
+input set is reported beside it as `same_input_set` with --same-input.
 
 Prints ONE JSON line.  Besides the headline it reports the roofline of the
 dominant kernel (HIP-event timing of the same launches; HBM bytes and the
@@ -39,6 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["genomic_lm_amd/csrc/chunk_mfma.hip", "genomic_lm_amd/csrc/mfma_common.hpp",
                   "genomic_lm_amd/csrc/common.hpp"]
 CPU_SAMPLE_S = 12.0                          # wall time the CPU oracle is given
+INPUT_SETS = 4                               # activation sets the timed steps rotate over
 
 
 def kernel_hash() -> str:
@@ -57,6 +61,8 @@ def parse():
     ap.add_argument("--algo", default="mfma", choices=["mfma", "fft", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--same-input", action="store_true",
+                    help="also time the step repeated on one input set (last-level cache hits)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -161,13 +167,30 @@ def main():
     par = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
     x1, x2, v = to(w.x1), to(w.x2), to(w.v)
     lam, res, skip = par(w.log_poles), par(w.residues), par(w.skip)
-    y = torch.empty_like(x1)
     st = torch.empty((B, D, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # Consecutive steps take consecutive input sets (the workload's streams,
+    # then copies with the channels rotated) and write separate outputs, so
+    # that no step reads what an earlier one left in the 256 MB last-level
+    # cache: a model's layers never see the same activations twice.
+    sets = [(x1, x2, v)]
+    for k in range(1, INPUT_SETS):
+        sets.append(tuple(torch.roll(t, shifts=k * (D // INPUT_SETS) + 1, dims=1).contiguous()
+                          for t in (x1, x2, v)))
+    ys = [torch.empty_like(x1) for _ in range(INPUT_SETS)]
 
-    def step():
-        G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo=args.algo, out=y, state_out=st)
+    def rotating(f):
+        n = [0]
 
+        def g():
+            f(n[0] % INPUT_SETS)
+            n[0] += 1
+        return g
+
+    def head(k):
+        G.chunk_fwd(*sets[k], lam, res, CHUNK, skip, algo=args.algo, out=ys[k], state_out=st)
+
+    step = rotating(head)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -181,8 +204,12 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     t_step = e0.elapsed_time(e1) / 1e3 / args.steps
-    if not torch.isfinite(y.float()).all():
-        raise RuntimeError("non-finite output")
+    for yk in ys:
+        if not torch.isfinite(yk.float()).all():
+            raise RuntimeError("non-finite output")
+    # for context (--same-input): the same step repeated on one input set,
+    # whose reads then partly hit the last-level cache
+    t_same = timed(lambda: head(0), args.steps, 2, stream) if args.same_input else None
 
     tc = B * D * L
     alg_bytes = 8 * tc                       # x1, x2, v read + y written, bf16
@@ -214,27 +241,30 @@ def main():
         fft_ws = torch.empty(max(G.fftconv_workspace_size(B, D, L, w.N, x1.dtype), 16),
                              dtype=torch.uint8, device=dev)
         runs = {
-            "chunk_fft": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="fft", out=y, state_out=st),
-            "chunk_mfma": lambda: G.chunk_fwd(x1, x2, v, lam, res, CHUNK, skip, algo="mfma", out=y, state_out=st),
-            "fftconv_single_pass": lambda: G.fftconv_fwd(x1, x2, v, lam, res, skip, out=y,
-                                                         workspace=fft_ws),
-            "fir7": lambda: G.fir_fwd(x1, x2, v, taps7, skip, out=y),
-            "fir128": lambda: G.fir_fwd(x1, x2, v, taps128, skip, out=y),
+            "chunk_fft": rotating(lambda k: G.chunk_fwd(*sets[k], lam, res, CHUNK, skip, algo="fft",
+                                                        out=ys[k], state_out=st)),
+            "chunk_mfma": rotating(lambda k: G.chunk_fwd(*sets[k], lam, res, CHUNK, skip, algo="mfma",
+                                                         out=ys[k], state_out=st)),
+            "fftconv_single_pass": rotating(lambda k: G.fftconv_fwd(*sets[k], lam, res, skip,
+                                                                    out=ys[k], workspace=fft_ws)),
+            "fir7": rotating(lambda k: G.fir_fwd(*sets[k], taps7, skip, out=ys[k])),
+            "fir128": rotating(lambda k: G.fir_fwd(*sets[k], taps128, skip, out=ys[k])),
         }
         # the same prefill as 32 calls of one chunk each, the state handed over
-        xs = [(t[..., t0:t0 + CHUNK].contiguous() for t in (x1, x2, v)) for t0 in range(0, L, CHUNK)]
-        xs = [tuple(g) for g in xs]
-        ys = [torch.empty_like(c[0]) for c in xs]
+        nch = (L + CHUNK - 1) // CHUNK
+        xs = [[tuple(t[..., t0:t0 + CHUNK].contiguous() for t in sk) for t0 in range(0, L, CHUNK)]
+              for sk in sets]
+        ycs = [[torch.empty_like(c[0]) for c in xk] for xk in xs]
         sts = [torch.empty_like(st), torch.empty_like(st)]
 
-        def per_chunk_calls():
+        def per_chunk_calls(k):
             s_in = None
-            for i, (a, b, c) in enumerate(xs):
+            for i, (a, b, c) in enumerate(xs[k]):
                 G.chunk_fwd(a, b, c, lam, res, CHUNK, skip, state_in=s_in, algo=args.algo,
-                            out=ys[i], state_out=sts[i & 1])
+                            out=ycs[k][i], state_out=sts[i & 1])
                 s_in = sts[i & 1]
 
-        runs[f"chunk_{args.algo}_x{len(xs)}_calls"] = per_chunk_calls
+        runs[f"chunk_{args.algo}_x{nch}_calls"] = rotating(per_chunk_calls)
         # one decode step per row from the caches (B=1, D=4096: latency-bound)
         tok = [t[..., L - 1].contiguous() for t in (x1, x2, v)]
         y1 = torch.empty_like(tok[0])
@@ -250,26 +280,26 @@ def main():
         lc, rc = W.complex_modes(D, 8, seed=5)
         lc_d, rc_d = torch.from_numpy(lc).to(dev), torch.from_numpy(rc).to(dev)
         stc = torch.empty((B, D, 8), dtype=torch.complex64, device=dev)
-        runs["fftconv_cpx_single_pass"] = lambda: G.fftconv_fwd_cpx(x1, x2, v, lc_d, rc_d, skip,
-                                                                     out=y, workspace=fft_ws)
-        runs["chunk_cpx_fft"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip,
-                                                        algo="fft", out=y, state_out=stc)
-        runs["chunk_cpx_mfma"] = lambda: G.chunk_fwd_cpx(x1, x2, v, lc_d, rc_d, CHUNK, skip,
-                                                         algo="mfma", out=y, state_out=stc)
+        runs["fftconv_cpx_single_pass"] = rotating(lambda k: G.fftconv_fwd_cpx(
+            *sets[k], lc_d, rc_d, skip, out=ys[k], workspace=fft_ws))
+        runs["chunk_cpx_fft"] = rotating(lambda k: G.chunk_fwd_cpx(
+            *sets[k], lc_d, rc_d, CHUNK, skip, algo="fft", out=ys[k], state_out=stc))
+        runs["chunk_cpx_mfma"] = rotating(lambda k: G.chunk_fwd_cpx(
+            *sets[k], lc_d, rc_d, CHUNK, skip, algo="mfma", out=ys[k], state_out=stc))
         # the same prefill read straight from in_proj's token-major layout
         # (B, L, 3D), channels interleaved per triple, y written (B, L, D)
-        xin = torch.stack((x1, x2, v), -1).permute(0, 2, 1, 3).contiguous().view(B, L, 3 * D)
-        y_tm = torch.empty((B, L, D), dtype=torch.bfloat16, device=dev)
+        xins = [torch.stack(sk, -1).permute(0, 2, 1, 3).contiguous().view(B, L, 3 * D) for sk in sets]
+        y_tms = [torch.empty((B, L, D), dtype=torch.bfloat16, device=dev) for _ in sets]
         tm_ws = torch.empty(max(G.chunk_tokmajor_workspace_size(B, D, L, w.N), 16),
                             dtype=torch.uint8, device=dev)
-        runs["chunk_tokmajor"] = lambda: G.chunk_fwd_tokmajor(xin, lam, res, skip, out=y_tm,
-                                                              state_out=st, workspace=tm_ws)
+        runs["chunk_tokmajor"] = rotating(lambda k: G.chunk_fwd_tokmajor(
+            xins[k], lam, res, skip, out=y_tms[k], state_out=st, workspace=tm_ws))
         win6 = torch.empty((B, D, 6), dtype=torch.float32, device=dev)
         win127 = torch.empty((B, D, 127), dtype=torch.float32, device=dev)
-        runs["fir7_tokmajor"] = lambda: G.fir_fwd_tokmajor(xin, taps7, skip, out=y_tm,
-                                                           window_out=win6)
-        runs["fir128_tokmajor"] = lambda: G.fir_fwd_tokmajor(xin, taps128, skip, out=y_tm,
-                                                             window_out=win127)
+        runs["fir7_tokmajor"] = rotating(lambda k: G.fir_fwd_tokmajor(
+            xins[k], taps7, skip, out=y_tms[k], window_out=win6))
+        runs["fir128_tokmajor"] = rotating(lambda k: G.fir_fwd_tokmajor(
+            xins[k], taps128, skip, out=y_tms[k], window_out=win127))
         one_token = {"modal_decode_step", "fir128_window_step"}   # B*D token·channels
         for name, fn in runs.items():
             t = timed(fn, comp_steps, 2, stream)
@@ -292,7 +322,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "32k chunked prefill (B=1 D=4096 L=32768, bf16 I/O, N=16, chunk 1024)",
                    "entry": "hyena_chunk_fwd", "algo": args.algo, "B": B, "D": D, "L": L,
-                   "chunk": CHUNK, "modes": w.N, "io": "bf16"},
+                   "chunk": CHUNK, "modes": w.N, "io": "bf16", "input_sets": INPUT_SETS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -302,6 +332,9 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "components": comps,
     }
+    if t_same is not None:
+        out["same_input_set"] = {"ms_per_step": round(t_same * 1e3, 4),
+                                 "value": round(tc / t_same / 1e9, 3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
