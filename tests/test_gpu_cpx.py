@@ -58,7 +58,7 @@ def test_modal_filter_cpx(L):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("L", [100, 1024, 3001, 16384, 20001, 40000])
+@pytest.mark.parametrize("L", [100, 1024, 3001, 16384, 20001, 24000, 40000])
 def test_fftconv_cpx(io, L):
     w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2 if L < 5000 else 1)
     log(f"fftconv_cpx io={io} L={L}")
