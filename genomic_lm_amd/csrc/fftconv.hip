@@ -18,8 +18,8 @@
 //  * Z = U * H, repacked for the inverse real transform, inverse size-S DFT
 //    per parity, and the two halves are recombined with one twiddle:
 //    c_z[m] = (B_0[m] + exp(2*pi*i*m/M) B_1[m]) / M.
-// Only one size-S transform lives in LDS at a time.  Up to S = 4096 one
-// workgroup takes both halves.  From S = 8192 (L > 8192) the two halves are
+// Only one size-S transform lives in LDS at a time.  Up to S = 2048 one
+// workgroup takes both halves.  From S = 4096 (L > 4096) the two halves are
 // two launches with one workgroup per (row, half): the even half writes its
 // inverse transform B_0 (S complex, fp32) to a caller workspace and the odd
 // half reads it back for the recombination -- 4 bytes per token each way,
@@ -296,7 +296,7 @@ static int64_t split_batch_rows(int64_t rows, int S) {
 template <int S, int T, typename IO, bool VEC, bool CPX>
 static void launch_k(const FftconvArgs& a) {
   const int64_t rows = static_cast<int64_t>(a.B) * a.D;
-  if constexpr (S <= 4096) {
+  if constexpr (S <= 2048) {
     launch_part<S, T, IO, VEC, CPX, 0>(a, 0, rows);
   } else {
     const int64_t nb = split_batch_rows(rows, S);
@@ -320,20 +320,21 @@ static hipError_t launch_s(const FftconvArgs& a, bool vec) {
 template <typename IO>
 static hipError_t launch_io(const FftconvArgs& a, int S, bool vec) {
   switch (S) {
-    // One workgroup for both halves up to S = 4096, 8 points per thread
+    // One workgroup for both halves up to S = 2048, 8 points per thread
     // wherever the workgroup size allows (at 16 points the two-half kernel
-    // needs more than 256 registers per thread).  From S = 8192 on, one
+    // needs more than 256 registers per thread).  From S = 4096 on, one
     // workgroup per half, 16 points per thread: at S = 8192 that is two
-    // 512-thread workgroups per CU instead of one of 1024 threads, and
-    // L = 16384 took 1.14 -> 0.89 ms at D = 4096 (at S = 4096 the split gained
-    // 4 %, at S = 2048 it lost 4 %).  S = 16384 needs 132 KB of LDS, one
-    // workgroup per CU either way, and runs about as fast as the four-step
+    // 512-thread workgroups per CU instead of one of 1024 threads (L = 16384
+    // 1.14 -> 0.89 ms at D = 4096), at S = 4096 four of 256 instead of two of
+    // 512 (L = 8192 0.33 -> 0.29 ms, once the loads were branch-free); at
+    // S = 2048 it made no difference.  S = 16384 needs 132 KB of LDS, one
+    // workgroup per CU either way, and ran about as fast as the four-step
     // path (2.29 ms at L = 32768) with a quarter of its workspace.
     case 256: return launch_s<256, 64, IO>(a, vec);
     case 512: return launch_s<512, 64, IO>(a, vec);
     case 1024: return launch_s<1024, 128, IO>(a, vec);
     case 2048: return launch_s<2048, 256, IO>(a, vec);
-    case 4096: return launch_s<4096, 512, IO>(a, vec);
+    case 4096: return launch_s<4096, 256, IO>(a, vec);
     case 8192: return launch_s<8192, 512, IO>(a, vec);
     case 16384: return launch_s<16384, 1024, IO>(a, vec);
     default: return hipErrorInvalidValue;
@@ -349,7 +350,7 @@ int fftconv_onchip_S(int64_t L) {
 
 size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L) {
   const int S = fftconv_onchip_S(L);
-  if (S <= 4096 || B <= 0 || D <= 0) return 0;
+  if (S <= 2048 || B <= 0 || D <= 0) return 0;
   return static_cast<size_t>(split_batch_rows(B * D, S) * 8 * S);
 }
 

@@ -121,7 +121,7 @@ hipError_t launch_fir(const FirArgs& a);        // picks the kernel below or the
 hipError_t launch_fir_mfma(const FirArgs& a);   // bf16, K <= 128
 
 // Sub-transform size S of the on-chip single-pass kernel for length L, or 0
-// when L is too long for it (L > 32768).  From S = 8192 on (L > 8192) the
+// when L is too long for it (L > 32768).  From S = 4096 on (L > 4096) the
 // parity halves are two launches that pass the even half's result through a
 // workspace of fftconv_onchip_workspace bytes (0 below).
 int fftconv_onchip_S(int64_t L);

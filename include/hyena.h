@@ -144,8 +144,8 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
  *   workspace : device buffer of at least hyena_fftconv_workspace_size(...)
  *               bytes, 16-byte aligned, owned by the caller, contents
  *               scratch (may be NULL when that size is 0).  Rows with
- *               L <= 8192 are transformed on chip and need none; rows with
- *               8192 < L <= 32768 hand one half-transform between two
+ *               L <= 4096 are transformed on chip and need none; rows with
+ *               4096 < L <= 32768 hand one half-transform between two
  *               launches through it (2 * Nfft bytes per row); longer rows go
  *               through the four-step path (8 * Nfft bytes per row).  Either
  *               way rows are processed in batches of at most 1 GiB of
@@ -161,7 +161,7 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when one launch
- * transforms the rows on chip (L <= 8192) or the shape is empty or
+ * transforms the rows on chip (L <= 4096) or the shape is empty or
  * unsupported. */
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                     hyena_dtype_t io);

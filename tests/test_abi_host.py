@@ -132,10 +132,12 @@ def test_fftconv_validation():
         assert f(*a) == want, (idx, val)
     ws = G.lib().hyena_fftconv_workspace_size
     assert ws(1, 4, 1024, 16, G.BF16) == 0                     # on-chip path, no workspace
-    assert ws(1, 4, 8192, 16, G.BF16) == 0
-    # 8192 < L <= 32768: two on-chip launches, the even half's result
+    assert ws(1, 4, 4096, 16, G.BF16) == 0
+    # 4096 < L <= 32768: two on-chip launches, the even half's result
     # (S = 4096 ... 16384 complex fp32 per row) through the workspace, up to
     # 1 GiB of rows
+    assert ws(1, 4, 4097, 16, G.BF16) == 4 * 8 * 4096
+    assert ws(1, 4, 8192, 16, G.BF16) == 4 * 8 * 4096
     assert ws(1, 4, 8193, 16, G.BF16) == 4 * 8 * 8192
     assert ws(1, 4, 16384, 16, G.BF16) == 4 * 8 * 8192
     assert ws(1, 4, 16385, 16, G.BF16) == 4 * 8 * 16384

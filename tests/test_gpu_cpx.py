@@ -125,8 +125,9 @@ def test_decode_cpx_after_prefill(algo, io):
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_cpx_misaligned_rows(io):
     """Complex entry points with activations one element off 16-byte alignment,
-    on chip and four-step, then a decode step from offset single tokens."""
-    for L in (4096, 20000):
+    on chip, in two launches and four-step, then a decode step from offset
+    single tokens."""
+    for L in (4096, 20000, 40000):
         w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=L, B=2 if L < 5000 else 1)
         x1, x2, v = (offset_copy(t) for t in (d.x1, d.x2, d.v))
         assert x1.data_ptr() % 16 != 0

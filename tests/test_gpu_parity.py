@@ -444,8 +444,9 @@ def test_misaligned_rows(io):
         gate(G.fir_fwd(x1, x2, v, taps, d.skip, out=y), ref_f, io, label=f"fir{K} misaligned")
         yw, _ = G.fir_fwd_window(x1, x2, v, taps, d.skip, out=y)
         gate(yw, ref_f, io, label=f"fir{K} window misaligned")
-    # the single pass through the four-step path
-    wl = small(io, D=2, L=20000)
-    dl = DevWorkload(wl)
-    yl = G.fftconv_fwd(*(offset_copy(t) for t in (dl.x1, dl.x2, dl.v)), dl.lam, dl.res, dl.skip)
-    gate(yl, oracle_modal(wl)[0], io, label="fftconv four-step misaligned")
+    # the single pass in two launches (L <= 32768) and through the four-step path
+    for Ll, kind in ((20000, "two-launch"), (40000, "four-step")):
+        wl = small(io, D=2, L=Ll)
+        dl = DevWorkload(wl)
+        yl = G.fftconv_fwd(*(offset_copy(t) for t in (dl.x1, dl.x2, dl.v)), dl.lam, dl.res, dl.skip)
+        gate(yl, oracle_modal(wl)[0], io, label=f"fftconv {kind} misaligned")
