@@ -387,14 +387,20 @@ static hipError_t launch_chunk_s(const ChunkArgs& a, int C, bool vec) {
   return hipGetLastError();
 }
 
+// Threads per row: one wave up to S = 512, then 8 points per thread.  At 16
+// points per thread (S = 1024 ... 4096 on 64 ... 256 threads) the kernel
+// needed all 256 registers and spilled into AGPRs, one wave per SIMD; at 8
+// it fits 166-188 and C = 2048 / 4096 / 8192 at D = 4096, L = 32768 took
+// 1.72 / 1.95 / 2.34 -> 0.89 / 1.18 / 1.57 ms (4 points per thread were
+// slower again, and so was S = 512 on two waves).
 template <typename IO>
 static hipError_t launch_chunk_io(const ChunkArgs& a, int S, int C, bool vec) {
   switch (S) {
     case 256: return launch_chunk_s<256, 64, IO>(a, C, vec);
     case 512: return launch_chunk_s<512, 64, IO>(a, C, vec);
-    case 1024: return launch_chunk_s<1024, 64, IO>(a, C, vec);
-    case 2048: return launch_chunk_s<2048, 128, IO>(a, C, vec);
-    case 4096: return launch_chunk_s<4096, 256, IO>(a, C, vec);
+    case 1024: return launch_chunk_s<1024, 128, IO>(a, C, vec);
+    case 2048: return launch_chunk_s<2048, 256, IO>(a, C, vec);
+    case 4096: return launch_chunk_s<4096, 512, IO>(a, C, vec);
     default: return hipErrorInvalidValue;
   }
 }
