@@ -129,9 +129,9 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
       const int ch = l + 64 * h;
       const uint4 w4 = tout[swz(ch)];
       const int64_t pos = t0 + 8 * ch;
-      if (full) {
+      if (full || (vec && pos < L)) {       // vec: L is a multiple of 8, chunks are whole
         *reinterpret_cast<uint4*>(yr + pos) = w4;
-      } else {
+      } else if (!vec) {
         const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -180,7 +180,34 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
     lds_sync();
     tile(tin_a, static_cast<int64_t>(k) << 10, true);
   }
-  // remaining tokens (and rows that are not 16-byte aligned): bounded loads
+  // remaining tokens: with vec at most one partial tile, staged like a full
+  // one -- L is a multiple of 8, so its 8-token chunks are whole or absent;
+  // chunks at or past L re-read the tile's first chunk (an in-bounds
+  // address) and are then zeroed in LDS, as the bounded loads below would
+  // leave them.  Rows that are not 16-byte aligned take bounded element loads.
+  if (vec && (static_cast<int64_t>(nfull) << 10) < L) {
+    const int64_t t0 = static_cast<int64_t>(nfull) << 10;
+    wait_vmem<0>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = unswz(64 * h + l);
+      const int64_t src = (t0 + 8 * ch < L) ? t0 + 8 * ch : t0;
+      dma16(x1r + src, &tin_a[0][64 * h]);
+      dma16(vr + src, &tin_a[1][64 * h]);
+      dma16(x2r + src, &tin_a[2][64 * h]);
+    }
+    wait_vmem<0>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (t0 + 8 * unswz(64 * h + l) >= L) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a) tin_a[a][64 * h + l] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    lds_sync();
+    tile(tin_a, t0, false);
+    return;
+  }
 #pragma unroll 1
   for (int64_t t0 = static_cast<int64_t>(nfull) << 10; t0 < L; t0 += 1024) {
 #pragma unroll

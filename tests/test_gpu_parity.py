@@ -126,7 +126,8 @@ def test_fir_small(io, K, L):
 
 
 @pytest.mark.parametrize("K", [1, 2, 7, 33, 64, 100, 128])
-@pytest.mark.parametrize("L,B", [(1024, 1), (3000, 2), (4096, 1), (777, 1), (100, 1), (5120, 1)])
+@pytest.mark.parametrize("L,B", [(1024, 1), (3000, 2), (4096, 1), (777, 1), (100, 1), (5120, 1),
+                                 (8, 32), (512, 2), (2056, 1)])
 def test_fir_mfma_cases(K, L, B):
     """bf16 FIR with K <= 128 runs on the matrix cores: every diagonal count
     (1..5), whole tiles, a ragged last tile, rows shorter than a tile, rows not
