@@ -191,6 +191,23 @@ def test_chunk_mfma_partial_tile(L):
         state_gate(s, ref_s, rows, label=f"chunk/mfma L={L}")
 
 
+def test_chunk_mfma_one_tile_rows_many():
+    # one 1024-token chunk per row and more rows than the chip holds waves
+    # at once (2 per SIMD), so later waves start as earlier ones retire;
+    # sampled channels of both batch items, state in and out
+    w = small("bf16", D=3000, L=1024, B=2)
+    d = DevWorkload(w)
+    s0 = W.random_state(w.B, w.D, w.N, seed=11)
+    rows = sample_rows(w.D, k=10)
+    log("chunk/mfma one tile, B=2 D=3000 L=1024")
+    for state in (None, s0):
+        sin = None if state is None else par_to_dev(state)
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, state_in=sin, algo="mfma")
+        ref_y, ref_s = oracle_modal(w, rows, C=1024, state_in=state)
+        gate(y, ref_y, "bf16", rows, label=f"chunk/mfma rows>waves state={'yes' if state is not None else 'no'}")
+        state_gate(s, ref_s, rows, label="chunk/mfma rows>waves")
+
+
 @pytest.mark.parametrize("N", [1, 3, 17, 64])
 def test_mode_counts(N):
     """From one mode to the maximum of 64: single pass, chunked with AUTO (the
