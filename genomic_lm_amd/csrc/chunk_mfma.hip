@@ -514,13 +514,13 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
         lds_sync();
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<uint4*>(yr + t0 + 8 * (l + 64 * h)) = tout[swz(l + 64 * h)];
+          store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
       } else if (staged) {
         lds_sync();
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           if (t0 + 8 * (l + 64 * h) < L)
-            *reinterpret_cast<uint4*>(yr + t0 + 8 * (l + 64 * h)) = tout[swz(l + 64 * h)];
+            store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
       }
     }
   };

@@ -29,6 +29,10 @@ template <typename T> struct Io;
 template <> struct Io<float> {
   static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
   static __device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+  // non-temporal: for outputs that this launch never reads back
+  static __device__ __forceinline__ void st_nt(float* p, int64_t i, float x) {
+    __builtin_nontemporal_store(x, p + i);
+  }
   // two consecutive elements [i, i+1]; requires 8-byte alignment of p + i
   static __device__ __forceinline__ float2 ld2(const float* p, int64_t i) {
     return *reinterpret_cast<const float2*>(p + i);
@@ -41,6 +45,9 @@ template <> struct Io<float> {
 template <> struct Io<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+  static __device__ __forceinline__ void st_nt(bf16_t* p, int64_t i, float x) {
+    __builtin_nontemporal_store(f32_to_bf16(x), p + i);
+  }
   // requires 4-byte alignment of p + i
   static __device__ __forceinline__ float2 ld2(const bf16_t* p, int64_t i) {
     uint32_t w = *reinterpret_cast<const uint32_t*>(p + i);

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
       const uint4 w4 = tout[swz(ch)];
       const int64_t pos = t0 + 8 * ch;
       if (full || (vec && pos < L)) {       // vec: L is a multiple of 8, chunks are whole
-        *reinterpret_cast<uint4*>(yr + pos) = w4;
+        store16_nt(yr + pos, w4);
       } else if (!vec) {
         const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(TM_G) void tm_outputs(
           s[n + 1] = fmaf(pf[n + 1], s[n + 1], u[tt]);
           z1 = fmaf(R[n + 1], s[n + 1], z1);
         }
-        if (live) Io<IO>::st(yb, int64_t(t0 + tt) * D, fmaf(x2[tt], z0 + z1, sk * u[tt]));
+        if (live) Io<IO>::st_nt(yb, int64_t(t0 + tt) * D, fmaf(x2[tt], z0 + z1, sk * u[tt]));
       }
     }
     buf ^= 1;
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(TM_THREADS) void tm_fir(
         zz = z[q];                             // LPC = 1: element q is token q of this channel
       }
       if (i < nt && gbase + ce < D)
-        Io<IO>::st(y, (int64_t(b) * L + t0 + i) * D + gbase + ce, fmaf(x2e[q], zz, ske[q] * ue[q]));
+        Io<IO>::st_nt(y, (int64_t(b) * L + t0 + i) * D + gbase + ce, fmaf(x2e[q], zz, ske[q] * ue[q]));
     }
     buf ^= 1;
   }
