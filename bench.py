@@ -8,6 +8,8 @@ Inputs are resident in HBM before timing starts; consecutive steps take four
 different input sets in turn (and write four outputs), so no step reads data
 an earlier step left in the last-level cache.  The same step repeated on one
 input set is reported beside it as `same_input_set` with --same-input.
+`step_ms` gives the median, min and max of single steps, each timed on its
+own in a separate pass after the headline's timed region.
 
 Prints ONE JSON line.  Besides the headline it reports the roofline of the
 dominant kernel (HIP-event timing of the same launches; HBM bytes and the
@@ -93,6 +95,19 @@ def copy_bandwidth(stream):
     t = timed(lambda: dst.copy_(src), 10, 3, stream)
     del src, dst
     return 2 * n / t / 1e9
+
+
+def per_step_ms(fn, steps, stream):
+    """Each of `steps` calls timed on its own (an event after every call on
+    `stream`): the spread of single steps, beside the headline's average."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
 
 
 def timed(fn, steps, warmup, stream):
@@ -210,6 +225,8 @@ def main():
     # for context (--same-input): the same step repeated on one input set,
     # whose reads then partly hit the last-level cache
     t_same = timed(lambda: head(0), args.steps, 2, stream) if args.same_input else None
+    # single steps of the same rotation, timed after the headline's region
+    spread = per_step_ms(step, args.steps, stream)
 
     tc = B * D * L
     alg_bytes = 8 * tc                       # x1, x2, v read + y written, bf16
@@ -330,6 +347,8 @@ def main():
         "hbm_copy": {"measured_GBps": round(copy_gbs, 1),
                      "frac": round(achieved / copy_gbs, 4)},
         "wall_s_timed": round(t_wall, 3),
+        "step_ms": {"median": round(spread[len(spread) // 2], 4), "min": round(spread[0], 4),
+                    "max": round(spread[-1], 4), "n": len(spread)},
         "components": comps,
     }
     if t_same is not None:
