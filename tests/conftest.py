@@ -8,4 +8,4 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: full-size case, minutes on the GPU box")
+    config.addinivalue_line("markers", "slow: full-size case, minutes on the GPU")
