@@ -20,6 +20,7 @@
 #include "common.hpp"
 #include "fft.hpp"
 #include "launch.hpp"
+#include "pow_pair.hpp"
 
 namespace hyena {
 
@@ -122,22 +123,27 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   // thread's anchors of the carried-term ladder p^(2t+1) and of the
   // state-weight ladder p^(2T-2-2t).  Partial chunks recompute theirs.
   __shared__ float s_p[W * CHUNK_MAXN], s_step[W * CHUNK_MAXN], s_pf[W * CHUNK_MAXN];
+  __shared__ float s_pfl[W * CHUNK_MAXN];       // p^(2S) = s_pf + s_pfl (pow_pair)
   constexpr bool TAB = (T == 64);
   __shared__ float t_ea[TAB ? CHUNK_NG * T : 1], t_wa[TAB ? CHUNK_NG * T : 1];
   const bool use_tab = TAB && NR <= CHUNK_NG;
   for (int n = t; n < N; n += T) {
     if constexpr (CPX) {
       const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
-      const float2 p = cexp_at(md, 1.0f), st = cexp_at(md, static_cast<float>(2 * T)),
-                   pf = cexp_at(md, static_cast<float>(2 * S));
+      const float2 p = cexp_at(md, 1.0f), st = cexp_at(md, static_cast<float>(2 * T));
+      float2 pfl;
+      const float2 pf = cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(2 * S), pfl);
       s_p[2 * n] = p.x;     s_p[2 * n + 1] = p.y;
       s_step[2 * n] = st.x; s_step[2 * n + 1] = st.y;
       s_pf[2 * n] = pf.x;   s_pf[2 * n + 1] = pf.y;
+      s_pfl[2 * n] = pfl.x; s_pfl[2 * n + 1] = pfl.y;
     } else {
       const float l = s_lam[n];
       s_p[n] = expf(l);
       s_step[n] = expf(l * static_cast<float>(2 * T));
-      s_pf[n] = expf(l * static_cast<float>(2 * S));
+      const float2 pf = pow_pair(l, static_cast<float>(2 * S));
+      s_pf[n] = pf.x;
+      s_pfl[n] = pf.y;
     }
   }
   if (use_tab) {
@@ -320,17 +326,21 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         if constexpr (CPX) {
           s_tot[n] = tot;                  // the complex update needs both slots
         } else {
-          const float pc = full ? s_pf[n] : expf(s_lam[n] * static_cast<float>(Cp));
-          s_st[n] = fmaf(pc, s_st[n], tot);
+          const float2 pc = full ? make_float2(s_pf[n], s_pfl[n])
+                                 : pow_pair(s_lam[n], static_cast<float>(Cp));
+          s_st[n] = fmaf(pc.x, s_st[n], fmaf(pc.y, s_st[n], tot));
         }
       }
       __syncthreads();                     // red reusable
     }
     if constexpr (CPX) {
       for (int n = t; n < N; n += T) {
-        const float2 pc = full ? make_float2(s_pf[2 * n], s_pf[2 * n + 1])
-                               : cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
-        const float2 sn = cadd(cmul(pc, make_float2(s_st[2 * n], s_st[2 * n + 1])),
+        float2 pl;
+        const float2 ph = full ? (pl = make_float2(s_pfl[2 * n], s_pfl[2 * n + 1]),
+                                  make_float2(s_pf[2 * n], s_pf[2 * n + 1]))
+                               : cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(Cp), pl);
+        const float2 so = make_float2(s_st[2 * n], s_st[2 * n + 1]);
+        const float2 sn = cadd(cadd(cmul(ph, so), cmul(pl, so)),
                                make_float2(s_tot[2 * n], s_tot[2 * n + 1]));
         s_st[2 * n] = sn.x;
         s_st[2 * n + 1] = sn.y;

@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "pow_pair.hpp"
 #include "launch.hpp"
 
 namespace hyena {
@@ -46,15 +47,20 @@ __global__ __launch_bounds__(256) void modal_decode_kernel(
     const int64_t si = row * N + n;
     // read before write: state_out may be state_in
     if constexpr (CPX) {
-      const float2 p = cexp_at(cpx_mode(lam[2 * pi], lam[2 * pi + 1]), 1.0f);
+      // the pole as hi + lo: decode steps compound its rounding (pow_pair.hpp)
+      float2 pl;
+      const float2 ph = cpow_pair(lam[2 * pi], lam[2 * pi + 1], 1.0f, pl);
       const float2 s0 = state_in ? make_float2(state_in[2 * si], state_in[2 * si + 1])
                                  : make_float2(0.0f, 0.0f);
-      const float2 s = make_float2(cmul(p, s0).x + u, cmul(p, s0).y);
+      const float2 ps = cadd(cmul(ph, s0), cmul(pl, s0));
+      const float2 s = make_float2(ps.x + u, ps.y);
       state_out[2 * si] = s.x;
       state_out[2 * si + 1] = s.y;
       part = fmaf(res[2 * pi], s.x, -res[2 * pi + 1] * s.y);
     } else {
-      const float s = fmaf(expf(lam[pi]), state_in ? state_in[si] : 0.0f, u);
+      const float2 p = pow_pair(lam[pi], 1.0f);        // hi + lo (pow_pair.hpp)
+      const float s0 = state_in ? state_in[si] : 0.0f;
+      const float s = fmaf(p.x, s0, fmaf(p.y, s0, u));
       state_out[si] = s;
       part = res[pi] * s;
     }

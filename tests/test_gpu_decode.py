@@ -55,6 +55,40 @@ def test_modal_decode_step(io, N):
         s_dev = s1
 
 
+# Thousands of one-token steps: the state is decayed once per step, so a
+# rounding bias in the decay factor compounds over a slow mode's memory
+# (|lam| ~ 1e-3 keeps a token for thousands of steps).  With the pole as an
+# fp32 pair the per-element error stays at the output's own rounding; with a
+# single fp32 pole a CPU emulation of 4000 steps drifts to ~8e-5 of the rms,
+# which the per-element gate (floor 1e-3 of the rms) would read as ~0.08.
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_long_run(io):
+    w = _wl(io, D=8, L=4096, B=1)
+    d = DevWorkload(w)
+    log(f"decode long run io={io} L={w.L}")
+    s = torch.zeros((w.B, w.D, w.N), dtype=torch.float32, device=d.x1.device)
+    y = torch.empty_like(d.x1)
+    for t in range(w.L):
+        yt, s = G.modal_decode(_tok(d.x1, t), _tok(d.x2, t), _tok(d.v, t), d.lam, d.res, d.skip,
+                               state_in=s, state_out=s)
+        y[..., t] = yt
+    ref, ref_s = oracle_modal(w)
+    gate(y, ref, io, label="decode x4096")
+    state_gate(s, ref_s, label="decode x4096", tol=1e-5)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_chunk_fft_one_token_chunks(io):
+    # the FFT chunk algorithm with C = 1: one decay of the carried state per token
+    w = _wl(io, D=8, L=4096, B=1)
+    d = DevWorkload(w)
+    log(f"chunk/fft C=1 io={io} L={w.L}")
+    y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1, d.skip, algo="fft")
+    ref, ref_s = oracle_modal(w)
+    gate(y, ref, io, label="chunk/fft C=1")
+    state_gate(s, ref_s, label="chunk/fft C=1", tol=1e-5)
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", ["mfma", "fft"])
 def test_decode_after_prefill(io, algo):
