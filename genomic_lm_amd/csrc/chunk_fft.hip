@@ -26,6 +26,12 @@ namespace hyena {
 
 constexpr int CHUNK_MAXN = 64;
 constexpr int CHUNK_NG = 16;             // modes per reduction group
+// Chunks up to this length decay the state by the pole power as an fp32 pair
+// (pow_pair.hpp): there a slow mode's memory spans many chunks, and a single
+// fp32 factor's rounding would compound over them.  Longer chunks decay it a
+// few dozen times per 32k tokens, where that bias is ~1e-6, and take the fp32
+// factor, whose fp64 pair would cost ~5 % of the complex kernel's time.
+constexpr int CHUNK_PAIR_MAX_C = 256;
 
 // CPX: complex modes, lam and res as (re, im) pairs, complex state (B, D, N)
 // as (re, im) pairs; h = Re sum_n R_n exp(lam_n t) and the carried term is
@@ -118,12 +124,12 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     if (q == 0 && t == 0) h_nyq = a[0].x - a[0].y;
   }
 
-  // ---- chunk-invariant mode factors, once per row: p, p^(2T) and the full
-  // chunk's p^(2S) per mode, and (one wave per row, up to 16 real slots) each
-  // thread's anchors of the carried-term ladder p^(2t+1) and of the
-  // state-weight ladder p^(2T-2-2t).  Partial chunks recompute theirs.
-  __shared__ float s_p[W * CHUNK_MAXN], s_step[W * CHUNK_MAXN], s_pf[W * CHUNK_MAXN];
-  __shared__ float s_pfl[W * CHUNK_MAXN];       // p^(2S) = s_pf + s_pfl (pow_pair)
+  // ---- chunk-invariant mode factors, once per row: p, p^(2T), and (one
+  // wave per row, up to 16 real slots) each thread's anchors of the
+  // carried-term ladder p^(2t+1) and of the state-weight ladder
+  // p^(2T-2-2t).  Partial chunks recompute the ladders' weights.
+  __shared__ float s_p[W * CHUNK_MAXN], s_step[W * CHUNK_MAXN];
+  __shared__ float s_pc[W * CHUNK_MAXN];         // p^C, the fp32 decay of a whole chunk
   constexpr bool TAB = (T == 64);
   __shared__ float t_ea[TAB ? CHUNK_NG * T : 1], t_wa[TAB ? CHUNK_NG * T : 1];
   const bool use_tab = TAB && NR <= CHUNK_NG;
@@ -131,19 +137,15 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     if constexpr (CPX) {
       const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
       const float2 p = cexp_at(md, 1.0f), st = cexp_at(md, static_cast<float>(2 * T));
-      float2 pfl;
-      const float2 pf = cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(2 * S), pfl);
+      const float2 pc = cexp_at(md, static_cast<float>(C));
       s_p[2 * n] = p.x;     s_p[2 * n + 1] = p.y;
+      s_pc[2 * n] = pc.x;   s_pc[2 * n + 1] = pc.y;
       s_step[2 * n] = st.x; s_step[2 * n + 1] = st.y;
-      s_pf[2 * n] = pf.x;   s_pf[2 * n + 1] = pf.y;
-      s_pfl[2 * n] = pfl.x; s_pfl[2 * n + 1] = pfl.y;
     } else {
       const float l = s_lam[n];
       s_p[n] = expf(l);
       s_step[n] = expf(l * static_cast<float>(2 * T));
-      const float2 pf = pow_pair(l, static_cast<float>(2 * S));
-      s_pf[n] = pf.x;
-      s_pfl[n] = pf.y;
+      s_pc[n] = expf(l * static_cast<float>(C));
     }
   }
   if (use_tab) {
@@ -326,8 +328,11 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         if constexpr (CPX) {
           s_tot[n] = tot;                  // the complex update needs both slots
         } else {
-          const float2 pc = full ? make_float2(s_pf[n], s_pfl[n])
-                                 : pow_pair(s_lam[n], static_cast<float>(Cp));
+          // made here: kept per row in LDS the pairs would cost a workgroup per CU
+          const float2 pc = (C <= CHUNK_PAIR_MAX_C)
+                                ? pow_pair(s_lam[n], static_cast<float>(Cp))
+                                : make_float2(Cp == C ? s_pc[n] : expf(s_lam[n] * static_cast<float>(Cp)),
+                                              0.0f);
           s_st[n] = fmaf(pc.x, s_st[n], fmaf(pc.y, s_st[n], tot));
         }
       }
@@ -335,10 +340,13 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     }
     if constexpr (CPX) {
       for (int n = t; n < N; n += T) {
-        float2 pl;
-        const float2 ph = full ? (pl = make_float2(s_pfl[2 * n], s_pfl[2 * n + 1]),
-                                  make_float2(s_pf[2 * n], s_pf[2 * n + 1]))
-                               : cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(Cp), pl);
+        float2 ph, pl = make_float2(0.0f, 0.0f);
+        if (C <= CHUNK_PAIR_MAX_C)
+          ph = cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(Cp), pl);
+        else if (Cp == C)
+          ph = make_float2(s_pc[2 * n], s_pc[2 * n + 1]);
+        else
+          ph = cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
         const float2 so = make_float2(s_st[2 * n], s_st[2 * n + 1]);
         const float2 sn = cadd(cadd(cmul(ph, so), cmul(pl, so)),
                                make_float2(s_tot[2 * n], s_tot[2 * n + 1]));
