@@ -152,8 +152,11 @@ def test_fir_mfma_fp32_taps(K):
 
 
 # ------------------------------------------------------------------ chunked
-CHUNK_CASES = [(1, 50), (7, 300), (64, 1000), (128, 1024), (1000, 4096), (1024, 3000),
-               (1024, 5000), (4096, 8192), (8192, 8192), (2048, 1500)]
+# (256, 3000) and (257, 3000): the FFT chunk algorithm's last chunk length
+# with the state decayed by an fp32 pair, and the first with one fp32 factor
+CHUNK_CASES = [(1, 50), (7, 300), (64, 1000), (128, 1024), (256, 3000), (257, 3000),
+               (1000, 4096), (1024, 3000), (1024, 5000), (4096, 8192), (8192, 8192),
+               (2048, 1500)]
 
 
 @pytest.mark.parametrize("algo", ["mfma", "fft"])
