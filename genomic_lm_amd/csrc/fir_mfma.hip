@@ -150,7 +150,11 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
     lds_sync();
   };
 
+  // Issued at raised wave priority, as in the chunk kernel: FIR-128 at
+  // D = 4096, L = 32768 went from 203.8-205.2 to 196.6-197.2 us (three
+  // alternating measurements, rotating inputs), FIR-7 stayed at ~204 us.
   auto prefetch = [&](int64_t t0, uint4 (*tin)[128]) {
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ch = unswz(64 * h + l);
@@ -158,6 +162,7 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
       dma16(vr + t0 + 8 * ch, &tin[1][64 * h]);
       dma16(x2r + t0 + 8 * ch, &tin[2][64 * h]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int nfull = vec ? (L >> 10) : 0;
