@@ -515,13 +515,10 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
           if (pos + e < L) Io<IO>::st(yr, pos + e, o[e]);
       }
     }
+    // bf16 full tiles leave y staged in tout; flush_y stores it once the
+    // next tile's DMA has been waited for (below)
     if constexpr (sizeof(IO) == 2) {
-      if (full) {
-        lds_sync();
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
-      } else if (staged) {
+      if (!full && staged) {
         lds_sync();
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -529,6 +526,14 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
             store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
       }
     }
+  };
+
+  // y of the full bf16 tile starting at t0, staged in tout by tile(): 16-byte
+  // coalesced non-temporal stores
+  auto flush_y = [&](int64_t t0) {
+    lds_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
   };
 
   // ---- full tiles, the next one in flight while the current one computes
@@ -539,22 +544,22 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     const TileIn<IO> none{};
     // Two tiles in flight: tile k is read out of its buffer at the top of
     // its computation, and the buffer is refilled at once with tile k + 2.
-    // vmcnt retires in issue order, so waiting for tile k means allowing
-    // the operations issued after its DMA to stay in flight: the y stores of
-    // tiles k-2 and k-1 (2 each) and the DMA of tile k+1 (6), where they
-    // exist.  Tiles 0 and 1 were issued before the constant setup.
+    // The waits assume only that one wave's LDS-DMA loads complete in the
+    // order they were issued (the property AMD's ck_tile async pipelines
+    // rely on when they wait with vmcnt(n) for all but the n DMA loads
+    // issued last), and nothing about stores against loads: each counts the
+    // DMA loads issued after tile k's (those of tile k + 1, 6 per lane,
+    // when it exists).  Any store issued before them must then have
+    // completed too, so y of tile k - 1 is stored only after tile k's wait
+    // (flush_y), a whole tile after it was issued rather than just before.
+    // Tiles 0 and 1 were issued before the constant setup.
     int k = 0;
 #pragma unroll 1
     for (; k + 1 < nfull; k += 2) {
       const int64_t t0 = static_cast<int64_t>(k) << 10;
-      if (k == 0) {
-        wait_vmem<6>();                   // nfull > 1 here: DMA(1) may fly
-      } else if (k + 1 < nfull) {
-        wait_vmem<10>();
-      } else {
-        wait_vmem<4>();
-      }
+      wait_vmem<6>();                     // tile k + 1 < nfull may still fly
       lds_sync();                         // tile k in tin_a
+      if (k > 0) flush_y(t0 - 1024);
       {
         bf16x8 um[NU][2];
         tile(none, t0, true, um, tin_a, true, [&] {
@@ -562,12 +567,9 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
           if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
         });
       }
-      if (k + 2 < nfull) {
-        if (k == 0) wait_vmem<8>(); else wait_vmem<10>();
-      } else {
-        if (k == 0) wait_vmem<2>(); else wait_vmem<4>();
-      }
+      if (k + 2 < nfull) wait_vmem<6>(); else wait_vmem<0>();
       lds_sync();                         // tile k+1 in tin_b
+      flush_y(t0);
       {
         bf16x8 um[NU][2];
         tile(none, t0 + 1024, true, um, tin_b, true, [&] {
@@ -577,11 +579,13 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       }
     }
     if (k < nfull) {
-      if (k == 0) wait_vmem<0>(); else wait_vmem<4>();
+      wait_vmem<0>();
       lds_sync();
+      if (k > 0) flush_y((static_cast<int64_t>(k) << 10) - 1024);
       bf16x8 um[NU][2];
       tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true, [] {});
     }
+    if (nfull > 0) flush_y(static_cast<int64_t>(nfull - 1) << 10);
   } else {
     TileIn<IO> ta, tb;
     if (nfull > 0) ta.load(x1r, vr, x2r, lane_off);

@@ -124,12 +124,14 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
       reinterpret_cast<uint2*>(&tout[slot])[hf] = make_uint2(cvt2(o0, o1), cvt2(o2, o3));
     }
     lds_sync();
+    // full tiles leave y staged over tin[0]; flush_y stores it after the
+    // next tile's DMA wait
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2 && !full; ++h) {
       const int ch = l + 64 * h;
       const uint4 w4 = tout[swz(ch)];
       const int64_t pos = t0 + 8 * ch;
-      if (full || (vec && pos < L)) {       // vec: L is a multiple of 8, chunks are whole
+      if (vec && pos < L) {                 // vec: L is a multiple of 8, chunks are whole
         store16_nt(yr + pos, w4);
       } else if (!vec) {
         const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
@@ -165,26 +167,43 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // y of the full tile at t0, staged over tin[0] of its buffer
+  auto flush_y = [&](uint4 (*tin)[128], int64_t t0) {
+    lds_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) store16_nt(yr + t0 + 8 * (l + 64 * h), tin[0][swz(l + 64 * h)]);
+    lds_sync();                               // read out before the buffer is refilled
+  };
+
+  // One tile in flight: tile k + 1 is issued once tile k has arrived and
+  // tile k - 1's y has left its buffer.  When tile k is waited for, no DMA
+  // was issued after it, so the wait is vmcnt(0), and y of tile k - 1 is
+  // stored only after that wait: the stores it covers were issued a tile
+  // earlier.  No ordering between loads and stores is assumed.
   const int nfull = vec ? (L >> 10) : 0;
   if (nfull > 0) prefetch(0, tin_a);
   int k = 0;
 #pragma unroll 1
   for (; k + 1 < nfull; k += 2) {
     const int64_t t0 = static_cast<int64_t>(k) << 10;
-    if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
+    wait_vmem<0>();
     lds_sync();
+    if (k > 0) flush_y(tin_b, t0 - 1024);
     prefetch(t0 + 1024, tin_b);
     tile(tin_a, t0, true);
-    wait_vmem<2>();
+    wait_vmem<0>();
     lds_sync();
+    flush_y(tin_a, t0);
     if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
     tile(tin_b, t0 + 1024, true);
   }
   if (k < nfull) {
-    if (k == 0) wait_vmem<0>(); else wait_vmem<2>();
+    wait_vmem<0>();
     lds_sync();
+    if (k > 0) flush_y(tin_b, (static_cast<int64_t>(k) << 10) - 1024);
     tile(tin_a, static_cast<int64_t>(k) << 10, true);
   }
+  if (nfull > 0) flush_y((nfull & 1) ? tin_a : tin_b, static_cast<int64_t>(nfull - 1) << 10);
   // remaining tokens: with vec at most one partial tile, staged like a full
   // one -- L is a multiple of 8, so its 8-token chunks are whole or absent;
   // chunks at or past L re-read the tile's first chunk (an in-bounds

@@ -224,8 +224,13 @@ __device__ __forceinline__ void read_staged_runs(const uint4 (*tin)[128], int i3
 }
 
 // Wait until at most N vector memory operations of this wave are
-// outstanding.  They retire in issue order, so this waits for everything
-// issued before the last N.  (s_waitcnt simm16 on gfx9: vmcnt[3:0] in bits
+// outstanding.  The callers pass N = the number of LDS-DMA loads issued after
+// the one they wait for and rely only on DMA loads of one wave completing in
+// issue order; stores may be outstanding or not, either way the wait holds.
+// (The compiler's own wait insertion for gfx950 counts plain loads and
+// stores as one in-order stream but falls back to vmcnt(0) while an LDS DMA
+// is pending, so no ordering between DMAs and stores is assumed here.)
+// (s_waitcnt simm16 on gfx9: vmcnt[3:0] in bits
 // 3:0, expcnt in bits 6:4, lgkmcnt in bits 11:8, vmcnt[5:4] in bits 15:14;
 // expcnt and lgkmcnt are left free.)
 template <int N>
