@@ -12,6 +12,7 @@ Entry points (names follow the C ABI):
   fftconv_fwd(x1, x2, v, log_poles, residues, skip=None)    -> y
   chunk_fwd(x1, x2, v, log_poles, residues, C, skip=None,
             state_in=None, algo="auto")                      -> (y, state_out)
+            (algo "auto" calls hyena_chunk_fwd, "fft" / "mfma" hyena_chunk_fwd_algo)
   modal_decode(x1, x2, v, log_poles, residues, skip=None,
                state_in=None)       (x of shape (B, D))       -> (y, state_out)
   fir_fwd_window(x1, x2, v, taps, skip=None, window_in=None) -> (y, window_out)
@@ -22,6 +23,10 @@ Entry points (names follow the C ABI):
 Complex-pole variants (log_poles / residues complex64 (D, N), states
 complex64 (B, D, N)): modal_filter_cpx, fftconv_fwd_cpx, chunk_fwd_cpx,
 modal_decode_cpx.
+
+Every function is also available under the C name (hyena_fftconv_fwd, ...),
+and the submodule hyena_op gives the four core calls the short names
+fftconv, fir, chunk and modal_filter.
 """
 from __future__ import annotations
 
@@ -61,7 +66,9 @@ EXPORTS = {
                                  _p, _size, _p]),
     "hyena_fftconv_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
     "hyena_chunk_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
-                               _i64, _int, _int, _p]),
+                               _i64, _int, _p]),
+    "hyena_chunk_fwd_algo": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
+                                    _i64, _int, _int, _p]),
     "hyena_modal_decode": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _int,
                                   _p]),
     "hyena_fir_fwd_window": (_int, [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
@@ -70,7 +77,9 @@ EXPORTS = {
     "hyena_fftconv_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
                                      _p, _size, _p]),
     "hyena_chunk_fwd_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
-                                   _i64, _int, _int, _p]),
+                                   _i64, _int, _p]),
+    "hyena_chunk_fwd_cpx_algo": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64,
+                                        _i64, _i64, _int, _int, _p]),
     "hyena_modal_decode_cpx": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64,
                                       _int, _p]),
     "hyena_chunk_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
@@ -243,10 +252,12 @@ def chunk_fwd(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
         state_out = torch.empty((B, D, N), dtype=torch.float32, device=x1.device)
     else:
         _param("state_out", state_out, (B, D, N), x1.device)
-    _check("hyena_chunk_fwd", lib().hyena_chunk_fwd(
-        _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip),
-        _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, int(C), _io(x1), ALGOS[algo],
-        _stream(x1)))
+    args = (_ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip),
+            _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, int(C), _io(x1))
+    if algo == "auto":
+        _check("hyena_chunk_fwd", lib().hyena_chunk_fwd(*args, _stream(x1)))
+    else:
+        _check("hyena_chunk_fwd_algo", lib().hyena_chunk_fwd_algo(*args, ALGOS[algo], _stream(x1)))
     return y, state_out
 
 
@@ -389,9 +400,13 @@ def chunk_fwd_cpx(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=No
     if state_out is None:
         state_out = torch.empty((B, D, N), dtype=torch.complex64, device=x1.device)
     so = _cstate("state_out", state_out, (B, D, N), x1.device)
-    _check("hyena_chunk_fwd_cpx", lib().hyena_chunk_fwd_cpx(
-        _ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
-        _ptr(y), B, D, L, int(C), _io(x1), ALGOS[algo], _stream(x1)))
+    args = (_ptr(x1), _ptr(x2), _ptr(v), _ptr(lp), _ptr(rs), N, _ptr(skip), _ptr(si), _ptr(so),
+            _ptr(y), B, D, L, int(C), _io(x1))
+    if algo == "auto":
+        _check("hyena_chunk_fwd_cpx", lib().hyena_chunk_fwd_cpx(*args, _stream(x1)))
+    else:
+        _check("hyena_chunk_fwd_cpx_algo",
+               lib().hyena_chunk_fwd_cpx_algo(*args, ALGOS[algo], _stream(x1)))
     return y, state_out
 
 
@@ -488,3 +503,25 @@ def fir_fwd_tokmajor(xin, taps, skip=None, window_in=None, pos=(0, 1, 2), out=No
         _ptr(xin), int(pos[0]), int(pos[1]), int(pos[2]), _ptr(taps), K, _ptr(skip),
         _ptr(window_in), _ptr(window_out), _ptr(y), B, D, L, _io(xin), _stream(xin)))
     return y, window_out
+
+
+# The same functions under the names of the C entry points they call
+# (chunk_fwd / chunk_fwd_cpx call the *_algo entry point when algo is not
+# "auto").
+hyena_modal_filter = modal_filter
+hyena_fir_fwd = fir_fwd
+hyena_fftconv_fwd = fftconv_fwd
+hyena_fftconv_workspace_size = fftconv_workspace_size
+hyena_chunk_fwd = chunk_fwd
+hyena_modal_decode = modal_decode
+hyena_fir_fwd_window = fir_fwd_window
+hyena_modal_filter_cpx = modal_filter_cpx
+hyena_fftconv_fwd_cpx = fftconv_fwd_cpx
+hyena_chunk_fwd_cpx = chunk_fwd_cpx
+hyena_modal_decode_cpx = modal_decode_cpx
+hyena_chunk_fwd_tokmajor = chunk_fwd_tokmajor
+hyena_chunk_tokmajor_workspace_size = chunk_tokmajor_workspace_size
+hyena_fir_fwd_tokmajor = fir_fwd_tokmajor
+__all__ += [n for n in list(globals()) if n.startswith("hyena_") and callable(globals()[n])]
+
+from . import hyena_op  # noqa: E402,F401  (short names of the four core calls)

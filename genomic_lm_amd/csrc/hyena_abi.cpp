@@ -47,8 +47,6 @@ hyena_status_t check_modal(const float* lam, const float* res, int64_t N, const 
   return HYENA_OK;
 }
 
-hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
-
 int64_t next_pow2(int64_t x) {
   int64_t p = 1;
   while (p < x) p <<= 1;
@@ -59,7 +57,7 @@ int64_t next_pow2(int64_t x) {
 // share them (cpx: parameters and states as (re, im) pairs)
 
 hyena_status_t modal_filter_impl(const float* log_poles, const float* residues, int64_t D,
-                                 int64_t N, int64_t L, float* h, bool cpx, void* stream) {
+                                 int64_t N, int64_t L, float* h, bool cpx, hipStream_t stream) {
   if (D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
   if (N < 1 || N > HYENA_MAX_MODES) return HYENA_ERR_INVALID_ARG;
   if (D == 0 || L == 0) return HYENA_OK;
@@ -70,14 +68,14 @@ hyena_status_t modal_filter_impl(const float* log_poles, const float* residues, 
     return HYENA_ERR_UNSUPPORTED;
   return from_hip(hyena::launch_modal_filter(log_poles, residues, static_cast<int>(D),
                                              static_cast<int>(N), static_cast<int>(L), h,
-                                             cpx, as_stream(stream)));
+                                             cpx, stream));
 }
 
 hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
                            const float* log_poles, const float* residues, int64_t N,
                            const float* skip, const float* state_in, float* state_out,
                            void* y, int64_t B, int64_t D, hyena_dtype_t io, bool cpx,
-                           void* stream) {
+                           hipStream_t stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, 1, io, &empty);
   if (st != HYENA_OK) return st;
@@ -89,7 +87,7 @@ hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
     return HYENA_ERR_INVALID_ARG;
   hyena::DecodeArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                       state_out, y, static_cast<int>(B), static_cast<int>(D),
-                      io == HYENA_BF16, as_stream(stream), cpx};
+                      io == HYENA_BF16, stream, cpx};
   return from_hip(hyena::launch_modal_decode(a));
 }
 
@@ -97,7 +95,7 @@ hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
                             const float* log_poles, const float* residues, int64_t N,
                             const float* skip, void* y, int64_t B, int64_t D, int64_t L,
                             hyena_dtype_t io, void* workspace, size_t ws_bytes, bool cpx,
-                            void* stream) {
+                            hipStream_t stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
   if (st != HYENA_OK) return st;
@@ -108,7 +106,7 @@ hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
   if (st != HYENA_OK) return st;
   hyena::FftconvArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, y,
                        static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
-                       io == HYENA_BF16, workspace, ws_bytes, as_stream(stream), cpx};
+                       io == HYENA_BF16, workspace, ws_bytes, stream, cpx};
   if (hyena::fftconv_onchip_S(L) != 0) {
     const size_t need = hyena::fftconv_onchip_workspace(B, D, L);
     if (need > 0 && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
@@ -125,7 +123,7 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
                           const float* log_poles, const float* residues, int64_t N,
                           const float* skip, const float* state_in, float* state_out,
                           void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                          hyena_dtype_t io, hyena_chunk_algo_t algo, bool cpx, void* stream) {
+                          hyena_dtype_t io, hyena_chunk_algo_t algo, bool cpx, hipStream_t stream) {
   if (algo != HYENA_CHUNK_AUTO && algo != HYENA_CHUNK_FFT && algo != HYENA_CHUNK_MFMA)
     return HYENA_ERR_INVALID_ARG;
   bool empty = false;
@@ -138,7 +136,7 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
       return HYENA_ERR_INVALID_ARG;
     if (B * D > kMaxInt) return HYENA_ERR_UNSUPPORTED;
     return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N * (cpx ? 2 : 1),
-                                             as_stream(stream)));
+                                             stream));
   }
   if (st != HYENA_OK) return st;
   if (C < 1) return HYENA_ERR_INVALID_ARG;
@@ -157,7 +155,7 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
   hyena::ChunkArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                      state_out, y, static_cast<int>(B), static_cast<int>(D),
                      static_cast<int>(L), static_cast<int>(Ceff), io == HYENA_BF16,
-                     as_stream(stream), cpx};
+                     stream, cpx};
   return from_hip(use == HYENA_CHUNK_MFMA ? hyena::launch_chunk_mfma(a) : hyena::launch_chunk_fft(a));
 }
 
@@ -166,7 +164,7 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
                                    int64_t N, const float* skip, const float* state_in,
                                    float* state_out, void* y, int64_t B, int64_t D, int64_t L,
                                    hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                   void* stream) {
+                                   hipStream_t stream) {
   if (!valid_io(io) || B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
   const bool perm = pos_x1 >= 0 && pos_x2 >= 0 && pos_v >= 0 && pos_x1 < 3 && pos_x2 < 3 &&
                     pos_v < 3 && pos_x1 != pos_x2 && pos_x1 != pos_v && pos_x2 != pos_v;
@@ -177,7 +175,7 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
   if (!state_out || !aligned_to(state_out, 4) || (state_in && !aligned_to(state_in, 4)))
     return HYENA_ERR_INVALID_ARG;
   if (L == 0)   // no token: the state passes through unchanged
-    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N, as_stream(stream)));
+    return from_hip(hyena::launch_state_copy(state_in, state_out, B * D * N, stream));
   if (B * D > std::numeric_limits<int64_t>::max() / (3 * L)) return HYENA_ERR_UNSUPPORTED;
   const size_t a = io_size(io);
   if (!xin || !y || !aligned_to(xin, a) || !aligned_to(y, a)) return HYENA_ERR_INVALID_ARG;
@@ -189,14 +187,14 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
   hyena::TokmajorArgs args{xin, pos_x1, pos_x2, pos_v, log_poles, residues,
                            static_cast<int>(N), skip, state_in, state_out, y,
                            static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
-                           io == HYENA_BF16, workspace, as_stream(stream)};
+                           io == HYENA_BF16, workspace, stream};
   return from_hip(hyena::launch_tokmajor(args));
 }
 
 hyena_status_t fir_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_x2, int32_t pos_v,
                                  const float* taps, int64_t K, const float* skip,
                                  const float* window_in, float* window_out, void* y, int64_t B,
-                                 int64_t D, int64_t L, hyena_dtype_t io, void* stream) {
+                                 int64_t D, int64_t L, hyena_dtype_t io, hipStream_t stream) {
   if (!valid_io(io) || B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
   const bool perm = pos_x1 >= 0 && pos_x2 >= 0 && pos_v >= 0 && pos_x1 < 3 && pos_x2 < 3 &&
                     pos_v < 3 && pos_x1 != pos_x2 && pos_x1 != pos_v && pos_x2 != pos_v;
@@ -215,7 +213,7 @@ hyena_status_t fir_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_x2
   hyena::TokmajorFirArgs args{xin, pos_x1, pos_x2, pos_v, taps, static_cast<int>(K), skip,
                               window_in, window_out, y, static_cast<int>(B),
                               static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16,
-                              as_stream(stream)};
+                              stream};
   return from_hip(hyena::launch_tokmajor_fir(args));
 }
 
@@ -237,13 +235,13 @@ const char* hyena_status_string(hyena_status_t status) {
 }
 
 hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues, int64_t D,
-                                  int64_t N, int64_t L, float* h, void* stream) {
+                                  int64_t N, int64_t L, float* h, hipStream_t stream) {
   return modal_filter_impl(log_poles, residues, D, N, L, h, false, stream);
 }
 
 hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, const float* taps,
                              int64_t K, const float* skip, void* y, int64_t B, int64_t D,
-                             int64_t L, hyena_dtype_t io, void* stream) {
+                             int64_t L, hyena_dtype_t io, hipStream_t stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
   if (st != HYENA_OK) return st;
@@ -253,7 +251,7 @@ hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v, cons
   if (!taps || !aligned_to(taps, 4) || (skip && !aligned_to(skip, 4))) return HYENA_ERR_INVALID_ARG;
   if (B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;   // grid.y
   hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
-                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, stream};
   return from_hip(hyena::launch_fir(a));
 }
 
@@ -261,7 +259,7 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  const float* log_poles, const float* residues, int64_t N,
                                  const float* skip, void* y, int64_t B, int64_t D, int64_t L,
                                  hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+                                 hipStream_t stream) {
   return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
                       ws_bytes, false, stream);
 }
@@ -279,7 +277,17 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
                                const float* log_poles, const float* residues, int64_t N,
                                const float* skip, const float* state_in, float* state_out,
                                void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                               hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
+                               hyena_dtype_t io, hipStream_t stream) {
+  return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
+                    C, io, HYENA_CHUNK_AUTO, false, stream);
+}
+
+hyena_status_t hyena_chunk_fwd_algo(const void* x1, const void* x2, const void* v,
+                                    const float* log_poles, const float* residues, int64_t N,
+                                    const float* skip, const float* state_in, float* state_out,
+                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                                    hyena_dtype_t io, hyena_chunk_algo_t algo,
+                                    hipStream_t stream) {
   return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
                     C, io, algo, false, stream);
 }
@@ -288,7 +296,7 @@ hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
                                   const float* log_poles, const float* residues, int64_t N,
                                   const float* skip, const float* state_in, float* state_out,
                                   void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                  void* stream) {
+                                  hipStream_t stream) {
   return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
                      false, stream);
 }
@@ -297,7 +305,7 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
                                     const float* taps, int64_t K, const float* skip,
                                     const float* window_in, float* window_out, void* y,
                                     int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                    void* stream) {
+                                    hipStream_t stream) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
   // L = 0 still moves the window over; only B = 0 or D = 0 is a no-op
@@ -311,12 +319,12 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
     return HYENA_ERR_INVALID_ARG;
   if (L > K - 1 && B * D > 65535 && !(io == HYENA_BF16 && K <= 128)) return HYENA_ERR_UNSUPPORTED;
   hyena::FirArgs a{x1, x2, v, taps, static_cast<int>(K), skip, y, static_cast<int>(B),
-                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, as_stream(stream)};
+                   static_cast<int>(D), static_cast<int>(L), io == HYENA_BF16, stream};
   return from_hip(hyena::launch_fir_window(a, window_in, window_out));
 }
 
 hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues, int64_t D,
-                                      int64_t N, int64_t L, float* h, void* stream) {
+                                      int64_t N, int64_t L, float* h, hipStream_t stream) {
   return modal_filter_impl(log_poles, residues, D, N, L, h, true, stream);
 }
 
@@ -324,7 +332,7 @@ hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void*
                                      const float* log_poles, const float* residues, int64_t N,
                                      const float* skip, void* y, int64_t B, int64_t D, int64_t L,
                                      hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                     void* stream) {
+                                     hipStream_t stream) {
   return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
                       ws_bytes, true, stream);
 }
@@ -333,7 +341,17 @@ hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v
                                    const float* log_poles, const float* residues, int64_t N,
                                    const float* skip, const float* state_in, float* state_out,
                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                                   hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream) {
+                                   hyena_dtype_t io, hipStream_t stream) {
+  return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
+                    C, io, HYENA_CHUNK_AUTO, true, stream);
+}
+
+hyena_status_t hyena_chunk_fwd_cpx_algo(const void* x1, const void* x2, const void* v,
+                                        const float* log_poles, const float* residues, int64_t N,
+                                        const float* skip, const float* state_in,
+                                        float* state_out, void* y, int64_t B, int64_t D,
+                                        int64_t L, int64_t C, hyena_dtype_t io,
+                                        hyena_chunk_algo_t algo, hipStream_t stream) {
   return chunk_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, L,
                     C, io, algo, true, stream);
 }
@@ -342,7 +360,7 @@ hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void
                                       const float* log_poles, const float* residues, int64_t N,
                                       const float* skip, const float* state_in, float* state_out,
                                       void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                      void* stream) {
+                                      hipStream_t stream) {
   return decode_impl(x1, x2, v, log_poles, residues, N, skip, state_in, state_out, y, B, D, io,
                      true, stream);
 }
@@ -352,7 +370,7 @@ hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t
                                         const float* residues, int64_t N, const float* skip,
                                         const float* state_in, float* state_out, void* y,
                                         int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                        void* workspace, size_t ws_bytes, void* stream) {
+                                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   return chunk_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, log_poles, residues, N, skip, state_in,
                              state_out, y, B, D, L, io, workspace, ws_bytes, stream);
 }
@@ -361,7 +379,7 @@ hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t p
                                       int32_t pos_v, const float* taps, int64_t K,
                                       const float* skip, const float* window_in,
                                       float* window_out, void* y, int64_t B, int64_t D, int64_t L,
-                                      hyena_dtype_t io, void* stream) {
+                                      hyena_dtype_t io, hipStream_t stream) {
   return fir_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, taps, K, skip, window_in, window_out, y,
                            B, D, L, io, stream);
 }

@@ -42,8 +42,8 @@
  *    must not overlap inputs (except state_out == state_in, which is allowed).
  *    Base pointers must be aligned to their element size; 16-byte alignment
  *    enables the vectorised paths.
- *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *    Every call is asynchronous on that stream and never synchronises the
+ *  - `stream` is the HIP stream the call is enqueued on (NULL = the null
+ *    stream).  Every call is asynchronous on that stream and never synchronises the
  *    host; device faults surface at the caller's next synchronisation.
  *  - Arguments are validated on the host before any launch.  Nothing is
  *    printed and nothing throws across the ABI.  Sizes of 0 are accepted and
@@ -62,11 +62,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 6
+#define HYENA_ABI_VERSION 7
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -81,8 +83,9 @@ typedef enum hyena_dtype {
     HYENA_BF16 = 1,
 } hyena_dtype_t;
 
-/* Algorithm for hyena_chunk_fwd and hyena_chunk_fwd_cpx.  Both compute the
- * same function. */
+/* Algorithm of hyena_chunk_fwd_algo and hyena_chunk_fwd_cpx_algo (the entry
+ * points without the suffix take AUTO).  Both algorithms compute the same
+ * function. */
 typedef enum hyena_chunk_algo {
     HYENA_CHUNK_AUTO = 0,        /* MFMA when the modes fit it (below), else FFT */
     HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms */
@@ -114,7 +117,7 @@ const char* hyena_status_string(hyena_status_t status);
  */
 hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues,
                                   int64_t D, int64_t N, int64_t L,
-                                  float* h, void* stream);
+                                  float* h, hipStream_t stream);
 
 /*
  * hyena_fir_fwd -- gated explicit-FIR Hyena operator (hcs: K = 7, hcm: K = 128).
@@ -129,7 +132,7 @@ hyena_status_t hyena_modal_filter(const float* log_poles, const float* residues,
 hyena_status_t hyena_fir_fwd(const void* x1, const void* x2, const void* v,
                              const float* taps, int64_t K, const float* skip,
                              void* y, int64_t B, int64_t D, int64_t L,
-                             hyena_dtype_t io, void* stream);
+                             hyena_dtype_t io, hipStream_t stream);
 
 /*
  * hyena_fftconv_fwd -- single-pass modal Hyena operator.
@@ -158,7 +161,7 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  const float* log_poles, const float* residues,
                                  int64_t N, const float* skip, void* y,
                                  int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                 void* workspace, size_t ws_bytes, void* stream);
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when one launch
  * transforms the rows on chip (L <= 4096) or the shape is empty or
@@ -183,15 +186,34 @@ size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
  *   log_poles, residues : (D, N) fp32;  skip : (D) fp32 or NULL
  *   state_in  : (B, D, N) fp32 or NULL (zero state)
  *   state_out : (B, D, N) fp32, written (may equal state_in)
- *   C >= 1; algo HYENA_CHUNK_FFT needs C <= HYENA_MAX_FFT_CHUNK.
+ *   C >= 1.  The algorithm is HYENA_CHUNK_AUTO: the matrix-core blocked
+ *   Toeplitz for N <= 16 modes, else per-chunk FFTs (then C' <=
+ *   HYENA_MAX_FFT_CHUNK, else HYENA_ERR_UNSUPPORTED).
  */
 hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
                                const float* log_poles, const float* residues,
                                int64_t N, const float* skip,
                                const float* state_in, float* state_out,
                                void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                               hyena_dtype_t io, hyena_chunk_algo_t algo,
-                               void* stream);
+                               hyena_dtype_t io, hipStream_t stream);
+
+/*
+ * hyena_chunk_fwd_algo -- hyena_chunk_fwd with the algorithm chosen by the
+ * caller (same function, same arguments, same errors):
+ *   HYENA_CHUNK_AUTO  as hyena_chunk_fwd;
+ *   HYENA_CHUNK_FFT   per chunk a zero-padded FFT product of length 2C', any
+ *                     N, C' <= HYENA_MAX_FFT_CHUNK;
+ *   HYENA_CHUNK_MFMA  blocked Toeplitz on the matrix cores, any C, N <= 16
+ *                     (N > 16 -> HYENA_ERR_UNSUPPORTED);
+ *   anything else -> HYENA_ERR_INVALID_ARG.
+ */
+hyena_status_t hyena_chunk_fwd_algo(const void* x1, const void* x2, const void* v,
+                                    const float* log_poles, const float* residues,
+                                    int64_t N, const float* skip,
+                                    const float* state_in, float* state_out,
+                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                                    hyena_dtype_t io, hyena_chunk_algo_t algo,
+                                    hipStream_t stream);
 
 /*
  * hyena_modal_decode -- one decode step of the modal operator from its cache.
@@ -212,7 +234,7 @@ hyena_status_t hyena_modal_decode(const void* x1, const void* x2, const void* v,
                                   int64_t N, const float* skip,
                                   const float* state_in, float* state_out,
                                   void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                  void* stream);
+                                  hipStream_t stream);
 
 /*
  * hyena_fir_fwd_window -- explicit FIR continuing a sequence from its cache.
@@ -234,7 +256,7 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
                                     const float* taps, int64_t K, const float* skip,
                                     const float* window_in, float* window_out,
                                     void* y, int64_t B, int64_t D, int64_t L,
-                                    hyena_dtype_t io, void* stream);
+                                    hyena_dtype_t io, hipStream_t stream);
 
 /*
  * Complex-pole modal filters.  Evo 1's Hyena filter is given by modal-form
@@ -253,28 +275,38 @@ hyena_status_t hyena_fir_fwd_window(const void* x1, const void* x2, const void* 
 /* h (D, L) fp32, as hyena_modal_filter. */
 hyena_status_t hyena_modal_filter_cpx(const float* log_poles, const float* residues,
                                       int64_t D, int64_t N, int64_t L, float* h,
-                                      void* stream);
+                                      hipStream_t stream);
 
 /* Single pass, as hyena_fftconv_fwd (same workspace size). */
 hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void* v,
                                      const float* log_poles, const float* residues,
                                      int64_t N, const float* skip, void* y,
                                      int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                     void* workspace, size_t ws_bytes, void* stream);
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Chunked prefill with the complex modal state carried in and out, as
  * hyena_chunk_fwd:
  *   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + Re sum_n R_n p_n^(t-t0+1) s_n,
  *   s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j].
- * HYENA_CHUNK_MFMA takes N <= 8 complex modes (each a pair of real lanes of
- * its scan), HYENA_CHUNK_FFT any N with C' <= HYENA_MAX_FFT_CHUNK; AUTO picks
- * MFMA for N <= 8. */
+ * The algorithm is AUTO: the matrix cores for N <= 8 complex modes (each a
+ * pair of real lanes of its scan), per-chunk FFTs otherwise. */
 hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
                                    const float* log_poles, const float* residues,
                                    int64_t N, const float* skip,
                                    const float* state_in, float* state_out,
                                    void* y, int64_t B, int64_t D, int64_t L, int64_t C,
-                                   hyena_dtype_t io, hyena_chunk_algo_t algo, void* stream);
+                                   hyena_dtype_t io, hipStream_t stream);
+
+/* hyena_chunk_fwd_cpx with the algorithm chosen by the caller:
+ * HYENA_CHUNK_MFMA takes N <= 8 complex modes, HYENA_CHUNK_FFT any N with
+ * C' <= HYENA_MAX_FFT_CHUNK, AUTO as hyena_chunk_fwd_cpx. */
+hyena_status_t hyena_chunk_fwd_cpx_algo(const void* x1, const void* x2, const void* v,
+                                        const float* log_poles, const float* residues,
+                                        int64_t N, const float* skip,
+                                        const float* state_in, float* state_out,
+                                        void* y, int64_t B, int64_t D, int64_t L, int64_t C,
+                                        hyena_dtype_t io, hyena_chunk_algo_t algo,
+                                        hipStream_t stream);
 
 /* One decode step, as hyena_modal_decode: s_n <- p_n s_n + u,
  * y = x2 * Re sum_n R_n s_n + skip * u. */
@@ -283,7 +315,7 @@ hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void
                                       int64_t N, const float* skip,
                                       const float* state_in, float* state_out,
                                       void* y, int64_t B, int64_t D, hyena_dtype_t io,
-                                      void* stream);
+                                      hipStream_t stream);
 
 /*
  * hyena_chunk_fwd_tokmajor -- the modal operator on the token-major layout
@@ -319,7 +351,7 @@ hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t
                                         const float* residues, int64_t N, const float* skip,
                                         const float* state_in, float* state_out, void* y,
                                         int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
-                                        void* workspace, size_t ws_bytes, void* stream);
+                                        void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * hyena_fir_fwd_tokmajor -- the explicit-FIR operator (hcm K = 128, hcs
@@ -341,7 +373,7 @@ hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t p
                                       int32_t pos_v, const float* taps, int64_t K,
                                       const float* skip, const float* window_in,
                                       float* window_out, void* y, int64_t B, int64_t D, int64_t L,
-                                      hyena_dtype_t io, void* stream);
+                                      hyena_dtype_t io, hipStream_t stream);
 
 /* Workspace bytes hyena_chunk_fwd_tokmajor needs for this shape: B * P * D * N
  * floats for its P segments, 0 when the sequence is one segment or the shape

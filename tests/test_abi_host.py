@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 6
+    assert G.abi_version() == 7
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -169,23 +169,35 @@ def test_fftconv_validation():
 
 def test_chunk_validation():
     f = G.lib().hyena_chunk_fwd
+    # x1 x2 v lam res N skip s_in s_out y B D L C io stream  (AUTO algorithm)
     good = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, None, FAKE, FAKE, 1, 4, 1024, 1024,
-            G.BF16, 0, None]
+            G.BF16, None]
     for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (8, None, G.ERR_INVALID_ARG),
-                           (13, 0, G.ERR_INVALID_ARG), (15, 3, G.ERR_INVALID_ARG),
+                           (13, 0, G.ERR_INVALID_ARG), (14, 3, G.ERR_INVALID_ARG),
                            (5, 65, G.ERR_INVALID_ARG), (8, MISALIGNED, G.ERR_INVALID_ARG)]:
         a = list(good); a[idx] = val
         assert f(*a) == want, (idx, val)
-    a = list(good); a[5] = 32; a[15] = G.ALGOS["mfma"]        # MFMA kernel holds <= 16 modes
-    assert f(*a) == G.ERR_UNSUPPORTED
-    a = list(good); a[13] = 16384; a[15] = G.ALGOS["fft"]; a[12] = 16384
-    assert f(*a) == G.ERR_UNSUPPORTED                          # FFT chunk > 8192
+    a = list(good); a[5] = 32; a[13] = 16384; a[12] = 16384   # AUTO: > 16 modes take FFT chunks
+    assert f(*a) == G.ERR_UNSUPPORTED                          # ... of at most 8192
     a = list(good); a[10] = 0                                  # empty batch
     assert f(*a) == G.OK
+    # the same with the algorithm chosen: one more argument before the stream
+    fa = G.lib().hyena_chunk_fwd_algo
+    ga = good[:15] + [0, None]
+    a = list(ga); a[15] = 3
+    assert fa(*a) == G.ERR_INVALID_ARG
+    a = list(ga); a[5] = 32; a[15] = G.ALGOS["mfma"]          # MFMA kernel holds <= 16 modes
+    assert fa(*a) == G.ERR_UNSUPPORTED
+    a = list(ga); a[13] = 16384; a[15] = G.ALGOS["fft"]; a[12] = 16384
+    assert fa(*a) == G.ERR_UNSUPPORTED                         # FFT chunk > 8192
+    a = list(ga); a[13] = 16384; a[15] = G.ALGOS["auto"]; a[12] = 16384; a[8] = None
+    assert fa(*a) == G.ERR_INVALID_ARG
+    a = list(ga); a[10] = 0
+    assert fa(*a) == G.OK
 
 
 def test_chunk_cpx_validation():
-    f = G.lib().hyena_chunk_fwd_cpx
+    f = G.lib().hyena_chunk_fwd_cpx_algo
     good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, None, FAKE, FAKE, 1, 4, 1024, 1024,
             G.BF16, 0, None]
     a = list(good); a[5] = 9; a[15] = G.ALGOS["mfma"]         # 9 complex modes: 18 real lanes
@@ -196,6 +208,65 @@ def test_chunk_cpx_validation():
     assert f(*a) == G.ERR_INVALID_ARG
     a = list(good); a[10] = 0                                  # empty batch
     assert f(*a) == G.OK
+    fa = G.lib().hyena_chunk_fwd_cpx                           # AUTO, no algorithm argument
+    a = good[:15] + [None]
+    a[5] = 0
+    assert fa(*a) == G.ERR_INVALID_ARG
+    a[5] = 8; a[10] = 0
+    assert fa(*a) == G.OK
+
+
+def _declaration(name):
+    """Parameter list of `name` in the header, as [(type, name)]."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = []
+    if m.group(1).strip() == "void":
+        return params
+    for p in m.group(1).split(","):
+        p = " ".join(p.split())
+        typ, nm = p.rsplit(" ", 1)
+        while nm.startswith("*"):
+            typ, nm = typ + "*", nm[1:]
+        params.append((typ.replace(" *", "*"), nm))
+    return params
+
+
+def test_chunk_fwd_has_the_scope_table_signature():
+    """hyena_chunk_fwd takes exactly the boundary's parameter list: the
+    activations, the modal parameters, the state in and out, the sizes, the
+    chunk length, the I/O type and a HIP stream -- no algorithm selector."""
+    want = [("const void*", "x1"), ("const void*", "x2"), ("const void*", "v"),
+            ("const float*", "log_poles"), ("const float*", "residues"), ("int64_t", "N"),
+            ("const float*", "skip"), ("const float*", "state_in"), ("float*", "state_out"),
+            ("void*", "y"), ("int64_t", "B"), ("int64_t", "D"), ("int64_t", "L"),
+            ("int64_t", "C"), ("hyena_dtype_t", "io"), ("hipStream_t", "stream")]
+    assert _declaration("hyena_chunk_fwd") == want
+    assert _declaration("hyena_chunk_fwd_algo") == want[:15] + [
+        ("hyena_chunk_algo_t", "algo"), ("hipStream_t", "stream")]
+    assert _declaration("hyena_fftconv_fwd")[-1] == ("hipStream_t", "stream")
+    assert _declaration("hyena_fir_fwd") == [
+        ("const void*", "x1"), ("const void*", "x2"), ("const void*", "v"),
+        ("const float*", "taps"), ("int64_t", "K"), ("const float*", "skip"), ("void*", "y"),
+        ("int64_t", "B"), ("int64_t", "D"), ("int64_t", "L"), ("hyena_dtype_t", "io"),
+        ("hipStream_t", "stream")]
+    # every entry point that launches work takes its stream as a hipStream_t
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    assert "void* stream" not in text
+    for name in declared_functions():
+        params = _declaration(name)
+        if any(n == "stream" for _, n in params):
+            assert params[-1] == ("hipStream_t", "stream"), name
+
+
+def test_python_names_follow_the_boundary():
+    from genomic_lm_amd import hyena_op
+    assert hyena_op.fftconv is G.fftconv_fwd and hyena_op.chunk is G.chunk_fwd
+    assert hyena_op.fir is G.fir_fwd and hyena_op.modal_filter is G.modal_filter
+    for name in declared_functions() - {"hyena_abi_version", "hyena_status_string",
+                                        "hyena_chunk_fwd_algo", "hyena_chunk_fwd_cpx_algo"}:
+        assert callable(getattr(G, name)), name
 
 
 def test_chunk_tokmajor_validation():
