@@ -9,4 +9,5 @@ from .hyena_oracle import (  # noqa: F401
     modal_filter_cpx, hyena_fwd_cpx, modal_state_cpx, chunk_fwd_cpx, modal_decode_cpx,
     tokmajor_streams, chunk_fwd_tokmajor, fir_fwd_tokmajor,
 )
-from .metrics import compare, passes, REL_L2_MAX, ELEM_REL_MAX, TAU  # noqa: F401
+from .metrics import (compare, passes, channel_stats, from_stats,  # noqa: F401
+                      REL_L2_MAX, ELEM_REL_MAX, TAU)

@@ -148,40 +148,60 @@ def _seqs(cfg: Config):
 
 
 def _draw_rows(ss: np.random.SeedSequence, rows: int, L: int, scale=None,
-               io="bf16", threads=None) -> np.ndarray:
+               io="bf16", threads=None, keep=None) -> np.ndarray:
     """Draw a (rows, L) N(0,1) activation, row block by row block.
 
     Block i of _ROW_BLOCK rows comes from the i-th grandchild of `ss`, so blocks
-    are independent streams and can be drawn in parallel.
+    are independent streams and can be drawn in parallel.  `keep`, a list of
+    (start, stop) row ranges, draws only the blocks those ranges touch and
+    returns their rows stacked in order: the same values as those rows of
+    the full draw.  `scale` is indexed by the full row number.
     """
     nblk = (rows + _ROW_BLOCK - 1) // _ROW_BLOCK
     kids = ss.spawn(nblk)
-    out = np.empty((rows, L), dtype=np.uint16 if io == "bf16" else np.float32)
+    ranges = [(0, rows)] if keep is None else list(keep)
+    n_out = sum(b - a for a, b in ranges)
+    out = np.empty((n_out, L), dtype=np.uint16 if io == "bf16" else np.float32)
+    jobs = []                    # (block, first row of the block kept, rows kept, output row)
+    o = 0
+    for a, b in ranges:
+        r = a
+        while r < b:
+            i = r // _ROW_BLOCK
+            r_end = min(b, (i + 1) * _ROW_BLOCK)
+            jobs.append((i, r, r_end, o))
+            o += r_end - r
+            r = r_end
 
-    def one(i):
+    def one(job):
+        i, ra, rb, o = job
         r0 = i * _ROW_BLOCK
         r1 = min(rows, r0 + _ROW_BLOCK)
         g = np.random.Generator(np.random.PCG64(kids[i]))
-        a = g.standard_normal((r1 - r0, L))
+        a = g.standard_normal((r1 - r0, L))[ra - r0:rb - r0]
         if scale is not None:
-            a *= scale[r0:r1, None]
+            a *= scale[ra:rb, None]
         a32 = a.astype(np.float32)
-        out[r0:r1] = f32_to_bf16_bits(a32) if io == "bf16" else a32
+        out[o:o + rb - ra] = f32_to_bf16_bits(a32) if io == "bf16" else a32
 
     nt = threads or min(16, os.cpu_count() or 1)
-    if nblk == 1 or nt == 1:
-        for i in range(nblk):
-            one(i)
+    if len(jobs) == 1 or nt == 1:
+        for j in jobs:
+            one(j)
     else:
         with ThreadPoolExecutor(nt) as ex:
-            list(ex.map(one, range(nblk)))
+            list(ex.map(one, jobs))
     return out
 
 
 def make(name: str, *, B: int | None = None, D: int | None = None,
          L: int | None = None, N: int | None = None,
-         lam_lo: float | None = None) -> Workload:
-    """Build a seeded workload; overrides shrink it for fast tests."""
+         lam_lo: float | None = None, channels: tuple | None = None) -> Workload:
+    """Build a seeded workload; overrides shrink it for fast tests.
+
+    channels=(c0, c1) keeps only channels c0 <= c < c1 of the workload (every
+    batch item), drawing only those rows: the arrays equal the same channels
+    of the whole workload, and D is then c1 - c0."""
     cfg = CONFIGS[name]
     B = cfg.B if B is None else B
     D = cfg.D if D is None else D
@@ -206,20 +226,25 @@ def make(name: str, *, B: int | None = None, D: int | None = None,
     for K, key in ((7, "taps7"), (128, "taps128")):
         taps[K] = _round_param(param_rng(key).normal(0.0, math.sqrt(1.0 / K), (D, K)), bf16)
 
+    c0, c1 = (0, D) if channels is None else (int(channels[0]), int(channels[1]))
+    assert 0 <= c0 <= c1 <= D, (channels, D)
+    keep = None if channels is None else [(b * D + c0, b * D + c1) for b in range(B)]
     acts = {}
     for key in ("x1", "x2", "v"):
         sc = None
         if key == "x1" and scale is not None:
             sc = np.tile(scale, B)
-        acts[key] = _draw_rows(ss[key], B * D, L, scale=sc, io=cfg.io).reshape(B, D, L)
+        acts[key] = _draw_rows(ss[key], B * D, L, scale=sc, io=cfg.io,
+                               keep=keep).reshape(B, c1 - c0, L)
 
     return Workload(
-        cfg=cfg, B=B, D=D, L=L, io=cfg.io,
+        cfg=cfg, B=B, D=c1 - c0, L=L, io=cfg.io,
         x1=acts["x1"], x2=acts["x2"], v=acts["v"],
-        log_poles=lam.astype(np.float32),
-        residues=res.astype(np.float32),
-        skip=_round_param(skip, bf16),
-        taps=taps, scale=scale,
+        log_poles=lam.astype(np.float32)[c0:c1],
+        residues=res.astype(np.float32)[c0:c1],
+        skip=_round_param(skip, bf16)[c0:c1],
+        taps={K: t[c0:c1] for K, t in taps.items()},
+        scale=None if scale is None else scale[c0:c1],
     )
 
 
