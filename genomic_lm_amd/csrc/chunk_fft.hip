@@ -26,12 +26,15 @@ namespace hyena {
 
 constexpr int CHUNK_MAXN = 64;
 constexpr int CHUNK_NG = 16;             // modes per reduction group
-// Chunks up to this length decay the state by the pole power as an fp32 pair
-// (pow_pair.hpp): there a slow mode's memory spans many chunks, and a single
-// fp32 factor's rounding would compound over them.  Longer chunks decay it a
-// few dozen times per 32k tokens, where that bias is ~1e-6, and take the fp32
-// factor, whose fp64 pair would cost ~5 % of the complex kernel's time.
-constexpr int CHUNK_PAIR_MAX_C = 256;
+// The state is decayed by the pole power p^C' as an fp32 pair (pow_pair.hpp)
+// at every chunk length: a single fp32 factor's rounding d compounds over the
+// chunks a mode remembers, 1 / (|lam| C) of them, a bias of d / (|lam| C)
+// of its state -- ~1e-6 for |lam| = 1e-5 even at C = 4096, which two slow
+// modes with nearly equal poles and opposite residues raise many times over
+// relative to the output.  Real modes take one fp64 exp per mode and chunk;
+// complex modes keep the whole-chunk pair in the registers of the thread
+// that owns the mode (N <= 64 <= T) and make a pair only for a shorter last
+// chunk.
 
 // CPX: complex modes, lam and res as (re, im) pairs, complex state (B, D, N)
 // as (re, im) pairs; h = Re sum_n R_n exp(lam_n t) and the carried term is
@@ -48,9 +51,11 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   constexpr int LG_N = LG_M + 1;
   __shared__ float2 lds[lds_padded_size(S)];
   constexpr int W = CPX ? 2 : 1;                 // floats per mode parameter / state
+  static_assert(T >= CHUNK_MAXN, "each thread owns at most one mode (n = t)");
   __shared__ float s_lam[W * CHUNK_MAXN], s_res[W * CHUNK_MAXN], s_st[W * CHUNK_MAXN];
   __shared__ float s_tot[W * CHUNK_MAXN];
-  __shared__ float red[T * (CHUNK_NG + 1)];      // partial sums of one mode group
+  constexpr int NW = T / 64;                     // waves of the workgroup
+  __shared__ float red[NW * (CHUNK_NG + 1)];     // per-wave sums of one mode group
 
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -129,7 +134,6 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   // carried-term ladder p^(2t+1) and of the state-weight ladder
   // p^(2T-2-2t).  Partial chunks recompute the ladders' weights.
   __shared__ float s_p[W * CHUNK_MAXN], s_step[W * CHUNK_MAXN];
-  __shared__ float s_pc[W * CHUNK_MAXN];         // p^C, the fp32 decay of a whole chunk
   constexpr bool TAB = (T == 64);
   __shared__ float t_ea[TAB ? CHUNK_NG * T : 1], t_wa[TAB ? CHUNK_NG * T : 1];
   const bool use_tab = TAB && NR <= CHUNK_NG;
@@ -137,16 +141,18 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     if constexpr (CPX) {
       const CpxMode md = cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]);
       const float2 p = cexp_at(md, 1.0f), st = cexp_at(md, static_cast<float>(2 * T));
-      const float2 pc = cexp_at(md, static_cast<float>(C));
       s_p[2 * n] = p.x;     s_p[2 * n + 1] = p.y;
-      s_pc[2 * n] = pc.x;   s_pc[2 * n + 1] = pc.y;
       s_step[2 * n] = st.x; s_step[2 * n + 1] = st.y;
     } else {
       const float l = s_lam[n];
       s_p[n] = expf(l);
       s_step[n] = expf(l * static_cast<float>(2 * T));
-      s_pc[n] = expf(l * static_cast<float>(C));
     }
+  }
+  // CPX: p^C of the mode this thread owns (n = t), as hi + lo
+  float2 pc_hi = make_float2(0.0f, 0.0f), pc_lo = make_float2(0.0f, 0.0f);
+  if constexpr (CPX) {
+    if (t < N) pc_hi = cpow_pair(s_lam[2 * t], s_lam[2 * t + 1], static_cast<float>(C), pc_lo);
   }
   if (use_tab) {
     for (int n = 0; n < N; ++n) {
@@ -280,8 +286,11 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
                                  fmaf(u[i].x, w0.y, fmaf(u[i].y, w.y, part.y)));
             }
           }
-          red[t * (CHUNK_NG + 1) + g] = part.x;
-          red[t * (CHUNK_NG + 1) + g + 1] = part.y;
+          const float sx = wave_sum(part.x), sy = wave_sum(part.y);
+          if ((t & 63) == 0) {
+            red[(t >> 6) * (CHUNK_NG + 1) + g] = sx;
+            red[(t >> 6) * (CHUNK_NG + 1) + g + 1] = sy;
+          }
         }
       } else {
         for (int g = 0; g < ng; ++g) {
@@ -317,22 +326,26 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
               part = fmaf(u[i].y, w, part);                              // zero beyond Cp anyway
             }
           }
-          red[t * (CHUNK_NG + 1) + g] = part;
+          const float sw = wave_sum(part);
+          if ((t & 63) == 0) red[(t >> 6) * (CHUNK_NG + 1) + g] = sw;
         }
       }
+      // The partials are summed as a tree, a wave's lanes by wave_sum and
+      // then the NW waves' sums: a sequential fp32 sum of the T per-thread
+      // partials put ~sqrt(T) roundings of the chunk's contribution into the
+      // carried state in every chunk (at C = 4096, T = 512, ~1e-6 of a slow
+      // mode's state over the chunks it remembers).
       __syncthreads();                     // partials written; old state no longer read
       for (int g = t; g < ng; g += T) {
         float tot = 0.0f;
-        for (int j = 0; j < T; ++j) tot += red[j * (CHUNK_NG + 1) + g];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) tot += red[j * (CHUNK_NG + 1) + g];
         const int n = n0 + g;
         if constexpr (CPX) {
           s_tot[n] = tot;                  // the complex update needs both slots
         } else {
           // made here: kept per row in LDS the pairs would cost a workgroup per CU
-          const float2 pc = (C <= CHUNK_PAIR_MAX_C)
-                                ? pow_pair(s_lam[n], static_cast<float>(Cp))
-                                : make_float2(Cp == C ? s_pc[n] : expf(s_lam[n] * static_cast<float>(Cp)),
-                                              0.0f);
+          const float2 pc = pow_pair(s_lam[n], static_cast<float>(Cp));
           s_st[n] = fmaf(pc.x, s_st[n], fmaf(pc.y, s_st[n], tot));
         }
       }
@@ -340,13 +353,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     }
     if constexpr (CPX) {
       for (int n = t; n < N; n += T) {
-        float2 ph, pl = make_float2(0.0f, 0.0f);
-        if (C <= CHUNK_PAIR_MAX_C)
-          ph = cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(Cp), pl);
-        else if (Cp == C)
-          ph = make_float2(s_pc[2 * n], s_pc[2 * n + 1]);
-        else
-          ph = cexp_at(cpx_mode(s_lam[2 * n], s_lam[2 * n + 1]), static_cast<float>(Cp));
+        float2 ph = pc_hi, pl = pc_lo;     // n == t: the thread's own mode
+        if (Cp != C) ph = cpow_pair(s_lam[2 * n], s_lam[2 * n + 1], static_cast<float>(Cp), pl);
         const float2 so = make_float2(s_st[2 * n], s_st[2 * n + 1]);
         const float2 sn = cadd(cadd(cmul(ph, so), cmul(pl, so)),
                                make_float2(s_tot[2 * n], s_tot[2 * n + 1]));

@@ -41,6 +41,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
+#include "pow_pair.hpp"
 
 namespace hyena {
 
@@ -112,6 +113,54 @@ __device__ __forceinline__ void build_state_weights_cpx(const CpxMode& md, int k
         return k ? e.y : e.x;
       },
       part, hf, ref, pa, pb, pc);
+}
+
+// Double-float values hi + lo (an unevaluated sum of two floats) for the
+// scan's carried state.  The carry is multiplied by p^1024 once per tile
+// along the whole row; rounded to fp32 at every tile (or every 128 tokens,
+// as the scan over blocks first did) it would collect one rounding per step
+// over the ~1 / (1024 |lam|) steps a slow mode remembers, and a single fp32
+// factor's rounding would compound into a bias (~1e-4 of the state for
+// |lam| = 1e-5 at one step per 128 tokens).  Two slow modes with nearly
+// equal poles and opposite residues make that many times the output's rms.
+// Carried as a pair, each step is exact to ~2^-44.  No FP contraction in
+// these helpers: fusing a product into the sum after it would change the
+// value whose rounding error the next line computes.
+struct DF {
+  float hi, lo;
+};
+
+__device__ __forceinline__ DF df_two_sum(float a, float b) {
+#pragma clang fp contract(off)
+  const float s = a + b;
+  const float bb = s - a;
+  return {s, (a - (s - bb)) + (b - bb)};
+}
+
+// (ah + al) (c.hi + c.lo) + e
+__device__ __forceinline__ DF df_step(float ah, float al, DF c, float e) {
+#pragma clang fp contract(off)
+  const float p = ah * c.hi;
+  const float pe = fmaf(ah, c.hi, -p);          // exact: ah c.hi = p + pe
+  const DF sm = df_two_sum(p, e);
+  const float lo = (sm.lo + pe) + fmaf(ah, c.lo, al * c.hi);
+  return df_two_sum(sm.hi, lo);
+}
+
+// (ah + al) (c.hi + c.lo) + (bh + bl) (cp.hi + cp.lo) + e: one component of
+// a complex product with the state, cp the partner component
+__device__ __forceinline__ DF df_step_cpx(float ah, float al, DF c, float bh, float bl, DF cp,
+                                          float e) {
+#pragma clang fp contract(off)
+  const float p1 = ah * c.hi;
+  const float e1 = fmaf(ah, c.hi, -p1);
+  const float p2 = bh * cp.hi;
+  const float e2 = fmaf(bh, cp.hi, -p2);
+  const DF s1 = df_two_sum(p1, p2);
+  const DF s2 = df_two_sum(s1.hi, e);
+  const float lo = ((s2.lo + s1.lo) + (e1 + e2)) +
+                   fmaf(ah, c.lo, fmaf(al, c.hi, fmaf(bh, cp.lo, bl * cp.hi)));
+  return df_two_sum(s2.hi, lo);
 }
 
 // VEC: rows of whole 16-byte chunks, 16-byte aligned (full tiles take the
@@ -227,7 +276,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   for (int j = 0; j < 8; ++j) {
     if (8 * hf + j >= NS) g_res[j] = 0.0f;
   }
-  float carry = (part == 0 && n_sc < NS && state_in) ? st_ld : 0.0f;
+  DF carry = {(part == 0 && n_sc < NS && state_in) ? st_ld : 0.0f, 0.0f};
 
   // ---- per-row constants
   // h[d], d < 32.  The mode loop has its fixed maximum trip count so that
@@ -296,7 +345,8 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
   }
   // p^32, p^64, p^96, p^128: real part (CPX: and the imaginary part times
-  // the sign of the partner term, -1 for a Re slot, +1 for an Im slot)
+  // the sign of the partner term, -1 for a Re slot, +1 for an Im slot), in
+  // fp32: within a tile each is applied once to a value.
   float a1, a2, a3, a4, b1 = 0.0f, b2 = 0.0f, b3 = 0.0f, b4 = 0.0f;
   if constexpr (CPX) {
     const float sg = kc ? 1.0f : -1.0f;
@@ -307,6 +357,45 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   } else {
     a1 = expf(lam_n * 32.0f); a2 = expf(lam_n * 64.0f);
     a3 = expf(lam_n * 96.0f); a4 = expf(lam_n * 128.0f);
+  }
+  // The state carried from tile to tile is multiplied by p^1024 once per
+  // tile along the whole row.  Every factor that reaches it is an fp32 pair
+  // hi + lo from an fp64 exp (pow_pair.hpp) and the carry itself a
+  // double-float (DF above): p^128 for the chain over a tile's 8 runs,
+  // p^(128 rho) for the carry-in of run rho = 2q + hf, p^1024 for the carry
+  // out.  (CPX: Re and sign * Im parts as for a1..a4.)
+  float c4h, c4l, c4bh = 0.0f, c4bl = 0.0f;            // p^128
+  float fh[5], fl[5], fbh[5], fbl[5];                  // p^(128 (2q + hf)), q < 4; [4]: p^1024
+  {
+    // one fp64 exp for p^128, the other powers by fp64 products (each
+    // exact to ~2^-53, far below the pairs' 2^-48)
+    const double la = n_sc < NS ? lam_ld : 0.0;
+    const double lb = CPX ? (n_sc < NS ? lam_ld_im : 0.0) : 0.0;
+    const float sg = kc ? 1.0f : -1.0f;
+    const double m = exp(la * 128.0);
+    const double e_re = CPX ? m * cos(lb * 128.0) : m, e_im = CPX ? m * sin(lb * 128.0) : 0.0;
+    auto put = [&](double re, double im, float& h, float& lo, float& bh, float& bl) {
+      const float2 r = split_pair(re);
+      h = r.x;
+      lo = r.y;
+      if constexpr (CPX) {
+        const float2 i = split_pair(im);
+        bh = sg * i.x;
+        bl = sg * i.y;
+      }
+    };
+    put(e_re, e_im, c4h, c4l, c4bh, c4bl);
+    const double s_re = e_re * e_re - e_im * e_im, s_im = 2.0 * e_re * e_im;   // p^256
+    double f_re = hf ? e_re : 1.0, f_im = hf ? e_im : 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      put(f_re, f_im, fh[q], fl[q], fbh[q], fbl[q]);
+      const double t = f_re * s_re - f_im * s_im;
+      f_im = f_re * s_im + f_im * s_re;
+      f_re = t;
+    }
+    const double q_re = s_re * s_re - s_im * s_im, q_im = 2.0 * s_re * s_im;   // p^512
+    put(q_re * q_re - q_im * q_im, 2.0 * q_re * q_im, fh[4], fl[4], fbh[4], fbl[4]);
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -322,19 +411,34 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   pin(a2);
   pin(a3);
   pin(a4);
+  pin(c4h);
+  pin(c4l);
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    pin(fh[q]);
+    pin(fl[q]);
+  }
   if constexpr (CPX) {
     pin(b1);
     pin(b2);
     pin(b3);
     pin(b4);
+    pin(c4bh);
+    pin(c4bl);
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      pin(fbh[q]);
+      pin(fbl[q]);
+    }
   }
   // consume the state load here: a load still pending at the loop would make
   // the compiler wait for all vector memory (the DMAs in flight included) at
   // its first use in every iteration
-  asm volatile("" : "+v"(carry));
+  asm volatile("" : "+v"(carry.hi));
 
   // One 1024-token tile: inputs in `in` (u = x1 * v, gate x2), output to y.
-  // Returns nothing; updates `carry` (state after the tile, in part-0 lanes)
+  // Returns nothing; updates `carry` (state after the tile, in part-0 lanes,
+  // as a double-float)
   // and leaves sbuf holding the state before each block of the tile.
   // Runs of the tile: from `in` (registers) or, for bf16 tiles staged in
   // LDS, from the staged chunks.  All inputs are read first; `released` is
@@ -445,31 +549,57 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       own[q] = x[4 * q + 3];
       oth[q] = xor32(own[q], hf);
     }
-    // run rho = 2q + half covers blocks 4*rho .. 4*rho+3; cin[rho] = state before it
-    float cin[9];
-    cin[0] = carry;
+    // run rho = 2q + half covers blocks 4*rho .. 4*rho+3.  loc[rho]: the
+    // state before run rho from a zero state at the tile's start (the chain
+    // over the runs, fp32 with p^128 as a pair: its rounding stays within the
+    // tile); the true state adds p^(128 rho) times the carry.
+    float loc[9];
+    loc[0] = 0.0f;
 #pragma unroll
     for (int rho = 0; rho < 8; ++rho) {
       const float end = ((rho & 1) == hf) ? own[rho >> 1] : oth[rho >> 1];
-      cin[rho + 1] = step(a4, b4, cin[rho], end);
+      if constexpr (CPX) {
+        const float xp = xor1(loc[rho]);
+        loc[rho + 1] = fmaf(c4h, loc[rho], fmaf(c4bh, xp, fmaf(c4l, loc[rho], fmaf(c4bl, xp, end))));
+      } else {
+        loc[rho + 1] = fmaf(c4h, loc[rho], fmaf(c4l, loc[rho], end));
+      }
     }
+    const DF cpy = CPX ? DF{xor1(carry.hi), xor1(carry.lo)} : DF{0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float ci = hf ? cin[2 * q + 1] : cin[2 * q];
+      const int rho = 2 * q + hf;
+      // carry-in of the run, rounded once: p^(128 rho) carry + loc[rho]
+      float ci;
+      if constexpr (CPX) {
+        ci = fmaf(fh[q], carry.hi, fmaf(fbh[q], cpy.hi, fmaf(fh[q], carry.lo, fmaf(fbh[q], cpy.lo,
+             fmaf(fl[q], carry.hi, fmaf(fbl[q], cpy.hi, loc[rho]))))));
+      } else {
+        ci = fmaf(fh[q], carry.hi, fmaf(fh[q], carry.lo, fmaf(fl[q], carry.hi, loc[rho])));
+      }
       x[4 * q + 0] = step(a1, b1, ci, x[4 * q + 0]);
       x[4 * q + 1] = step(a2, b2, ci, x[4 * q + 1]);
       x[4 * q + 2] = step(a3, b3, ci, x[4 * q + 2]);
       x[4 * q + 3] = step(a4, b4, ci, x[4 * q + 3]);
     }
     // state before block b+1 = x for block b (b = 31 lands in the unused row
-    // 32); before block 0 = cin[0], identical in both half-waves
+    // 32); before block 0 = the carry, identical in both half-waves
 #pragma unroll
     for (int r = 0; r < 16; ++r) sbuf[part][blk_tok(r, hf) + 1][n_sc] = x[r];
-    sbuf[part][0][n_sc] = cin[0];
+    sbuf[part][0][n_sc] = carry.hi + carry.lo;
     {
-      const float fin = cin[8];
-      const float tot = fin + xor16(fin, l);
-      carry = (part == 0) ? tot : 0.0f;
+      // carry out: p^1024 carry + loc[8], then the two parts' states summed
+      // into the part-0 lane's carry
+      DF fin;
+      if constexpr (CPX) {
+        fin = df_step_cpx(fh[4], fl[4], carry, fbh[4], fbl[4], cpy, loc[8]);
+      } else {
+        fin = df_step(fh[4], fl[4], carry, loc[8]);
+      }
+      const DF oth2 = {xor16(fin.hi, l), xor16(fin.lo, l)};
+      const DF sm = df_two_sum(fin.hi, oth2.hi);
+      const DF tot = df_two_sum(sm.hi, sm.lo + (fin.lo + oth2.lo));
+      carry = (part == 0) ? tot : DF{0.0f, 0.0f};
     }
     lds_sync();
     // B = state before block i32, modes 8hf + j (column pair summed)
@@ -612,7 +742,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   }
   lds_sync();
   if (nfull > 0 && (static_cast<int64_t>(nfull) << 10) == L) {
-    if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry;
+    if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry.hi + carry.lo;
     return;
   }
 
@@ -659,7 +789,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     float (*sbuf)[33][17] = sbufs[0];
     const int64_t rem = L - t0;
     if (rem == 1024) {
-      if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry;
+      if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry.hi + carry.lo;
     } else if (rem < 1024) {
       // the sequence ends inside this tile: state after token L-1
       const int bstar = static_cast<int>(rem - 1) >> 5;

@@ -103,6 +103,45 @@ __device__ __forceinline__ float2 twiddle(int num, int lg) {
   return make_float2(__builtin_amdgcn_cosf(x), __builtin_amdgcn_sinf(x));
 }
 
+// ------------------------------------------------------------------ lane exchanges
+// x of lane l ^ 32 (the other half-wave).  v_permlane32_swap exchanges the
+// upper half-wave of its first operand with the lower half-wave of its
+// second; with x in both, the first result holds lanes 0..31 of x in both
+// halves and the second lanes 32..63.  A VALU op, unlike ds_bpermute.
+__device__ __forceinline__ float xor32(float x, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(hf ? r[0] : r[1]);
+}
+
+// x of lane l ^ 16.  v_permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second.
+__device__ __forceinline__ float xor16(float x, int l) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((l & 16) ? r[0] : r[1]);
+}
+
+// x of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2; a VALU op).
+__device__ __forceinline__ float xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+
+// Sum of x over the 64 lanes of the wave, returned in every lane: a tree of
+// six additions, each lane adding a partner's partial -- quad permutations
+// (lanes ^ 1, ^ 2), the half-row and row mirrors (the other quad of 8 lanes,
+// the other half of 16), then the row and half-wave swaps.  All VALU (DPP and
+// permlane), no LDS; ~sqrt(6) roundings of the sum instead of one per term
+// of a sequential sum.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // half mirror
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row mirror
+  const int l = static_cast<int>(threadIdx.x);
+  x += xor16(x, l);
+  x += xor32(x, (l >> 5) & 1);
+  return x;
+}
+
 // ------------------------------------------------------------------ complex modes
 // A complex mode exp(lam x), lam = a + i b, evaluated for real x >= 0 (up to
 // 2^20).  The phase b x is reduced in revolutions at double-float precision:

@@ -31,4 +31,10 @@ __device__ __forceinline__ float2 cpow_pair(float a, float b, float x, float2& l
   return hi;
 }
 
+// An fp64 value as an fp32 pair: .x its rounding, .y the rest.
+__device__ __forceinline__ float2 split_pair(double e) {
+  const float hi = static_cast<float>(e);
+  return make_float2(hi, static_cast<float>(e - static_cast<double>(hi)));
+}
+
 }  // namespace hyena
