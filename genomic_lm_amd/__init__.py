@@ -37,7 +37,8 @@ import torch
 
 __all__ = [
     "HyenaError", "HyenaNotBuilt", "lib", "LIB_PATH", "abi_version",
-    "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "chunk_fwd",
+    "modal_filter", "fir_fwd", "fftconv_fwd", "fftconv_workspace_size", "fftconv_fwd_noalloc",
+    "chunk_fwd",
     "modal_decode", "fir_fwd_window",
     "modal_filter_cpx", "fftconv_fwd_cpx", "chunk_fwd_cpx", "modal_decode_cpx",
     "chunk_fwd_tokmajor", "chunk_tokmajor_workspace_size", "fir_fwd_tokmajor",
@@ -65,6 +66,8 @@ EXPORTS = {
     "hyena_fftconv_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
                                  _p, _size, _p]),
     "hyena_fftconv_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
+    "hyena_fftconv_fwd_noalloc": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _int,
+                                         _p]),
     "hyena_chunk_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
                                _i64, _int, _p]),
     "hyena_chunk_fwd_algo": (_int, [_p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
@@ -230,6 +233,25 @@ def fftconv_fwd(x1, x2, v, log_poles, residues, skip=None, out=None, workspace=N
     _check("hyena_fftconv_fwd", lib().hyena_fftconv_fwd(
         _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip), _ptr(y),
         B, D, L, _io(x1), _ptr(workspace), ws_bytes, _stream(x1)))
+    return y
+
+
+def fftconv_fwd_noalloc(x1, x2, v, log_poles, residues, skip=None, out=None) -> torch.Tensor:
+    """fftconv_fwd through the library's device scratch instead of a
+    workspace (hyena_fftconv_fwd_noalloc): no device memory is allocated
+    when `out` is given."""
+    _act("x1", x1)
+    _act("x2", x2, x1)
+    _act("v", v, x1)
+    B, D, L = x1.shape
+    N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
+    _param("log_poles", log_poles, (D, N), x1.device)
+    _param("residues", residues, (D, N), x1.device)
+    _param("skip", skip, (D,), x1.device, optional=True)
+    y = torch.empty_like(x1) if out is None else _act("out", out, x1)
+    _check("hyena_fftconv_fwd_noalloc", lib().hyena_fftconv_fwd_noalloc(
+        _ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip), _ptr(y),
+        B, D, L, _io(x1), _stream(x1)))
     return y
 
 
@@ -512,6 +534,7 @@ hyena_modal_filter = modal_filter
 hyena_fir_fwd = fir_fwd
 hyena_fftconv_fwd = fftconv_fwd
 hyena_fftconv_workspace_size = fftconv_workspace_size
+hyena_fftconv_fwd_noalloc = fftconv_fwd_noalloc
 hyena_chunk_fwd = chunk_fwd
 hyena_modal_decode = modal_decode
 hyena_fir_fwd_window = fir_fwd_window

@@ -287,9 +287,11 @@ static void launch_part(const FftconvArgs& a, int64_t row0, int64_t rows) {
 }
 
 // Rows of the split form per pass through the workspace (8 S bytes each, at
-// most 1 GiB).
-static int64_t split_batch_rows(int64_t rows, int S) {
-  const int64_t cap = (int64_t(1) << 30) / (8 * static_cast<int64_t>(S));
+// most `bytes`, 1 GiB by default).
+static int64_t split_batch_rows(int64_t rows, int S, size_t bytes = 0) {
+  const size_t b = bytes ? bytes : (size_t(1) << 30);
+  int64_t cap = static_cast<int64_t>(b / (8 * static_cast<size_t>(S)));
+  if (cap < 1) cap = 1;
   return rows < cap ? rows : cap;
 }
 
@@ -299,7 +301,7 @@ static void launch_k(const FftconvArgs& a) {
   if constexpr (S <= 2048) {
     launch_part<S, T, IO, VEC, CPX, 0>(a, 0, rows);
   } else {
-    const int64_t nb = split_batch_rows(rows, S);
+    const int64_t nb = split_batch_rows(rows, S, a.batch_bytes);
     for (int64_t r0 = 0; r0 < rows; r0 += nb) {
       const int64_t n = rows - r0 < nb ? rows - r0 : nb;
       launch_part<S, T, IO, VEC, CPX, 1>(a, r0, n);
@@ -348,10 +350,10 @@ int fftconv_onchip_S(int64_t L) {
   return S <= 16384 ? static_cast<int>(S) : 0;
 }
 
-size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L) {
+size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L, size_t batch_bytes) {
   const int S = fftconv_onchip_S(L);
   if (S <= 2048 || B <= 0 || D <= 0) return 0;
-  return static_cast<size_t>(split_batch_rows(B * D, S) * 8 * S);
+  return static_cast<size_t>(split_batch_rows(B * D, S, batch_bytes) * 8 * S);
 }
 
 hipError_t launch_fftconv_onchip(const FftconvArgs& a) {

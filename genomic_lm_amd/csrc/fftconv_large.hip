@@ -317,9 +317,9 @@ int64_t large_S(int64_t L) {
   return (S / S2 <= MAX_S1) ? S : 0;
 }
 
-int64_t batch_rows(int64_t rows, int64_t S) {
+int64_t batch_rows(int64_t rows, int64_t S, size_t bytes = 0) {
   const int64_t per_row = 32 * S;
-  int64_t r = static_cast<int64_t>(BATCH_BYTES) / per_row;
+  int64_t r = static_cast<int64_t>(bytes ? bytes : BATCH_BYTES) / per_row;
   if (r < 1) r = 1;
   return r < rows ? r : rows;
 }
@@ -335,7 +335,7 @@ hipError_t launch_large_io(const FftconvArgs& a, int64_t S) {
   const int S1 = static_cast<int>(S / S2);
   const int lgS1 = ilog2(S1);
   const int64_t rows = int64_t(a.B) * a.D;
-  const int64_t nb = batch_rows(rows, S);
+  const int64_t nb = batch_rows(rows, S, a.batch_bytes);
   const IO* x1 = static_cast<const IO*>(a.x1);
   const IO* x2 = static_cast<const IO*>(a.x2);
   const IO* v = static_cast<const IO*>(a.v);
@@ -365,11 +365,11 @@ hipError_t launch_large_io(const FftconvArgs& a, int64_t S) {
 
 }  // namespace
 
-size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L) {
+size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L, size_t batch_bytes) {
   if (B <= 0 || D <= 0 || L <= 0) return 0;
   const int64_t S = large_S(L);
   if (S == 0 || fftconv_onchip_S(L) != 0) return 0;
-  return static_cast<size_t>(batch_rows(B * D, S) * 32 * S);
+  return static_cast<size_t>(batch_rows(B * D, S, batch_bytes) * 32 * S);
 }
 
 hipError_t launch_fftconv_large(const FftconvArgs& a) {

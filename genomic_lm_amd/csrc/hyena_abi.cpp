@@ -91,11 +91,13 @@ hyena_status_t decode_impl(const void* x1, const void* x2, const void* v,
   return from_hip(hyena::launch_modal_decode(a));
 }
 
+// noalloc: the workspace is the library's device scratch; rows then go
+// through it in batches that fit it, and a row longer than it is refused.
 hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
                             const float* log_poles, const float* residues, int64_t N,
                             const float* skip, void* y, int64_t B, int64_t D, int64_t L,
                             hyena_dtype_t io, void* workspace, size_t ws_bytes, bool cpx,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool noalloc = false) {
   bool empty = false;
   hyena_status_t st = check_acts(x1, x2, v, y, B, D, L, io, &empty);
   if (st != HYENA_OK) return st;
@@ -104,19 +106,23 @@ hyena_status_t fftconv_impl(const void* x1, const void* x2, const void* v,
   if (empty) return HYENA_OK;
   st = check_modal(log_poles, residues, N, skip);
   if (st != HYENA_OK) return st;
+  size_t batch = 0;
+  if (noalloc) {
+    const hipError_t e = hyena::noalloc_scratch(&workspace, &ws_bytes);
+    if (e != hipSuccess) return HYENA_ERR_LAUNCH;
+    batch = ws_bytes;
+  }
   hyena::FftconvArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, y,
                        static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
-                       io == HYENA_BF16, workspace, ws_bytes, stream, cpx};
-  if (hyena::fftconv_onchip_S(L) != 0) {
-    const size_t need = hyena::fftconv_onchip_workspace(B, D, L);
-    if (need > 0 && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
-      return HYENA_ERR_WORKSPACE;
-    return from_hip(hyena::launch_fftconv_onchip(a));
-  }
-  const size_t need = hyena::fftconv_large_workspace(B, D, L);
-  if (need == 0) return HYENA_ERR_UNSUPPORTED;
-  if (!workspace || ws_bytes < need || !aligned_to(workspace, 16)) return HYENA_ERR_WORKSPACE;
-  return from_hip(hyena::launch_fftconv_large(a));
+                       io == HYENA_BF16, workspace, ws_bytes, stream, cpx, batch};
+  const bool onchip = hyena::fftconv_onchip_S(L) != 0;
+  const size_t need = onchip ? hyena::fftconv_onchip_workspace(B, D, L, batch)
+                             : hyena::fftconv_large_workspace(B, D, L, batch);
+  if (!onchip && need == 0) return HYENA_ERR_UNSUPPORTED;
+  if (noalloc && need > ws_bytes) return HYENA_ERR_UNSUPPORTED;   // one row beyond the scratch
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
+    return HYENA_ERR_WORKSPACE;
+  return from_hip(onchip ? hyena::launch_fftconv_onchip(a) : hyena::launch_fftconv_large(a));
 }
 
 hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
@@ -262,6 +268,15 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  hipStream_t stream) {
   return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, workspace,
                       ws_bytes, false, stream);
+}
+
+hyena_status_t hyena_fftconv_fwd_noalloc(const void* x1, const void* x2, const void* v,
+                                         const float* log_poles, const float* residues,
+                                         int64_t N, const float* skip, void* y, int64_t B,
+                                         int64_t D, int64_t L, hyena_dtype_t io,
+                                         hipStream_t stream) {
+  return fftconv_impl(x1, x2, v, log_poles, residues, N, skip, y, B, D, L, io, nullptr, 0,
+                      false, stream, true);
 }
 
 size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N, hyena_dtype_t io) {

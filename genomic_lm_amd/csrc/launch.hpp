@@ -31,6 +31,7 @@ struct FftconvArgs {
   size_t ws_bytes;
   hipStream_t stream;
   bool cpx = false;
+  size_t batch_bytes = 0;   // workspace per batch of rows; 0: the default 1 GiB
 };
 
 struct FirArgs {
@@ -125,11 +126,16 @@ hipError_t launch_fir_mfma(const FirArgs& a);   // bf16, K <= 128
 // parity halves are two launches that pass the even half's result through a
 // workspace of fftconv_onchip_workspace bytes (0 below).
 int fftconv_onchip_S(int64_t L);
-size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L);
+size_t fftconv_onchip_workspace(int64_t B, int64_t D, int64_t L, size_t batch_bytes = 0);
 hipError_t launch_fftconv_onchip(const FftconvArgs& a);
 
+// The device scratch of hyena_fftconv_fwd_noalloc (noalloc.hip): its address
+// on the current device, looked up on the first call per device and kept.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // Multi-kernel single pass for L > 32768 through a caller workspace.
-size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L);
+size_t fftconv_large_workspace(int64_t B, int64_t D, int64_t L, size_t batch_bytes = 0);
 hipError_t launch_fftconv_large(const FftconvArgs& a);
 
 hipError_t launch_chunk_fft(const ChunkArgs& a);

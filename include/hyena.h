@@ -50,9 +50,10 @@
  *    do nothing (except hyena_chunk_fwd with L = 0, which copies state_in to
  *    state_out, or zeroes it when state_in is NULL).  Non-finite inputs
  *    propagate to the outputs; they are not an error.
- *  - The library keeps no global or per-device state and allocates nothing;
- *    all entry points are reentrant and may be called from several host
- *    threads.  No entry point allocates, clears memory with a memset or
+ *  - The library allocates nothing; apart from the device scratch of
+ *    hyena_fftconv_fwd_noalloc (below) it keeps no global or per-device
+ *    state.  All entry points are reentrant and may be called from several
+ *    host threads.  No entry point allocates, clears memory with a memset or
  *    synchronises, so every one may be captured into a HIP graph and
  *    replayed (the pointers it was captured with stay in use).
  */
@@ -99,6 +100,7 @@ typedef enum hyena_chunk_algo {
 #define HYENA_MAX_FIR_TAPS_TOKMAJOR 128  /* K of hyena_fir_fwd_tokmajor */
 #define HYENA_MAX_FFT_LEN (1 << 20)      /* single-pass FFT length, next pow2 >= 2L */
 #define HYENA_MAX_FFT_CHUNK 8192         /* C for HYENA_CHUNK_FFT (FFT length 2C <= 16384) */
+#define HYENA_NOALLOC_SCRATCH_BYTES (64u << 20)  /* device scratch of hyena_fftconv_fwd_noalloc */
 
 int hyena_abi_version(void);
 const char* hyena_status_string(hyena_status_t status);
@@ -162,6 +164,31 @@ hyena_status_t hyena_fftconv_fwd(const void* x1, const void* x2, const void* v,
                                  int64_t N, const float* skip, void* y,
                                  int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
                                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hyena_fftconv_fwd_noalloc -- hyena_fftconv_fwd for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  It takes no workspace; rows that need one
+ * (L > 4096) go through a scratch array of HYENA_NOALLOC_SCRATCH_BYTES (64
+ * MiB) that is part of the library's device code: every GPU the library is
+ * loaded on holds its own copy from the load until the process ends.  Its
+ * address on a device is looked up on the first call there and kept.  Rows
+ * are processed in batches that fit the scratch (fewer rows per launch than
+ * hyena_fftconv_fwd at L > 4096, the same results bit for bit); a shape
+ * whose single row needs more than the scratch -> HYENA_ERR_UNSUPPORTED
+ * (none within HYENA_MAX_FFT_LEN: the longest row needs 8 MiB).  The
+ * scratch's contents are left from the last call and nothing in it needs to
+ * start at zero.  All calls on one GPU share the scratch: calls that overlap
+ * in time on one GPU (different streams without ordering between them) race
+ * and give wrong results; calls on one stream are ordered.  Arguments,
+ * layouts and errors are otherwise those of hyena_fftconv_fwd; no memory is
+ * allocated and nothing synchronises.
+ */
+hyena_status_t hyena_fftconv_fwd_noalloc(const void* x1, const void* x2, const void* v,
+                                         const float* log_poles, const float* residues,
+                                         int64_t N, const float* skip, void* y,
+                                         int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                         hipStream_t stream);
 
 /* Workspace bytes hyena_fftconv_fwd needs for this shape: 0 when one launch
  * transforms the rows on chip (L <= 4096) or the shape is empty or

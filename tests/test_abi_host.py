@@ -167,6 +167,23 @@ def test_fftconv_validation():
     assert f(*mid) == G.ERR_WORKSPACE
 
 
+def test_fftconv_noalloc_validation():
+    """The scratch-free single pass validates like hyena_fftconv_fwd, before
+    it looks up its scratch or launches anything."""
+    f = G.lib().hyena_fftconv_fwd_noalloc
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, FAKE, 1, 4, 1024, G.BF16, None]
+    for idx, val, want in [(0, None, G.ERR_INVALID_ARG), (3, None, G.ERR_INVALID_ARG),
+                           (5, 0, G.ERR_INVALID_ARG), (5, 65, G.ERR_INVALID_ARG),
+                           (10, -1, G.ERR_INVALID_ARG), (11, 2, G.ERR_INVALID_ARG),
+                           (1, MISALIGNED, G.ERR_INVALID_ARG),
+                           (10, 1 << 20, G.ERR_UNSUPPORTED)]:
+        a = list(good); a[idx] = val
+        assert f(*a) == want, (idx, val)
+    a = list(good); a[9] = 0; a[0] = None                     # D = 0: nothing to do
+    assert f(*a) == G.OK
+    assert _declaration("hyena_fftconv_fwd_noalloc")[-1] == ("hipStream_t", "stream")
+
+
 def test_chunk_validation():
     f = G.lib().hyena_chunk_fwd
     # x1 x2 v lam res N skip s_in s_out y B D L C io stream  (AUTO algorithm)
