@@ -74,6 +74,10 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
   }
   __syncthreads();
 
+  // one step serves every twiddle ladder: exp(-2 pi i T / M) = exp(-2 pi i 2T / Nfft)
+  const float2 tst = twiddle(T, LG_M);
+  float2 tw = make_float2(1.0f, 0.0f);
+
   // ---- spectrum of h[0:C) for both parity halves, kept for every chunk
   float2 hs[2][P];
   float h_nyq = 0.0f;
@@ -97,9 +101,9 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         }
       } else {
         const float l = s_lam[n];
-        const float p = expf(l);
-        const float step = expf(l * static_cast<float>(2 * T));
-        float e = s_res[n] * expf(l * static_cast<float>(2 * t));
+        const float p = fast_exp(l);
+        const float step = fast_exp(l * static_cast<float>(2 * T));
+        float e = s_res[n] * fast_exp(l * static_cast<float>(2 * t));
 #pragma unroll
         for (int i = 0; i < P; ++i) {
           a[i].x += e;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       const int m = t + T * i;
       if (2 * m >= C) a[i].x = 0.0f;
       if (2 * m + 1 >= C) a[i].y = 0.0f;
-      if (q) a[i] = cmul(a[i], twiddle(m, LG_M));
+      if (q) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
     }
     fft_forward<S, T>(a, lds, t);
     __syncthreads();
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     for (int i = 0; i < P; ++i) {
       const int k = t + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      hs[q][i] = real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+      hs[q][i] = real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * t + q, 2 * T, LG_N, tw, tst));
     }
     if (q == 0 && t == 0) h_nyq = a[0].x - a[0].y;
   }
@@ -145,8 +149,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       s_step[2 * n] = st.x; s_step[2 * n + 1] = st.y;
     } else {
       const float l = s_lam[n];
-      s_p[n] = expf(l);
-      s_step[n] = expf(l * static_cast<float>(2 * T));
+      s_p[n] = fast_exp(l);
+      s_step[n] = fast_exp(l * static_cast<float>(2 * T));
     }
   }
   // CPX: p^C of the mode this thread owns (n = t), as hi + lo
@@ -166,8 +170,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         t_wa[(2 * n + 1) * T + t] = wa.y;
       } else {
         const float l = s_lam[n];
-        t_ea[n * T + t] = expf(l * static_cast<float>(2 * t + 1));
-        t_wa[n * T + t] = expf(l * static_cast<float>(2 * T - 2 - 2 * t));
+        t_ea[n * T + t] = fast_exp(l * static_cast<float>(2 * t + 1));
+        t_wa[n * T + t] = fast_exp(l * static_cast<float>(2 * T - 2 - 2 * t));
       }
     }
   }
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
-      for (int i = 0; i < P; ++i) a[i] = q ? cmul(u[i], twiddle(t + T * i, LG_M)) : u[i];
+      for (int i = 0; i < P; ++i) a[i] = q ? cmul(u[i], tw_next(i, t, T, LG_M, tw, tst)) : u[i];
       fft_forward<S, T>(a, lds, t);
       __syncthreads();
 #pragma unroll
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
       for (int i = 0; i < P; ++i) {
         const int k = t + T * i;
         const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-        z[i] = cmul(real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)), hs[q][i]);
+        z[i] = cmul(real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * t + q, 2 * T, LG_N, tw, tst)),
+                    hs[q][i]);
       }
       if (q == 0 && t == 0) zm_nyq = (a[0].x - a[0].y) * h_nyq;
       __syncthreads();
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
         const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
         float2 zmir = lds[lds_pad(kk)];
         if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
-        a[i] = inverse_pack(z[i], zmir, twiddle(2 * k + q, LG_N));
+        a[i] = inverse_pack(z[i], zmir, tw_next(i, 2 * t + q, 2 * T, LG_N, tw, tst));
       }
       fft_inverse<S, T>(a, lds, t);
       if (q == 0) {
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
     float2 zz[P];
 #pragma unroll
     for (int i = 0; i < P; ++i)
-      zz[i] = cscale(cadd(b0[i], cmul(cconj(twiddle(t + T * i, LG_M)), a[i])), inv_m);
+      zz[i] = cscale(cadd(b0[i], cmul(cconj(tw_next(i, t, T, LG_M, tw, tst)), a[i])), inv_m);
 
     // carried term sum_n R_n p_n^(tau+1) s_n (old state), and the state
     // partials, reduced over the workgroup 16 modes at a time
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
           const float p = s_p[n];
           const float step = s_step[n];
           float e = s_res[n] * s_st[n] *
-                    (use_tab ? t_ea[n * T + t] : expf(l * static_cast<float>(2 * t + 1)));
+                    (use_tab ? t_ea[n * T + t] : fast_exp(l * static_cast<float>(2 * t + 1)));
 #pragma unroll
           for (int i = 0; i < P; ++i) {
             zz[i].x += e;
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
           float part = 0.0f;
           if (full) {
             float w = use_tab ? t_wa[n * T + t]
-                              : expf(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
+                              : fast_exp(l * static_cast<float>(Cp - 2 - 2 * (t + T * (P - 1))));
 #pragma unroll
             for (int i = P - 1; i >= 0; --i) {
               part = fmaf(u[i].x, w * p, part);
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(T) void chunk_fft_kernel(
 #pragma unroll
             for (int i = 0; i < P; ++i) {
               const int m2 = 2 * (t + T * i);
-              const float w = expf(l * static_cast<float>(max(Cp - 2 - m2, 0)));
+              const float w = fast_exp(l * static_cast<float>(max(Cp - 2 - m2, 0)));
               part = fmaf(u[i].x, (m2 + 1 < Cp) ? w * p : w, part);   // m2 = Cp-1: weight p^0
               part = fmaf(u[i].y, w, part);                              // zero beyond Cp anyway
             }

@@ -98,7 +98,7 @@ __device__ __forceinline__ void state_weight_operands(F&& w, int part, int hf, i
 __device__ __forceinline__ void build_state_weights(float lam_n, int part, int hf, int ref,
                                                     bf16x8 (&pa)[2], bf16x8 (&pb)[2],
                                                     bf16x8 (&pc)[2]) {
-  state_weight_operands([&](int d) { return expf(lam_n * static_cast<float>(d)); }, part, hf,
+  state_weight_operands([&](int d) { return fast_exp(lam_n * static_cast<float>(d)); }, part, hf,
                         ref, pa, pb, pc);
 }
 
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     } else {
 #pragma unroll
       for (int n = 0; n < MFMA_MAXN; ++n) {
-        if (n < N) hd = fmaf(resc[n], expf(lamc[n] * static_cast<float>(i32)), hd);
+        if (n < N) hd = fmaf(resc[n], fast_exp(lamc[n] * static_cast<float>(i32)), hd);
       }
     }
     if (hf == 0) hbuf[i32] = hd;
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       const float2 rp = cmul(make_float2(g_res[j0], g_res[j0 + 1]), e);
       return (j & 1) ? -rp.y : rp.x;          // padding slots: g_res = 0
     } else {
-      return g_res[j] * expf(g_lam[j] * static_cast<float>(i32 + 1));
+      return g_res[j] * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
     }
   };
   bf16x8 gm[3];
@@ -355,8 +355,8 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     a1 = e1.x; a2 = e2.x; a3 = e3.x; a4 = e4.x;
     b1 = sg * e1.y; b2 = sg * e2.y; b3 = sg * e3.y; b4 = sg * e4.y;
   } else {
-    a1 = expf(lam_n * 32.0f); a2 = expf(lam_n * 64.0f);
-    a3 = expf(lam_n * 96.0f); a4 = expf(lam_n * 128.0f);
+    a1 = fast_exp(lam_n * 32.0f); a2 = fast_exp(lam_n * 64.0f);
+    a3 = fast_exp(lam_n * 96.0f); a4 = fast_exp(lam_n * 128.0f);
   }
   // The state carried from tile to tile is multiplied by p^1024 once per
   // tile along the whole row.  Every factor that reaches it is an fp32 pair
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
           const float sg = kc ? 1.0f : -1.0f;
           fin = fmaf(pe.x, sbuf[part][bstar][n_sc], fmaf(sg * pe.y, sbuf[part][bstar][n_sc ^ 1], ev));
         } else {
-          fin = fmaf(expf(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev);
+          fin = fmaf(fast_exp(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev);
         }
       }
       const float tot = fin + __shfl_xor(fin, 16);

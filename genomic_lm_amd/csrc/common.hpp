@@ -89,6 +89,15 @@ __device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2
 __device__ __forceinline__ float2 cmul_mi(float2 a) { return make_float2(a.y, -a.x); }
 __device__ __forceinline__ float2 cmul_pi(float2 a) { return make_float2(-a.y, a.x); }
 
+// exp(x), x <= 0, as v_exp_f32 of x * log2(e): two instructions against the
+// fourteen of expf's exactly rounded range reduction.  The product's rounding
+// moves the exponent by up to |x| 2^-24, so the relative error is about
+// (|x| + 1) 2^-24 and the absolute error at most about 2^-24 / e: the size of
+// the rounding of the terms these weights multiply.  Used for the filter's
+// and the weights' exponentials; the factors that compound along a row (the
+// carried state's decays) come from fp64 (pow_pair.hpp), not from here.
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
 // exp(-2*pi*i * num / 2^lg), 0 <= num < 2^lg.  v_sin_f32 / v_cos_f32 take
 // the angle in revolutions; -num / 2^lg is exact in fp32, and on gfx950 the
 // result is within 1.3e-7 of the true value for such arguments (checked
@@ -169,7 +178,7 @@ __device__ __forceinline__ float2 cexp_at(const CpxMode& m, float x) {
   const float p = m.fhi * x;
   const float e = fmaf(m.fhi, x, -p);              // exact: fhi x = p + e
   const float r = (p - rintf(p)) + fmaf(m.flo, x, e);
-  const float mag = expf(m.a * x);
+  const float mag = fast_exp(m.a * x);
   return make_float2(mag * __builtin_amdgcn_cosf(r), mag * __builtin_amdgcn_sinf(r));
 }
 

@@ -246,6 +246,17 @@ __device__ __forceinline__ int seq_idx(int t) {
 __device__ __forceinline__ void seq_keep(float2& x) { asm volatile("" : "+v"(x.x), "+v"(x.y)); }
 constexpr int SEQ = 4;
 
+// Twiddles exp(-2 pi i (a + d i) / 2^lg) of a thread's elements i = 0, 1, 2,
+// ... taken in order (i a compile-time constant): every SEQ-th from
+// twiddle(), whose v_cos / v_sin issue at a quarter of the vector rate, the
+// ones between as the previous twiddle times `step` = twiddle(d, lg), one
+// complex product (at most SEQ - 1 roundings more than twiddle's).  `w`
+// carries the last twiddle from one call to the next.
+__device__ __forceinline__ float2 tw_next(int i, int a, int d, int lg, float2& w, float2 step) {
+  w = (i % SEQ == 0) ? twiddle(a + d * i, lg) : cmul(w, step);
+  return w;
+}
+
 // ------------------------------------------------------------- real signals
 // A real length-Nfft signal x is transformed as the complex length-M signal
 // c[m] = x[2m] + i x[2m+1], M = Nfft / 2.  Its spectrum X[K] (K < M) follows

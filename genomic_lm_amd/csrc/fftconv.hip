@@ -40,9 +40,9 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
   for (int i = 0; i < P; ++i) a[i] = make_float2(0.0f, 0.0f);
   for (int n = 0; n < N; ++n) {
     const float l = lam[n];
-    const float p = expf(l);
-    const float step = expf(l * static_cast<float>(2 * T));
-    float e = res[n] * expf(l * static_cast<float>(2 * t));
+    const float p = fast_exp(l);
+    const float step = fast_exp(l * static_cast<float>(2 * T));
+    float e = res[n] * fast_exp(l * static_cast<float>(2 * t));
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       a[i].x += e;
@@ -128,6 +128,9 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
   // Both parity halves are unrolled: as a loop, the address and twiddle
   // arithmetic common to the two iterations was hoisted out of it and held
   // in registers across both transforms.
+  // one step serves every ladder below: exp(-2 pi i T / M) = exp(-2 pi i 2T / Nfft)
+  const float2 tst = twiddle(T, LG_M);
+  float2 tw = make_float2(1.0f, 0.0f);
 #pragma unroll
   for (int q = Q0; q <= Q1; ++q) {
     float2 a[P];
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
         p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
       }
       a[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
-      if (q) a[i] = cmul(a[i], twiddle(m, LG_M));
+      if (q) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
     }
     fft_forward<S, T>(a, lds, t);
     __syncthreads();
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       if (i % SEQ == 0) ts = seq_idx(t);
       const int k = ts + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      z[i] = real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N));
+      z[i] = real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
       seq_keep(z[i]);
     }
     if (q == 0 && t == 0) um_nyq = a[0].x - a[0].y;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       modal_pairs<P, T>(a, lamc, resc, N, t, L);
     if (q) {
 #pragma unroll
-      for (int i = 0; i < P; ++i) a[i] = cmul(a[i], twiddle(t + T * i, LG_M));
+      for (int i = 0; i < P; ++i) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
     }
     fft_forward<S, T>(a, lds, t);
     __syncthreads();
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       if (i % SEQ == 0) ts = seq_idx(t);
       const int k = ts + T * i;
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      z[i] = cmul(z[i], real_spectrum(a[i], lds[lds_pad(kk)], twiddle(2 * k + q, LG_N)));
+      z[i] = cmul(z[i], real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst)));
       seq_keep(z[i]);
     }
     if (q == 0 && t == 0) zm_nyq = um_nyq * (a[0].x - a[0].y);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
       const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
       float2 zmir = lds[lds_pad(kk)];
       if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
-      a[i] = inverse_pack(z[i], zmir, twiddle(2 * k + q, LG_N));
+      a[i] = inverse_pack(z[i], zmir, tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
       seq_keep(a[i]);
     }
     fft_inverse<S, T>(a, lds, t);
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
 #pragma unroll
           for (int j = 0; j < GG; ++j) {
             const int m = ts + T * (g0 + j);
-            const float2 zz = cscale(cadd(e0[j], cmul(cconj(twiddle(m, LG_M)), a[g0 + j])), inv_m);
+            const float2 zz = cscale(cadd(e0[j], cmul(cconj(tw_next(g0 + j, ts, T, LG_M, tw, tst)),
+                                                      a[g0 + j])), inv_m);
             const float2 p1 = r1[j].get(), p2 = r2[j].get(), g = rg[j].get();
             const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
                                            fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
@@ -260,12 +264,13 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
         for (int i = 0; i < P; ++i) {
           if (i % SEQ == 0) ts = seq_idx(t);
           const int m = ts + T * i;
+          const float2 wm = tw_next(i, ts, T, LG_M, tw, tst);     // the ladder advances for every i
           if (2 * m >= L) continue;
           float2 e0;
           if constexpr (PART == 2) e0 = (wsr + T * i)[ts];
           else if constexpr (B0_LDS) e0 = b0s[ts + T * i];
           else e0 = b0[i];
-          const float2 zz = cscale(cadd(e0, cmul(cconj(twiddle(m, LG_M)), a[i])), inv_m);
+          const float2 zz = cscale(cadd(e0, cmul(cconj(wm), a[i])), inv_m);
           const float2 p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
           const float2 p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
           const float2 g = ld_pair<IO, VEC>(x2r, 2 * m, L);

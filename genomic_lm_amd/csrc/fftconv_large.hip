@@ -117,9 +117,9 @@ __global__ __launch_bounds__(NTC) void fftconv_cols_fwd(
         }
       } else {
         const float l = lamc[n];
-        const float p = expf(l);
-        const float step = expf(l * static_cast<float>(2 * S1 * CT));
-        float e = resc[n] * expf(l * static_cast<float>(2 * (m1 + S1 * t)));
+        const float p = fast_exp(l);
+        const float step = fast_exp(l * static_cast<float>(2 * S1 * CT));
+        float e = resc[n] * fast_exp(l * static_cast<float>(2 * (m1 + S1 * t)));
 #pragma unroll
         for (int i = 0; i < CP; ++i) {
           d[i].x += e;
