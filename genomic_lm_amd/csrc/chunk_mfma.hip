@@ -831,6 +831,320 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   }
 }
 
+// One-tile rows: bf16, whole 16-byte chunks, 1 <= L <= 1024 -- one chunk per
+// call in chunk-by-chunk prefill (TurboQuant-Bio int4 Evo 2 checkpoints,
+// 'Chunk size': 1024-token chunks).  The products are those of
+// chunk_mfma_kernel's single tile, but a call of one tile is dominated by
+// setting up the per-row operands, so they are formed more cheaply and only
+// right before the products that use them, within 128 VGPRs: 4 waves per
+// SIMD keep 4096 rows resident at once (the general kernel, 2 waves per
+// SIMD, takes two rounds).
+//  - h and G share their exponentials: lane (i, hf) forms R_n p_n^(i+1) for
+//    the 8 modes of its G slots and the two half-waves' sums give h[i+1].
+//  - The end-state weights of a run of 4 consecutive tokens come from one
+//    exp and 3 products.
+//  - The carry factors are plain fp32 exps: the state enters and leaves the
+//    call as fp32, so the pair factors that keep a long scan of many tiles
+//    exact have nothing to preserve here.
+// LDS: the staged inputs (6 KB) are read into registers before the block
+// states and the staged y are written over them; with h, 6.5 KB.
+__global__ __launch_bounds__(64, 4) void chunk_one_kernel(
+    const bf16_t* __restrict__ x1, const bf16_t* __restrict__ x2, const bf16_t* __restrict__ v,
+    const float* __restrict__ lam, const float* __restrict__ res, int N,
+    const float* __restrict__ skip, const float* state_in, float* state_out,
+    bf16_t* __restrict__ y, int D, int L) {
+  constexpr int kTinBytes = 3 * 128 * 16;
+  constexpr int kSbufBytes = (2 * 33 * 17 * 4 + 15) / 16 * 16;
+  constexpr int kLdsBytes = (kSbufBytes + 128 * 16 > kTinBytes) ? kSbufBytes + 128 * 16 : kTinBytes;
+  __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
+  __shared__ float hbuf[32];
+  const uint4 (*const tin)[128] = reinterpret_cast<const uint4 (*)[128]>(lds_raw);
+  uint4 (*const tin_w)[128] = reinterpret_cast<uint4 (*)[128]>(lds_raw);
+  float (*const sbuf)[33][17] = reinterpret_cast<float (*)[33][17]>(lds_raw);
+  uint4* const tout = reinterpret_cast<uint4*>(lds_raw + kSbufBytes);
+
+  const int l = threadIdx.x;
+  const int hf = l >> 5;
+  const int i32 = l & 31;
+  const int part = i32 >> 4;
+  const int n_sc = i32 & 15;
+  const int64_t row = blockIdx.x;
+  const int c = static_cast<int>(row % D);
+  const float* lamc = lam + static_cast<int64_t>(c) * N;
+  const float* resc = res + static_cast<int64_t>(c) * N;
+  const bf16_t* x1r = x1 + row * L;
+  const bf16_t* x2r = x2 + row * L;
+  const bf16_t* vr = v + row * L;
+  bf16_t* yr = y + row * L;
+  const bool whole = (L == 1024);
+
+  // per-lane loads first (used after the inputs have arrived), then the
+  // inputs: chunks at or past L re-read the row's first chunk, an in-bounds
+  // address, and their runs are zeroed after they are read out
+  const float lam_ld = lamc[min(n_sc, N - 1)];
+  const float st_ld = state_in ? state_in[row * N + min(n_sc, N - 1)] : 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ch = unswz(64 * h + l);
+    const int src = (8 * ch < L) ? 8 * ch : 0;
+    dma16(x1r + src, &tin_w[0][64 * h]);
+    dma16(vr + src, &tin_w[1][64 * h]);
+    dma16(x2r + src, &tin_w[2][64 * h]);
+  }
+
+  // ---- h and G while the inputs are in flight (parameters: uniform loads)
+  float gv[8];                                 // G[i32][8 hf + j] = R_n p_n^(i32+1)
+  float hpart = 0.0f, h0part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int nlo = min(j, N - 1), nhi = min(8 + j, N - 1);
+    const float la = hf ? lamc[nhi] : lamc[nlo];
+    const float r = ((hf ? 8 + j : j) < N) ? (hf ? resc[nhi] : resc[nlo]) : 0.0f;
+    gv[j] = r * fast_exp(la * static_cast<float>(i32 + 1));
+    hpart += gv[j];
+    h0part += r;
+  }
+  const float hnext = hpart + xor32(hpart, hf);            // h[i32 + 1]
+  const float h0 = h0part + xor32(h0part, hf);             // h[0]
+  if (hf == 0) {
+    if (i32 < 31) hbuf[i32 + 1] = hnext;
+    if (i32 == 0) hbuf[0] = h0;
+  }
+  bf16x8 gm[3];
+  {
+    u32x4 w0, w1, w2;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t a, b, cc;
+      split3_pair(gv[2 * jj], gv[2 * jj + 1], a, b, cc);
+      w0[jj] = a;
+      w1[jj] = b;
+      w2[jj] = cc;
+    }
+    gm[0] = __builtin_bit_cast(bf16x8, w0);
+    gm[1] = __builtin_bit_cast(bf16x8, w1);
+    gm[2] = __builtin_bit_cast(bf16x8, w2);
+  }
+  lds_sync();
+  bf16x8 tm[3][2];                             // T[i32][tok] = h[i32 - tok], tok <= i32
+  split3_slots(
+      [&](int s, int j) {
+        const int d = i32 - blk_tok(8 * s + j, hf);
+        return (d >= 0) ? hbuf[d] : 0.0f;
+      },
+      tm);
+
+  // ---- the inputs: u = x1 v (two exact bf16 parts), skip * u, the gate
+  wait_vmem<0>();
+  Raw4<bf16_t> rx[4], rv[4], rg[4];
+  read_staged_runs(tin, i32, hf, rx, rv, rg);
+  if (!whole) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (32 * i32 + 4 * hf + 8 * q >= L) {
+        rx[q].w = make_uint2(0u, 0u);
+        rv[q].w = make_uint2(0u, 0u);
+        rg[q].w = make_uint2(0u, 0u);
+      }
+    }
+  }
+  const float sk = skip ? skip[c] : 0.0f;
+  float su[16];
+  bf16x8 um[2][2];
+  {
+    u32x4 uw[2][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const int r = 4 * q + e;
+        const float u0 = rx[q].get(e) * rv[q].get(e);
+        const float u1 = rx[q].get(e + 1) * rv[q].get(e + 1);
+        su[r] = sk * u0;
+        su[r + 1] = sk * u1;
+        const uint32_t p0 = cvt2(u0, u1);
+        uw[0][r >> 3][(r & 7) >> 1] = p0;
+        uw[1][r >> 3][(r & 7) >> 1] = cvt2(u0 - lo_f(p0), u1 - hi_f(p0));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      um[k][0] = __builtin_bit_cast(bf16x8, uw[k][0]);
+      um[k][1] = __builtin_bit_cast(bf16x8, uw[k][1]);
+    }
+  }
+  // in-block Toeplitz part of z
+  f32x16 cz = {};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    cz = mfma(tm[0][s], um[0][s], cz);
+    cz = mfma(tm[0][s], um[1][s], cz);
+    cz = mfma(tm[1][s], um[0][s], cz);
+    cz = mfma(tm[1][s], um[1][s], cz);
+    cz = mfma(tm[2][s], um[0][s], cz);
+  }
+
+  // ---- block-local end states, E^T = U^T P^T.  Scan lane: mode n_sc, part
+  // `part`; padded modes have p = 1 (their states never reach y: R = 0).
+  const float lam_n = (n_sc < N) ? lam_ld : 0.0f;
+  const float p1 = fast_exp(lam_n);
+  // weights p^(31 - tok): run m of the lane holds tokens 8m + 4hf + e, whose
+  // weight is p^(28 - 8m - 4hf) p^(3 - e)
+  auto run_weights = [&](float lam_v, int top, float (&w)[16]) {
+    const float p2 = p1 * p1, p3 = p2 * p1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d3 = top - 8 * m - 4 * hf - 3;
+      const float b = fast_exp(lam_v * static_cast<float>(d3));
+      w[4 * m + 3] = b;
+      w[4 * m + 2] = b * p1;
+      w[4 * m + 1] = b * p2;
+      w[4 * m + 0] = b * p3;
+    }
+  };
+  // slot (s, j) of the B operand holds run m = 2s + (j >> 2), element j & 3
+  auto weight_operands = [&](const float (&w)[16], bf16x8 (&pa)[2], bf16x8 (&pb)[2]) {
+    bf16x8 parts[3][2];
+    split3_slots([&](int s, int j) { return w[8 * s + j]; }, parts);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 q0 = __builtin_bit_cast(u32x4, parts[0][s]);
+      const u32x4 q1 = __builtin_bit_cast(u32x4, parts[1][s]);
+      const u32x4 q2 = __builtin_bit_cast(u32x4, parts[2][s]);
+      pa[s] = __builtin_bit_cast(bf16x8, part ? q1 : q0);
+      pb[s] = __builtin_bit_cast(bf16x8, part ? zero : q2);
+    }
+  };
+  f32x16 ce = {};
+  {
+    float w[16];
+    run_weights(lam_n, 31, w);
+    bf16x8 pa[2], pb[2];
+    weight_operands(w, pa, pb);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ce = mfma(um[0][s], pa[s], ce);
+      ce = mfma(um[1][s], pa[s], ce);
+      ce = mfma(um[0][s], pb[s], ce);
+    }
+  }
+
+  // ---- scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
+  const float a1 = fast_exp(lam_n * 32.0f), a2 = fast_exp(lam_n * 64.0f);
+  const float a3 = fast_exp(lam_n * 96.0f), a4 = fast_exp(lam_n * 128.0f);   // a4 = p^128
+  const float carry = (part == 0 && n_sc < N) ? st_ld : 0.0f;
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = ce[r];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int e = 1; e < 4; ++e) x[4 * q + e] = fmaf(a1, x[4 * q + e - 1], x[4 * q + e]);
+  }
+  // loc[rho]: state before run rho = 2q + half from a zero state at the
+  // tile's start; the true state adds p^(128 rho) carry
+  float loc[9];
+  loc[0] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float own = x[4 * q + 3], oth = xor32(own, hf);
+    loc[2 * q + 1] = fmaf(a4, loc[2 * q], hf ? oth : own);
+    loc[2 * q + 2] = fmaf(a4, loc[2 * q + 1], hf ? own : oth);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rho = 2 * q + hf;
+    const float ci = fmaf(fast_exp(lam_n * (128.0f * static_cast<float>(rho))), carry,
+                          hf ? loc[2 * q + 1] : loc[2 * q]);
+    x[4 * q + 0] = fmaf(a1, ci, x[4 * q + 0]);
+    x[4 * q + 1] = fmaf(a2, ci, x[4 * q + 1]);
+    x[4 * q + 2] = fmaf(a3, ci, x[4 * q + 2]);
+    x[4 * q + 3] = fmaf(a4, ci, x[4 * q + 3]);
+  }
+  // the inputs are in registers (read_staged_runs waited for its reads), so
+  // the states may go over them
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sbuf[part][blk_tok(r, hf) + 1][n_sc] = x[r];
+  sbuf[part][0][n_sc] = carry;
+  lds_sync();
+  // ---- z += G S, S = state before block i32 (the two parts summed)
+  {
+    u32x4 sw[3];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const int n = 8 * hf + j;
+      uint32_t s0, s1, s2;
+      split3_pair(sbuf[0][i32][n] + sbuf[1][i32][n], sbuf[0][i32][n + 1] + sbuf[1][i32][n + 1],
+                  s0, s1, s2);
+      sw[0][j >> 1] = s0;
+      sw[1][j >> 1] = s1;
+      sw[2][j >> 1] = s2;
+    }
+    const bf16x8 sm0 = __builtin_bit_cast(bf16x8, sw[0]);
+    const bf16x8 sm1 = __builtin_bit_cast(bf16x8, sw[1]);
+    const bf16x8 sm2 = __builtin_bit_cast(bf16x8, sw[2]);
+    cz = mfma(gm[0], sm0, cz);
+    cz = mfma(gm[0], sm1, cz);
+    cz = mfma(gm[1], sm0, cz);
+    cz = mfma(gm[1], sm1, cz);
+    cz = mfma(gm[0], sm2, cz);
+    cz = mfma(gm[2], sm0, cz);
+  }
+  // ---- y = x2 z + skip u, staged and stored in coalesced 16-byte chunks
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = fmaf(rg[q].get(e), cz[4 * q + e], su[4 * q + e]);
+    reinterpret_cast<uint2*>(&tout[swz(4 * i32 + q)])[hf] =
+        make_uint2(cvt2(o[0], o[1]), cvt2(o[2], o[3]));
+  }
+  lds_sync();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (whole || 8 * (l + 64 * h) < L) store16_nt(yr + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
+
+  // ---- state after token L - 1
+  if (whole) {
+    // p^1024 carry + loc[8], the two parts summed
+    const float fin = fmaf(fast_exp(lam_n * 1024.0f), carry, loc[8]);
+    const float tot = fin + xor16(fin, l);
+    if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
+  } else {
+    // the sequence ends in block bstar after token estar: p^(estar+1) times
+    // the state before the block plus the block's own end state at estar
+    const int bstar = (L - 1) >> 5;
+    const int estar = (L - 1) & 31;
+    float w[16];
+    run_weights(lam_n, estar, w);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int tok = blk_tok(8 * (k >> 3) + (k & 7), hf);
+      if (tok > estar) w[k] = 0.0f;
+    }
+    bf16x8 qa[2], qb[2];
+    weight_operands(w, qa, qb);
+    f32x16 cf = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      cf = mfma(um[0][s], qa[s], cf);
+      cf = mfma(um[1][s], qa[s], cf);
+      cf = mfma(um[0][s], qb[s], cf);
+    }
+    const bool mine = (((bstar >> 2) & 1) == hf);
+    const int rs = 4 * (bstar >> 3) + (bstar & 3);
+    float ev = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ev = (r == rs) ? cf[r] : ev;
+    const float fin =
+        mine ? fmaf(fast_exp(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev)
+             : 0.0f;
+    const float tot = fin + xor16(fin, l);
+    if (mine && part == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
+  }
+}
+
 template <typename IO, bool VEC, bool PIPE, bool CPX>
 static hipError_t launch_mfma_k(const ChunkArgs& a) {
   dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
@@ -847,6 +1161,16 @@ static hipError_t launch_mfma_modes(const ChunkArgs& a) {
   if (!a.bf16)
     return vec ? launch_mfma_k<float, true, false, CPX>(a) : launch_mfma_k<float, false, false, CPX>(a);
   if (!vec) return launch_mfma_k<bf16_t, false, false, CPX>(a);
+  if constexpr (!CPX) {
+    if (a.L <= 1024) {
+      dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
+      chunk_one_kernel<<<grid, block, 0, a.stream>>>(
+          static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
+          static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
+          static_cast<bf16_t*>(a.y), a.D, a.L);
+      return hipGetLastError();
+    }
+  }
   return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true, CPX>(a)
                      : launch_mfma_k<bf16_t, true, false, CPX>(a);
 }

@@ -213,6 +213,24 @@ def test_chunk_mfma_one_tile_rows_many():
         state_gate(s, ref_s, rows, label="chunk/mfma rows>waves")
 
 
+@pytest.mark.parametrize("N", [1, 5, 16])
+@pytest.mark.parametrize("L", [1024, 520])
+def test_chunk_one_tile_mode_counts(N, L):
+    """Rows of at most one 1024-token tile (one chunk per call) with fewer
+    modes than scan lanes: the padded lanes' states reach neither y nor
+    state_out; a whole tile and a partial one, state in and out."""
+    w = W.make("7b_layer_set", B=2, D=6, L=L, N=N)
+    d = DevWorkload(w)
+    s0 = W.random_state(w.B, w.D, w.N, seed=N + L)
+    for state in (None, s0):
+        sin = None if state is None else par_to_dev(state)
+        log(f"chunk one tile N={N} L={L} state={'yes' if state is not None else 'no'}")
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, state_in=sin, algo="mfma")
+        ref_y, ref_s = oracle_modal(w, C=1024, state_in=state)
+        gate(y, ref_y, "bf16", label=f"chunk one tile N={N} L={L}")
+        state_gate(s, ref_s, label=f"chunk one tile N={N} L={L}")
+
+
 @pytest.mark.parametrize("N", [1, 3, 17, 64])
 def test_mode_counts(N):
     """From one mode to the maximum of 64: single pass, chunked with AUTO (the
@@ -289,13 +307,15 @@ def test_chunked_equals_single_pass_on_gpu():
 
 
 @pytest.mark.parametrize("algo,C", [("mfma", 1024), ("mfma", 4096), ("fft", 1024), ("fft", 4096),
-                                    ("fftconv", 0)])
+                                    ("fftconv", 0), ("mfma_calls", 1024)])
 def test_slow_cancelling_modes(algo, C):
     """Two slow modes (|lam| ~ 1e-5, remembered for ~1e5 tokens) with nearly
     equal poles and opposite residues: each mode's carried term is many times
     the output, so a relative error of the carried state that a long scan
     compounds (a decay factor rounded once and applied thousands of times)
-    shows up in the output at full size."""
+    shows up in the output at full size.  mfma_calls: 128 calls of one
+    1024-token chunk each, the fp32 state handed from call to call (the
+    one-tile kernel, whose decay factors are single fp32 values)."""
     w = W.make("262k", D=8, L=131072)
     rng = np.random.default_rng(17)
     lam = w.log_poles.copy()
@@ -312,7 +332,15 @@ def test_slow_cancelling_modes(algo, C):
         y = G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)
         gate(y, ref, "bf16", label="fftconv slow modes")
         return
-    y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
+    if algo == "mfma_calls":
+        ys, s = [], None
+        for t0 in range(0, w.L, C):
+            sl = [t[..., t0:t0 + C].contiguous() for t in (d.x1, d.x2, d.v)]
+            yc, s = G.chunk_fwd(*sl, d.lam, d.res, C, d.skip, state_in=s, algo="mfma")
+            ys.append(yc)
+        y = torch.cat(ys, -1)
+    else:
+        y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, C, d.skip, algo=algo)
     gate(y, ref, "bf16", label=f"chunk/{algo} C={C} slow modes")
     state_gate(s, ref_s, label=f"chunk/{algo} C={C} slow modes")
 
