@@ -549,6 +549,20 @@ def main():
                 s_in = sts[i & 1]
 
         runs[f"chunk_{algo_used}_x{nch}_calls"] = rotating(per_chunk_calls, INPUT_SETS)
+        # the same calls captured once per input set in a HIP graph and
+        # replayed, as a serving loop would issue them: the kernels back to
+        # back without the binding's per-call host work (argument checks,
+        # stream lookup, the foreign call)
+        graphs = []
+        for k in range(INPUT_SETS):
+            per_chunk_calls(k)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                per_chunk_calls(k)
+            graphs.append(g)
+        runs[f"chunk_{algo_used}_x{nch}_calls_graph"] = rotating(lambda k: graphs[k].replay(),
+                                                                 INPUT_SETS)
         # one decode step per row from the caches (B=1, D=4096: latency-bound)
         tok = [t[..., L - 1].contiguous() for t in (x1, x2, v)]
         y1 = torch.empty_like(tok[0])
@@ -590,7 +604,7 @@ def main():
             n_tc = B * D if name in one_token else tc
             comps[name] = {"ms": round(t * 1e3, 4), "Gtc_per_s": round(n_tc / t / 1e9, 2),
                            "hbm_frac": round(8 * n_tc / t / 1e9 / HBM_PEAK_GBS, 4)}
-        del xs, ycs, xins, y_tms, tm_ws, fft_ws
+        del xs, ycs, xins, y_tms, tm_ws, fft_ws, graphs
         torch.cuda.empty_cache()
 
     pool = None if args.no_cpu_baseline else OraclePool()

@@ -878,11 +878,19 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   bf16_t* yr = y + row * L;
   const bool whole = (L == 1024);
 
-  // per-lane loads first (used after the inputs have arrived), then the
-  // inputs: chunks at or past L re-read the row's first chunk, an in-bounds
-  // address, and their runs are zeroed after they are read out
-  const float lam_ld = lamc[min(n_sc, N - 1)];
+  // The parameters first, then the inputs: chunks at or past L re-read the
+  // row's first chunk, an in-bounds address, and their runs are zeroed after
+  // they are read out.  Everything before the inputs' 6 DMA loads is waited
+  // for with vmcnt(6), so the setup below runs while the inputs are in flight.
+  const float lam_ld = lamc[min(n_sc, N - 1)];           // the scan lane's pole
   const float st_ld = state_in ? state_in[row * N + min(n_sc, N - 1)] : 0.0f;
+  float g_lam[8], g_res[8];                              // G's slots: modes 8 hf + j
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = min(8 * hf + j, N - 1);
+    g_lam[j] = lamc[n];
+    g_res[j] = resc[n];
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int ch = unswz(64 * h + l);
@@ -892,15 +900,25 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
     dma16(x2r + src, &tin_w[2][64 * h]);
   }
 
-  // ---- h and G while the inputs are in flight (parameters: uniform loads)
+  // ---- h and G while the inputs are in flight.  The loaded values pass
+  // through an empty asm after the wait, so that no use of them is scheduled
+  // above it (the compiler would guard such a use with a wait for every
+  // load, the DMAs included).
+  wait_vmem<6>();
+  float lam_sc = lam_ld, st_sc = st_ld;
+  pin(lam_sc);
+  pin(st_sc);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pin(g_lam[j]);
+    pin(g_res[j]);
+  }
   float gv[8];                                 // G[i32][8 hf + j] = R_n p_n^(i32+1)
   float hpart = 0.0f, h0part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int nlo = min(j, N - 1), nhi = min(8 + j, N - 1);
-    const float la = hf ? lamc[nhi] : lamc[nlo];
-    const float r = ((hf ? 8 + j : j) < N) ? (hf ? resc[nhi] : resc[nlo]) : 0.0f;
-    gv[j] = r * fast_exp(la * static_cast<float>(i32 + 1));
+    const float r = (8 * hf + j < N) ? g_res[j] : 0.0f;
+    gv[j] = r * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
     hpart += gv[j];
     h0part += r;
   }
@@ -933,6 +951,62 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
         return (d >= 0) ? hbuf[d] : 0.0f;
       },
       tm);
+
+  // ---- the scan lane's operands, also before the inputs arrive: the
+  // end-state weights and the scan's decay factors.  Scan lane: mode n_sc,
+  // part `part`; padded modes have p = 1 (their states never reach y: R = 0).
+  const float lam_n = (n_sc < N) ? lam_sc : 0.0f;
+  const float p1 = fast_exp(lam_n);
+  // weights p^(31 - tok): run m of the lane holds tokens 8m + 4hf + e, whose
+  // weight is p^(28 - 8m - 4hf) p^(3 - e)
+  auto run_weights = [&](float lam_v, int top, float (&w)[16]) {
+    const float p2 = p1 * p1, p3 = p2 * p1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d3 = top - 8 * m - 4 * hf - 3;
+      const float b = fast_exp(lam_v * static_cast<float>(d3));
+      w[4 * m + 3] = b;
+      w[4 * m + 2] = b * p1;
+      w[4 * m + 1] = b * p2;
+      w[4 * m + 0] = b * p3;
+    }
+  };
+  // slot (s, j) of the B operand holds run m = 2s + (j >> 2), element j & 3
+  auto weight_operands = [&](const float (&w)[16], bf16x8 (&pa)[2], bf16x8 (&pb)[2]) {
+    bf16x8 parts[3][2];
+    split3_slots([&](int s, int j) { return w[8 * s + j]; }, parts);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 q0 = __builtin_bit_cast(u32x4, parts[0][s]);
+      const u32x4 q1 = __builtin_bit_cast(u32x4, parts[1][s]);
+      const u32x4 q2 = __builtin_bit_cast(u32x4, parts[2][s]);
+      pa[s] = __builtin_bit_cast(bf16x8, part ? q1 : q0);
+      pb[s] = __builtin_bit_cast(bf16x8, part ? zero : q2);
+    }
+  };
+  bf16x8 pa[2], pb[2];
+  {
+    float w[16];
+    run_weights(lam_n, 31, w);
+    weight_operands(w, pa, pb);
+  }
+  float a1 = fast_exp(lam_n * 32.0f), a2 = fast_exp(lam_n * 64.0f);
+  float a3 = fast_exp(lam_n * 96.0f), a4 = fast_exp(lam_n * 128.0f);   // a4 = p^128
+  float fr[4];                                 // p^(128 rho), rho = 2q + hf
+#pragma unroll
+  for (int q = 0; q < 4; ++q) fr[q] = fast_exp(lam_n * (128.0f * static_cast<float>(2 * q + hf)));
+  const float p1024 = fast_exp(lam_n * 1024.0f);
+  // formed here, not next to their uses after the wait below
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    pin(pa[s]);
+    pin(pb[s]);
+  }
+  pin(a1);
+  pin(a2);
+  pin(a3);
+  pin(a4);
 
   // ---- the inputs: u = x1 v (two exact bf16 parts), skip * u, the gate
   wait_vmem<0>();
@@ -984,56 +1058,17 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
     cz = mfma(tm[2][s], um[0][s], cz);
   }
 
-  // ---- block-local end states, E^T = U^T P^T.  Scan lane: mode n_sc, part
-  // `part`; padded modes have p = 1 (their states never reach y: R = 0).
-  const float lam_n = (n_sc < N) ? lam_ld : 0.0f;
-  const float p1 = fast_exp(lam_n);
-  // weights p^(31 - tok): run m of the lane holds tokens 8m + 4hf + e, whose
-  // weight is p^(28 - 8m - 4hf) p^(3 - e)
-  auto run_weights = [&](float lam_v, int top, float (&w)[16]) {
-    const float p2 = p1 * p1, p3 = p2 * p1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int d3 = top - 8 * m - 4 * hf - 3;
-      const float b = fast_exp(lam_v * static_cast<float>(d3));
-      w[4 * m + 3] = b;
-      w[4 * m + 2] = b * p1;
-      w[4 * m + 1] = b * p2;
-      w[4 * m + 0] = b * p3;
-    }
-  };
-  // slot (s, j) of the B operand holds run m = 2s + (j >> 2), element j & 3
-  auto weight_operands = [&](const float (&w)[16], bf16x8 (&pa)[2], bf16x8 (&pb)[2]) {
-    bf16x8 parts[3][2];
-    split3_slots([&](int s, int j) { return w[8 * s + j]; }, parts);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const u32x4 q0 = __builtin_bit_cast(u32x4, parts[0][s]);
-      const u32x4 q1 = __builtin_bit_cast(u32x4, parts[1][s]);
-      const u32x4 q2 = __builtin_bit_cast(u32x4, parts[2][s]);
-      pa[s] = __builtin_bit_cast(bf16x8, part ? q1 : q0);
-      pb[s] = __builtin_bit_cast(bf16x8, part ? zero : q2);
-    }
-  };
+  // ---- block-local end states, E^T = U^T P^T
   f32x16 ce = {};
-  {
-    float w[16];
-    run_weights(lam_n, 31, w);
-    bf16x8 pa[2], pb[2];
-    weight_operands(w, pa, pb);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      ce = mfma(um[0][s], pa[s], ce);
-      ce = mfma(um[1][s], pa[s], ce);
-      ce = mfma(um[0][s], pb[s], ce);
-    }
+  for (int s = 0; s < 2; ++s) {
+    ce = mfma(um[0][s], pa[s], ce);
+    ce = mfma(um[1][s], pa[s], ce);
+    ce = mfma(um[0][s], pb[s], ce);
   }
 
   // ---- scan over the 32 blocks; register r holds block 8(r>>2) + 4hf + (r&3)
-  const float a1 = fast_exp(lam_n * 32.0f), a2 = fast_exp(lam_n * 64.0f);
-  const float a3 = fast_exp(lam_n * 96.0f), a4 = fast_exp(lam_n * 128.0f);   // a4 = p^128
-  const float carry = (part == 0 && n_sc < N) ? st_ld : 0.0f;
+  const float carry = (part == 0 && n_sc < N) ? st_sc : 0.0f;
   float x[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = ce[r];
@@ -1054,9 +1089,7 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int rho = 2 * q + hf;
-    const float ci = fmaf(fast_exp(lam_n * (128.0f * static_cast<float>(rho))), carry,
-                          hf ? loc[2 * q + 1] : loc[2 * q]);
+    const float ci = fmaf(fr[q], carry, hf ? loc[2 * q + 1] : loc[2 * q]);
     x[4 * q + 0] = fmaf(a1, ci, x[4 * q + 0]);
     x[4 * q + 1] = fmaf(a2, ci, x[4 * q + 1]);
     x[4 * q + 2] = fmaf(a3, ci, x[4 * q + 2]);
@@ -1108,7 +1141,7 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   // ---- state after token L - 1
   if (whole) {
     // p^1024 carry + loc[8], the two parts summed
-    const float fin = fmaf(fast_exp(lam_n * 1024.0f), carry, loc[8]);
+    const float fin = fmaf(p1024, carry, loc[8]);
     const float tot = fin + xor16(fin, l);
     if (part == 0 && hf == 0 && n_sc < N) state_out[row * N + n_sc] = tot;
   } else {

@@ -10,7 +10,7 @@ import torch
 
 import genomic_lm_amd as G
 import workloads as W
-from tests.gpu_util import DevWorkload, act_to_dev, log
+from tests.gpu_util import DevWorkload, act_to_dev, gate, log, oracle_modal, state_gate
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +122,50 @@ def test_graph_capture_and_replay():
         for k in lists:
             for a, b in zip(cap[k], ref[k]):
                 assert torch.equal(a, b), (rep, k)
+
+
+@pytest.mark.parametrize("C", [1024, 512, 3072])
+def test_chunk_calls_graph_replay(C):
+    """A prefill as one call per chunk, the state handed from call to call
+    (the form a serving loop replays without per-call host work): every
+    replay equals the eager calls bit for bit, and those pass the oracle
+    gates.  C = 1024 and 512 run the one-tile kernel (whole and partial
+    tiles), 3072 the general one."""
+    w = W.make("7b_layer_set", B=2, D=48, L=6 * 1024)
+    d = DevWorkload(w)
+    dev = d.x1.device
+    chunks = [[t[..., t0:t0 + C].contiguous() for t in (d.x1, d.x2, d.v)]
+              for t0 in range(0, w.L, C)]
+    ys = [torch.empty_like(c[0]) for c in chunks]
+    sts = [torch.empty((w.B, w.D, w.N), dtype=torch.float32, device=dev) for _ in range(2)]
+    last = (len(chunks) - 1) & 1
+
+    def calls():
+        s_in = None
+        for i, (a, b, c) in enumerate(chunks):
+            G.chunk_fwd(a, b, c, d.lam, d.res, C, d.skip, state_in=s_in, out=ys[i],
+                        state_out=sts[i & 1])
+            s_in = sts[i & 1]
+
+    log(f"graph replay of {len(chunks)} chunk calls, C={C}: eager")
+    calls()
+    torch.cuda.synchronize()
+    y_eager = torch.cat(ys, -1)
+    s_eager = sts[last].clone()
+    ref, ref_s = oracle_modal(w)
+    gate(y_eager, ref, "bf16", label=f"chunk calls C={C} eager")
+    state_gate(s_eager, ref_s, label=f"chunk calls C={C} eager")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        for t in ys + sts:
+            t.fill_(float("nan"))
+        G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip)     # unrelated eager work
+        torch.cuda.synchronize()
+        log(f"  replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(ys, -1), y_eager), f"replay {rep}: y differs"
+        assert torch.equal(sts[last], s_eager), f"replay {rep}: state differs"
