@@ -592,6 +592,8 @@ def main():
                             dtype=torch.uint8, device=dev)
         runs["chunk_tokmajor"] = rotating(lambda k: G.chunk_fwd_tokmajor(
             xins[k], lam, res, skip, out=y_tms[k], state_out=st, workspace=tm_ws), INPUT_SETS)
+        runs["chunk_tokmajor_mfma"] = rotating(lambda k: G.chunk_fwd_tokmajor(
+            xins[k], lam, res, skip, out=y_tms[k], state_out=st, algo="mfma"), INPUT_SETS)
         win6 = torch.empty((B, D, 6), dtype=torch.float32, device=dev)
         win127 = torch.empty((B, D, 127), dtype=torch.float32, device=dev)
         runs["fir7_tokmajor"] = rotating(lambda k: G.fir_fwd_tokmajor(

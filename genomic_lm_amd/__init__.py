@@ -51,6 +51,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena.so
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "fft": 1, "mfma": 2}
+TOKMAJOR_ALGOS = {"auto": 0, "mfma": 2, "recurrence": 3}
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -88,6 +89,9 @@ EXPORTS = {
     "hyena_chunk_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
                                         _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int, _p,
                                         _size, _p]),
+    "hyena_chunk_fwd_tokmajor_algo": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             _p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int,
+                                             _int, _p, _size, _p]),
     "hyena_chunk_tokmajor_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
     "hyena_fir_fwd_tokmajor": (_int, [_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _p,
                                       _i64, _p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
@@ -458,10 +462,13 @@ def chunk_tokmajor_workspace_size(B: int, D: int, L: int, N: int, dtype=torch.bf
 
 
 def chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None, pos=(0, 1, 2),
-                       out=None, state_out=None, workspace=None):
+                       out=None, state_out=None, workspace=None, algo: str = "auto"):
     """The modal operator on in_proj's token-major layout: xin (B, L, 3D) with
     channel c's x1, x2, v at columns 3c + pos[0], 3c + pos[1], 3c + pos[2];
-    returns (y (B, L, D), state_out (B, D, N))."""
+    returns (y (B, L, D), state_out (B, D, N)).  algo "auto" calls
+    hyena_chunk_fwd_tokmajor, "mfma" / "recurrence" hyena_chunk_fwd_tokmajor_algo."""
+    if algo not in TOKMAJOR_ALGOS:
+        raise ValueError(f"algo must be one of {sorted(TOKMAJOR_ALGOS)}")
     _act("xin", xin)
     B, L, D3 = xin.shape
     if D3 % 3:
@@ -488,10 +495,14 @@ def chunk_fwd_tokmajor(xin, log_poles, residues, skip=None, state_in=None, pos=(
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=xin.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hyena_chunk_fwd_tokmajor", lib().hyena_chunk_fwd_tokmajor(
-        _ptr(xin), int(pos[0]), int(pos[1]), int(pos[2]), _ptr(log_poles), _ptr(residues), N,
-        _ptr(skip), _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, _io(xin),
-        _ptr(workspace), ws_bytes, _stream(xin)))
+    args = (_ptr(xin), int(pos[0]), int(pos[1]), int(pos[2]), _ptr(log_poles), _ptr(residues), N,
+            _ptr(skip), _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, _io(xin))
+    if algo == "auto":
+        _check("hyena_chunk_fwd_tokmajor", lib().hyena_chunk_fwd_tokmajor(
+            *args, _ptr(workspace), ws_bytes, _stream(xin)))
+    else:
+        _check("hyena_chunk_fwd_tokmajor_algo", lib().hyena_chunk_fwd_tokmajor_algo(
+            *args, TOKMAJOR_ALGOS[algo], _ptr(workspace), ws_bytes, _stream(xin)))
     return y, state_out
 
 

@@ -163,33 +163,146 @@ __device__ __forceinline__ DF df_step_cpx(float ah, float al, DF c, float bh, fl
   return df_two_sum(s2.hi, lo);
 }
 
+// TM (below): the per-wave block states go through LDS in asm blocks.  With
+// 8 waves a workgroup indexes its state buffers by the wave, which the
+// compiler cannot tell apart from the tile buffers that DMA loads are
+// filling, so it would make every plain access wait for all of them.
+// States after the lane's 16 blocks, sbuf[part][blk + 1][n_sc], and the state
+// before block 0, sbuf[part][0][n_sc] (rows of 17 floats, 68 bytes): `wr` is
+// &sbuf[part][4 hf + 1][n_sc], `w0` &sbuf[part][0][n_sc].
+__device__ __forceinline__ void sbuf_store_asm(uint32_t wr, uint32_t w0, const float (&x)[16],
+                                               float carry) {
+  asm volatile(
+      "ds_write_b32 %0, %2\n\t"
+      "ds_write_b32 %0, %3 offset:68\n\t"
+      "ds_write_b32 %0, %4 offset:136\n\t"
+      "ds_write_b32 %0, %5 offset:204\n\t"
+      "ds_write_b32 %0, %6 offset:544\n\t"
+      "ds_write_b32 %0, %7 offset:612\n\t"
+      "ds_write_b32 %0, %8 offset:680\n\t"
+      "ds_write_b32 %0, %9 offset:748\n\t"
+      "ds_write_b32 %0, %10 offset:1088\n\t"
+      "ds_write_b32 %0, %11 offset:1156\n\t"
+      "ds_write_b32 %0, %12 offset:1224\n\t"
+      "ds_write_b32 %0, %13 offset:1292\n\t"
+      "ds_write_b32 %0, %14 offset:1632\n\t"
+      "ds_write_b32 %0, %15 offset:1700\n\t"
+      "ds_write_b32 %0, %16 offset:1768\n\t"
+      "ds_write_b32 %0, %17 offset:1836\n\t"
+      "ds_write_b32 %1, %18"
+      :
+      : "v"(wr), "v"(w0), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),
+        "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]),
+        "v"(x[13]), "v"(x[14]), "v"(x[15]), "v"(carry)
+      : "memory");
+}
+
+// sbuf[0][i32][8 hf + j] + sbuf[1][i32][8 hf + j], j < 8 (the parts are 33
+// rows = 2244 bytes apart); `rd` is &sbuf[0][i32][8 hf].  Waits for its reads.
+__device__ __forceinline__ void sbuf_load_asm(uint32_t rd, float (&sv)[8]) {
+  float a[16];
+  asm volatile(
+      "ds_read_b32 %0, %16\n\t"
+      "ds_read_b32 %1, %16 offset:4\n\t"
+      "ds_read_b32 %2, %16 offset:8\n\t"
+      "ds_read_b32 %3, %16 offset:12\n\t"
+      "ds_read_b32 %4, %16 offset:16\n\t"
+      "ds_read_b32 %5, %16 offset:20\n\t"
+      "ds_read_b32 %6, %16 offset:24\n\t"
+      "ds_read_b32 %7, %16 offset:28\n\t"
+      "ds_read_b32 %8, %16 offset:2244\n\t"
+      "ds_read_b32 %9, %16 offset:2248\n\t"
+      "ds_read_b32 %10, %16 offset:2252\n\t"
+      "ds_read_b32 %11, %16 offset:2256\n\t"
+      "ds_read_b32 %12, %16 offset:2260\n\t"
+      "ds_read_b32 %13, %16 offset:2264\n\t"
+      "ds_read_b32 %14, %16 offset:2268\n\t"
+      "ds_read_b32 %15, %16 offset:2272\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7]), "=&v"(a[8]), "=&v"(a[9]), "=&v"(a[10]), "=&v"(a[11]),
+        "=&v"(a[12]), "=&v"(a[13]), "=&v"(a[14]), "=&v"(a[15])
+      : "v"(rd)
+      : "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sv[j] = a[j] + a[8 + j];
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)(p)));
+}
+
 // VEC: rows of whole 16-byte chunks, 16-byte aligned (full tiles take the
 // unchecked path).  PIPE (bf16, VEC, L >= 2048): at least two full tiles, so
 // the first two DMAs are issued without a branch.  CPX: N complex modes as
 // 2N slots (above).
-template <typename IO, bool VEC, bool PIPE, bool CPX>
-__global__ __launch_bounds__(64) void chunk_mfma_kernel(
+//
+// TM: the token-major layout of in_proj's output, xin (B, L, 3D) with each
+// channel's x1, x2, v side by side at elements 3c + pos1 / pos2 / posv
+// (Hyena channels interleaved per triple: evo2_flash README, Limitations),
+// y (B, L, D) for out_proj.  A workgroup of 8 waves takes 8 consecutive
+// channels, one wave per channel running the per-wave computation above
+// unchanged; only the staging differs.  A tile's 1024 token rows of the
+// block's 48-byte span (3 x 16-byte chunks per row, 6 DMA loads per thread as
+// in the channel-major case) go to LDS row by row, slot 3 tm_swz(t) + j for
+// chunk j of token t, and each wave gathers its channel's runs from
+// there (the three chunks of a row side by side, so that one DMA instruction
+// reads whole 48-byte pieces of ~21 rows: one piece per lane measured 0.47
+// against 0.26 ms with the same bytes read contiguously); y goes back through
+// a token-major tile (16 bytes = the block's 8 channels per token) and leaves
+// as one 16-byte piece per token row.  The
+// rows are read and written 48 / 16 bytes at a time, so each group of 8
+// neighbouring channel blocks (whole 128-byte lines) is put on one XCD
+// (workgroups are dispatched round-robin over the 8 XCDs), where they share
+// the L2 lines, and the groups an XCD holds at once lie 64 blocks apart along
+// the row, spread over its L2 channels.  Measured at B=1 D=4096 L=32768:
+// 0.41 ms, against 0.86 ms with the blocks in launch order and 0.44 ms with
+// the groups of one XCD side by side.
+// Every input byte is read once and y written once: 8 bytes per token and
+// channel at bf16.  Waves of a workgroup meet at s_barrier where a tile
+// buffer or the y tile changes hands (wg_sync below).
+template <typename IO, bool VEC, bool PIPE, bool CPX, bool TM = false>
+__global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, const float* state_in,
-    float* state_out, IO* __restrict__ y, int D, int L) {
+    float* state_out, IO* __restrict__ y, int D, int L, int pos1, int pos2, int posv) {
+  static_assert(!TM || (sizeof(IO) == 2 && VEC && !CPX), "TM: bf16 rows of 16-byte chunks, real modes");
   // parts of u: x1*v of two bf16 values is exactly two bf16 parts
   constexpr int NU = (sizeof(IO) == 2) ? 2 : 3;
-  __shared__ float hbuf[32];
-  // state before block b, per part and mode (row 32: unused); two copies
-  // used by alternate tiles, so a tile's writes never meet the previous
-  // tile's reads
-  __shared__ float sbufs[1][2][33][17];
-  // staged x1, v, x2 tiles (bf16, swizzled chunks), two tiles in turn, and
-  // the staged y tile
-  __shared__ uint4 tin_a[3][128], tin_b[3][128];
-  __shared__ uint4 tout[128];
+  constexpr int NWV = TM ? 8 : 1;             // waves (channels) per workgroup
+  __shared__ float hbufs[NWV][32];
+  // state before block b, per part and mode (row 32: unused)
+  __shared__ float sbufs[NWV][2][33][17];
+  // staged x1, v, x2 tiles (bf16, swizzled chunks; TM: 3 chunks of each of
+  // 1024 token rows), two tiles in turn, and the staged y tile
+  __shared__ uint4 tin_a_s[TM ? 3 * 1024 : 3 * 128], tin_b_s[TM ? 3 * 1024 : 3 * 128];
+  __shared__ uint4 tout[TM ? 1024 : 128];
+  uint4 (*const tin_a)[128] = reinterpret_cast<uint4 (*)[128]>(tin_a_s);
+  uint4 (*const tin_b)[128] = reinterpret_cast<uint4 (*)[128]>(tin_b_s);
 
-  const int l = threadIdx.x;
+  const int l = static_cast<int>(threadIdx.x & 63);
+  // (a scalar, so that the channel's parameters are scalar loads)
+  const int wv = TM ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) : 0;
+  float* const hbuf = hbufs[wv];
   const int hf = l >> 5;                      // half-wave
   const int i32 = l & 31;                     // row of A / column of B and C
-  const int64_t row = blockIdx.x;
-  const int c = static_cast<int>(row % D);
+  int64_t row;
+  int c;
+  int64_t bat = 0;                            // TM: batch item and channel block
+  int cblk = 0;
+  if constexpr (TM) {
+    const int64_t nwg = gridDim.x, g = blockIdx.x;
+    const int64_t lg = (nwg % 64 == 0) ? 64 * (g / 64) + 8 * (g % 8) + (g / 8) % 8 : g;
+    const int nblk = D >> 3;
+    bat = lg / nblk;
+    cblk = static_cast<int>(lg % nblk);
+    c = 8 * cblk + wv;
+    row = bat * D + c;
+  } else {
+    row = blockIdx.x;
+    c = static_cast<int>(row % D);
+  }
   const int NS = CPX ? 2 * N : N;             // slots: floats per channel of lam, res, state
   const float* lamc = lam + static_cast<int64_t>(c) * NS;
   const float* resc = res + static_cast<int64_t>(c) * NS;
@@ -206,14 +319,37 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // that they leave before the other wave on the SIMD resumes its MFMA / scan
   // work: 205.0-206.0 -> 202.7-203.1 us per 32k-token step at D = 4096 (four
   // alternating measurements, rotating input sets).
+  // TM: token rows of the channel block; instruction k of wave wv fills
+  // slots [64 (6 wv + k), +64): chunk j = slot % 3 of token tm_swz(slot / 3)
+  const int64_t ld3 = 3 * static_cast<int64_t>(D);
+  const IO* const xb = x1 + bat * L * ld3 + 24 * cblk;
+  IO* const yb = y + bat * L * static_cast<int64_t>(D) + 8 * cblk;
+  // (byte offsets within a tile fit 32 bits: 1024 rows of 6 D bytes)
+  auto prefetch_tm = [&](int64_t t0, uint4 (*tin)[128], bool clamp) {
+    uint4* const tf = &tin[0][0];
+    const char* const xt = reinterpret_cast<const char*>(xb + t0 * ld3);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int g = 6 * wv + k;
+      const int s = 64 * g + l;
+      const int tt = tm_swz(s / 3);
+      const int te = (clamp && t0 + tt >= L) ? 0 : tt;
+      dma16_shared(xt + (static_cast<uint32_t>(te) * static_cast<uint32_t>(2 * ld3) + 16u * (s % 3)),
+                   tf + 64 * g);
+    }
+  };
   auto prefetch = [&](int64_t t0, uint4 (*tin)[128]) {
     __builtin_amdgcn_s_setprio(2);
+    if constexpr (TM) {
+      prefetch_tm(t0, tin, false);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ch = unswz(64 * h + l);
-      dma16(x1r + t0 + 8 * ch, &tin[0][64 * h]);
-      dma16(vr + t0 + 8 * ch, &tin[1][64 * h]);
-      dma16(x2r + t0 + 8 * ch, &tin[2][64 * h]);
+      for (int h = 0; h < 2; ++h) {
+        const int ch = unswz(64 * h + l);
+        dma16(x1r + t0 + 8 * ch, &tin[0][64 * h]);
+        dma16(vr + t0 + 8 * ch, &tin[1][64 * h]);
+        dma16(x2r + t0 + 8 * ch, &tin[2][64 * h]);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -222,6 +358,10 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // tile's first chunk, an in-bounds address, and their runs are zeroed after
   // they are read out.
   auto prefetch_part = [&](int64_t t0, uint4 (*tin)[128]) {
+    if constexpr (TM) {
+      prefetch_tm(t0, tin, true);
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ch = unswz(64 * h + l);
@@ -282,6 +422,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // h[d], d < 32.  The mode loop has its fixed maximum trip count so that
   // all parameter loads are issued together (a loop over the runtime N
   // waited on one load per mode, the bulk of a one-tile call's set-up).
+  float hsh = 0.0f;
   {
     float hd = 0.0f;
     if constexpr (CPX) {
@@ -298,15 +439,25 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
         if (n < N) hd = fmaf(resc[n], fast_exp(lamc[n] * static_cast<float>(i32)), hd);
       }
     }
-    if (hf == 0) hbuf[i32] = hd;
+    if constexpr (TM) {
+      hsh = hd;                               // both half-waves hold h[i32]
+    } else {
+      if (hf == 0) hbuf[i32] = hd;
+    }
   }
   lds_sync();
   // A = T (row i32, slot (s,j) -> token blk_tok): T[i][tok] = h[i - tok] for tok <= i
+  // (TM: h[d] from lane d by a shuffle, which touches no LDS memory)
   bf16x8 tm[3][2];
   split3_slots(
       [&](int s, int j) {
         const int d = i32 - blk_tok(8 * s + j, hf);
-        return (d >= 0) ? hbuf[d] : 0.0f;
+        if constexpr (TM) {
+          const float hv = __shfl(hsh, d & 31);
+          return (d >= 0) ? hv : 0.0f;
+        } else {
+          return (d >= 0) ? hbuf[d] : 0.0f;
+        }
       },
       tm);
   // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1);
@@ -445,15 +596,27 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
   // called once they are in registers, so the caller may refill `tin`.
   auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2],
                   uint4 (*tin)[128], bool staged, auto&& released) {
-    float (*sbuf)[33][17] = sbufs[0];
+    float (*sbuf)[33][17] = sbufs[wv];
     Raw4<IO> rx[4], rv[4], rg[4];              // x1, v, gate x2
     if constexpr (sizeof(IO) == 2) {
       if (staged) {
-        read_staged_runs(tin, i32, hf, rx, rv, rg);
+        if constexpr (TM) {
+          read_tm_runs(&tin[0][0], i32, hf, 3 * wv + pos1, 3 * wv + posv, 3 * wv + pos2, rx, rv, rg);
+        } else {
+          read_staged_runs(tin, i32, hf, rx, rv, rg);
+        }
         if (!full) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (t0 + lane_off + 8 * q >= L) {   // a run is whole or past L
+            const int64_t tq = t0 + lane_off + 8 * q;
+            if constexpr (TM) {
+              // token by token: any L
+              const uint32_t m0 = (tq < L ? 0xFFFFu : 0u) | (tq + 1 < L ? 0xFFFF0000u : 0u);
+              const uint32_t m1 = (tq + 2 < L ? 0xFFFFu : 0u) | (tq + 3 < L ? 0xFFFF0000u : 0u);
+              rx[q].w.x &= m0; rx[q].w.y &= m1;
+              rv[q].w.x &= m0; rv[q].w.y &= m1;
+              rg[q].w.x &= m0; rg[q].w.y &= m1;
+            } else if (tq >= L) {   // a run is whole or past L
               rx[q].w = make_uint2(0u, 0u);
               rv[q].w = make_uint2(0u, 0u);
               rg[q].w = make_uint2(0u, 0u);
@@ -584,9 +747,14 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     }
     // state before block b+1 = x for block b (b = 31 lands in the unused row
     // 32); before block 0 = the carry, identical in both half-waves
+    if constexpr (TM) {
+      sbuf_store_asm(lds_addr(&sbuf[part][4 * hf + 1][n_sc]), lds_addr(&sbuf[part][0][n_sc]), x,
+                     carry.hi + carry.lo);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sbuf[part][blk_tok(r, hf) + 1][n_sc] = x[r];
-    sbuf[part][0][n_sc] = carry.hi + carry.lo;
+      for (int r = 0; r < 16; ++r) sbuf[part][blk_tok(r, hf) + 1][n_sc] = x[r];
+      sbuf[part][0][n_sc] = carry.hi + carry.lo;
+    }
     {
       // carry out: p^1024 carry + loc[8], then the two parts' states summed
       // into the part-0 lane's carry
@@ -604,12 +772,17 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     lds_sync();
     // B = state before block i32, modes 8hf + j (column pair summed)
     u32x4 sw[3];
+    float sv[8];
+    if constexpr (TM) {
+      sbuf_load_asm(lds_addr(&sbuf[0][i32][8 * hf]), sv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = sbuf[0][i32][8 * hf + j] + sbuf[1][i32][8 * hf + j];
+    }
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const int n = 8 * hf + j;
       uint32_t p0, p1, p2;
-      split3_pair(sbuf[0][i32][n] + sbuf[1][i32][n], sbuf[0][i32][n + 1] + sbuf[1][i32][n + 1],
-                  p0, p1, p2);
+      split3_pair(sv[j], sv[j + 1], p0, p1, p2);
       sw[0][j >> 1] = p0;
       sw[1][j >> 1] = p1;
       sw[2][j >> 1] = p2;
@@ -634,7 +807,19 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
       }
       const int64_t pos = t0 + lane_off + 8 * q;
       if (full || staged) {
-        if constexpr (sizeof(IO) == 2) {
+        if constexpr (TM) {
+          // token t = 32 i32 + 8q + 4hf + e of the tile -> element wv of slot
+          // tm_swz(t): index 256 i32 + wv + ((64 q + 8 e) ^ 8 ((i32 & 15) ^ 4 hf))
+          uint32_t yl = 256u * static_cast<uint32_t>(i32) + static_cast<uint32_t>(wv);
+          uint32_t m8 = 8u * static_cast<uint32_t>((i32 & 15) ^ (4 * hf));
+          asm volatile("" : "+v"(yl), "+v"(m8));   // formed here, not kept across tiles
+          uint16_t* const yt = reinterpret_cast<uint16_t*>(tout);
+          const uint32_t p01 = cvt2(o[0], o[1]), p23 = cvt2(o[2], o[3]);
+          yt[yl + ((64u * q + 0u) ^ m8)] = static_cast<uint16_t>(p01);
+          yt[yl + ((64u * q + 8u) ^ m8)] = static_cast<uint16_t>(p01 >> 16);
+          yt[yl + ((64u * q + 16u) ^ m8)] = static_cast<uint16_t>(p23);
+          yt[yl + ((64u * q + 24u) ^ m8)] = static_cast<uint16_t>(p23 >> 16);
+        } else if constexpr (sizeof(IO) == 2) {
           reinterpret_cast<uint2*>(&tout[swz(4 * i32 + q)])[hf] = make_uint2(cvt2(o[0], o[1]), cvt2(o[2], o[3]));
         } else {
           *reinterpret_cast<float4*>(yr + pos) = make_float4(o[0], o[1], o[2], o[3]);
@@ -647,7 +832,17 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     }
     // bf16 full tiles leave y staged in tout; flush_y stores it once the
     // next tile's DMA has been waited for (below)
-    if constexpr (sizeof(IO) == 2) {
+    if constexpr (TM) {
+      if (!full) {
+        wg_sync();                        // every wave's y of the tile in tout
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int sl = static_cast<int>(threadIdx.x) + 512 * h;
+          const int64_t t = t0 + tm_swz(sl);
+          if (t < L) *reinterpret_cast<uint4*>(yb + t * D) = tout[sl];
+        }
+      }
+    } else if constexpr (sizeof(IO) == 2) {
       if (!full && staged) {
         lds_sync();
 #pragma unroll
@@ -660,10 +855,27 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
 
   // y of the full bf16 tile starting at t0, staged in tout by tile(): 16-byte
   // coalesced non-temporal stores
+  // TM: all waves' y, after a workgroup barrier, one token row's 16 bytes
+  // per store (plain stores: neighbouring channel blocks fill the rest of
+  // each line, which the L2 merges before writing it back).
   auto flush_y = [&](int64_t t0) {
-    lds_sync();
+    if constexpr (TM) {
+      wg_sync();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
+      for (int h = 0; h < 2; ++h) {
+        const int sl = static_cast<int>(threadIdx.x) + 512 * h;
+        *reinterpret_cast<uint4*>(yb + (t0 + tm_swz(sl)) * D) = tout[sl];
+      }
+    } else {
+      lds_sync();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) store16_nt(yr + t0 + 8 * (l + 64 * h), tout[swz(l + 64 * h)]);
+    }
+  };
+  // A staged tile is complete for the workgroup / a buffer read out by it:
+  // TM needs every wave, the single-wave workgroup only its own LDS work.
+  auto sync_tile = [&] {
+    if constexpr (TM) wg_sync(); else lds_sync();
   };
 
   // ---- full tiles, the next one in flight while the current one computes
@@ -688,32 +900,34 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     for (; k + 1 < nfull; k += 2) {
       const int64_t t0 = static_cast<int64_t>(k) << 10;
       wait_vmem<6>();                     // tile k + 1 < nfull may still fly
-      lds_sync();                         // tile k in tin_a
+      sync_tile();                        // tile k in tin_a
       if (k > 0) flush_y(t0 - 1024);
       {
         bf16x8 um[NU][2];
         tile(none, t0, true, um, tin_a, true, [&] {
-          lds_sync();                     // tin_a read out
+          sync_tile();                    // tin_a read out (TM: and tout)
           if (k + 2 < nfull) prefetch(t0 + 2048, tin_a);
         });
       }
       if (k + 2 < nfull) wait_vmem<6>(); else wait_vmem<0>();
-      lds_sync();                         // tile k+1 in tin_b
+      sync_tile();                        // tile k+1 in tin_b
       flush_y(t0);
       {
         bf16x8 um[NU][2];
         tile(none, t0 + 1024, true, um, tin_b, true, [&] {
-          lds_sync();                     // tin_b read out
+          sync_tile();                    // tin_b read out (TM: and tout)
           if (k + 3 < nfull) prefetch(t0 + 3072, tin_b);
         });
       }
     }
     if (k < nfull) {
       wait_vmem<0>();
-      lds_sync();
+      sync_tile();
       if (k > 0) flush_y((static_cast<int64_t>(k) << 10) - 1024);
       bf16x8 um[NU][2];
-      tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true, [] {});
+      tile(none, static_cast<int64_t>(k) << 10, true, um, tin_a, true, [&] {
+        if constexpr (TM) wg_sync();      // tout read out by every thread
+      });
     }
     if (nfull > 0) flush_y(static_cast<int64_t>(nfull - 1) << 10);
   } else {
@@ -757,7 +971,7 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
         prefetch_part(t0, tin_a);
       }
       wait_vmem<0>();
-      lds_sync();
+      sync_tile();
       staged = true;
     } else {
 #pragma unroll
@@ -785,8 +999,10 @@ __global__ __launch_bounds__(64) void chunk_mfma_kernel(
     }
     }
     bf16x8 um[NU][2];
-    tile(in, t0, false, um, tin_a, staged, [] {});
-    float (*sbuf)[33][17] = sbufs[0];
+    tile(in, t0, false, um, tin_a, staged, [&] {
+      if constexpr (TM) wg_sync();        // tout read out by every thread
+    });
+    float (*sbuf)[33][17] = sbufs[wv];
     const int64_t rem = L - t0;
     if (rem == 1024) {
       if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry.hi + carry.lo;
@@ -1183,7 +1399,7 @@ static hipError_t launch_mfma_k(const ChunkArgs& a) {
   dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
   chunk_mfma_kernel<IO, VEC, PIPE, CPX><<<grid, block, 0, a.stream>>>(
       static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
-      a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L);
+      a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -1206,6 +1422,43 @@ static hipError_t launch_mfma_modes(const ChunkArgs& a) {
   }
   return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true, CPX>(a)
                      : launch_mfma_k<bf16_t, true, false, CPX>(a);
+}
+
+// Token-major input and output (TM above): bf16, real modes, N <= 16, D a
+// multiple of 8 (below 349526) and xin, y 16-byte aligned.
+bool tokmajor_mfma_supported(const TokmajorArgs& a) {
+  return a.bf16 && a.N <= MFMA_MAXN && a.D % 8 == 0 && a.L > 0 && a.B > 0 &&
+         int64_t(a.D) * 6 * 1024 <= INT32_MAX && aligned_all(16, a.xin, a.y);
+}
+
+// Where the one-pass kernel is the faster token-major path: its workgroups
+// (one per 8 channels, one per CU) fill the 256 CUs, and the prefill is at
+// most 32 tile steps (1024 tokens each) per CU.  Measured against the
+// per-token segments (B, D, L: ms one-pass / per-token): 1,4096,8192
+// 0.110/0.148; 2,2048,16384 0.201/0.226; 1,4096,32768 0.409/0.391;
+// 4,4096,8192 0.411/0.381; 1,8192,32768 0.874/0.711; 1,1024,32768
+// 0.178/0.155 (128 workgroups).  Longer prefills lose to the per-token
+// segments, whose requests to the L2 are whole lines.
+bool tokmajor_mfma_preferred(const TokmajorArgs& a) {
+  const int64_t wgs = int64_t(a.B) * (a.D / 8);
+  return wgs >= 256 && wgs * ((int64_t(a.L) + 1023) / 1024) <= 256 * 32;
+}
+
+hipError_t launch_chunk_mfma_tokmajor(const TokmajorArgs& a) {
+  if (!tokmajor_mfma_supported(a)) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(a.B * (a.D / 8))), block(512);
+  const bf16_t* xin = static_cast<const bf16_t*>(a.xin);
+  bf16_t* y = static_cast<bf16_t*>(a.y);
+  if (a.L >= 2048) {
+    chunk_mfma_kernel<bf16_t, true, true, false, true><<<grid, block, 0, a.stream>>>(
+        xin, nullptr, nullptr, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L,
+        a.pos_x1, a.pos_x2, a.pos_v);
+  } else {
+    chunk_mfma_kernel<bf16_t, true, false, false, true><<<grid, block, 0, a.stream>>>(
+        xin, nullptr, nullptr, a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, y, a.D, a.L,
+        a.pos_x1, a.pos_x2, a.pos_v);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {

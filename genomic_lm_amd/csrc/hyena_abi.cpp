@@ -169,8 +169,11 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
                                    int32_t pos_v, const float* log_poles, const float* residues,
                                    int64_t N, const float* skip, const float* state_in,
                                    float* state_out, void* y, int64_t B, int64_t D, int64_t L,
-                                   hyena_dtype_t io, void* workspace, size_t ws_bytes,
-                                   hipStream_t stream) {
+                                   hyena_dtype_t io, hyena_chunk_algo_t algo, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (algo == HYENA_CHUNK_FFT) return HYENA_ERR_UNSUPPORTED;
+  if (algo != HYENA_CHUNK_AUTO && algo != HYENA_CHUNK_MFMA && algo != HYENA_CHUNK_RECURRENCE)
+    return HYENA_ERR_INVALID_ARG;
   if (!valid_io(io) || B < 0 || D < 0 || L < 0) return HYENA_ERR_INVALID_ARG;
   const bool perm = pos_x1 >= 0 && pos_x2 >= 0 && pos_v >= 0 && pos_x1 < 3 && pos_x2 < 3 &&
                     pos_v < 3 && pos_x1 != pos_x2 && pos_x1 != pos_v && pos_x2 != pos_v;
@@ -187,13 +190,17 @@ hyena_status_t chunk_tokmajor_impl(const void* xin, int32_t pos_x1, int32_t pos_
   if (!xin || !y || !aligned_to(xin, a) || !aligned_to(y, a)) return HYENA_ERR_INVALID_ARG;
   hyena_status_t st = check_modal(log_poles, residues, N, skip);
   if (st != HYENA_OK) return st;
-  const size_t need = hyena::tokmajor_workspace(B, D, L, N, io == HYENA_BF16);
-  if (need && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
-    return HYENA_ERR_WORKSPACE;
   hyena::TokmajorArgs args{xin, pos_x1, pos_x2, pos_v, log_poles, residues,
                            static_cast<int>(N), skip, state_in, state_out, y,
                            static_cast<int>(B), static_cast<int>(D), static_cast<int>(L),
                            io == HYENA_BF16, workspace, stream};
+  const bool mfma = hyena::tokmajor_mfma_supported(args);
+  if (algo == HYENA_CHUNK_MFMA && !mfma) return HYENA_ERR_UNSUPPORTED;
+  if (algo == HYENA_CHUNK_MFMA || (algo == HYENA_CHUNK_AUTO && mfma && hyena::tokmajor_mfma_preferred(args)))
+    return from_hip(hyena::launch_chunk_mfma_tokmajor(args));
+  const size_t need = hyena::tokmajor_workspace(B, D, L, N, io == HYENA_BF16);
+  if (need && (!workspace || ws_bytes < need || !aligned_to(workspace, 16)))
+    return HYENA_ERR_WORKSPACE;
   return from_hip(hyena::launch_tokmajor(args));
 }
 
@@ -387,7 +394,19 @@ hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t
                                         int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
                                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   return chunk_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, log_poles, residues, N, skip, state_in,
-                             state_out, y, B, D, L, io, workspace, ws_bytes, stream);
+                             state_out, y, B, D, L, io, HYENA_CHUNK_AUTO, workspace, ws_bytes,
+                             stream);
+}
+
+hyena_status_t hyena_chunk_fwd_tokmajor_algo(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                             int32_t pos_v, const float* log_poles,
+                                             const float* residues, int64_t N, const float* skip,
+                                             const float* state_in, float* state_out, void* y,
+                                             int64_t B, int64_t D, int64_t L, hyena_dtype_t io,
+                                             hyena_chunk_algo_t algo, void* workspace,
+                                             size_t ws_bytes, hipStream_t stream) {
+  return chunk_tokmajor_impl(xin, pos_x1, pos_x2, pos_v, log_poles, residues, N, skip, state_in,
+                             state_out, y, B, D, L, io, algo, workspace, ws_bytes, stream);
 }
 
 hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,

@@ -140,6 +140,12 @@ hipError_t launch_fftconv_large(const FftconvArgs& a);
 
 hipError_t launch_chunk_fft(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
+// The matrix-core chunk kernel on the token-major layout (chunk_mfma.hip):
+// bf16, N <= 16, D a multiple of 8, xin and y 16-byte aligned; and whether
+// it is the faster token-major path for the shape.
+bool tokmajor_mfma_supported(const TokmajorArgs& a);
+bool tokmajor_mfma_preferred(const TokmajorArgs& a);
+hipError_t launch_chunk_mfma_tokmajor(const TokmajorArgs& a);
 
 // One token per row from the modal state (decode.hip).
 hipError_t launch_modal_decode(const DecodeArgs& a);

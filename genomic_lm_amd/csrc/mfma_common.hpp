@@ -139,6 +139,14 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, kNonTemporal);
 }
 
+// The same with the default cache policy, for data whose cache lines other
+// loads of the workgroup or of its neighbours read too (token-major rows,
+// where one 128-byte line holds several channel blocks' pieces): non-temporal
+// loads of such pieces measured ~4x the algorithmic bytes fetched from HBM.
+__device__ __forceinline__ void dma16_shared(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+}
+
 // One 16-byte output chunk per lane, stored non-temporal (the output is not
 // read back by this launch).  Measured on MI355X with new inputs every launch:
 // the chunk kernel goes from ~219 to ~204 us per step at 32k tokens x 4096
@@ -200,6 +208,76 @@ __device__ __forceinline__ void read_staged_runs(const uint4 (*tin)[128], int i3
     b[q].w = make_uint2(static_cast<uint32_t>(r[3 * q + 1]), static_cast<uint32_t>(r[3 * q + 1] >> 32));
     g[q].w = make_uint2(static_cast<uint32_t>(r[3 * q + 2]), static_cast<uint32_t>(r[3 * q + 2] >> 32));
   }
+}
+
+// Token-major staging of a block of 8 channels (24 elements, 48 bytes per
+// token row): LDS slot 3 tm_swz(t) + j holds chunk j (elements 8j .. 8j+7)
+// of token row t of the tile, so that the three chunks of a row are adjacent
+// and one DMA instruction (64 consecutive slots) fetches whole 48-byte pieces
+// of ~21 rows.  tm_swz is an involution on [0, 1024) that spreads the rows a
+// wave reads together (t = 32 i + const, i < 32) over the 16 groups of 4 LDS
+// banks a 16-byte slot spans (3 tm_swz(t) mod 16 takes 16 values).
+__device__ __forceinline__ int tm_swz(int t) { return t ^ ((t >> 5) & 15); }
+
+// The runs of one channel of a token-major tile, as read_staged_runs gives
+// them for the channel-major layout: x1, v, x2 at tokens 32 i32 + 8q + 4hf + e
+// (e < 4), elements e1, ev, e2 of the span.  Per run, 12 two-byte reads in
+// one asm block that waits for them itself, for the reason given at
+// read_staged_runs; outputs early-clobber, all used.
+__device__ __forceinline__ void read_tm_runs(const uint4* tin, int i32, int hf, int e1, int ev,
+                                             int e2, Raw4<bf16_t> (&a)[4], Raw4<bf16_t> (&b)[4],
+                                             Raw4<bf16_t> (&g)[4]) {
+  // token t = 32 i32 + c (c = 8q + 4hf + e < 32) is row tm_swz(t) = 32 i32 + ((8q + e) ^ m),
+  // m = (i32 & 15) ^ 4 hf, at byte 48 tm_swz(t) of the tile.  The lane's
+  // bases pass through an empty asm, so the addresses are formed here on
+  // every call instead of being kept in registers across the tile loop.
+  uint32_t lb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)(tin))) +
+                1536u * static_cast<uint32_t>(i32);
+  uint32_t m = static_cast<uint32_t>((i32 & 15) ^ (4 * hf));
+  asm volatile("" : "+v"(lb), "+v"(m));
+  auto off = [](int e) { return static_cast<uint32_t>((e >> 3) * 16 + (e & 7) * 2); };
+  const uint32_t bs[3] = {lb + off(e1), lb + off(ev), lb + off(e2)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t ad[12];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = 48u * ((8u * q + e) ^ m);
+#pragma unroll
+      for (int st = 0; st < 3; ++st) ad[3 * e + st] = bs[st] + x;
+    }
+    uint32_t r[12];
+    asm volatile(
+        "ds_read_u16 %0, %12\n\t"
+        "ds_read_u16 %1, %13\n\t"
+        "ds_read_u16 %2, %14\n\t"
+        "ds_read_u16 %3, %15\n\t"
+        "ds_read_u16 %4, %16\n\t"
+        "ds_read_u16 %5, %17\n\t"
+        "ds_read_u16 %6, %18\n\t"
+        "ds_read_u16 %7, %19\n\t"
+        "ds_read_u16 %8, %20\n\t"
+        "ds_read_u16 %9, %21\n\t"
+        "ds_read_u16 %10, %22\n\t"
+        "ds_read_u16 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+          "v"(ad[7]), "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11])
+        : "memory");
+    // r[3e + st]: stream st (x1, v, x2) at token e of the run
+    a[q].w = make_uint2(r[0] | (r[3] << 16), r[6] | (r[9] << 16));
+    b[q].w = make_uint2(r[1] | (r[4] << 16), r[7] | (r[10] << 16));
+    g[q].w = make_uint2(r[2] | (r[5] << 16), r[8] | (r[11] << 16));
+  }
+}
+
+// Both half-waves of every wave of the workgroup meet here, with their LDS
+// operations complete.  No wait for vector memory: DMA loads issued for later
+// tiles stay in flight (a __syncthreads() fence would wait for them).
+__device__ __forceinline__ void wg_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait until at most N vector memory operations of this wave are

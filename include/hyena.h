@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define HYENA_ABI_VERSION 7
+#define HYENA_ABI_VERSION 8
 
 typedef enum hyena_status {
     HYENA_OK = 0,
@@ -84,14 +84,18 @@ typedef enum hyena_dtype {
     HYENA_BF16 = 1,
 } hyena_dtype_t;
 
-/* Algorithm of hyena_chunk_fwd_algo and hyena_chunk_fwd_cpx_algo (the entry
- * points without the suffix take AUTO).  Both algorithms compute the same
- * function. */
+/* Algorithm of hyena_chunk_fwd_algo, hyena_chunk_fwd_cpx_algo and
+ * hyena_chunk_fwd_tokmajor_algo (the entry points without the suffix take
+ * AUTO).  Every algorithm computes the same function. */
 typedef enum hyena_chunk_algo {
-    HYENA_CHUNK_AUTO = 0,        /* MFMA when the modes fit it (below), else FFT */
-    HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms */
+    HYENA_CHUNK_AUTO = 0,        /* MFMA when the modes fit it (below), else FFT;
+                                    token-major: see hyena_chunk_fwd_tokmajor */
+    HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms
+                                    (channel-major entries only) */
     HYENA_CHUNK_MFMA = 2,        /* blocked Toeplitz on bf16x3 MFMA + modal state scan;
                                     N <= 16 real or N <= 8 complex modes */
+    HYENA_CHUNK_RECURRENCE = 3,  /* per token, the modal state recurrence over segments
+                                    run in parallel (token-major entry only) */
 } hyena_chunk_algo_t;
 
 /* Limits of this build. */
@@ -366,12 +370,23 @@ hyena_status_t hyena_modal_decode_cpx(const void* x1, const void* x2, const void
  *               is 0); calls sharing one workspace must be ordered.
  * The result is that of hyena_chunk_fwd on the same streams, for any C:
  *   y[b, t, c] = x2 * (sum_{k<=t} h[c, t-k] u[k] + sum_n R_n p_n^(t+1) s_in_n)
- *                + skip[c] * u[t],  u = x1 * v,
- * evaluated per token with the decode step's recurrence s_n <- p_n s_n + u,
- * over segments of the sequence that run in parallel: each segment's end
- * state from zero, a scan of those over the segments, then every segment from
- * its true entering state.  B <= 65535.  L = 0 copies state_in to state_out.
- * Workspace NULL, short or misaligned when one is needed -> HYENA_ERR_WORKSPACE.
+ *                + skip[c] * u[t],  u = x1 * v.
+ * Two evaluations (AUTO picks one by shape; hyena_chunk_fwd_tokmajor_algo
+ * names one):
+ *   HYENA_CHUNK_MFMA: the matrix-core chunk evaluation of hyena_chunk_fwd,
+ *     one pass over blocks of 8 channels, inputs read once and y written
+ *     once; bf16 with N <= 16, D a multiple of 8 below 349526, xin and y
+ *     16-byte aligned (else HYENA_ERR_UNSUPPORTED); the workspace is not
+ *     used and may be NULL.
+ *   HYENA_CHUNK_RECURRENCE: per token with the decode step's recurrence
+ *     s_n <- p_n s_n + u, over segments of the sequence that run in
+ *     parallel: each segment's end state from zero, a scan of those over the
+ *     segments, then every segment from its true entering state.
+ * AUTO takes MFMA where it applies and the shape is at most 32 tiles of 1024
+ * tokens per CU on at least 256 blocks of 8 channels (B D / 8 >= 256 and
+ * B (D / 8) ceil(L / 1024) <= 8192), RECURRENCE otherwise.  B <= 65535.
+ * L = 0 copies state_in to state_out.  Workspace NULL, short or misaligned
+ * when one is needed -> HYENA_ERR_WORKSPACE.
  */
 hyena_status_t hyena_chunk_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t pos_x2,
                                         int32_t pos_v, const float* log_poles,
@@ -402,9 +417,23 @@ hyena_status_t hyena_fir_fwd_tokmajor(const void* xin, int32_t pos_x1, int32_t p
                                       float* window_out, void* y, int64_t B, int64_t D, int64_t L,
                                       hyena_dtype_t io, hipStream_t stream);
 
-/* Workspace bytes hyena_chunk_fwd_tokmajor needs for this shape: B * P * D * N
- * floats for its P segments, 0 when the sequence is one segment or the shape
- * is empty or unsupported. */
+/* hyena_chunk_fwd_tokmajor with the evaluation named: HYENA_CHUNK_AUTO,
+ * HYENA_CHUNK_MFMA or HYENA_CHUNK_RECURRENCE (HYENA_CHUNK_FFT ->
+ * HYENA_ERR_UNSUPPORTED, any other value -> HYENA_ERR_INVALID_ARG). */
+hyena_status_t hyena_chunk_fwd_tokmajor_algo(const void* xin, int32_t pos_x1, int32_t pos_x2,
+                                             int32_t pos_v, const float* log_poles,
+                                             const float* residues, int64_t N,
+                                             const float* skip, const float* state_in,
+                                             float* state_out, void* y, int64_t B, int64_t D,
+                                             int64_t L, hyena_dtype_t io, hyena_chunk_algo_t algo,
+                                             void* workspace, size_t ws_bytes,
+                                             hipStream_t stream);
+
+/* Workspace bytes hyena_chunk_fwd_tokmajor needs for this shape on the
+ * per-token path: B * P * D * N floats for its P segments, 0 when the sequence
+ * is one segment or the shape is empty or unsupported.  (The matrix-core path
+ * needs none; the size covers either, as the alignment of the buffers is not
+ * known here.) */
 size_t hyena_chunk_tokmajor_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                            hyena_dtype_t io);
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert G.abi_version() == 7
+    assert G.abi_version() == 8
     for st in range(5):
         assert G.status_string(st).startswith("HYENA_")
     assert "UNKNOWN" in G.status_string(99)
@@ -282,7 +282,8 @@ def test_python_names_follow_the_boundary():
     assert hyena_op.fftconv is G.fftconv_fwd and hyena_op.chunk is G.chunk_fwd
     assert hyena_op.fir is G.fir_fwd and hyena_op.modal_filter is G.modal_filter
     for name in declared_functions() - {"hyena_abi_version", "hyena_status_string",
-                                        "hyena_chunk_fwd_algo", "hyena_chunk_fwd_cpx_algo"}:
+                                        "hyena_chunk_fwd_algo", "hyena_chunk_fwd_cpx_algo",
+                                        "hyena_chunk_fwd_tokmajor_algo"}:
         assert callable(getattr(G, name)), name
 
 
@@ -320,6 +321,20 @@ def test_chunk_tokmajor_validation():
     assert f(*big) == G.ERR_WORKSPACE
     big[15] = P(0x10008); big[16] = need
     assert f(*big) == G.ERR_WORKSPACE
+    # the same arguments with the evaluation named (algo after io)
+    fa = G.lib().hyena_chunk_fwd_tokmajor_algo
+    ga = good[:15] + [0] + good[15:]
+    for algo, want in [(1, G.ERR_UNSUPPORTED), (4, G.ERR_INVALID_ARG), (-1, G.ERR_INVALID_ARG)]:
+        a = list(ga); a[15] = algo
+        assert fa(*a) == want, algo
+    # D = 4 is not a multiple of 8: the matrix-core evaluation does not apply
+    a = list(ga); a[15] = 2
+    assert fa(*a) == G.ERR_UNSUPPORTED
+    # the recurrence, named or taken by AUTO, still asks for its workspace
+    a = list(ga); a[15] = 3; a[13] = 4096
+    assert fa(*a) == G.ERR_WORKSPACE
+    a = list(ga); a[15] = 0; a[13] = 4096
+    assert fa(*a) == G.ERR_WORKSPACE
 
 
 def test_fir_tokmajor_validation():

@@ -51,41 +51,75 @@ def _gate_tm(y_dev, ref, io, rows=None, label=""):
     return gate(y_dev.transpose(1, 2), np.moveaxis(ref, 1, 2), io, rows, label=label)
 
 
+def _mfma_applies(io, D, N=16):
+    return io == "bf16" and D % 8 == 0 and N <= 16
+
+
+@pytest.mark.parametrize("algo", ["auto", "mfma", "recurrence"])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("D,L", [(256, 1000), (300, 777), (64, 2048), (520, 67), (8, 5)])
 @pytest.mark.parametrize("pos", [(0, 1, 2), (2, 0, 1)])
-def test_tokmajor_small(io, D, L, pos):
+def test_tokmajor_small(io, D, L, pos, algo):
     w, xin, xd = _setup(io, B=2, D=D, L=L, pos=pos)
     d = DevWorkload(w)
-    log(f"tokmajor io={io} D={D} L={L} pos={pos}")
-    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=pos)
+    log(f"tokmajor io={io} D={D} L={L} pos={pos} algo={algo}")
+    if algo == "mfma" and not _mfma_applies(io, D):
+        with pytest.raises(G.HyenaError, match="UNSUPPORTED"):
+            G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=pos, algo=algo)
+        return
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=pos, algo=algo)
     ref, ref_s = _ref(w, xin, pos)
     assert y.shape == (2, L, D)
-    _gate_tm(y, ref, io, label=f"tokmajor D={D} L={L}")
-    state_gate(s, ref_s, label=f"tokmajor D={D} L={L}")
+    _gate_tm(y, ref, io, label=f"tokmajor D={D} L={L} {algo}")
+    state_gate(s, ref_s, label=f"tokmajor D={D} L={L} {algo}")
 
 
-@pytest.mark.parametrize("N", [1, 3, 8, 17, 33, 64])
-def test_tokmajor_mode_counts(N):
-    """Every per-lane mode array size (8, 16, 32, 64), with padding."""
-    w, xin, xd = _setup("bf16", B=1, D=260, L=2000, N=N)
+# The one-pass matrix-core evaluation: every triple order, lengths around the
+# 1024-token tile (one token, partial tiles, whole tiles, one past, the
+# two-tile pipeline and its odd tail), fewer modes than lanes, carried state.
+@pytest.mark.parametrize("pos", [(0, 1, 2), (1, 0, 2), (2, 1, 0), (1, 2, 0)])
+@pytest.mark.parametrize("L", [1, 3, 1023, 1024, 1025, 2048, 3071, 5000])
+def test_tokmajor_mfma_lengths(pos, L):
+    N = 16 if L != 1023 else 5
+    w, xin, xd = _setup("bf16", B=1, D=16, L=L, N=N, pos=pos)
     d = DevWorkload(w)
-    log(f"tokmajor N={N}")
-    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip)
+    s0 = W.random_state(1, 16, N, seed=L)
+    log(f"tokmajor mfma L={L} pos={pos}")
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, pos=pos, algo="mfma",
+                                state_in=torch.from_numpy(s0).to(xd.device))
+    ref, ref_s = _ref(w, xin, pos, state_in=s0)
+    _gate_tm(y, ref, "bf16", label=f"tokmajor mfma L={L}")
+    state_gate(s, ref_s, label=f"tokmajor mfma L={L}")
+
+
+@pytest.mark.parametrize("D,algo", [(260, "auto"), (264, "mfma")])
+@pytest.mark.parametrize("N", [1, 3, 8, 17, 33, 64])
+def test_tokmajor_mode_counts(N, D, algo):
+    """Every per-lane mode array size (8, 16, 32, 64), with padding; the
+    matrix-core evaluation takes N <= 16."""
+    w, xin, xd = _setup("bf16", B=1, D=D, L=2000, N=N)
+    d = DevWorkload(w)
+    log(f"tokmajor N={N} D={D} {algo}")
+    if algo == "mfma" and N > 16:
+        with pytest.raises(G.HyenaError, match="UNSUPPORTED"):
+            G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, algo=algo)
+        return
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, algo=algo)
     ref, ref_s = _ref(w, xin, (0, 1, 2))
     _gate_tm(y, ref, "bf16", label=f"tokmajor N={N}")
     state_gate(s, ref_s, label=f"tokmajor N={N}")
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_tokmajor_state_in_and_in_place(io):
+@pytest.mark.parametrize("io,algo", [("bf16", "auto"), ("f32", "auto"), ("bf16", "mfma")])
+def test_tokmajor_state_in_and_in_place(io, algo):
     """A carried state in, updated in place (state_out is state_in)."""
     B, D, L = 2, 384, 1200
     w, xin, xd = _setup(io, B=B, D=D, L=L)
     d = DevWorkload(w)
     s0 = W.random_state(B, D, w.N, seed=3)
     s_dev = torch.from_numpy(s0).to(xd.device)
-    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, state_in=s_dev, state_out=s_dev)
+    y, s = G.chunk_fwd_tokmajor(xd, d.lam, d.res, d.skip, state_in=s_dev, state_out=s_dev,
+                                algo=algo)
     assert s.data_ptr() == s_dev.data_ptr()
     ref, ref_s = _ref(w, xin, (0, 1, 2), state_in=s0)
     _gate_tm(y, ref, io, label="tokmajor state in place")
@@ -150,18 +184,23 @@ def test_tokmajor_misaligned_and_tiny(io):
     assert y0.shape == (2, 0, 264) and torch.equal(s0, s1)
 
 
-def test_tokmajor_32k_shape():
-    """B = 1, D = 4096, L = 32768, bf16, N = 16: the 32 kb shape the benchmark
-    times, in its launch configuration, on sampled channels."""
-    w = W.make("32k_chunked")
+@pytest.mark.parametrize("L,algo", [(32768, "auto"), (32768, "mfma"), (8192, "auto")])
+def test_tokmajor_32k_shape(L, algo):
+    """B = 1, D = 4096, bf16, N = 16: the 32 kb shape the benchmark times
+    (AUTO takes the per-token segments there) and the matrix-core evaluation
+    on it, and an 8 kb prefill, where AUTO takes the matrix cores; sampled
+    channels of both halves of the channel range, every output finite."""
+    w = W.make("32k_chunked", L=L)
     xin = W.interleave_triples(w.x1, w.x2, w.v)
     xd = act_to_dev(xin, "bf16")
     lam, res, skip = par_to_dev(w.log_poles), par_to_dev(w.residues), par_to_dev(w.skip)
-    y, s = G.chunk_fwd_tokmajor(xd, lam, res, skip)
-    rows = sample_rows(w.D)
+    y = torch.full((1, L, w.D), float("nan"), dtype=torch.bfloat16, device=xd.device)
+    y, s = G.chunk_fwd_tokmajor(xd, lam, res, skip, out=y, algo=algo)
+    assert bool(torch.isfinite(y).all())
+    rows = sample_rows(w.D, k=16)
     ref, ref_s = _ref(w, xin, (0, 1, 2), rows)
-    _gate_tm(y, ref, "bf16", rows, label="32k tokmajor")
-    state_gate(s, ref_s, rows, label="32k tokmajor")
+    _gate_tm(y, ref, "bf16", rows, label=f"{L} tokmajor {algo}")
+    state_gate(s, ref_s, rows, label=f"{L} tokmajor {algo}")
 
 
 # ------------------------------------------------------------------ FIR
