@@ -255,6 +255,236 @@ __global__ __launch_bounds__(64) void fir_mfma_kernel(
 
 int fir_mfma_diagonals(int K) { return (K - 1 + 31) / 32 + 1; }
 
+// Token-major form (in_proj's (B, L, 3D) with each channel's x1, x2, v at
+// elements 3c + pos1 / pos2 / posv, y (B, L, D), u for t < 0 from the
+// caller's window): a workgroup of 8 waves takes 8 consecutive channels, one
+// wave per channel running the tile computation above.  A tile's 1024 token
+// rows of the block's 48-byte span are loaded into registers one tile ahead
+// (6 x 16 bytes per thread, three consecutive threads per row) and stored to
+// LDS row by row, slot 3 tm_swz(t) + j for chunk j of token t, once every
+// wave has read the previous tile; each wave gathers its channel's runs from
+// there.  Staging through registers leaves no LDS-DMA in flight, so the
+// per-wave u buffers are ordinary LDS accesses.  y goes back through a
+// token-major LDS tile as one 16-byte piece per token row; workgroups are
+// grouped on the XCDs as in chunk_mfma.hip's token-major form.
+template <int ND>
+__global__ __launch_bounds__(512) void fir_mfma_tm_kernel(
+    const bf16_t* __restrict__ xin, int pos1, int pos2, int posv, const float* __restrict__ taps,
+    int K, const float* __restrict__ skip, const float* __restrict__ win_in,
+    bf16_t* __restrict__ y, int D, int L) {
+  constexpr int NB = 32 + ND - 1;
+  constexpr int NWV = 8;
+  __shared__ float wbufs[NWV][32 * ND];
+  __shared__ uint4 tin[3 * 1024];
+  __shared__ uint4 ubs[NWV][2][NB * 4];
+  __shared__ uint4 tout[1024];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = l >> 5;
+  const int i32 = l & 31;
+  const int64_t nwg = gridDim.x, g = blockIdx.x;
+  const int64_t lg = (nwg % 64 == 0) ? 64 * (g / 64) + 8 * (g % 8) + (g / 8) % 8 : g;
+  const int nblk = D >> 3;
+  const int64_t bat = lg / nblk;
+  const int cblk = static_cast<int>(lg % nblk);
+  const int c = 8 * cblk + wv;
+  const int64_t row = bat * D + c;
+  const int64_t ld3 = 3 * static_cast<int64_t>(D);
+  const bf16_t* const xb = xin + bat * L * ld3 + 24 * cblk;
+  bf16_t* const yb = y + bat * L * static_cast<int64_t>(D) + 8 * cblk;
+  const float sk = skip ? skip[c] : 0.0f;
+  float* const wbuf = wbufs[wv];
+  uint4 (*const ub)[NB * 4] = ubs[wv];
+
+  // taps, and the halo before the first tile: u[t] for -32 (ND-1) <= t < 0
+  // from the window (its last K-1 entries), else zero, as two bf16 parts
+  for (int j = l; j < 32 * ND; j += 64) wbuf[j] = (j < K) ? taps[static_cast<int64_t>(c) * K + j] : 0.0f;
+  for (int j = l; j < 2 * NB * 4; j += 64) ub[j / (NB * 4)][j % (NB * 4)] = make_uint4(0, 0, 0, 0);
+  lds_sync();
+  if (win_in) {
+    uint16_t* const u16 = reinterpret_cast<uint16_t*>(&ub[0][0]);
+    for (int k = l; k < 32 * (ND - 1); k += 64) {
+      const int t = k - 32 * (ND - 1);
+      const float w = (t >= -(K - 1)) ? win_in[row * (K - 1) + (K - 1) + t] : 0.0f;
+      const uint32_t pw = cvt2(w, 0.0f);
+      const float w0 = lo_f(pw);
+      const uint32_t pr = cvt2(w - w0, 0.0f);
+      const int e = 8 * swz(4 * (k >> 5) + ((k & 31) >> 3)) + (k & 7);
+      u16[e] = static_cast<uint16_t>(pw);
+      u16[8 * NB * 4 + e] = static_cast<uint16_t>(pr);
+    }
+    lds_sync();
+  }
+
+  // A operands: T_d parts, as in fir_mfma_kernel
+  bf16x8 ta[ND][2][2];
+  uint32_t lo_bits = 0;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int idx = 32 * d + i32 - blk_tok(8 * s + j, hf);
+        const float w = (idx >= 0 && idx < 32 * ND) ? wbuf[idx] : 0.0f;
+        const __bf16 w0 = static_cast<__bf16>(w);
+        const __bf16 w1 = static_cast<__bf16>(w - static_cast<float>(w0));
+        ta[d][0][s][j] = w0;
+        ta[d][1][s][j] = w1;
+        lo_bits |= __builtin_bit_cast(uint16_t, w1);
+      }
+      pin(ta[d][0][s]);
+      pin(ta[d][1][s]);
+    }
+  }
+  const bool exact_taps = !__any(lo_bits != 0);
+
+  // tile loads: thread tid takes slots tid + 512 k, k < 6 (chunk s % 3 of
+  // token tm_swz(s / 3)); rows at or past L load as zeros
+  uint4 pre[6];
+  auto load_tile = [&](int64_t t0) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int s = tid + 512 * k;
+      const int64_t t = t0 + tm_swz(s / 3);
+      pre[k] = (t < L) ? *reinterpret_cast<const uint4*>(xb + t * ld3 + 8 * (s % 3))
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  const int nt = (L + 1023) >> 10;
+  if (nt > 0) load_tile(0);
+  const int e1 = 3 * wv + pos1, ev = 3 * wv + posv, e2 = 3 * wv + pos2;
+#pragma unroll 1
+  for (int kt = 0; kt < nt; ++kt) {
+    const int64_t t0 = static_cast<int64_t>(kt) << 10;
+    wg_sync();                                // every wave has read the previous tile and y
+#pragma unroll
+    for (int k = 0; k < 6; ++k) tin[tid + 512 * k] = pre[k];
+    if (kt + 1 < nt) load_tile(t0 + 1024);
+    wg_sync();                                // the tile is in LDS
+    // this lane's runs: token 32 i32 + 8q + 4hf + e at row tm_swz(t) = 32 i32 + ((8q + e) ^ m)
+    uint32_t rb = 768u * static_cast<uint32_t>(i32);     // 24 elements per row
+    uint32_t m = static_cast<uint32_t>((i32 & 15) ^ (4 * hf));
+    asm volatile("" : "+v"(rb), "+v"(m));     // formed here, not kept across tiles
+    const uint16_t* const tu = reinterpret_cast<const uint16_t*>(tin);
+    float su[16];
+    uint2 up[2][4];
+    uint2 gq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float u[4];
+      uint32_t gw[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t r = rb + 24u * ((8u * q + e) ^ m);
+        const float xa = __uint_as_float(static_cast<uint32_t>(tu[r + e1]) << 16);
+        const float xv = __uint_as_float(static_cast<uint32_t>(tu[r + ev]) << 16);
+        gw[e >> 1] |= static_cast<uint32_t>(tu[r + e2]) << (16 * (e & 1));
+        u[e] = xa * xv;
+        su[4 * q + e] = sk * u[e];
+      }
+      gq[q] = make_uint2(gw[0], gw[1]);
+      const uint32_t a0 = cvt2(u[0], u[1]), a1 = cvt2(u[2], u[3]);
+      up[0][q] = make_uint2(a0, a1);
+      up[1][q] = make_uint2(cvt2(u[0] - lo_f(a0), u[1] - hi_f(a0)), cvt2(u[2] - lo_f(a1), u[3] - hi_f(a1)));
+      const int us = swz(4 * (i32 + ND - 1) + q);
+      reinterpret_cast<uint2*>(&ub[0][us])[hf] = up[0][q];
+      reinterpret_cast<uint2*>(&ub[1][us])[hf] = up[1][q];
+    }
+    lds_sync();
+    f32x16 cz = {};
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int blk = i32 + ND - 1 - d;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 b[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint2 r0 = reinterpret_cast<const uint2*>(&ub[p][swz(4 * blk + 2 * s)])[hf];
+          const uint2 r1 = reinterpret_cast<const uint2*>(&ub[p][swz(4 * blk + 2 * s + 1)])[hf];
+          const u32x4 w4 = {r0.x, r0.y, r1.x, r1.y};
+          b[p] = __builtin_bit_cast(bf16x8, w4);
+        }
+        cz = mfma(ta[d][0][s], b[0], cz);
+        cz = mfma(ta[d][0][s], b[1], cz);
+        if (!exact_taps) {
+          cz = mfma(ta[d][1][s], b[0], cz);
+          cz = mfma(ta[d][1][s], b[1], cz);
+        }
+      }
+    }
+    lds_sync();                               // ub read out before the halo moves
+    // the last ND-1 blocks become the next tile's halo
+    if (ND > 1 && i32 >= 33 - ND) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int hs = swz(4 * (i32 - (33 - ND)) + q);
+        reinterpret_cast<uint2*>(&ub[0][hs])[hf] = up[0][q];
+        reinterpret_cast<uint2*>(&ub[1][hs])[hf] = up[1][q];
+      }
+    }
+    // y = x2 z + skip u into the token-major y tile: token t -> element wv
+    // of slot tm_swz(t)
+    {
+      uint32_t yl = 256u * static_cast<uint32_t>(i32) + static_cast<uint32_t>(wv);
+      uint32_t m8 = 8u * static_cast<uint32_t>((i32 & 15) ^ (4 * hf));
+      asm volatile("" : "+v"(yl), "+v"(m8));
+      uint16_t* const yt = reinterpret_cast<uint16_t*>(tout);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float o0 = fmaf(lo_f(gq[q].x), cz[4 * q + 0], su[4 * q + 0]);
+        const float o1 = fmaf(hi_f(gq[q].x), cz[4 * q + 1], su[4 * q + 1]);
+        const float o2 = fmaf(lo_f(gq[q].y), cz[4 * q + 2], su[4 * q + 2]);
+        const float o3 = fmaf(hi_f(gq[q].y), cz[4 * q + 3], su[4 * q + 3]);
+        const uint32_t p01 = cvt2(o0, o1), p23 = cvt2(o2, o3);
+        yt[yl + ((64u * q + 0u) ^ m8)] = static_cast<uint16_t>(p01);
+        yt[yl + ((64u * q + 8u) ^ m8)] = static_cast<uint16_t>(p01 >> 16);
+        yt[yl + ((64u * q + 16u) ^ m8)] = static_cast<uint16_t>(p23);
+        yt[yl + ((64u * q + 24u) ^ m8)] = static_cast<uint16_t>(p23 >> 16);
+      }
+    }
+    wg_sync();                                // every wave's y in tout
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sl = tid + 512 * h;
+      const int64_t t = t0 + tm_swz(sl);
+      if (t < L) *reinterpret_cast<uint4*>(yb + t * D) = tout[sl];
+    }
+  }
+}
+
+// bf16, K <= 128, D a multiple of 8 below 349526, xin and y 16-byte aligned.
+bool tokmajor_fir_mfma_supported(const TokmajorFirArgs& a) {
+  return a.bf16 && a.K <= 128 && a.D % 8 == 0 && a.L > 0 && a.B > 0 &&
+         int64_t(a.D) * 6 * 1024 <= INT32_MAX && aligned_all(16, a.xin, a.y);
+}
+
+hipError_t launch_fir_mfma_tokmajor(const TokmajorFirArgs& a) {
+  if (!tokmajor_fir_mfma_supported(a)) return hipErrorInvalidValue;
+  const int nd = fir_mfma_diagonals(a.K);
+  dim3 grid(static_cast<unsigned>(a.B * (a.D / 8))), block(512);
+  const bf16_t* x = static_cast<const bf16_t*>(a.xin);
+  bf16_t* y = static_cast<bf16_t*>(a.y);
+#define HYENA_FIR_TM(NDV)                                                                      \
+  fir_mfma_tm_kernel<NDV><<<grid, block, 0, a.stream>>>(x, a.pos_x1, a.pos_x2, a.pos_v, a.taps, \
+                                                         a.K, a.skip, a.win_in, y, a.D, a.L)
+  switch (nd) {
+    case 1: HYENA_FIR_TM(1); break;
+    case 2: HYENA_FIR_TM(2); break;
+    case 3: HYENA_FIR_TM(3); break;
+    case 4: HYENA_FIR_TM(4); break;
+    case 5: HYENA_FIR_TM(5); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef HYENA_FIR_TM
+  return hipGetLastError();
+}
+
+
+
 hipError_t launch_fir_mfma(const FirArgs& a) {
   const int nd = fir_mfma_diagonals(a.K);
   const bool vec = (a.L % 8 == 0) && aligned_all(16, a.x1, a.x2, a.v, a.y);

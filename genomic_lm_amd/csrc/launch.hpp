@@ -161,6 +161,11 @@ hipError_t launch_tokmajor(const TokmajorArgs& a);
 // Token-major explicit FIR (K <= 128), then window_out when requested.
 void tokmajor_fir_segments(int64_t B, int64_t D, int64_t L, int K, int* TS, int* P);
 hipError_t launch_tokmajor_fir(const TokmajorFirArgs& a);
+// The matrix-core FIR on the token-major layout (fir_mfma.hip): bf16,
+// K <= 128, D a multiple of 8, xin and y 16-byte aligned; y only (the
+// window is written by the caller's window kernel).
+bool tokmajor_fir_mfma_supported(const TokmajorFirArgs& a);
+hipError_t launch_fir_mfma_tokmajor(const TokmajorFirArgs& a);
 
 // state_out <- state_in (or 0 when state_in is null), count floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t count,

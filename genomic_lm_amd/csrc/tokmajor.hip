@@ -603,6 +603,20 @@ void tokmajor_fir_segments(int64_t B, int64_t D, int64_t L, int K, int* TS, int*
 }
 
 hipError_t launch_tokmajor_fir(const TokmajorFirArgs& a) {
+  // bf16 with more than 32 taps: the matrix-core kernel (fir_mfma.hip), then
+  // the window kernel.  The fp32 tap loop below costs 2K flops per token and
+  // channel; the matrix-core kernel's cost hardly depends on K.  Measured at
+  // B=1 D=4096 L=32768 (ms, tap loop / matrix cores): K=7 0.211/0.446,
+  // K=20 0.368/0.453, K=33 0.496/0.457, K=64 0.510/0.480, K=128 0.788/0.517.
+  if (a.K > 32 && tokmajor_fir_mfma_supported(a)) {
+    hipError_t e = launch_fir_mfma_tokmajor(a);
+    if (e != hipSuccess || !a.win_out) return e;
+    const int64_t rows = int64_t(a.B) * a.D;
+    tm_fir_window<bf16_t><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, a.stream>>>(
+        static_cast<const bf16_t*>(a.xin), a.pos_x1, a.pos_v, a.win_in, a.win_out, a.K - 1, a.D,
+        a.L, rows);
+    return hipGetLastError();
+  }
   int TS = 0, P = 0;
   tokmajor_fir_segments(a.B, a.D, a.L, a.K, &TS, &P);
   const size_t esz = a.bf16 ? 2 : 4;

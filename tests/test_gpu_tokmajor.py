@@ -262,6 +262,27 @@ def test_tokmajor_fir_pieces_and_decode(K):
     assert np.array_equal(win.cpu().numpy(), ref_w.astype(np.float32))
 
 
+@pytest.mark.parametrize("K", [50, 128])
+def test_tokmajor_fir_fp32_taps_and_window(K):
+    """Taps that are not bf16 values (their second bf16 part is not zero) and a
+    window of arbitrary fp32 values, on the matrix-core path (bf16, D a
+    multiple of 8, K > 32); the window comes out as [window_in, u] shifted."""
+    w, xin, xd = _setup("bf16", B=2, D=64, L=3000, pos=(0, 2, 1))
+    d = DevWorkload(w)
+    taps = W.random_taps(K, w.D, seed=K + 7, bf16=False)
+    assert not np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(taps)), taps)
+    rng = np.random.default_rng(K)
+    win0 = rng.standard_normal((2, w.D, K - 1)).astype(np.float32)
+    wi = torch.from_numpy(win0).to(xd.device)
+    log(f"tokmajor fir fp32 taps K={K}")
+    for L in (3000, 40):
+        y, wo = G.fir_fwd_tokmajor(xd[:, :L].contiguous(), par_to_dev(taps), d.skip, pos=(0, 2, 1),
+                                   window_in=wi)
+        ref, ref_w = _ref_fir(w, xin[:, :L], (0, 2, 1), taps, window_in=win0)
+        _gate_tm(y, ref, "bf16", label=f"tokmajor fir fp32 taps K={K} L={L}")
+        assert np.array_equal(wo.cpu().numpy(), ref_w.astype(np.float32))
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_tokmajor_fir_misaligned(io):
     w, xin, xd = _setup(io, B=2, D=256, L=900)
