@@ -474,6 +474,40 @@ __global__ __launch_bounds__(256) void tm_fir_window(const IO* __restrict__ xin,
   }
 }
 
+// The same for L >= W, where every entry comes from this call's input:
+// window_out[b, c, k] = u[b, L - W + k, c], one thread per entry, consecutive
+// threads on consecutive channels (the reads of one token row coalesce).
+// (window_in is not read, so window_out may be window_in.)
+template <typename IO>
+__global__ __launch_bounds__(256) void tm_fir_window_par(const IO* __restrict__ xin, int pos1,
+                                                         int posv, float* __restrict__ win_out,
+                                                         int W, int D, int L, int64_t total) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int c = static_cast<int>(i % D);
+  const int64_t rk = i / D;
+  const int k = static_cast<int>(rk % W);
+  const int64_t b = rk / W;
+  const int64_t ld = 3 * int64_t(D);
+  const IO* xr = xin + (b * L + (L - W + k)) * ld + 3 * c;
+  win_out[(b * D + c) * W + k] = Io<IO>::ld(xr, pos1) * Io<IO>::ld(xr, posv);
+}
+
+template <typename IO>
+hipError_t launch_tm_fir_window(const TokmajorFirArgs& a) {
+  const int W = a.K - 1;
+  if (a.L >= W) {
+    const int64_t total = int64_t(a.B) * W * a.D;
+    tm_fir_window_par<IO><<<static_cast<unsigned>((total + 255) / 256), 256, 0, a.stream>>>(
+        static_cast<const IO*>(a.xin), a.pos_x1, a.pos_v, a.win_out, W, a.D, a.L, total);
+  } else {
+    const int64_t rows = int64_t(a.B) * a.D;
+    tm_fir_window<IO><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, a.stream>>>(
+        static_cast<const IO*>(a.xin), a.pos_x1, a.pos_v, a.win_in, a.win_out, W, a.D, a.L, rows);
+  }
+  return hipGetLastError();
+}
+
 // Tap blocks and tile lengths: K <= 8 -> one block of 8 taps, K <= 32 -> one
 // block of 32 (tiles of 8 tokens); K <= 64 -> two blocks, K <= 128 -> four
 // (tiles of TM_FIR_FT_WIDE tokens: longer tiles amortise the window reads
@@ -508,12 +542,7 @@ hipError_t launch_tm_fir_k(const TokmajorFirArgs& a, int TS, int P) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (want_win && !in_kernel) {
-    const int64_t rows = int64_t(a.B) * a.D;
-    tm_fir_window<IO><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, a.stream>>>(
-        static_cast<const IO*>(a.xin), a.pos_x1, a.pos_v, a.win_in, a.win_out, a.K - 1, a.D,
-        a.L, rows);
-  }
+  if (want_win && !in_kernel) return launch_tm_fir_window<IO>(a);
   return hipGetLastError();
 }
 
@@ -611,11 +640,7 @@ hipError_t launch_tokmajor_fir(const TokmajorFirArgs& a) {
   if (a.K > 32 && tokmajor_fir_mfma_supported(a)) {
     hipError_t e = launch_fir_mfma_tokmajor(a);
     if (e != hipSuccess || !a.win_out) return e;
-    const int64_t rows = int64_t(a.B) * a.D;
-    tm_fir_window<bf16_t><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, a.stream>>>(
-        static_cast<const bf16_t*>(a.xin), a.pos_x1, a.pos_v, a.win_in, a.win_out, a.K - 1, a.D,
-        a.L, rows);
-    return hipGetLastError();
+    return launch_tm_fir_window<bf16_t>(a);
   }
   int TS = 0, P = 0;
   tokmajor_fir_segments(a.B, a.D, a.L, a.K, &TS, &P);
