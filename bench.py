@@ -580,6 +580,16 @@ def main():
         stc = torch.empty((B, D, 8), dtype=torch.complex64, device=dev)
         runs["fftconv_cpx_single_pass"] = rotating(lambda k: G.fftconv_fwd_cpx(
             *sets[k], lc_d, rc_d, skip, out=ys[k], workspace=fft_ws), INPUT_SETS)
+        # 32 real modes (the workload's 16 and the same poles scaled by 0.7,
+        # residues halved and negated): the matrix cores' one-mode-per-lane
+        # form, and the per-chunk FFTs that serve larger mode counts
+        lam32 = torch.cat([lam, 0.7 * lam], 1).contiguous()
+        res32 = torch.cat([res, -0.5 * res], 1).contiguous()
+        st32 = torch.empty((B, D, 32), dtype=torch.float32, device=dev)
+        runs["chunk_mfma_32modes"] = rotating(lambda k: G.chunk_fwd(
+            *sets[k], lam32, res32, CHUNK, skip, algo="mfma", out=ys[k], state_out=st32), INPUT_SETS)
+        runs["chunk_fft_32modes"] = rotating(lambda k: G.chunk_fwd(
+            *sets[k], lam32, res32, CHUNK, skip, algo="fft", out=ys[k], state_out=st32), INPUT_SETS)
         runs["chunk_cpx_fft"] = rotating(lambda k: G.chunk_fwd_cpx(
             *sets[k], lc_d, rc_d, CHUNK, skip, algo="fft", out=ys[k], state_out=stc), INPUT_SETS)
         runs["chunk_cpx_mfma"] = rotating(lambda k: G.chunk_fwd_cpx(

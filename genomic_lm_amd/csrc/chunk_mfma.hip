@@ -95,6 +95,19 @@ __device__ __forceinline__ void state_weight_operands(F&& w, int part, int hf, i
   }
 }
 
+// The three parts w0, w1, w2 of the same weights as B operands, for the
+// kernel with one mode per lane (32 slots), whose end-state product sums
+// U0.W0 + U1.W0 + U0.W1 + U1.W1 + U0.W2 (+ U2.W0) in one column per mode.
+template <typename F>
+__device__ __forceinline__ void state_weight_parts(F&& w, int hf, int ref, bf16x8 (&parts)[3][2]) {
+  split3_slots(
+      [&](int s, int j) {
+        const int tok = blk_tok(8 * s + j, hf);
+        return (tok <= ref) ? w(ref - tok) : 0.0f;
+      },
+      parts);
+}
+
 __device__ __forceinline__ void build_state_weights(float lam_n, int part, int hf, int ref,
                                                     bf16x8 (&pa)[2], bf16x8 (&pb)[2],
                                                     bf16x8 (&pc)[2]) {
@@ -261,19 +274,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Every input byte is read once and y written once: 8 bytes per token and
 // channel at bf16.  Waves of a workgroup meet at s_barrier where a tile
 // buffer or the y tile changes hands (wg_sync below).
-template <typename IO, bool VEC, bool PIPE, bool CPX, bool TM = false>
+// NSL: mode slots per wave.  16: each scan lane carries one part (the
+// column pair of the end-state product) of mode i32 & 15.  32 (17 to 32 real
+// or 9 to 16 complex modes): one mode per lane and one column per mode, G.S
+// in two K-steps of 16 modes; 32 MFMAs per bf16 tile instead of 22.
+template <typename IO, bool VEC, bool PIPE, bool CPX, bool TM = false, int NSL = 16>
 __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
     const IO* __restrict__ x1, const IO* __restrict__ x2, const IO* __restrict__ v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, const float* state_in,
     float* state_out, IO* __restrict__ y, int D, int L, int pos1, int pos2, int posv) {
   static_assert(!TM || (sizeof(IO) == 2 && VEC && !CPX), "TM: bf16 rows of 16-byte chunks, real modes");
+  static_assert(NSL == 16 || NSL == 32, "16 or 32 mode slots");
+  static_assert(!TM || NSL == 16, "TM: 16 slots (its state buffers are read and written in asm)");
+  constexpr int NPT = (NSL == 16) ? 2 : 1;    // end-state column parts per mode
+  constexpr int NK = NSL / 16;                // K-steps of G.S
   // parts of u: x1*v of two bf16 values is exactly two bf16 parts
   constexpr int NU = (sizeof(IO) == 2) ? 2 : 3;
   constexpr int NWV = TM ? 8 : 1;             // waves (channels) per workgroup
   __shared__ float hbufs[NWV][32];
   // state before block b, per part and mode (row 32: unused)
-  __shared__ float sbufs[NWV][2][33][17];
+  __shared__ float sbufs[NWV][NPT][33][NSL + 1];
   // staged x1, v, x2 tiles (bf16, swizzled chunks; TM: 3 chunks of each of
   // 1024 token rows), two tiles in turn, and the staged y tile
   __shared__ uint4 tin_a_s[TM ? 3 * 1024 : 3 * 128], tin_b_s[TM ? 3 * 1024 : 3 * 128];
@@ -374,8 +395,8 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
 
   // ---- per-lane parameters, then the first two tiles in flight while the
   // per-row constants are set up
-  const int part = i32 >> 4;                  // scan lane: mode n_sc, part 0 or 1
-  const int n_sc = i32 & 15;
+  const int part = (NSL == 16) ? (i32 >> 4) : 0;   // scan lane: mode n_sc, part 0 or 1
+  const int n_sc = (NSL == 16) ? (i32 & 15) : i32;
   // Every load is issued unconditionally from an in-bounds address (index
   // clamped, the value dropped afterwards), so that they are all in flight
   // together.
@@ -384,12 +405,15 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
   const int lam_i = CPX ? 2 * min(m_sc, N - 1) : min(n_sc, N - 1);
   const float lam_ld = lamc[lam_i];
   const float lam_ld_im = CPX ? lamc[lam_i + 1] : 0.0f;
-  float g_lam[8], g_res[8];                   // slots 8 hf + j of G
+  float g_lam[8 * NK], g_res[8 * NK];         // slots 16 k + 8 hf + j of G, [8 k + j]
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int n = min(8 * hf + j, NS - 1);
-    g_lam[j] = lamc[n];
-    g_res[j] = resc[n];
+  for (int k = 0; k < NK; ++k) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = min(16 * k + 8 * hf + j, NS - 1);
+      g_lam[8 * k + j] = lamc[n];
+      g_res[8 * k + j] = resc[n];
+    }
   }
   const float* sp = state_in ? state_in + row * NS + min(n_sc, NS - 1) : lamc;
   const float st_ld = *sp;
@@ -400,6 +424,10 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
                "v"(g_lam[3]), "v"(g_lam[4]), "v"(g_lam[5]), "v"(g_lam[6]), "v"(g_lam[7]),
                "v"(g_res[0]), "v"(g_res[1]), "v"(g_res[2]), "v"(g_res[3]), "v"(g_res[4]),
                "v"(g_res[5]), "v"(g_res[6]), "v"(g_res[7]) : "memory");
+  if constexpr (NK == 2) {
+#pragma unroll
+    for (int j = 8; j < 16; ++j) asm volatile("" ::"v"(g_lam[j]), "v"(g_res[j]) : "memory");
+  }
   if constexpr (sizeof(IO) == 2) {
     if (PIPE || nfull > 0) prefetch(0, tin_a);
     if (PIPE || nfull > 1) prefetch(1024, tin_b);
@@ -413,8 +441,11 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
   const CpxMode md = cpx_mode(n_sc < NS ? lam_ld : 0.0f, n_sc < NS ? lam_ld_im : 0.0f);
   const int kc = n_sc & 1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (8 * hf + j >= NS) g_res[j] = 0.0f;
+  for (int k = 0; k < NK; ++k) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (16 * k + 8 * hf + j >= NS) g_res[8 * k + j] = 0.0f;
+    }
   }
   DF carry = {(part == 0 && n_sc < NS && state_in) ? st_ld : 0.0f, 0.0f};
 
@@ -427,7 +458,7 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
     float hd = 0.0f;
     if constexpr (CPX) {
 #pragma unroll
-      for (int n = 0; n < MFMA_MAXN / 2; ++n) {
+      for (int n = 0; n < NSL / 2; ++n) {
         if (n < N) {
           const float2 e = cexp_at(cpx_mode(lamc[2 * n], lamc[2 * n + 1]), static_cast<float>(i32));
           hd = fmaf(resc[2 * n], e.x, fmaf(-resc[2 * n + 1], e.y, hd));
@@ -435,7 +466,7 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
       }
     } else {
 #pragma unroll
-      for (int n = 0; n < MFMA_MAXN; ++n) {
+      for (int n = 0; n < NSL; ++n) {
         if (n < N) hd = fmaf(resc[n], fast_exp(lamc[n] * static_cast<float>(i32)), hd);
       }
     }
@@ -460,37 +491,54 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
         }
       },
       tm);
-  // A = G (row i32, slot j -> mode 8*hf + j): G[i][n] = R_n p_n^(i+1);
+  // A = G (row i32, K-step k, slot j -> mode 16k + 8*hf + j): G[i][n] = R_n p_n^(i+1);
   // CPX: slot 2m holds Re(R_m p_m^(i+1)), slot 2m + 1 holds -Im(R_m p_m^(i+1))
-  auto gval = [&](int j) {
+  // Padding slots (16k + 8hf + slot >= NS) are zero without evaluating
+  // anything: their loads hold the last slot's values, for complex modes an
+  // imaginary part, which as the real part of a pole could overflow
+  // p^(i+1) and make 0 * inf.
+  auto gval = [&](int j) {                    // j = 8 k + slot
+    if (16 * (j >> 3) + 8 * hf + (j & 7) >= NS) return 0.0f;
     if constexpr (CPX) {
       const int j0 = j & ~1;
       const float2 e = cexp_at(cpx_mode(g_lam[j0], g_lam[j0 + 1]), static_cast<float>(i32 + 1));
       const float2 rp = cmul(make_float2(g_res[j0], g_res[j0 + 1]), e);
-      return (j & 1) ? -rp.y : rp.x;          // padding slots: g_res = 0
+      return (j & 1) ? -rp.y : rp.x;
     } else {
       return g_res[j] * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
     }
   };
-  bf16x8 gm[3];
-  {
+  bf16x8 gm[NK][3];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
     u32x4 w0, w1, w2;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       uint32_t a, b, c;
-      split3_pair(gval(2 * jj), gval(2 * jj + 1), a, b, c);
+      split3_pair(gval(8 * k + 2 * jj), gval(8 * k + 2 * jj + 1), a, b, c);
       w0[jj] = a;
       w1[jj] = b;
       w2[jj] = c;
     }
-    gm[0] = __builtin_bit_cast(bf16x8, w0);
-    gm[1] = __builtin_bit_cast(bf16x8, w1);
-    gm[2] = __builtin_bit_cast(bf16x8, w2);
+    gm[k][0] = __builtin_bit_cast(bf16x8, w0);
+    gm[k][1] = __builtin_bit_cast(bf16x8, w1);
+    gm[k][2] = __builtin_bit_cast(bf16x8, w2);
   }
   // scan lane: mode n_sc (part 0 or 1 of the column pair) for all 32
   // blocks; padded modes have p = 1 and R = 0
+  // (NSL = 32: the three parts wp[k] of the lane's own mode column instead)
   bf16x8 pa[2], pb[2], pc[2];
-  if constexpr (CPX) {
+  bf16x8 wp[NSL == 32 ? 3 : 1][2];
+  if constexpr (NSL == 32) {
+    if constexpr (CPX) {
+      state_weight_parts([&](int d) {
+        const float2 e = cexp_at(md, static_cast<float>(d));
+        return kc ? e.y : e.x;
+      }, hf, 31, wp);
+    } else {
+      state_weight_parts([&](int d) { return fast_exp(lam_n * static_cast<float>(d)); }, hf, 31, wp);
+    }
+  } else if constexpr (CPX) {
     build_state_weights_cpx(md, kc, part, hf, 31, pa, pb, pc);
   } else {
     build_state_weights(lam_n, part, hf, 31, pa, pb, pc);
@@ -550,14 +598,22 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    pin(pa[s]);
-    pin(pb[s]);
-    if constexpr (NU == 3) pin(pc[s]);
+    if constexpr (NSL == 32) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) pin(wp[k][s]);
+    } else {
+      pin(pa[s]);
+      pin(pb[s]);
+      if constexpr (NU == 3) pin(pc[s]);
+    }
 #pragma unroll
     for (int k = 0; k < 3; ++k) pin(tm[k][s]);
   }
 #pragma unroll
-  for (int k = 0; k < 3; ++k) pin(gm[k]);
+  for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) pin(gm[kk][k]);
+  }
   pin(a1);
   pin(a2);
   pin(a3);
@@ -596,7 +652,7 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
   // called once they are in registers, so the caller may refill `tin`.
   auto tile = [&](const TileIn<IO>& in, int64_t t0, bool full, bf16x8 (&um)[NU][2],
                   uint4 (*tin)[128], bool staged, auto&& released) {
-    float (*sbuf)[33][17] = sbufs[wv];
+    float (*sbuf)[33][NSL + 1] = sbufs[wv];
     Raw4<IO> rx[4], rv[4], rg[4];              // x1, v, gate x2
     if constexpr (sizeof(IO) == 2) {
       if (staged) {
@@ -675,10 +731,19 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
     f32x16 ce = {};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      ce = mfma(um[0][s], pa[s], ce);
-      ce = mfma(um[1][s], pa[s], ce);
-      ce = mfma(um[0][s], pb[s], ce);
-      if constexpr (NU == 3) ce = mfma(um[NU - 1][s], pc[s], ce);
+      if constexpr (NSL == 32) {
+        ce = mfma(um[0][s], wp[0][s], ce);
+        ce = mfma(um[1][s], wp[0][s], ce);
+        ce = mfma(um[0][s], wp[1][s], ce);
+        ce = mfma(um[1][s], wp[1][s], ce);
+        ce = mfma(um[0][s], wp[2][s], ce);
+        if constexpr (NU == 3) ce = mfma(um[NU - 1][s], wp[0][s], ce);
+      } else {
+        ce = mfma(um[0][s], pa[s], ce);
+        ce = mfma(um[1][s], pa[s], ce);
+        ce = mfma(um[0][s], pb[s], ce);
+        if constexpr (NU == 3) ce = mfma(um[NU - 1][s], pc[s], ce);
+      }
     }
     // in-block Toeplitz part of z; independent of the scan, so the matrix
     // cores work on it while the scan runs on the vector ALUs
@@ -764,38 +829,49 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
       } else {
         fin = df_step(fh[4], fl[4], carry, loc[8]);
       }
-      const DF oth2 = {xor16(fin.hi, l), xor16(fin.lo, l)};
-      const DF sm = df_two_sum(fin.hi, oth2.hi);
-      const DF tot = df_two_sum(sm.hi, sm.lo + (fin.lo + oth2.lo));
-      carry = (part == 0) ? tot : DF{0.0f, 0.0f};
+      if constexpr (NSL == 32) {
+        carry = fin;                          // one column per mode: nothing to combine
+      } else {
+        const DF oth2 = {xor16(fin.hi, l), xor16(fin.lo, l)};
+        const DF sm = df_two_sum(fin.hi, oth2.hi);
+        const DF tot = df_two_sum(sm.hi, sm.lo + (fin.lo + oth2.lo));
+        carry = (part == 0) ? tot : DF{0.0f, 0.0f};
+      }
     }
     lds_sync();
-    // B = state before block i32, modes 8hf + j (column pair summed)
-    u32x4 sw[3];
-    float sv[8];
-    if constexpr (TM) {
-      sbuf_load_asm(lds_addr(&sbuf[0][i32][8 * hf]), sv);
-    } else {
+    // B = state before block i32, K-step k: modes 16k + 8hf + j (NSL = 16:
+    // the column pair summed)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = sbuf[0][i32][8 * hf + j] + sbuf[1][i32][8 * hf + j];
-    }
+    for (int k = 0; k < NK; ++k) {
+      u32x4 sw[3];
+      float sv[8];
+      if constexpr (TM) {
+        sbuf_load_asm(lds_addr(&sbuf[0][i32][8 * hf]), sv);
+      } else if constexpr (NSL == 32) {
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      uint32_t p0, p1, p2;
-      split3_pair(sv[j], sv[j + 1], p0, p1, p2);
-      sw[0][j >> 1] = p0;
-      sw[1][j >> 1] = p1;
-      sw[2][j >> 1] = p2;
+        for (int j = 0; j < 8; ++j) sv[j] = sbuf[0][i32][16 * k + 8 * hf + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = sbuf[0][i32][8 * hf + j] + sbuf[1][i32][8 * hf + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t p0, p1, p2;
+        split3_pair(sv[j], sv[j + 1], p0, p1, p2);
+        sw[0][j >> 1] = p0;
+        sw[1][j >> 1] = p1;
+        sw[2][j >> 1] = p2;
+      }
+      const bf16x8 sm[3] = {__builtin_bit_cast(bf16x8, sw[0]), __builtin_bit_cast(bf16x8, sw[1]),
+                            __builtin_bit_cast(bf16x8, sw[2])};
+      // z = T.U + G.S, products of order <= 2 (G.S added after the scan)
+      cz = mfma(gm[k][0], sm[0], cz);
+      cz = mfma(gm[k][0], sm[1], cz);
+      cz = mfma(gm[k][1], sm[0], cz);
+      cz = mfma(gm[k][1], sm[1], cz);
+      cz = mfma(gm[k][0], sm[2], cz);
+      cz = mfma(gm[k][2], sm[0], cz);
     }
-    const bf16x8 sm[3] = {__builtin_bit_cast(bf16x8, sw[0]), __builtin_bit_cast(bf16x8, sw[1]),
-                          __builtin_bit_cast(bf16x8, sw[2])};
-    // z = T.U + G.S, products of order <= 2 (G.S added after the scan)
-    cz = mfma(gm[0], sm[0], cz);
-    cz = mfma(gm[0], sm[1], cz);
-    cz = mfma(gm[1], sm[0], cz);
-    cz = mfma(gm[1], sm[1], cz);
-    cz = mfma(gm[0], sm[2], cz);
-    cz = mfma(gm[2], sm[0], cz);
     // y = x2 * z + skip * u
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1002,7 +1078,7 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
     tile(in, t0, false, um, tin_a, staged, [&] {
       if constexpr (TM) wg_sync();        // tout read out by every thread
     });
-    float (*sbuf)[33][17] = sbufs[wv];
+    float (*sbuf)[33][NSL + 1] = sbufs[wv];
     const int64_t rem = L - t0;
     if (rem == 1024) {
       if (part == 0 && hf == 0 && n_sc < NS) state_out[row * NS + n_sc] = carry.hi + carry.lo;
@@ -1010,19 +1086,41 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
       // the sequence ends inside this tile: state after token L-1
       const int bstar = static_cast<int>(rem - 1) >> 5;
       const int estar = static_cast<int>(rem - 1) & 31;
-      bf16x8 qa[2], qb[2], qc[2];
-      if constexpr (CPX) {
-        build_state_weights_cpx(md, kc, part, hf, estar, qa, qb, qc);
-      } else {
-        build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
-      }
       f32x16 cf = {};
+      if constexpr (NSL == 32) {
+        bf16x8 qp[3][2];
+        if constexpr (CPX) {
+          state_weight_parts([&](int d) {
+            const float2 e = cexp_at(md, static_cast<float>(d));
+            return kc ? e.y : e.x;
+          }, hf, estar, qp);
+        } else {
+          state_weight_parts([&](int d) { return fast_exp(lam_n * static_cast<float>(d)); }, hf,
+                             estar, qp);
+        }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        cf = mfma(um[0][s], qa[s], cf);
-        cf = mfma(um[1][s], qa[s], cf);
-        cf = mfma(um[0][s], qb[s], cf);
-        if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qc[s], cf);
+        for (int s = 0; s < 2; ++s) {
+          cf = mfma(um[0][s], qp[0][s], cf);
+          cf = mfma(um[1][s], qp[0][s], cf);
+          cf = mfma(um[0][s], qp[1][s], cf);
+          cf = mfma(um[1][s], qp[1][s], cf);
+          cf = mfma(um[0][s], qp[2][s], cf);
+          if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qp[0][s], cf);
+        }
+      } else {
+        bf16x8 qa[2], qb[2], qc[2];
+        if constexpr (CPX) {
+          build_state_weights_cpx(md, kc, part, hf, estar, qa, qb, qc);
+        } else {
+          build_state_weights(lam_n, part, hf, estar, qa, qb, qc);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          cf = mfma(um[0][s], qa[s], cf);
+          cf = mfma(um[1][s], qa[s], cf);
+          cf = mfma(um[0][s], qb[s], cf);
+          if constexpr (NU == 3) cf = mfma(um[NU - 1][s], qc[s], cf);
+        }
       }
       const bool mine = (((bstar >> 2) & 1) == hf);
       const int rs = 4 * (bstar >> 3) + (bstar & 3);
@@ -1040,7 +1138,7 @@ __global__ __launch_bounds__(TM ? 512 : 64) void chunk_mfma_kernel(
           fin = fmaf(fast_exp(lam_n * static_cast<float>(estar + 1)), sbuf[part][bstar][n_sc], ev);
         }
       }
-      const float tot = fin + __shfl_xor(fin, 16);
+      const float tot = (NSL == 16) ? fin + __shfl_xor(fin, 16) : fin;
       if (mine && part == 0 && n_sc < NS) state_out[row * NS + n_sc] = tot;
     }
     lds_sync();                           // sbuf reads done before the next tile writes
@@ -1133,8 +1231,10 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   float hpart = 0.0f, h0part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float r = (8 * hf + j < N) ? g_res[j] : 0.0f;
-    gv[j] = r * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
+    const bool live = 8 * hf + j < N;         // padding slots: zero, nothing evaluated
+    const float r = live ? g_res[j] : 0.0f;
+    const float ev = r * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
+    gv[j] = live ? ev : 0.0f;
     hpart += gv[j];
     h0part += r;
   }
@@ -1394,23 +1494,24 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   }
 }
 
-template <typename IO, bool VEC, bool PIPE, bool CPX>
+template <typename IO, bool VEC, bool PIPE, bool CPX, int NSL>
 static hipError_t launch_mfma_k(const ChunkArgs& a) {
   dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
-  chunk_mfma_kernel<IO, VEC, PIPE, CPX><<<grid, block, 0, a.stream>>>(
+  chunk_mfma_kernel<IO, VEC, PIPE, CPX, false, NSL><<<grid, block, 0, a.stream>>>(
       static_cast<const IO*>(a.x1), static_cast<const IO*>(a.x2), static_cast<const IO*>(a.v),
       a.lam, a.res, a.N, a.skip, a.state_in, a.state_out, static_cast<IO*>(a.y), a.D, a.L, 0, 0, 0);
   return hipGetLastError();
 }
 
-template <bool CPX>
+template <bool CPX, int NSL>
 static hipError_t launch_mfma_modes(const ChunkArgs& a) {
   const int esz = a.bf16 ? 2 : 4;
   const bool vec = (a.L % (16 / esz) == 0) && aligned_all(16, a.x1, a.x2, a.v, a.y);
   if (!a.bf16)
-    return vec ? launch_mfma_k<float, true, false, CPX>(a) : launch_mfma_k<float, false, false, CPX>(a);
-  if (!vec) return launch_mfma_k<bf16_t, false, false, CPX>(a);
-  if constexpr (!CPX) {
+    return vec ? launch_mfma_k<float, true, false, CPX, NSL>(a)
+               : launch_mfma_k<float, false, false, CPX, NSL>(a);
+  if (!vec) return launch_mfma_k<bf16_t, false, false, CPX, NSL>(a);
+  if constexpr (!CPX && NSL == 16) {
     if (a.L <= 1024) {
       dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
       chunk_one_kernel<<<grid, block, 0, a.stream>>>(
@@ -1420,8 +1521,8 @@ static hipError_t launch_mfma_modes(const ChunkArgs& a) {
       return hipGetLastError();
     }
   }
-  return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true, CPX>(a)
-                     : launch_mfma_k<bf16_t, true, false, CPX>(a);
+  return a.L >= 2048 ? launch_mfma_k<bf16_t, true, true, CPX, NSL>(a)
+                     : launch_mfma_k<bf16_t, true, false, CPX, NSL>(a);
 }
 
 // Token-major input and output (TM above): bf16, real modes, N <= 16, D a
@@ -1462,8 +1563,11 @@ hipError_t launch_chunk_mfma_tokmajor(const TokmajorArgs& a) {
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
-  if ((a.cpx ? 2 * a.N : a.N) > MFMA_MAXN) return hipErrorInvalidValue;
-  return a.cpx ? launch_mfma_modes<true>(a) : launch_mfma_modes<false>(a);
+  const int slots = a.cpx ? 2 * a.N : a.N;
+  if (slots > MFMA_MAXN_WIDE) return hipErrorInvalidValue;
+  if (slots > MFMA_MAXN)
+    return a.cpx ? launch_mfma_modes<true, 32>(a) : launch_mfma_modes<false, 32>(a);
+  return a.cpx ? launch_mfma_modes<true, 16>(a) : launch_mfma_modes<false, 16>(a);
 }
 
 }  // namespace hyena

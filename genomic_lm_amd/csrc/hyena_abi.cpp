@@ -155,8 +155,8 @@ hyena_status_t chunk_impl(const void* x1, const void* x2, const void* v,
   const int64_t Ceff = C < L ? C : L;
   const int64_t slots = cpx ? 2 * N : N;      // real lanes of the MFMA kernel's scan
   hyena_chunk_algo_t use = algo;
-  if (use == HYENA_CHUNK_AUTO) use = (slots <= 16) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
-  if (use == HYENA_CHUNK_MFMA && slots > 16) return HYENA_ERR_UNSUPPORTED;
+  if (use == HYENA_CHUNK_AUTO) use = (slots <= 32) ? HYENA_CHUNK_MFMA : HYENA_CHUNK_FFT;
+  if (use == HYENA_CHUNK_MFMA && slots > 32) return HYENA_ERR_UNSUPPORTED;
   if (use == HYENA_CHUNK_FFT && Ceff > HYENA_MAX_FFT_CHUNK) return HYENA_ERR_UNSUPPORTED;
   hyena::ChunkArgs a{x1, x2, v, log_poles, residues, static_cast<int>(N), skip, state_in,
                      state_out, y, static_cast<int>(B), static_cast<int>(D),

@@ -10,7 +10,8 @@ namespace hyena {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int MFMA_MAXN = 16;
+constexpr int MFMA_MAXN = 16;        // mode slots of the 16-slot kernels (one-tile, token-major)
+constexpr int MFMA_MAXN_WIDE = 32;   // slots of the chunk kernel's 32-slot form
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 

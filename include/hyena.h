@@ -93,7 +93,7 @@ typedef enum hyena_chunk_algo {
     HYENA_CHUNK_FFT = 1,         /* per chunk: zero-padded FFT of length 2C + modal state terms
                                     (channel-major entries only) */
     HYENA_CHUNK_MFMA = 2,        /* blocked Toeplitz on bf16x3 MFMA + modal state scan;
-                                    N <= 16 real or N <= 8 complex modes */
+                                    N <= 32 real or N <= 16 complex modes */
     HYENA_CHUNK_RECURRENCE = 3,  /* per token, the modal state recurrence over segments
                                     run in parallel (token-major entry only) */
 } hyena_chunk_algo_t;
@@ -218,7 +218,7 @@ size_t hyena_fftconv_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
  *   state_in  : (B, D, N) fp32 or NULL (zero state)
  *   state_out : (B, D, N) fp32, written (may equal state_in)
  *   C >= 1.  The algorithm is HYENA_CHUNK_AUTO: the matrix-core blocked
- *   Toeplitz for N <= 16 modes, else per-chunk FFTs (then C' <=
+ *   Toeplitz for N <= 32 modes, else per-chunk FFTs (then C' <=
  *   HYENA_MAX_FFT_CHUNK, else HYENA_ERR_UNSUPPORTED).
  */
 hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
@@ -234,8 +234,8 @@ hyena_status_t hyena_chunk_fwd(const void* x1, const void* x2, const void* v,
  *   HYENA_CHUNK_AUTO  as hyena_chunk_fwd;
  *   HYENA_CHUNK_FFT   per chunk a zero-padded FFT product of length 2C', any
  *                     N, C' <= HYENA_MAX_FFT_CHUNK;
- *   HYENA_CHUNK_MFMA  blocked Toeplitz on the matrix cores, any C, N <= 16
- *                     (N > 16 -> HYENA_ERR_UNSUPPORTED);
+ *   HYENA_CHUNK_MFMA  blocked Toeplitz on the matrix cores, any C, N <= 32
+ *                     (N > 32 -> HYENA_ERR_UNSUPPORTED);
  *   anything else -> HYENA_ERR_INVALID_ARG.
  */
 hyena_status_t hyena_chunk_fwd_algo(const void* x1, const void* x2, const void* v,
@@ -319,7 +319,7 @@ hyena_status_t hyena_fftconv_fwd_cpx(const void* x1, const void* x2, const void*
  * hyena_chunk_fwd:
  *   z[t] = sum_{k=t0}^{t} h[t-k] u[k] + Re sum_n R_n p_n^(t-t0+1) s_n,
  *   s_n <- p_n^C' s_n + sum_j p_n^(C'-1-j) u[t0+j].
- * The algorithm is AUTO: the matrix cores for N <= 8 complex modes (each a
+ * The algorithm is AUTO: the matrix cores for N <= 16 complex modes (each a
  * pair of real lanes of its scan), per-chunk FFTs otherwise. */
 hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v,
                                    const float* log_poles, const float* residues,
@@ -329,7 +329,7 @@ hyena_status_t hyena_chunk_fwd_cpx(const void* x1, const void* x2, const void* v
                                    hyena_dtype_t io, hipStream_t stream);
 
 /* hyena_chunk_fwd_cpx with the algorithm chosen by the caller:
- * HYENA_CHUNK_MFMA takes N <= 8 complex modes, HYENA_CHUNK_FFT any N with
+ * HYENA_CHUNK_MFMA takes N <= 16 complex modes, HYENA_CHUNK_FFT any N with
  * C' <= HYENA_MAX_FFT_CHUNK, AUTO as hyena_chunk_fwd_cpx. */
 hyena_status_t hyena_chunk_fwd_cpx_algo(const void* x1, const void* x2, const void* v,
                                         const float* log_poles, const float* residues,

@@ -194,7 +194,7 @@ def test_chunk_validation():
                            (5, 65, G.ERR_INVALID_ARG), (8, MISALIGNED, G.ERR_INVALID_ARG)]:
         a = list(good); a[idx] = val
         assert f(*a) == want, (idx, val)
-    a = list(good); a[5] = 32; a[13] = 16384; a[12] = 16384   # AUTO: > 16 modes take FFT chunks
+    a = list(good); a[5] = 33; a[13] = 16384; a[12] = 16384   # AUTO: > 32 modes take FFT chunks
     assert f(*a) == G.ERR_UNSUPPORTED                          # ... of at most 8192
     a = list(good); a[10] = 0                                  # empty batch
     assert f(*a) == G.OK
@@ -203,7 +203,7 @@ def test_chunk_validation():
     ga = good[:15] + [0, None]
     a = list(ga); a[15] = 3
     assert fa(*a) == G.ERR_INVALID_ARG
-    a = list(ga); a[5] = 32; a[15] = G.ALGOS["mfma"]          # MFMA kernel holds <= 16 modes
+    a = list(ga); a[5] = 33; a[15] = G.ALGOS["mfma"]          # MFMA kernel holds <= 32 modes
     assert fa(*a) == G.ERR_UNSUPPORTED
     a = list(ga); a[13] = 16384; a[15] = G.ALGOS["fft"]; a[12] = 16384
     assert fa(*a) == G.ERR_UNSUPPORTED                         # FFT chunk > 8192
@@ -217,7 +217,7 @@ def test_chunk_cpx_validation():
     f = G.lib().hyena_chunk_fwd_cpx_algo
     good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, None, FAKE, FAKE, 1, 4, 1024, 1024,
             G.BF16, 0, None]
-    a = list(good); a[5] = 9; a[15] = G.ALGOS["mfma"]         # 9 complex modes: 18 real lanes
+    a = list(good); a[5] = 17; a[15] = G.ALGOS["mfma"]        # 17 complex modes: 34 real lanes
     assert f(*a) == G.ERR_UNSUPPORTED
     a = list(good); a[15] = 3
     assert f(*a) == G.ERR_INVALID_ARG

@@ -84,17 +84,18 @@ def test_chunk_cpx(algo, io, C, L, with_state):
     assert err < 1e-4
 
 
-@pytest.mark.parametrize("N", [1, 3, 5, 8, 9])
+@pytest.mark.parametrize("N", [1, 3, 5, 8, 9, 12, 16, 17])
 def test_chunk_cpx_mode_counts(N):
-    """Complex mode counts through AUTO: N <= 8 on the matrix cores (padding
-    slots included), N = 9 on the FFT algorithm; and the unaligned path."""
+    """Complex mode counts through AUTO: N <= 16 on the matrix cores (padding
+    slots included; 9 to 16 on the 32-slot form), N = 17 on the FFT
+    algorithm; and the unaligned path."""
     w, d, lam, R, lam_d, R_d = _setup("bf16", D=6, L=2500, B=1, N=N, seed=30 + N)
     log(f"chunk_cpx auto N={N}")
     y, s = G.chunk_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, 1024, d.skip)
     ref, ref_s = _ref(w, lam, R)
     gate(y, ref, "bf16", label=f"chunk_cpx auto N={N}")
     assert _state_err(s, ref_s) < 1e-4
-    if N <= 8:
+    if N <= 16:
         y2, s2 = G.chunk_fwd_cpx(*(offset_copy(t) for t in (d.x1, d.x2, d.v)), lam_d, R_d, 1000,
                                  d.skip, algo="mfma")
         gate(y2, ref, "bf16", label=f"chunk_cpx mfma unaligned N={N}")

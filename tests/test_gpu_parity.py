@@ -231,22 +231,43 @@ def test_chunk_one_tile_mode_counts(N, L):
         state_gate(s, ref_s, label=f"chunk one tile N={N} L={L}")
 
 
-@pytest.mark.parametrize("N", [1, 3, 17, 64])
+@pytest.mark.parametrize("N", [1, 3, 17, 24, 32, 33, 64])
 def test_mode_counts(N):
     """From one mode to the maximum of 64: single pass, chunked with AUTO (the
-    matrix-core path up to 16 modes, FFT beyond), and each algorithm it has."""
+    matrix-core path up to 32 modes -- one scan lane per mode from 17 on --
+    FFT beyond), and each algorithm it has."""
     w = W.make("7b_layer_set", B=2, D=4, L=3000, N=N)
     d = DevWorkload(w)
     log(f"modes N={N}")
     ref, ref_s = oracle_modal(w)
     gate(G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip), ref, "bf16", label=f"fftconv N={N}")
-    for algo in (["auto", "fft", "mfma"] if N <= 16 else ["auto", "fft"]):
+    for algo in (["auto", "fft", "mfma"] if N <= 32 else ["auto", "fft"]):
         y, s = G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo=algo)
         gate(y, ref, "bf16", label=f"chunk/{algo} N={N}")
         state_gate(s, ref_s, label=f"chunk/{algo} N={N}")
-    if N > 16:
+    if N > 32:
         with pytest.raises(G.HyenaError, match="UNSUPPORTED"):
             G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="mfma")
+
+
+# The 32-slot form (17 to 32 real modes): fp32 and bf16 rows, whole tiles, a
+# partial last tile, rows of at most one tile, unaligned rows, carried state.
+@pytest.mark.parametrize("io,L,offset", [("bf16", 5000, False), ("bf16", 1016, False),
+                                         ("bf16", 2048, False), ("bf16", 777, True),
+                                         ("f32", 3000, False), ("f32", 640, True)])
+@pytest.mark.parametrize("N", [20, 32])
+def test_chunk_mfma_32_slots(N, io, L, offset):
+    w = W.make("tiny" if io == "f32" else "7b_layer_set", B=2, D=5, L=L, N=N)
+    d = DevWorkload(w)
+    s0 = W.random_state(w.B, w.D, w.N, seed=N + L)
+    xs = [offset_copy(t) for t in (d.x1, d.x2, d.v)] if offset else [d.x1, d.x2, d.v]
+    log(f"chunk/mfma 32 slots N={N} io={io} L={L} offset={offset}")
+    for state in (None, s0):
+        sin = None if state is None else par_to_dev(state)
+        y, s = G.chunk_fwd(*xs, d.lam, d.res, 1024, d.skip, state_in=sin, algo="mfma")
+        ref_y, ref_s = oracle_modal(w, C=1024, state_in=state)
+        gate(y, ref_y, io, label=f"chunk/mfma N={N} L={L} {io}")
+        state_gate(s, ref_s, label=f"chunk/mfma N={N} L={L} {io}")
 
 
 @pytest.mark.parametrize("algo", ["mfma", "fft"])
