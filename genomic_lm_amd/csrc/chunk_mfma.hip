@@ -1171,7 +1171,11 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   constexpr int kSbufBytes = (2 * 33 * 17 * 4 + 15) / 16 * 16;
   constexpr int kLdsBytes = (kSbufBytes + 128 * 16 > kTinBytes) ? kSbufBytes + 128 * 16 : kTinBytes;
   __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
-  __shared__ float hbuf[32];
+  // h's three bf16 parts by reversed lag: htab[0][k][x] = part k of
+  // h[31 - x], zero for x > 31 (lags below zero); htab[1] the same one entry
+  // later.  A lane's pair of T slots (lags d and d - 1) is then one aligned
+  // 32-bit word of one of the two copies.
+  __shared__ __align__(4) uint16_t htab[2][3][66];
   const uint4 (*const tin)[128] = reinterpret_cast<const uint4 (*)[128]>(lds_raw);
   uint4 (*const tin_w)[128] = reinterpret_cast<uint4 (*)[128]>(lds_raw);
   float (*const sbuf)[33][17] = reinterpret_cast<float (*)[33][17]>(lds_raw);
@@ -1240,9 +1244,24 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   }
   const float hnext = hpart + xor32(hpart, hf);            // h[i32 + 1]
   const float h0 = h0part + xor32(h0part, hf);             // h[0]
-  if (hf == 0) {
-    if (i32 < 31) hbuf[i32 + 1] = hnext;
-    if (i32 == 0) hbuf[0] = h0;
+  {
+    // lane (i32, 0): h[i32 + 1] at x = 30 - i32, lane 0 also h[0] at x = 31;
+    // lane (i32, 1): the zero at x = 32 + i32
+    uint32_t hp[3];
+    split3_pair(hf ? 0.0f : hnext, h0, hp[0], hp[1], hp[2]);
+    const int x = hf ? 32 + i32 : 30 - i32;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint16_t lo = static_cast<uint16_t>(hp[k]), hi = static_cast<uint16_t>(hp[k] >> 16);
+      if (x >= 0) {
+        htab[0][k][x] = lo;
+        htab[1][k][x + 1] = lo;
+      }
+      if (hf == 0 && i32 == 0) {
+        htab[0][k][31] = hi;
+        htab[1][k][32] = hi;
+      }
+    }
   }
   bf16x8 gm[3];
   {
@@ -1260,13 +1279,58 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
     gm[2] = __builtin_bit_cast(bf16x8, w2);
   }
   lds_sync();
-  bf16x8 tm[3][2];                             // T[i32][tok] = h[i32 - tok], tok <= i32
-  split3_slots(
-      [&](int s, int j) {
-        const int d = i32 - blk_tok(8 * s + j, hf);
-        return (d >= 0) ? hbuf[d] : 0.0f;
-      },
-      tm);
+  // T[i32][tok] = h[i32 - tok] (zero for tok > i32): slot pair (s, 2jj) at
+  // x = 31 - i32 + tok, tok = 4hf + t(s, jj), t in {0, 2, 8, 10, 16, 18, 24, 26};
+  // x has the parity of 31 - i32, so odd rows read copy 0 at x and even rows
+  // copy 1 at x + 1, both word-aligned.  One asm block that waits for its
+  // reads (the inputs' DMAs are in flight; see read_staged_runs).
+  bf16x8 tm[3][2];
+  {
+    const uint16_t* hb = (i32 & 1) ? &htab[0][0][31 - i32 + 4 * hf] : &htab[1][0][32 - i32 + 4 * hf];
+    const uint32_t ha = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)(hb)));
+    uint32_t r[24];
+    asm volatile(
+        "ds_read_b32 %0, %24\n\t"
+        "ds_read_b32 %1, %24 offset:4\n\t"
+        "ds_read_b32 %2, %24 offset:16\n\t"
+        "ds_read_b32 %3, %24 offset:20\n\t"
+        "ds_read_b32 %4, %24 offset:32\n\t"
+        "ds_read_b32 %5, %24 offset:36\n\t"
+        "ds_read_b32 %6, %24 offset:48\n\t"
+        "ds_read_b32 %7, %24 offset:52\n\t"
+        "ds_read_b32 %8, %24 offset:132\n\t"
+        "ds_read_b32 %9, %24 offset:136\n\t"
+        "ds_read_b32 %10, %24 offset:148\n\t"
+        "ds_read_b32 %11, %24 offset:152\n\t"
+        "ds_read_b32 %12, %24 offset:164\n\t"
+        "ds_read_b32 %13, %24 offset:168\n\t"
+        "ds_read_b32 %14, %24 offset:180\n\t"
+        "ds_read_b32 %15, %24 offset:184\n\t"
+        "ds_read_b32 %16, %24 offset:264\n\t"
+        "ds_read_b32 %17, %24 offset:268\n\t"
+        "ds_read_b32 %18, %24 offset:280\n\t"
+        "ds_read_b32 %19, %24 offset:284\n\t"
+        "ds_read_b32 %20, %24 offset:296\n\t"
+        "ds_read_b32 %21, %24 offset:300\n\t"
+        "ds_read_b32 %22, %24 offset:312\n\t"
+        "ds_read_b32 %23, %24 offset:316\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+          "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17]),
+          "=&v"(r[18]), "=&v"(r[19]), "=&v"(r[20]), "=&v"(r[21]), "=&v"(r[22]), "=&v"(r[23])
+        : "v"(ha)
+        : "memory");
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const u32x4 w = {r[8 * k + 4 * sl], r[8 * k + 4 * sl + 1], r[8 * k + 4 * sl + 2],
+                         r[8 * k + 4 * sl + 3]};
+        tm[k][sl] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
 
   // ---- the scan lane's operands, also before the inputs arrive: the
   // end-state weights and the scan's decay factors.  Scan lane: mode n_sc,
