@@ -1186,8 +1186,8 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   const int i32 = l & 31;
   const int part = i32 >> 4;
   const int n_sc = i32 & 15;
-  const int64_t row = blockIdx.x;
-  const int c = static_cast<int>(row % D);
+  const int c = static_cast<int>(blockIdx.x);                // grid (D, B): no division
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * D + c;
   const float* lamc = lam + static_cast<int64_t>(c) * N;
   const float* resc = res + static_cast<int64_t>(c) * N;
   const bf16_t* x1r = x1 + row * L;
@@ -1200,14 +1200,30 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   // row's first chunk, an in-bounds address, and their runs are zeroed after
   // they are read out.  Everything before the inputs' 6 DMA loads is waited
   // for with vmcnt(6), so the setup below runs while the inputs are in flight.
-  const float lam_ld = lamc[min(n_sc, N - 1)];           // the scan lane's pole
-  const float st_ld = state_in ? state_in[row * N + min(n_sc, N - 1)] : 0.0f;
+  // With fewer than 16 modes the padded slots read mode 0 and are given
+  // pole and residue 0 once loaded, so that they contribute R p^k = 0.
+  float lam_ld, st_ld = 0.0f;                            // the scan lane's pole and state
   float g_lam[8], g_res[8];                              // G's slots: modes 8 hf + j
+  if (N >= 16) {
+    lam_ld = lamc[n_sc];
+    if (state_in) st_ld = state_in[row * N + n_sc];
+    const float* const gl = lamc + 8 * hf;
+    const float* const gr = resc + 8 * hf;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int n = min(8 * hf + j, N - 1);
-    g_lam[j] = lamc[n];
-    g_res[j] = resc[n];
+    for (int j = 0; j < 8; ++j) {
+      g_lam[j] = gl[j];
+      g_res[j] = gr[j];
+    }
+  } else {
+    const bool live_sc = n_sc < N;
+    lam_ld = lamc[live_sc ? n_sc : 0];
+    if (state_in) st_ld = state_in[row * N + (live_sc ? n_sc : 0)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = (8 * hf + j < N) ? 8 * hf + j : 0;
+      g_lam[j] = lamc[n];
+      g_res[j] = resc[n];
+    }
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1231,16 +1247,21 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
     pin(g_lam[j]);
     pin(g_res[j]);
   }
+  if (N < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool live = 8 * hf + j < N;
+      g_lam[j] = live ? g_lam[j] : 0.0f;
+      g_res[j] = live ? g_res[j] : 0.0f;
+    }
+  }
   float gv[8];                                 // G[i32][8 hf + j] = R_n p_n^(i32+1)
   float hpart = 0.0f, h0part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool live = 8 * hf + j < N;         // padding slots: zero, nothing evaluated
-    const float r = live ? g_res[j] : 0.0f;
-    const float ev = r * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
-    gv[j] = live ? ev : 0.0f;
+    gv[j] = g_res[j] * fast_exp(g_lam[j] * static_cast<float>(i32 + 1));
     hpart += gv[j];
-    h0part += r;
+    h0part += g_res[j];
   }
   const float hnext = hpart + xor32(hpart, hf);            // h[i32 + 1]
   const float h0 = h0part + xor32(h0part, hf);             // h[0]
@@ -1278,6 +1299,10 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
     gm[1] = __builtin_bit_cast(bf16x8, w1);
     gm[2] = __builtin_bit_cast(bf16x8, w2);
   }
+  // split here, in the inputs' latency, not next to G S after the wait
+  pin(gm[0]);
+  pin(gm[1]);
+  pin(gm[2]);
   lds_sync();
   // T[i32][tok] = h[i32 - tok] (zero for tok > i32): slot pair (s, 2jj) at
   // x = 31 - i32 + tok, tok = 4hf + t(s, jj), t in {0, 2, 8, 10, 16, 18, 24, 26};
@@ -1393,6 +1418,7 @@ __global__ __launch_bounds__(64, 4) void chunk_one_kernel(
   Raw4<bf16_t> rx[4], rv[4], rg[4];
   read_staged_runs(tin, i32, hf, rx, rv, rg);
   if (!whole) {
+    asm volatile("");                        // a branch: whole tiles skip the selects
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (32 * i32 + 4 * hf + 8 * q >= L) {
@@ -1576,8 +1602,8 @@ static hipError_t launch_mfma_modes(const ChunkArgs& a) {
                : launch_mfma_k<float, false, false, CPX, NSL>(a);
   if (!vec) return launch_mfma_k<bf16_t, false, false, CPX, NSL>(a);
   if constexpr (!CPX && NSL == 16) {
-    if (a.L <= 1024) {
-      dim3 grid(static_cast<unsigned>(a.B * a.D)), block(64);
+    if (a.L <= 1024 && a.B <= 65535) {
+      dim3 grid(static_cast<unsigned>(a.D), static_cast<unsigned>(a.B)), block(64);
       chunk_one_kernel<<<grid, block, 0, a.stream>>>(
           static_cast<const bf16_t*>(a.x1), static_cast<const bf16_t*>(a.x2),
           static_cast<const bf16_t*>(a.v), a.lam, a.res, a.N, a.skip, a.state_in, a.state_out,
