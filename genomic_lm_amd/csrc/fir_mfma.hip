@@ -456,14 +456,337 @@ __global__ __launch_bounds__(512) void fir_mfma_tm_kernel(
   }
 }
 
+// Token-major FIR on blocks of 32 channels.  Each token row of the block is
+// one 192-byte span of xin and one 64-byte span of y, so a workgroup reads and
+// writes whole cache lines or halves of them instead of 48- and 16-byte
+// pieces: at B = 1, D = 4096, L = 32768 the 8-channel form above spends about
+// a third of its time on the request rate of those pieces.  With 32 channels
+// the tile is 256 tokens (48 KB of inputs), cut into 16-token blocks for the
+// 16x16x32 matrix instruction:
+//     z_n = sum_{d<ND} A_d . U_{n,d},   A_d[i][k] = w[i + 32d + 16 - k],
+// U_{n,d} the 32 tokens from 16(n - 2d - 1) on, so that output block n of
+// the tile (one column) needs the tile and the 32 ND - 16 tokens before it.
+// Wave w takes channels 4w .. 4w+3 of the block, one after the other, with
+// their A operands in registers (the first bf16 part of the taps; taps that
+// are not bf16 values form their second part from the tap array on every
+// tile, a slow path that bf16 models do not take).  The
+// sequence is cut into segments so that the grid fills the chip; a segment
+// after the first starts with one tile that only fills the u buffers.
+// LDS: the tile in rows of 256 bytes (192 used) with the 16-byte chunks of a
+// row permuted by bits of the row index, so that the 64 rows a wave gathers
+// from at once spread over the banks (also the tap table at setup); per wave
+// and channel both u parts of the tile and its halo; the y tile.  The four
+// channels of a wave are 24 adjacent bytes of a row, read as three 8-byte
+// words; u = x1 v takes the two elements of each triple that are not the
+// gate, so only the gate's position PG is needed, as a template parameter.
+template <int ND, int PG>
+__global__ __launch_bounds__(512) void fir_mfma_tm32_kernel(
+    const bf16_t* __restrict__ xin, int pos1, int pos2, int posv, const float* __restrict__ taps,
+    int K, const float* __restrict__ skip, const float* __restrict__ win_in,
+    bf16_t* __restrict__ y, int D, int L, int nseg, int seg_len) {
+  constexpr int HT = 32 * ND - 16;            // tokens before the tile that the products read
+  constexpr int UBC = (HT + 256) / 8;         // 16-byte chunks of one u part of one channel
+  constexpr int KP = 32 * ND + 16;            // tap table row: lag + 16
+  __shared__ uint4 tin[256 * 16];
+  __shared__ uint4 ubs[8][4][2][UBC];
+  __shared__ uint32_t tout[256 * 16];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = l & 15, g = l >> 4;
+  // neighbouring blocks (which share a 128-byte line of each row) on one XCD
+  const int ncb = D >> 5;
+  const int64_t nwg = gridDim.x, gid = blockIdx.x;
+  const int64_t lg = (nwg % 16 == 0) ? 16 * (gid / 16) + 2 * (gid % 8) + (gid / 8) % 2 : gid;
+  const int cb = static_cast<int>(lg % ncb);
+  const int64_t rest = lg / ncb;
+  const int seg = static_cast<int>(rest % nseg);
+  const int64_t bat = rest / nseg;
+  const int64_t ld3 = 3 * static_cast<int64_t>(D);
+  const bf16_t* const xb = xin + bat * L * ld3 + 96 * cb;
+  bf16_t* const yb = y + bat * L * static_cast<int64_t>(D) + 32 * cb;
+  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len;
+  const int64_t t_end = min(static_cast<int64_t>(L), t_begin + seg_len);
+
+  // taps of the block's channels by lag + 16 (zero outside [0, K)), and
+  // cleared u buffers
+  float* const wtab = reinterpret_cast<float*>(tin);
+  for (int x = tid; x < 32 * KP; x += 512) {
+    const int cl = x / KP, k = x % KP - 16;
+    wtab[x] = (k >= 0 && k < K) ? taps[static_cast<int64_t>(32 * cb + cl) * K + k] : 0.0f;
+  }
+  for (int x = tid; x < 8 * 4 * 2 * UBC; x += 512) (&ubs[0][0][0][0])[x] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  // A operands: lane (row n, k-group g) holds A_d[n][8g + e] = w[n + 32d + 16 - 8g - e]
+  bf16x8 ta[4][ND];
+  uint32_t lo_bits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* const wr = wtab + (4 * wv + j) * KP;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = wr[n + 32 * d + 32 - 8 * g - e];
+        const __bf16 w0 = static_cast<__bf16>(w);
+        ta[j][d][e] = w0;
+        lo_bits |= __builtin_bit_cast(uint16_t, static_cast<__bf16>(w - static_cast<float>(w0)));
+      }
+      pin(ta[j][d]);
+    }
+  }
+  // taps that are bf16 values have no second part anywhere in the wave
+  const bool exact_taps = !__any(lo_bits != 0);
+  // the first segment's halo from the window: u[t], -HT <= t < 0, as two bf16 parts
+  if (seg == 0 && win_in && K > 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = bat * D + 32 * cb + 4 * wv + j;
+      uint16_t* const u0 = reinterpret_cast<uint16_t*>(&ubs[wv][j][0][0]);
+      uint16_t* const u1 = reinterpret_cast<uint16_t*>(&ubs[wv][j][1][0]);
+      for (int p = l; p < HT; p += 64) {
+        const int t = p - HT;
+        const float w = (t >= -(K - 1)) ? win_in[row * (K - 1) + (K - 1) + t] : 0.0f;
+        const uint32_t pw = cvt2(w, 0.0f);
+        u0[p] = static_cast<uint16_t>(pw);
+        u1[p] = static_cast<uint16_t>(cvt2(w - lo_f(pw), 0.0f));
+      }
+    }
+  }
+  __syncthreads();                            // tap table read out before the tile goes over it
+
+  float sk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sk[j] = skip ? skip[32 * cb + 4 * wv + j] : 0.0f;
+  // tile loads: thread tid takes slots tid + 512 k (k < 6), chunk s % 12 of
+  // row s / 12, at a 32-bit byte offset from the tile's first row; only a
+  // tile that reaches past L tests its rows
+  uint4 pre[6];
+  const uint32_t rowb = static_cast<uint32_t>(2 * ld3);
+  auto load_tile = [&](int64_t t0, const int (&rw)[6], const int (&ck)[6]) {
+    const char* const base = reinterpret_cast<const char*>(xb + t0 * ld3);
+    if (t0 + 256 <= L) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k)
+        pre[k] = *reinterpret_cast<const uint4*>(base + (static_cast<uint32_t>(rw[k]) * rowb + 16u * ck[k]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 6; ++k)
+        pre[k] = (t0 + rw[k] < L)
+                     ? *reinterpret_cast<const uint4*>(base + (static_cast<uint32_t>(rw[k]) * rowb + 16u * ck[k]))
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto slots = [&](int (&rw)[6], int (&ck)[6]) {
+    int tt = tid;
+    asm volatile("" : "+v"(tt));              // formed per tile, not kept across the loop
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      rw[k] = (tt + 512 * k) / 12;
+      ck[k] = (tt + 512 * k) - 12 * rw[k];
+    }
+  };
+  int64_t t0 = (seg > 0) ? t_begin - 256 : t_begin;
+  {
+    int rw[6], ck[6];
+    slots(rw, ck);
+    load_tile(t0, rw, ck);
+  }
+  // the lane's tokens are rows 16n + 4g + e (e < 4) of the tile; their chunk
+  // permutation h = (row >> 2) & 15 is the same for all four
+  const uint32_t h = static_cast<uint32_t>((4 * n + g) & 15);
+#pragma unroll 1
+  for (; t0 < t_end; t0 += 256) {
+    wg_sync();                                // every wave has read the previous tile and y
+    {
+      int rw[6], ck[6];
+      slots(rw, ck);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) tin[16 * rw[k] + (ck[k] ^ ((rw[k] >> 2) & 15))] = pre[k];
+      if (t0 + 256 < t_end) load_tile(t0 + 256, rw, ck);
+    }
+    wg_sync();                                // the tile is in LDS
+    const bool emit = t0 >= t_begin;          // not the filling tile of a later segment
+    uint32_t rbase = 128u * static_cast<uint32_t>(16 * n + 4 * g);
+    uint32_t hl = h;
+    asm volatile("" : "+v"(rbase), "+v"(hl)); // formed here, not kept across tiles
+    // the four channels in phases, so that each phase's LDS latency is met
+    // once: their inputs, then their u parts into the buffers, then the
+    // products and y, then the halos.  Row 16n + 4g + e holds the wave's
+    // triples at bytes 24 wv .. 24 wv + 23: three 8-byte words, each inside
+    // one 16-byte chunk.
+    uint32_t wd[4][6];
+    {
+      const uint2* const t2 = reinterpret_cast<const uint2*>(tin);
+      uint32_t q8[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const uint32_t off = static_cast<uint32_t>(24 * wv + 8 * i);           // bytes in the row
+        q8[i] = (rbase >> 2) + 2u * ((off >> 4) ^ hl) + ((off >> 3) & 1u);    // in 8-byte units
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const uint2 w2 = t2[q8[i] + 32u * e];
+          wd[e][2 * i] = w2.x;
+          wd[e][2 * i + 1] = w2.y;
+        }
+      }
+    }
+    constexpr int PA = (PG == 0) ? 1 : 0, PB = (PG == 2) ? 1 : 2;     // the two factors of u
+    auto el = [&](int e, int k) {             // element k (< 12) of row e as the high half of a float
+      const uint32_t w = wd[e][k >> 1];
+      return (k & 1) ? (w & 0xFFFF0000u) : (w << 16);
+    };
+    float su[4][4];
+    uint32_t gw[4][2];
+    uint2 uh[4], ul[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] = __uint_as_float(el(e, 3 * j + PA)) * __uint_as_float(el(e, 3 * j + PB));
+        su[j][e] = sk[j] * u[e];
+      }
+      gw[j][0] = (el(0, 3 * j + PG) >> 16) | el(1, 3 * j + PG);
+      gw[j][1] = (el(2, 3 * j + PG) >> 16) | el(3, 3 * j + PG);
+      // u = x1 v is exactly two bf16 parts
+      const uint32_t p0 = cvt2(u[0], u[1]), p1 = cvt2(u[2], u[3]);
+      uh[j] = make_uint2(p0, p1);
+      ul[j] = make_uint2(cvt2(u[0] - lo_f(p0), u[1] - hi_f(p0)), cvt2(u[2] - lo_f(p1), u[3] - hi_f(p1)));
+    }
+    const int up = (HT + 16 * n + 4 * g) >> 2;            // in 8-byte units
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      reinterpret_cast<uint2*>(&ubs[wv][j][0][0])[up] = uh[j];
+      reinterpret_cast<uint2*>(&ubs[wv][j][1][0])[up] = ul[j];
+    }
+    lds_sync();
+    if (emit) {
+      float yv[4][4];                         // [channel][token]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cl = 4 * wv + j;
+        f32x4 cz = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int ci = HT / 8 + 2 * n - 4 * d - 2 + g;
+          const bf16x8 b0 = __builtin_bit_cast(bf16x8, ubs[wv][j][0][ci]);
+          const bf16x8 b1 = __builtin_bit_cast(bf16x8, ubs[wv][j][1][ci]);
+          cz = mfma16(ta[j][d], b0, cz);
+          cz = mfma16(ta[j][d], b1, cz);
+          if (!exact_taps) {
+            // the taps' second bf16 part, from the tap array
+            const float* const wc = taps + static_cast<int64_t>(32 * cb + cl) * K;
+            int kb = n + 32 * d + 16 - 8 * g;
+            asm volatile("" : "+v"(kb));      // per tile: not hoisted out of the loop
+            bf16x8 t1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int k = kb - e;
+              const float w = (k >= 0 && k < K) ? wc[k] : 0.0f;
+              t1[e] = static_cast<__bf16>(w - static_cast<float>(static_cast<__bf16>(w)));
+            }
+            cz = mfma16(t1, b0, cz);
+            cz = mfma16(t1, b1, cz);
+          }
+        }
+        // y = x2 z + skip u
+        yv[j][0] = fmaf(lo_f(gw[j][0]), cz[0], su[j][0]);
+        yv[j][1] = fmaf(hi_f(gw[j][0]), cz[1], su[j][1]);
+        yv[j][2] = fmaf(lo_f(gw[j][1]), cz[2], su[j][2]);
+        yv[j][3] = fmaf(hi_f(gw[j][1]), cz[3], su[j][3]);
+      }
+      // the y tile: row 16n + 4g + e, the wave's four channels as one 8-byte
+      // word, word wv of the row's eight permuted by h & 7
+      uint2* const y2 = reinterpret_cast<uint2*>(tout);
+      const uint32_t ya = 8u * static_cast<uint32_t>(16 * n + 4 * g) + (static_cast<uint32_t>(wv) ^ (hl & 7u));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y2[ya + 8u * e] = make_uint2(cvt2(yv[0][e], yv[1][e]), cvt2(yv[2][e], yv[3][e]));
+    }
+    // the last HT tokens become the next tile's halo (the reads above are
+    // issued first, and one wave's LDS accesses complete in order)
+    if (l < 2 * (HT / 8)) {
+      const int pp = l / (HT / 8), q = l % (HT / 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ubs[wv][j][pp][q] = ubs[wv][j][pp][32 + q];
+    }
+    wg_sync();                                // every wave's y in the tile
+    if (emit) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int sl = tid + 512 * hh;
+        const int row = sl >> 2, q = sl & 3;
+        const int64_t t = t0 + row;
+        const uint32_t hr = static_cast<uint32_t>((row >> 2) & 7);
+        const uint2* const yr = reinterpret_cast<const uint2*>(tout) + 8 * row;
+        const uint2 wa = yr[(2u * q) ^ hr], wb = yr[(2u * q + 1u) ^ hr];
+        const uint4 w4 = make_uint4(wa.x, wa.y, wb.x, wb.y);
+        if (t < t_end) *reinterpret_cast<uint4*>(yb + t * D + 8 * q) = w4;
+      }
+    }
+  }
+}
+
 // bf16, K <= 128, D a multiple of 8 below 349526, xin and y 16-byte aligned.
 bool tokmajor_fir_mfma_supported(const TokmajorFirArgs& a) {
   return a.bf16 && a.K <= 128 && a.D % 8 == 0 && a.L > 0 && a.B > 0 &&
          int64_t(a.D) * 6 * 1024 <= INT32_MAX && aligned_all(16, a.xin, a.y);
 }
 
+// The 32-channel form: D a multiple of 32.
+static bool tokmajor_fir_mfma32_supported(const TokmajorFirArgs& a) {
+  return tokmajor_fir_mfma_supported(a) && a.D % 32 == 0;
+}
+
+// 16-token blocks: output block n reads 32-token spans 16(n - 2d - 1) for
+// d < ND, which reach lag K - 1 at the block's first row.
+static int fir_mfma16_diagonals(int K) { return (K - 1 <= 16) ? 1 : (K - 17 + 31) / 32 + 1; }
+
+static hipError_t launch_fir_mfma_tokmajor32(const TokmajorFirArgs& a) {
+  const int64_t ncb = a.D / 32;
+  // segments of whole 256-token tiles, until the grid covers the CUs or a
+  // segment would drop below 2048 tokens
+  int64_t nseg = 1;
+  while (a.B * ncb * nseg < 256 && (a.L + 2 * nseg - 1) / (2 * nseg) >= 2048) nseg *= 2;
+  const int64_t seg_len = ((a.L + nseg - 1) / nseg + 255) / 256 * 256;
+  nseg = (a.L + seg_len - 1) / seg_len;
+  const int64_t nwg = a.B * ncb * nseg;
+  if (nwg > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(nwg)), block(512);
+  const bf16_t* x = static_cast<const bf16_t*>(a.xin);
+  bf16_t* y = static_cast<bf16_t*>(a.y);
+  if (a.pos_x2 < 0 || a.pos_x2 > 2) return hipErrorInvalidValue;
+#define HYENA_FIR_TM32(NDV, PGV)                                                                \
+  fir_mfma_tm32_kernel<NDV, PGV><<<grid, block, 0, a.stream>>>(                                 \
+      x, a.pos_x1, a.pos_x2, a.pos_v, a.taps, a.K, a.skip, a.win_in, y, a.D, a.L,               \
+      static_cast<int>(nseg), static_cast<int>(seg_len))
+#define HYENA_FIR_TM32_PG(NDV)                          \
+  switch (a.pos_x2) {                                   \
+    case 0: HYENA_FIR_TM32(NDV, 0); break;              \
+    case 1: HYENA_FIR_TM32(NDV, 1); break;              \
+    default: HYENA_FIR_TM32(NDV, 2); break;             \
+  }
+  switch (fir_mfma16_diagonals(a.K)) {
+    case 1: HYENA_FIR_TM32_PG(1); break;
+    case 2: HYENA_FIR_TM32_PG(2); break;
+    case 3: HYENA_FIR_TM32_PG(3); break;
+    case 4: HYENA_FIR_TM32_PG(4); break;
+    case 5: HYENA_FIR_TM32_PG(5); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef HYENA_FIR_TM32_PG
+#undef HYENA_FIR_TM32
+  return hipGetLastError();
+}
+
 hipError_t launch_fir_mfma_tokmajor(const TokmajorFirArgs& a) {
   if (!tokmajor_fir_mfma_supported(a)) return hipErrorInvalidValue;
+  if (tokmajor_fir_mfma32_supported(a)) return launch_fir_mfma_tokmajor32(a);
   const int nd = fir_mfma_diagonals(a.K);
   dim3 grid(static_cast<unsigned>(a.B * (a.D / 8))), block(512);
   const bf16_t* x = static_cast<const bf16_t*>(a.xin);

@@ -1,6 +1,6 @@
 // mfma_common.hpp -- pieces shared by the matrix-core kernels (chunk_mfma.hip,
-// fir_mfma.hip): bf16 operand vectors and splits, the 32x32x16 MFMA, the
-// per-lane token layout, and the LDS staging of 1024-token tiles.
+// fir_mfma.hip): bf16 operand vectors and splits, the 32x32x16 and 16x16x32
+// MFMAs, the per-lane token layout, and the LDS staging of 1024-token tiles.
 #pragma once
 
 #include "common.hpp"
@@ -27,6 +27,14 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32: lane l holds row l % 16 of A and column l % 16 of B, each with
+// K elements 8 (l / 16) .. + 7, and rows 4 (l / 16) .. + 3 of column l % 16
+// of the result (checked against a host product on gfx950).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // x = p0 + p1 + p2 + r with p_k = rne_bf16 of the remainder so far; |r| <= 2^-24 |x|

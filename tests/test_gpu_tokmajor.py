@@ -283,6 +283,25 @@ def test_tokmajor_fir_fp32_taps_and_window(K):
         assert np.array_equal(wo.cpu().numpy(), ref_w.astype(np.float32))
 
 
+@pytest.mark.parametrize("K", [33, 100, 128])
+def test_tokmajor_fir_segments(K):
+    """The 32-channel matrix-core form cuts the sequence into segments (here 4
+    of 2304 tokens, the last one short and ending in a partial tile), each
+    after the first refilling its halo from the inputs; B = 2, a window in,
+    channel triples in a permuted order."""
+    w, xin, xd = _setup("bf16", B=2, D=96, L=9000, pos=(2, 1, 0))
+    d = DevWorkload(w)
+    taps = _taps(w, K)
+    rng = np.random.default_rng(K + 1)
+    win0 = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((2, w.D, K - 1)).astype(np.float32)))
+    wi = torch.from_numpy(win0).to(xd.device)
+    log(f"tokmajor fir segments K={K}")
+    y, wo = G.fir_fwd_tokmajor(xd, par_to_dev(taps), d.skip, pos=(2, 1, 0), window_in=wi)
+    ref, ref_w = _ref_fir(w, xin, (2, 1, 0), taps, window_in=win0)
+    _gate_tm(y, ref, "bf16", label=f"tokmajor fir segments K={K}")
+    assert np.array_equal(wo.cpu().numpy(), ref_w.astype(np.float32))
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_tokmajor_fir_misaligned(io):
     w, xin, xd = _setup(io, B=2, D=256, L=900)
