@@ -238,12 +238,13 @@ def test_tokmajor_fir(io, K, D, L):
         assert win is None
 
 
-@pytest.mark.parametrize("K", [7, 128])
-def test_tokmajor_fir_pieces_and_decode(K):
+@pytest.mark.parametrize("K,D", [(7, 264), (128, 264), (128, 256)])
+def test_tokmajor_fir_pieces_and_decode(K, D):
     """A prefill call, calls of assorted lengths and single-token steps with
-    the window handed over (in place) equal one call over the sequence."""
+    the window handed over (in place) equal one call over the sequence (D = 256:
+    the 32-channel matrix-core form; 264: the 8-channel one)."""
     L = 2600
-    w, xin, xd = _setup("bf16", B=1, D=264, L=L, pos=(2, 0, 1))
+    w, xin, xd = _setup("bf16", B=1, D=D, L=L, pos=(2, 0, 1))
     d = DevWorkload(w)
     taps = par_to_dev(_taps(w, K))
     win = torch.zeros((1, w.D, K - 1), dtype=torch.float32, device=xd.device)
@@ -281,6 +282,19 @@ def test_tokmajor_fir_fp32_taps_and_window(K):
         ref, ref_w = _ref_fir(w, xin[:, :L], (0, 2, 1), taps, window_in=win0)
         _gate_tm(y, ref, "bf16", label=f"tokmajor fir fp32 taps K={K} L={L}")
         assert np.array_equal(wo.cpu().numpy(), ref_w.astype(np.float32))
+
+
+@pytest.mark.parametrize("L", [5, 256, 700])
+def test_tokmajor_fir_one_block(L):
+    """D = 32: a single channel block; a row shorter than one 256-token tile,
+    exactly one tile, and a partial second tile."""
+    w, xin, xd = _setup("bf16", B=3, D=32, L=L, pos=(0, 1, 2))
+    d = DevWorkload(w)
+    taps = _taps(w, 128)
+    y, win = G.fir_fwd_tokmajor(xd, par_to_dev(taps), d.skip, pos=(0, 1, 2))
+    ref, ref_w = _ref_fir(w, xin, (0, 1, 2), taps)
+    _gate_tm(y, ref, "bf16", label=f"tokmajor fir one block L={L}")
+    assert np.array_equal(win.cpu().numpy(), ref_w.astype(np.float32))
 
 
 @pytest.mark.parametrize("K", [33, 100, 128])
