@@ -329,6 +329,22 @@ def test_tokmajor_fir_misaligned(io):
         G.fir_fwd_tokmajor(xd, par_to_dev(_taps(w, 129)), d.skip)
 
 
+def test_tokmajor_fir_wide_d():
+    """D = 8192 (256 blocks of 32 channels: one segment, the workgroups grouped
+    in pairs per XCD), a ragged L, channels sampled over the whole width; every
+    output written and finite."""
+    w, xin, xd = _setup("bf16", B=1, D=8192, L=3000, pos=(1, 2, 0))
+    d = DevWorkload(w)
+    taps = _taps(w, 128)
+    y = torch.full((1, 3000, 8192), float("nan"), dtype=torch.bfloat16, device=xd.device)
+    y, win = G.fir_fwd_tokmajor(xd, par_to_dev(taps), d.skip, pos=(1, 2, 0), out=y)
+    assert bool(torch.isfinite(y).all())
+    rows = sample_rows(w.D, k=16)
+    ref, ref_w = _ref_fir(w, xin, (1, 2, 0), taps, rows)
+    _gate_tm(y, ref, "bf16", rows, label="tokmajor fir D=8192")
+    assert np.array_equal(win.cpu().numpy()[:, rows], ref_w.astype(np.float32))
+
+
 def test_tokmajor_fir_7b_shape():
     """D = 4096, L = 8192 (the 7B layer set), K = 7 and 128, sampled channels."""
     w = W.make("7b_layer_set")
