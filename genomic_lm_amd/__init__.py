@@ -163,7 +163,7 @@ def _act(name, t, like=None, dims=3):
     if (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype in _ACT_DTYPES and t.dim() == dims
             and t.is_contiguous() and (like is None or (t.shape == like.shape
                                                         and t.dtype == like.dtype
-                                                        and t.device == like.device))):
+                                                        and t.get_device() == like.get_device()))):
         return t
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -183,8 +183,9 @@ def _act(name, t, like=None, dims=3):
 
 
 def _param(name, t, shape, dev, optional=False):
-    if (isinstance(t, torch.Tensor) and t.dtype == torch.float32 and t.device == dev
-            and t.shape == tuple(shape) and t.is_contiguous()):
+    # (the device is compared by index: a tensor's .device builds a new object)
+    if (isinstance(t, torch.Tensor) and t.dtype == torch.float32 and t.get_device() == dev.index
+            and t.shape == shape and t.is_contiguous()):
         return t
     if t is None:
         if optional:
@@ -286,23 +287,25 @@ def chunk_fwd(x1, x2, v, log_poles, residues, C: int, skip=None, state_in=None,
     _act("v", v, x1)
     B, D, L = x1.shape
     N = log_poles.shape[-1] if isinstance(log_poles, torch.Tensor) and log_poles.dim() == 2 else -1
-    _param("log_poles", log_poles, (D, N), x1.device)
-    _param("residues", residues, (D, N), x1.device)
-    _param("skip", skip, (D,), x1.device, optional=True)
-    _param("state_in", state_in, (B, D, N), x1.device, optional=True)
+    dev = x1.device
+    _param("log_poles", log_poles, (D, N), dev)
+    _param("residues", residues, (D, N), dev)
+    _param("skip", skip, (D,), dev, optional=True)
+    _param("state_in", state_in, (B, D, N), dev, optional=True)
     if algo not in ALGOS:
         raise ValueError(f"algo must be one of {sorted(ALGOS)}")
     y = torch.empty_like(x1) if out is None else _act("out", out, x1)
     if state_out is None:
-        state_out = torch.empty((B, D, N), dtype=torch.float32, device=x1.device)
+        state_out = torch.empty((B, D, N), dtype=torch.float32, device=dev)
     else:
-        _param("state_out", state_out, (B, D, N), x1.device)
+        _param("state_out", state_out, (B, D, N), dev)
     args = (_ptr(x1), _ptr(x2), _ptr(v), _ptr(log_poles), _ptr(residues), N, _ptr(skip),
             _ptr(state_in), _ptr(state_out), _ptr(y), B, D, L, int(C), _io(x1))
+    h = lib()
     if algo == "auto":
-        _check("hyena_chunk_fwd", lib().hyena_chunk_fwd(*args, _stream(x1)))
+        _check("hyena_chunk_fwd", h.hyena_chunk_fwd(*args, _stream(x1)))
     else:
-        _check("hyena_chunk_fwd_algo", lib().hyena_chunk_fwd_algo(*args, ALGOS[algo], _stream(x1)))
+        _check("hyena_chunk_fwd_algo", h.hyena_chunk_fwd_algo(*args, ALGOS[algo], _stream(x1)))
     return y, state_out
 
 
