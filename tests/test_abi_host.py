@@ -2,11 +2,13 @@
 header declares, and rejects bad arguments on the host before any launch.
 
 Only calls whose arguments fail validation are made here; those return before
-any HIP call."""
+any HIP call.  The last test checks that the benchmark refuses to run on more
+than one GPU before it touches one."""
 import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -363,3 +365,12 @@ def test_binding_rejects_cpu_tensors_before_any_call():
         G.fir_fwd(x, x, x, torch.zeros(2, 7))
     with pytest.raises(ValueError):
         G.chunk_fwd(x, x, x, torch.zeros(2, 16), torch.zeros(2, 16), 4)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU's throughput is the measured value; a request for several exits before any work
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
