@@ -39,10 +39,13 @@ def flags() -> list[str]:
 
 
 # Extra flags per source file.  The MFMA kernels keep their accumulators in
-# ordinary VGPRs: they have the registers to spare, and the AGPR form costs a
-# v_accvgpr_read for every result element used by the vector ALUs.
+# ordinary VGPRs: the AGPR form costs a v_accvgpr_read for every result
+# element used by the vector ALUs, and in the FFT kernels, which generate h
+# on the matrix cores, its 32 AGPRs would come on top of the 128 registers
+# that four waves per SIMD leave each wave.
 EXTRA_FLAGS = {
     "chunk_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fftconv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fir_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

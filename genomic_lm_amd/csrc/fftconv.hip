@@ -29,6 +29,7 @@
 #include "common.hpp"
 #include "fft.hpp"
 #include "launch.hpp"
+#include "mfma_common.hpp"
 
 namespace hyena {
 
@@ -55,6 +56,76 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
     const int m2 = 2 * (t + T * i);
     if (m2 >= L) a[i].x = 0.0f;
     if (m2 + 1 >= L) a[i].y = 0.0f;
+  }
+}
+
+// The same pairs on the matrix cores, for 16 points per thread (T a multiple
+// of 64, every thread of the wave calling).  With t = 64 w + l, lane l of
+// wave w needs h at 2m and 2m + 1 for m = t + T i, i < 16, and
+//   h[2m] = sum_n R_n p_n^(2(64w + l%32)) * p_n^(64 (l/32) + 2T i),
+// a product over the modes of Y[n][c] = p_n^(2(64w + c)) (c < 32, one column
+// per lane pair) and X[rho][n] = R_n p_n^(64 hf + 2T i) (32 rows rho, each a
+// pair (i, hf)), h[2m + 1] the same with X p_n.  The rows are numbered so
+// that register r of a lane in half-wave hf of the 32x32 result (row
+// 8(r/4) + 4hf + r%4) is point i = r: rho gives i = 4(rho/8) + rho%4 and hf =
+// (rho/4)%2.  X, X p and Y are split into three bf16 parts and the six part
+// products of order <= 2 are summed in fp32 (about 2^-24 relative per term),
+// 16 modes per block of 12 MFMAs, the smallest products first.  This replaces
+// 16 x 3 vector operations per mode and point of the ladder above.
+template <int T>
+__device__ __forceinline__ void modal_pairs_mfma(float2 (&a)[16], const float* lam, const float* res,
+                                                 int N, int t, int L) {
+  static_assert(T % 64 == 0, "whole waves");
+  const int l = t & 63;
+  const int hf = l >> 5;
+  const int rho = l & 31;
+  const float xe = static_cast<float>(64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)));
+  const float ye = static_cast<float>(2 * ((t & ~63) + rho));
+  f32x16 de = {}, dd = {};
+  for (int n0 = 0; n0 < N; n0 += 16) {
+    uint32_t x0[4], x1[4], x2[4], o0[4], o1[4], o2[4], y0[4], y1[4], y2[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float xv[2], ov[2], yv[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int n = n0 + 8 * hf + j + k;
+        const bool live = n < N;
+        const int nc = live ? n : 0;
+        const float lm = live ? lam[nc] : 0.0f;
+        const float r = live ? res[nc] : 0.0f;
+        xv[k] = r * fast_exp(lm * xe);
+        ov[k] = r * fast_exp(lm * (xe + 1.0f));
+        yv[k] = live ? fast_exp(lm * ye) : 0.0f;
+      }
+      split3_pair(xv[0], xv[1], x0[j / 2], x1[j / 2], x2[j / 2]);
+      split3_pair(ov[0], ov[1], o0[j / 2], o1[j / 2], o2[j / 2]);
+      split3_pair(yv[0], yv[1], y0[j / 2], y1[j / 2], y2[j / 2]);
+    }
+    auto v8 = [](const uint32_t (&w)[4]) {
+      const u32x4 q = {w[0], w[1], w[2], w[3]};
+      return __builtin_bit_cast(bf16x8, q);
+    };
+    const bf16x8 X0 = v8(x0), X1 = v8(x1), X2 = v8(x2);
+    const bf16x8 O0 = v8(o0), O1 = v8(o1), O2 = v8(o2);
+    const bf16x8 Y0 = v8(y0), Y1 = v8(y1), Y2 = v8(y2);
+    de = mfma(X2, Y0, de);
+    de = mfma(X0, Y2, de);
+    de = mfma(X1, Y1, de);
+    de = mfma(X1, Y0, de);
+    de = mfma(X0, Y1, de);
+    de = mfma(X0, Y0, de);
+    dd = mfma(O2, Y0, dd);
+    dd = mfma(O0, Y2, dd);
+    dd = mfma(O1, Y1, dd);
+    dd = mfma(O1, Y0, dd);
+    dd = mfma(O0, Y1, dd);
+    dd = mfma(O0, Y0, dd);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m2 = 2 * (t + T * i);
+    a[i] = make_float2(m2 < L ? de[i] : 0.0f, m2 + 1 < L ? dd[i] : 0.0f);
   }
 }
 
@@ -91,7 +162,7 @@ __device__ __forceinline__ void modal_pairs_cpx(float2 (&a)[P], const float* lam
 // order m = t + T*i).  PART 2: the odd half, recombined with ws, gated and
 // stored.  A launch covers rows row0 .. row0 + gridDim.x - 1.
 template <int S, int T, typename IO, bool VEC, bool CPX, int PART>
-__global__ __launch_bounds__(T) void fftconv_kernel(
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1 : 4))) void fftconv_kernel(
     const IO* x1, const IO* x2, const IO* v,
     const float* __restrict__ lam, const float* __restrict__ res, int N,
     const float* __restrict__ skip, IO* __restrict__ y, int D, int L,
@@ -134,68 +205,86 @@ __global__ __launch_bounds__(T) void fftconv_kernel(
 #pragma unroll
   for (int q = Q0; q <= Q1; ++q) {
     float2 a[P];
-    // ---- u = x1 * v, packed in pairs, parity pre-twiddle
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int m = t + T * i;
-      float2 p1, p2;
-      if constexpr (VEC) {
-        // L even: clamped pair index, zero beyond L without a branch
-        const int64_t e = min(2 * m, L - 2);
-        Raw2<IO> r1, r2;
-        r1.load(x1r + e);
-        r2.load(vr + e);
-        const bool in = 2 * m < L;
-        p1 = in ? r1.get() : make_float2(0.0f, 0.0f);
-        p2 = in ? r2.get() : make_float2(0.0f, 0.0f);
-      } else {
-        p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
-        p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
-      }
-      a[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
-      if (q) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
-    }
-    fft_forward<S, T>(a, lds, t);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
-    __syncthreads();
     float2 z[P];
-    float um_nyq = 0.0f;
     int ts = t;
+    // Split halves of bf16 rows (one to four workgroups per CU, at most one
+    // from S = 16384 on) issue the loads of u first and generate and
+    // transform h while they are in flight: nothing else on the CU would
+    // hide their latency.  The pending pairs hold 2P registers, as many as
+    // the first spectrum holds through the second transform either way.
+    constexpr bool H_FIRST = PART != 0;
+    constexpr bool EARLY_U = H_FIRST && VEC && sizeof(IO) == 2;
+    Raw2<IO> r1[EARLY_U ? P : 1], r2[EARLY_U ? P : 1];
+    float hm_nyq = 0.0f, um_nyq = 0.0f;   // H[M], U[M] (real), only used by thread 0
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      if (i % SEQ == 0) ts = seq_idx(t);
-      const int k = ts + T * i;
-      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      z[i] = real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
-      seq_keep(z[i]);
+    for (int pass = 0; pass < 2; ++pass) {
+      // pass 0 transforms u and pass 1 h, or the other way round (H_FIRST)
+      const bool is_h = H_FIRST ? pass == 0 : pass == 1;
+      if (is_h) {
+        // ---- h, generated on chip, packed in pairs
+        if constexpr (CPX)
+          modal_pairs_cpx<P, T>(a, lamc, resc, N, t, L);
+        else if constexpr (P == 16)
+          modal_pairs_mfma<T>(a, lamc, resc, N, t, L);
+        else
+          modal_pairs<P, T>(a, lamc, resc, N, t, L);
+        if constexpr (EARLY_U) {
+#pragma unroll
+          for (int i = 0; i < P; ++i) {
+            const int64_t e = min(2 * (t + T * i), L - 2);
+            r1[i].load(x1r + e);
+            r2[i].load(vr + e);
+          }
+        }
+      } else {
+        // ---- u = x1 * v, packed in pairs
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int m = t + T * i;
+          float2 p1, p2;
+          if constexpr (EARLY_U) {
+            const bool in = 2 * m < L;
+            p1 = in ? r1[i].get() : make_float2(0.0f, 0.0f);
+            p2 = in ? r2[i].get() : make_float2(0.0f, 0.0f);
+          } else if constexpr (VEC) {
+            // L even: clamped pair index, zero beyond L without a branch
+            const int64_t e = min(2 * m, L - 2);
+            Raw2<IO> l1, l2;
+            l1.load(x1r + e);
+            l2.load(vr + e);
+            const bool in = 2 * m < L;
+            p1 = in ? l1.get() : make_float2(0.0f, 0.0f);
+            p2 = in ? l2.get() : make_float2(0.0f, 0.0f);
+          } else {
+            p1 = ld_pair<IO, VEC>(x1r, 2 * m, L);
+            p2 = ld_pair<IO, VEC>(vr, 2 * m, L);
+          }
+          a[i] = make_float2(p1.x * p2.x, p1.y * p2.y);
+        }
+      }
+      // parity pre-twiddle
+      if (q) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
+      }
+      fft_forward<S, T>(a, lds, t);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
+      __syncthreads();
+      // real spectrum; the second transform's is multiplied into the first's
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        if (i % SEQ == 0) ts = seq_idx(t);
+        const int k = ts + T * i;
+        const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
+        const float2 x = real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
+        z[i] = pass == 0 ? x : cmul(z[i], x);
+        seq_keep(z[i]);
+      }
+      if (q == 0 && t == 0) (is_h ? hm_nyq : um_nyq) = a[0].x - a[0].y;
     }
-    if (q == 0 && t == 0) um_nyq = a[0].x - a[0].y;
-
-    // ---- h, generated on chip, same packing
-    if constexpr (CPX)
-      modal_pairs_cpx<P, T>(a, lamc, resc, N, t, L);
-    else
-      modal_pairs<P, T>(a, lamc, resc, N, t, L);
-    if (q) {
-#pragma unroll
-      for (int i = 0; i < P; ++i) a[i] = cmul(a[i], tw_next(i, t, T, LG_M, tw, tst));
-    }
-    fft_forward<S, T>(a, lds, t);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      if (i % SEQ == 0) ts = seq_idx(t);
-      const int k = ts + T * i;
-      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      z[i] = cmul(z[i], real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst)));
-      seq_keep(z[i]);
-    }
-    if (q == 0 && t == 0) zm_nyq = um_nyq * (a[0].x - a[0].y);
+    if (q == 0 && t == 0) zm_nyq = um_nyq * hm_nyq;
 
     // ---- repack Z for the inverse real transform
     __syncthreads();
