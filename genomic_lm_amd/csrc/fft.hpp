@@ -257,6 +257,26 @@ __device__ __forceinline__ float2 tw_next(int i, int a, int d, int lg, float2& w
   return w;
 }
 
+// LDS slot of the real-spectrum partner of element i of thread ts (k = ts +
+// T i): lds_pad(kk) with kk = (S - k) mod S in the even parity half (q = 0)
+// and kk = S - 1 - k in the odd one.  T i is a multiple of 32, and for C a
+// multiple of 32 and 0 <= x <= C, lds_pad(C - x) = C + C/32 - x - ceil(x/32);
+// so with x = ts + q one per-thread base (mirror_base) and a constant per i
+// (mirror_off) give every slot, except k = 0 of the even half, whose partner
+// wraps to slot 0.  tests/test_fft_layout.py checks this for every shape.
+__device__ __forceinline__ int mirror_base(int ts, int q) {
+  const int x = ts + q;
+  return -x - ((x + 31) >> 5);
+}
+__host__ __device__ constexpr int mirror_off(int S, int T, int i) {
+  return (S - T * i) + ((S - T * i) >> 5);
+}
+template <int S, int T>
+__device__ __forceinline__ int mirror_slot(int base, int i, int q, int ts) {
+  const int slot = base + mirror_off(S, T, i);
+  return (i == 0 && q == 0 && ts == 0) ? 0 : slot;
+}
+
 // ------------------------------------------------------------- real signals
 // A real length-Nfft signal x is transformed as the complex length-M signal
 // c[m] = x[2m] + i x[2m+1], M = Nfft / 2.  Its spectrum X[K] (K < M) follows

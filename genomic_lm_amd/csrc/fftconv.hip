@@ -273,12 +273,15 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
       for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = a[i];
       __syncthreads();
       // real spectrum; the second transform's is multiplied into the first's
+      int mb = 0;
 #pragma unroll
       for (int i = 0; i < P; ++i) {
-        if (i % SEQ == 0) ts = seq_idx(t);
-        const int k = ts + T * i;
-        const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-        const float2 x = real_spectrum(a[i], lds[lds_pad(kk)], tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
+        if (i % SEQ == 0) {
+          ts = seq_idx(t);
+          mb = mirror_base(ts, q);
+        }
+        const float2 x = real_spectrum(a[i], lds[mirror_slot<S, T>(mb, i, q, ts)],
+                                       tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
         z[i] = pass == 0 ? x : cmul(z[i], x);
         seq_keep(z[i]);
       }
@@ -291,12 +294,15 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
 #pragma unroll
     for (int i = 0; i < P; ++i) lds[lds_pad(t + T * i)] = z[i];
     __syncthreads();
+    int mb = 0;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      if (i % SEQ == 0) ts = seq_idx(t);
+      if (i % SEQ == 0) {
+        ts = seq_idx(t);
+        mb = mirror_base(ts, q);
+      }
       const int k = ts + T * i;
-      const int kk = q ? (S - 1 - k) : ((S - k) & (S - 1));
-      float2 zmir = lds[lds_pad(kk)];
+      float2 zmir = lds[mirror_slot<S, T>(mb, i, q, ts)];
       if (q == 0 && k == 0) zmir = make_float2(zm_nyq, 0.0f);
       a[i] = inverse_pack(z[i], zmir, tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
       seq_keep(a[i]);

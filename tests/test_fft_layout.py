@@ -59,3 +59,33 @@ def test_pass_offsets_affine(S, T):
                     for r in range(R2):
                         assert pad(jp + r * Q) == pad(jp) + r * Q + ((r * Q) >> 5), (S, T, NS, t, b, r)
         NS *= R
+
+
+def mirror_slot(S, T, ts, i, q):
+    """The kernels' LDS slot of the real-spectrum partner (fft.hpp, mirror_*)."""
+    x = ts + q
+    base = -x - ((x + 31) >> 5)
+    C = S - T * i
+    slot = base + C + (C >> 5)
+    return 0 if (i == 0 and q == 0 and ts == 0) else slot
+
+
+# (S, T) of the kernels that read the partner through mirror_slot:
+# fftconv.hip (every S, 4 to 16 points per thread)
+MIRROR_SHAPES = [(256, 64), (512, 64), (1024, 128), (2048, 256), (4096, 256), (8192, 512),
+                 (16384, 1024)]
+
+
+@pytest.mark.parametrize("S,T", MIRROR_SHAPES)
+def test_mirror_slot(S, T):
+    """mirror_slot equals lds_pad of the partner index for every thread, point
+    and parity half: kk = (S - k) mod S (even half), S - 1 - k (odd half)."""
+    for q in (0, 1):
+        seen = set()
+        for ts in range(T):
+            for i in range(S // T):
+                k = ts + T * i
+                kk = (S - k) % S if q == 0 else S - 1 - k
+                assert mirror_slot(S, T, ts, i, q) == pad(kk), (S, T, q, ts, i)
+                seen.add(kk)
+        assert len(seen) == S
