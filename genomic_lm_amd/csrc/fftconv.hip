@@ -23,9 +23,10 @@
 // two launches with one workgroup per (row, half): the even half writes its
 // inverse transform B_0 (S complex, fp32) to a caller workspace and the odd
 // half reads it back for the recombination -- 4 bytes per token each way,
-// against the 48 of the four-step path that rows longer than 32768 take.  h is
-// generated per thread with short exp ladders (<= 16 multiplications from an
-// exact anchor) and never touches memory.
+// against the 48 of the four-step path that rows longer than 32768 take.  h
+// never touches memory: the split halves of real modes form it on the matrix
+// cores as a rank-N product (modal_pairs_mfma), the other kernels per thread
+// with short exp ladders (<= 16 multiplications from an exact anchor).
 #include "common.hpp"
 #include "fft.hpp"
 #include "launch.hpp"
