@@ -250,6 +250,40 @@ def test_mode_counts(N):
             G.chunk_fwd(d.x1, d.x2, d.v, d.lam, d.res, 1024, d.skip, algo="mfma")
 
 
+# The split single pass (L > 4096) forms h on the matrix cores, 16 modes per
+# block of products: mode counts on both sides of a block boundary and the
+# maximum, both split sizes (S = 4096 and 16384), bf16 and fp32 rows; then
+# modes at the extremes of the exponent range: two slow modes with nearly
+# equal poles and opposite residues (h a small difference of two large
+# terms), and fast ones whose terms underflow within a few tokens.
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [5000, 20001])
+@pytest.mark.parametrize("N", [1, 3, 15, 16, 17, 33, 64])
+def test_fftconv_split_mode_counts(N, L, io):
+    w = W.make("tiny" if io == "f32" else "7b_layer_set", B=1, D=3, L=L, N=N)
+    d = DevWorkload(w)
+    log(f"fftconv split modes N={N} L={L} io={io}")
+    ref, _ = oracle_modal(w)
+    gate(G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip), ref, io, label=f"fftconv N={N} L={L}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_fftconv_split_extreme_modes(io):
+    w = W.make("tiny" if io == "f32" else "7b_layer_set", B=1, D=6, L=32768, N=16)
+    rng = np.random.default_rng(23)
+    lam = w.log_poles.astype(np.float64).copy()
+    res = w.residues.astype(np.float64).copy()
+    lam[:, 0] = -1.0e-4 * (1.0 + 0.3 * rng.random(w.D))
+    lam[:, 1] = lam[:, 0] * (1.0 + 0.05 * rng.random(w.D))
+    res[:, 0], res[:, 1] = 0.4, -0.4
+    lam[:, 2:6] = -rng.uniform(5.0, 80.0, (w.D, 4))
+    w.log_poles, w.residues = lam.astype(np.float32), res.astype(np.float32)
+    d = DevWorkload(w)
+    log(f"fftconv split extreme modes io={io}")
+    ref, _ = oracle_modal(w)
+    gate(G.fftconv_fwd(d.x1, d.x2, d.v, d.lam, d.res, d.skip), ref, io, label="fftconv extreme modes")
+
+
 # The 32-slot form (17 to 32 real modes): fp32 and bf16 rows, whole tiles, a
 # partial last tile, rows of at most one tile, unaligned rows, carried state.
 @pytest.mark.parametrize("io,L,offset", [("bf16", 5000, False), ("bf16", 1016, False),
