@@ -308,6 +308,33 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
       a[i] = inverse_pack(z[i], zmir, tw_next(i, 2 * ts + q, 2 * T, LG_N, tw, tst));
       seq_keep(a[i]);
     }
+    // The gate's operands of a group of GG points (B_0, x1, v, x2), loaded
+    // together from pair indices clamped into the row.  The odd half issues
+    // the workspace loads of its first group before the inverse transform,
+    // whose passes then hide their latency (2 GG registers).
+    constexpr int GG = P < 8 ? P : 8;
+    constexpr bool PRE_GATE = PART == 2 && VEC;
+    Raw2<IO> g1[GG], g2[GG], gg[GG];
+    float2 ge[GG];
+    auto load_b0 = [&](int g0, int tt) {
+#pragma unroll
+      for (int j = 0; j < GG; ++j) {
+        const int i = g0 + j;
+        if constexpr (PART == 2) ge[j] = (wsr + T * i)[tt];
+        else if constexpr (B0_LDS) ge[j] = b0s[tt + T * i];
+        else ge[j] = b0[i];
+      }
+    };
+    auto load_acts = [&](int g0, int tt) {
+#pragma unroll
+      for (int j = 0; j < GG; ++j) {
+        const int64_t e = min(2 * (tt + T * (g0 + j)), L - 2);
+        g1[j].load(x1r + e);
+        g2[j].load(vr + e);
+        gg[j].load(x2r + e);
+      }
+    };
+    if constexpr (PRE_GATE) load_b0(0, t);
     fft_inverse<S, T>(a, lds, t);
 
     if (q == 0) {
@@ -322,34 +349,20 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
       const float sk = skip ? skip[c] : 0.0f;
       const float inv_m = 1.0f / static_cast<float>(M);
       if constexpr (VEC) {
-        // L is even: pair m is whole for 2m < L and absent beyond.  The
-        // operands of a group of 8 elements (B_0, x1, v, x2) are loaded
-        // together from pair indices clamped into the row, so no branch
-        // separates the loads and none waits for an earlier element's store;
-        // pairs beyond L are not stored.
-        constexpr int GG = P < 8 ? P : 8;
+        // L is even: pair m is whole for 2m < L and absent beyond.  No
+        // branch separates a group's loads and none waits for an earlier
+        // element's store; pairs beyond L are not stored.
 #pragma unroll
         for (int g0 = 0; g0 < P; g0 += GG) {
           ts = seq_idx(t);
-          Raw2<IO> r1[GG], r2[GG], rg[GG];
-          float2 e0[GG];
-#pragma unroll
-          for (int j = 0; j < GG; ++j) {
-            const int i = g0 + j;
-            const int64_t e = min(2 * (ts + T * i), L - 2);
-            if constexpr (PART == 2) e0[j] = (wsr + T * i)[ts];
-            else if constexpr (B0_LDS) e0[j] = b0s[ts + T * i];
-            else e0[j] = b0[i];
-            r1[j].load(x1r + e);
-            r2[j].load(vr + e);
-            rg[j].load(x2r + e);
-          }
+          if (!PRE_GATE || g0 > 0) load_b0(g0, ts);
+          load_acts(g0, ts);
 #pragma unroll
           for (int j = 0; j < GG; ++j) {
             const int m = ts + T * (g0 + j);
-            const float2 zz = cscale(cadd(e0[j], cmul(cconj(tw_next(g0 + j, ts, T, LG_M, tw, tst)),
+            const float2 zz = cscale(cadd(ge[j], cmul(cconj(tw_next(g0 + j, ts, T, LG_M, tw, tst)),
                                                       a[g0 + j])), inv_m);
-            const float2 p1 = r1[j].get(), p2 = r2[j].get(), g = rg[j].get();
+            const float2 p1 = g1[j].get(), p2 = g2[j].get(), g = gg[j].get();
             const float2 out = make_float2(fmaf(g.x, zz.x, sk * (p1.x * p2.x)),
                                            fmaf(g.y, zz.y, sk * (p1.y * p2.y)));
             if (2 * m < L) Io<IO>::st2(yr, 2 * m, out);
