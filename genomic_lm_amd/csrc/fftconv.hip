@@ -24,9 +24,10 @@
 // inverse transform B_0 (S complex, fp32) to a caller workspace and the odd
 // half reads it back for the recombination -- 4 bytes per token each way,
 // against the 48 of the four-step path that rows longer than 32768 take.  h
-// never touches memory: the split halves of real modes form it on the matrix
-// cores as a rank-N product (modal_pairs_mfma), the other kernels per thread
-// with short exp ladders (<= 16 multiplications from an exact anchor).
+// never touches memory: the split halves form it on the matrix cores as a
+// rank-N product (modal_pairs_mfma, modal_pairs_mfma_cpx), the other kernels
+// per thread with short exp ladders (<= 16 multiplications from an exact
+// anchor).
 #include "common.hpp"
 #include "fft.hpp"
 #include "launch.hpp"
@@ -102,6 +103,64 @@ __device__ __forceinline__ void modal_pairs_mfma(float2 (&a)[16], const float* l
       split3_pair(xv[0], xv[1], x0[j / 2], x1[j / 2], x2[j / 2]);
       split3_pair(ov[0], ov[1], o0[j / 2], o1[j / 2], o2[j / 2]);
       split3_pair(yv[0], yv[1], y0[j / 2], y1[j / 2], y2[j / 2]);
+    }
+    auto v8 = [](const uint32_t (&w)[4]) {
+      const u32x4 q = {w[0], w[1], w[2], w[3]};
+      return __builtin_bit_cast(bf16x8, q);
+    };
+    const bf16x8 X0 = v8(x0), X1 = v8(x1), X2 = v8(x2);
+    const bf16x8 O0 = v8(o0), O1 = v8(o1), O2 = v8(o2);
+    const bf16x8 Y0 = v8(y0), Y1 = v8(y1), Y2 = v8(y2);
+    de = mfma(X2, Y0, de);
+    de = mfma(X0, Y2, de);
+    de = mfma(X1, Y1, de);
+    de = mfma(X1, Y0, de);
+    de = mfma(X0, Y1, de);
+    de = mfma(X0, Y0, de);
+    dd = mfma(O2, Y0, dd);
+    dd = mfma(O0, Y2, dd);
+    dd = mfma(O1, Y1, dd);
+    dd = mfma(O1, Y0, dd);
+    dd = mfma(O0, Y1, dd);
+    dd = mfma(O0, Y0, dd);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m2 = 2 * (t + T * i);
+    a[i] = make_float2(m2 < L ? de[i] : 0.0f, m2 + 1 < L ? dd[i] : 0.0f);
+  }
+}
+
+// The same for complex modes (lam, res as (re, im) pairs): Re(R p^(a+b)) =
+// Re(R p^a) Re(p^b) - Im(R p^a) Im(p^b), so each mode takes two of the
+// product's 16 K slots (slot 8 hf + j of a lane: mode 4 hf + j/2, its real
+// part for even j), 8 modes per block, with X = (Re, -Im) of R p^(64 hf +
+// 2T i) and Y = (Re, Im) of p^(2(64w + c)).
+template <int T>
+__device__ __forceinline__ void modal_pairs_mfma_cpx(float2 (&a)[16], const float* lam,
+                                                     const float* res, int N, int t, int L) {
+  static_assert(T % 64 == 0, "whole waves");
+  const int l = t & 63;
+  const int hf = l >> 5;
+  const int rho = l & 31;
+  const float xe = static_cast<float>(64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)));
+  const float ye = static_cast<float>(2 * ((t & ~63) + rho));
+  f32x16 de = {}, dd = {};
+  for (int n0 = 0; n0 < N; n0 += 8) {
+    uint32_t x0[4], x1[4], x2[4], o0[4], o1[4], o2[4], y0[4], y1[4], y2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 4 * hf + j;
+      const bool live = n < N;
+      const int nc = live ? n : 0;
+      const CpxMode md = cpx_mode(live ? lam[2 * nc] : 0.0f, live ? lam[2 * nc + 1] : 0.0f);
+      const float2 r = live ? make_float2(res[2 * nc], res[2 * nc + 1]) : make_float2(0.0f, 0.0f);
+      const float2 xv = cmul(r, cexp_at(md, xe));
+      const float2 ov = cmul(r, cexp_at(md, xe + 1.0f));
+      const float2 yv = live ? cexp_at(md, ye) : make_float2(0.0f, 0.0f);
+      split3_pair(xv.x, -xv.y, x0[j], x1[j], x2[j]);
+      split3_pair(ov.x, -ov.y, o0[j], o1[j], o2[j]);
+      split3_pair(yv.x, yv.y, y0[j], y1[j], y2[j]);
     }
     auto v8 = [](const uint32_t (&w)[4]) {
       const u32x4 q = {w[0], w[1], w[2], w[3]};
@@ -223,7 +282,9 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
       const bool is_h = H_FIRST ? pass == 0 : pass == 1;
       if (is_h) {
         // ---- h, generated on chip, packed in pairs
-        if constexpr (CPX)
+        if constexpr (CPX && P == 16)
+          modal_pairs_mfma_cpx<T>(a, lamc, resc, N, t, L);
+        else if constexpr (CPX)
           modal_pairs_cpx<P, T>(a, lamc, resc, N, t, L);
         else if constexpr (P == 16)
           modal_pairs_mfma<T>(a, lamc, resc, N, t, L);

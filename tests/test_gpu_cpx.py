@@ -67,6 +67,30 @@ def test_fftconv_cpx(io, L):
     gate(y, ref, io, label=f"fftconv_cpx L={L}")
 
 
+# The split single pass (L > 4096) forms h on the matrix cores, 8 complex
+# modes (16 product slots) per block: counts on both sides of a block
+# boundary and up to 32 modes, both split sizes, bf16 and fp32 rows, and a
+# slow decay range (|Re log p| down to 1e-5).
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [5000, 20001])
+@pytest.mark.parametrize("N", [1, 7, 8, 9, 17, 32])
+def test_fftconv_cpx_split_mode_counts(N, L, io):
+    w, d, lam, R, lam_d, R_d = _setup(io, D=3, L=L, N=N, seed=40 + N)
+    log(f"fftconv_cpx split modes N={N} L={L} io={io}")
+    y = G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, d.skip)
+    ref, _ = _ref(w, lam, R)
+    gate(y, ref, io, label=f"fftconv_cpx N={N} L={L}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_fftconv_cpx_split_slow_modes(io):
+    w, d, lam, R, lam_d, R_d = _setup(io, D=4, L=32768, N=8, seed=77, lam_lo=1e-5)
+    log(f"fftconv_cpx split slow modes io={io}")
+    y = G.fftconv_fwd_cpx(d.x1, d.x2, d.v, lam_d, R_d, d.skip)
+    ref, _ = _ref(w, lam, R)
+    gate(y, ref, io, label="fftconv_cpx slow modes")
+
+
 @pytest.mark.parametrize("algo", ["fft", "mfma"])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("C,L", [(64, 1000), (1024, 3000), (1000, 4096), (4096, 9000), (8192, 8192)])
