@@ -89,3 +89,51 @@ def test_mirror_slot(S, T):
                 assert mirror_slot(S, T, ts, i, q) == pad(kk), (S, T, q, ts, i)
                 seen.add(kk)
         assert len(seen) == S
+
+
+# ---------------------------------------------------------------- matrix-core h
+# fftconv.hip (modal_pairs_mfma) forms lane l's h pairs (h[2m], h[2m + 1]),
+# m = t + T i, t = 64 w + l, from one 32x32x16 product per 16 modes.  The
+# model below takes the product's documented lane layout (A: lane l holds row
+# l % 32, K slots 8 (l / 32) .. + 7; B: lane l holds K slots 8 (l / 32) ..
+# + 7 of column l % 32; result register r of lane l: row 8 (r / 4) +
+# 4 (l / 32) + r % 4, column l % 32) and the kernel's exponent formulas, and
+# checks that every lane and register gets the h value of its point.
+def _mfma_h_model(T, w, lam, R, odd):
+    import numpy as np
+    N = lam.shape[0]
+    A = np.zeros((32, 16))
+    B = np.zeros((16, 32))
+    for lane in range(64):
+        hf, rho = lane >> 5, lane & 31
+        xe = 64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3))
+        ye = 2 * ((64 * w) + rho)
+        for j in range(8):
+            n = 8 * hf + j
+            if n < N:
+                A[rho, n] = R[n] * np.exp(lam[n] * (xe + odd))
+                B[n, rho] = np.exp(lam[n] * ye)
+    D = A @ B
+    out = np.zeros((64, 16))
+    for lane in range(64):
+        for r in range(16):
+            out[lane, r] = D[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane & 31]
+    return out
+
+
+@pytest.mark.parametrize("T", [256, 512, 1024])
+def test_mfma_h_layout(T):
+    import numpy as np
+    rng = np.random.default_rng(T)
+    N = 16
+    lam = -rng.uniform(1e-3, 1e-2, N)
+    R = rng.normal(0, 0.25, N)
+    for w in (0, 1, T // 64 - 1):
+        for odd in (0, 1):
+            got = _mfma_h_model(T, w, lam, R, odd)
+            for lane in range(64):
+                t = 64 * w + lane
+                for i in range(16):
+                    tok = 2 * (t + T * i) + odd
+                    ref = float(np.sum(R * np.exp(lam * tok)))
+                    assert abs(got[lane, i] - ref) <= 1e-12 * max(1.0, abs(ref)), (T, w, lane, i, odd)
