@@ -61,6 +61,53 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
   }
 }
 
+// Eight values of an MFMA operand (one lane's K slots), each split into
+// three bf16 parts x = p0 + p1 + p2 + O(2^-24 x), packed two per word.
+struct Split3x8 {
+  uint32_t p[3][4];
+  __device__ __forceinline__ void set(int j2, float a, float b) {   // slots 2 j2, 2 j2 + 1
+    split3_pair(a, b, p[0][j2], p[1][j2], p[2][j2]);
+  }
+  __device__ __forceinline__ bf16x8 part(int k) const {
+    const u32x4 q = {p[k][0], p[k][1], p[k][2], p[k][3]};
+    return __builtin_bit_cast(bf16x8, q);
+  }
+};
+
+// acc + X Y over the part products of order <= 2 (X0Y0, X0Y1, X1Y0, X1Y1,
+// X0Y2, X2Y0), the smallest first: about 2^-24 relative per term.
+__device__ __forceinline__ f32x16 mfma_split3(const Split3x8& x, const Split3x8& y, f32x16 acc) {
+  acc = mfma(x.part(2), y.part(0), acc);
+  acc = mfma(x.part(0), y.part(2), acc);
+  acc = mfma(x.part(1), y.part(1), acc);
+  acc = mfma(x.part(1), y.part(0), acc);
+  acc = mfma(x.part(0), y.part(1), acc);
+  return mfma(x.part(0), y.part(0), acc);
+}
+
+// a[i] = (de[i], dd[i]), zero at and beyond L (pairs m = t + T i).
+template <int T>
+__device__ __forceinline__ void pairs_from(float2 (&a)[16], const f32x16& de, const f32x16& dd,
+                                           int t, int L) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m2 = 2 * (t + T * i);
+    a[i] = make_float2(m2 < L ? de[i] : 0.0f, m2 + 1 < L ? dd[i] : 0.0f);
+  }
+}
+
+// Exponents of a lane's A row and B column in the 32x32x16 products below
+// (lane l of wave w, t = 64 w + l): row rho = l % 32 stands for point i =
+// 4(rho/8) + rho%4 of half-wave (rho/4)%2, column c = l % 32 for t = 64 w + c.
+template <int T>
+__device__ __forceinline__ float row_exponent(int t) {
+  const int rho = t & 31;
+  return static_cast<float>(64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)));
+}
+__device__ __forceinline__ float col_exponent(int t) {
+  return static_cast<float>(2 * ((t & ~63) + (t & 31)));
+}
+
 // The same pairs on the matrix cores, for 16 points per thread (T a multiple
 // of 64, every thread of the wave calling).  With t = 64 w + l, lane l of
 // wave w needs h at 2m and 2m + 1 for m = t + T i, i < 16, and
@@ -70,22 +117,19 @@ __device__ __forceinline__ void modal_pairs(float2 (&a)[P], const float* lam, co
 // pair (i, hf)), h[2m + 1] the same with X p_n.  The rows are numbered so
 // that register r of a lane in half-wave hf of the 32x32 result (row
 // 8(r/4) + 4hf + r%4) is point i = r: rho gives i = 4(rho/8) + rho%4 and hf =
-// (rho/4)%2.  X, X p and Y are split into three bf16 parts and the six part
-// products of order <= 2 are summed in fp32 (about 2^-24 relative per term),
-// 16 modes per block of 12 MFMAs, the smallest products first.  This replaces
-// 16 x 3 vector operations per mode and point of the ladder above.
+// (rho/4)%2.  X, X p and Y are split into three bf16 parts (mfma_split3), 16
+// modes per block of 12 MFMAs.  This replaces 16 x 3 vector operations per
+// mode and point of the ladder above.
 template <int T>
 __device__ __forceinline__ void modal_pairs_mfma(float2 (&a)[16], const float* lam, const float* res,
                                                  int N, int t, int L) {
   static_assert(T % 64 == 0, "whole waves");
-  const int l = t & 63;
-  const int hf = l >> 5;
-  const int rho = l & 31;
-  const float xe = static_cast<float>(64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)));
-  const float ye = static_cast<float>(2 * ((t & ~63) + rho));
+  const int hf = (t & 63) >> 5;
+  const float xe = row_exponent<T>(t);
+  const float ye = col_exponent(t);
   f32x16 de = {}, dd = {};
   for (int n0 = 0; n0 < N; n0 += 16) {
-    uint32_t x0[4], x1[4], x2[4], o0[4], o1[4], o2[4], y0[4], y1[4], y2[4];
+    Split3x8 x, o, y;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       float xv[2], ov[2], yv[2];
@@ -100,35 +144,14 @@ __device__ __forceinline__ void modal_pairs_mfma(float2 (&a)[16], const float* l
         ov[k] = r * fast_exp(lm * (xe + 1.0f));
         yv[k] = live ? fast_exp(lm * ye) : 0.0f;
       }
-      split3_pair(xv[0], xv[1], x0[j / 2], x1[j / 2], x2[j / 2]);
-      split3_pair(ov[0], ov[1], o0[j / 2], o1[j / 2], o2[j / 2]);
-      split3_pair(yv[0], yv[1], y0[j / 2], y1[j / 2], y2[j / 2]);
+      x.set(j / 2, xv[0], xv[1]);
+      o.set(j / 2, ov[0], ov[1]);
+      y.set(j / 2, yv[0], yv[1]);
     }
-    auto v8 = [](const uint32_t (&w)[4]) {
-      const u32x4 q = {w[0], w[1], w[2], w[3]};
-      return __builtin_bit_cast(bf16x8, q);
-    };
-    const bf16x8 X0 = v8(x0), X1 = v8(x1), X2 = v8(x2);
-    const bf16x8 O0 = v8(o0), O1 = v8(o1), O2 = v8(o2);
-    const bf16x8 Y0 = v8(y0), Y1 = v8(y1), Y2 = v8(y2);
-    de = mfma(X2, Y0, de);
-    de = mfma(X0, Y2, de);
-    de = mfma(X1, Y1, de);
-    de = mfma(X1, Y0, de);
-    de = mfma(X0, Y1, de);
-    de = mfma(X0, Y0, de);
-    dd = mfma(O2, Y0, dd);
-    dd = mfma(O0, Y2, dd);
-    dd = mfma(O1, Y1, dd);
-    dd = mfma(O1, Y0, dd);
-    dd = mfma(O0, Y1, dd);
-    dd = mfma(O0, Y0, dd);
+    de = mfma_split3(x, y, de);
+    dd = mfma_split3(o, y, dd);
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m2 = 2 * (t + T * i);
-    a[i] = make_float2(m2 < L ? de[i] : 0.0f, m2 + 1 < L ? dd[i] : 0.0f);
-  }
+  pairs_from<T>(a, de, dd, t, L);
 }
 
 // The same for complex modes (lam, res as (re, im) pairs): Re(R p^(a+b)) =
@@ -140,14 +163,12 @@ template <int T>
 __device__ __forceinline__ void modal_pairs_mfma_cpx(float2 (&a)[16], const float* lam,
                                                      const float* res, int N, int t, int L) {
   static_assert(T % 64 == 0, "whole waves");
-  const int l = t & 63;
-  const int hf = l >> 5;
-  const int rho = l & 31;
-  const float xe = static_cast<float>(64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)));
-  const float ye = static_cast<float>(2 * ((t & ~63) + rho));
+  const int hf = (t & 63) >> 5;
+  const float xe = row_exponent<T>(t);
+  const float ye = col_exponent(t);
   f32x16 de = {}, dd = {};
   for (int n0 = 0; n0 < N; n0 += 8) {
-    uint32_t x0[4], x1[4], x2[4], o0[4], o1[4], o2[4], y0[4], y1[4], y2[4];
+    Split3x8 x, o, y;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + 4 * hf + j;
@@ -158,35 +179,14 @@ __device__ __forceinline__ void modal_pairs_mfma_cpx(float2 (&a)[16], const floa
       const float2 xv = cmul(r, cexp_at(md, xe));
       const float2 ov = cmul(r, cexp_at(md, xe + 1.0f));
       const float2 yv = live ? cexp_at(md, ye) : make_float2(0.0f, 0.0f);
-      split3_pair(xv.x, -xv.y, x0[j], x1[j], x2[j]);
-      split3_pair(ov.x, -ov.y, o0[j], o1[j], o2[j]);
-      split3_pair(yv.x, yv.y, y0[j], y1[j], y2[j]);
+      x.set(j, xv.x, -xv.y);
+      o.set(j, ov.x, -ov.y);
+      y.set(j, yv.x, yv.y);
     }
-    auto v8 = [](const uint32_t (&w)[4]) {
-      const u32x4 q = {w[0], w[1], w[2], w[3]};
-      return __builtin_bit_cast(bf16x8, q);
-    };
-    const bf16x8 X0 = v8(x0), X1 = v8(x1), X2 = v8(x2);
-    const bf16x8 O0 = v8(o0), O1 = v8(o1), O2 = v8(o2);
-    const bf16x8 Y0 = v8(y0), Y1 = v8(y1), Y2 = v8(y2);
-    de = mfma(X2, Y0, de);
-    de = mfma(X0, Y2, de);
-    de = mfma(X1, Y1, de);
-    de = mfma(X1, Y0, de);
-    de = mfma(X0, Y1, de);
-    de = mfma(X0, Y0, de);
-    dd = mfma(O2, Y0, dd);
-    dd = mfma(O0, Y2, dd);
-    dd = mfma(O1, Y1, dd);
-    dd = mfma(O1, Y0, dd);
-    dd = mfma(O0, Y1, dd);
-    dd = mfma(O0, Y0, dd);
+    de = mfma_split3(x, y, de);
+    dd = mfma_split3(o, y, dd);
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m2 = 2 * (t + T * i);
-    a[i] = make_float2(m2 < L ? de[i] : 0.0f, m2 + 1 < L ? dd[i] : 0.0f);
-  }
+  pairs_from<T>(a, de, dd, t, L);
 }
 
 // The same pairs for complex modes (lam, res as (re, im) pairs):
