@@ -137,3 +137,48 @@ def test_mfma_h_layout(T):
                     tok = 2 * (t + T * i) + odd
                     ref = float(np.sum(R * np.exp(lam * tok)))
                     assert abs(got[lane, i] - ref) <= 1e-12 * max(1.0, abs(ref)), (T, w, lane, i, odd)
+
+
+def _mfma_h_model_cpx(T, w, lam, R, odd):
+    """modal_pairs_mfma_cpx: K slot 8 hf + j of a lane holds mode 4 hf + j/2,
+    (Re, -Im) of R p^(row exponent) in A and (Re, Im) of p^(column exponent)
+    in B, so the product over slots is Re sum_n R_n p_n^(row + column)."""
+    import numpy as np
+    N = lam.shape[0]
+    A = np.zeros((32, 16))
+    B = np.zeros((16, 32))
+    for lane in range(64):
+        hf, rho = lane >> 5, lane & 31
+        xe = 64 * ((rho >> 2) & 1) + 2 * T * (4 * (rho >> 3) + (rho & 3)) + odd
+        ye = 2 * ((64 * w) + rho)
+        for jj in range(4):
+            n = 4 * hf + jj
+            if n < N:
+                x = R[n] * np.exp(lam[n] * xe)
+                y = np.exp(lam[n] * ye)
+                A[rho, 8 * hf + 2 * jj], A[rho, 8 * hf + 2 * jj + 1] = x.real, -x.imag
+                B[8 * hf + 2 * jj, rho], B[8 * hf + 2 * jj + 1, rho] = y.real, y.imag
+    D = A @ B
+    out = np.zeros((64, 16))
+    for lane in range(64):
+        for r in range(16):
+            out[lane, r] = D[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane & 31]
+    return out
+
+
+@pytest.mark.parametrize("T", [256, 1024])
+def test_mfma_h_layout_cpx(T):
+    import numpy as np
+    rng = np.random.default_rng(T + 1)
+    N = 8
+    lam = -rng.uniform(1e-3, 1e-2, N) + 1j * rng.uniform(-np.pi, np.pi, N)
+    R = rng.normal(0, 0.25, N) + 1j * rng.normal(0, 0.25, N)
+    for w in (0, T // 64 - 1):
+        for odd in (0, 1):
+            got = _mfma_h_model_cpx(T, w, lam, R, odd)
+            for lane in range(64):
+                t = 64 * w + lane
+                for i in range(16):
+                    tok = 2 * (t + T * i) + odd
+                    ref = float(np.sum(R * np.exp(lam * tok)).real)
+                    assert abs(got[lane, i] - ref) <= 1e-12 * max(1.0, abs(ref)), (T, w, lane, i, odd)
