@@ -267,11 +267,12 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(PART == 0 ? 1
     float2 a[P];
     float2 z[P];
     int ts = t;
-    // Split halves of bf16 rows (one to four workgroups per CU, at most one
-    // from S = 16384 on) issue the loads of u first and generate and
-    // transform h while they are in flight: nothing else on the CU would
-    // hide their latency.  The pending pairs hold 2P registers, as many as
-    // the first spectrum holds through the second transform either way.
+    // Split halves (one to four workgroups per CU, at most one from
+    // S = 16384 on) take h first; bf16 rows then issue the loads of u right
+    // after h is generated and transform h while they are in flight: nothing
+    // else on the CU would hide their latency.  The pending pairs hold 2P
+    // registers, as many as the first spectrum holds through the second
+    // transform either way.
     constexpr bool H_FIRST = PART != 0;
     constexpr bool EARLY_U = H_FIRST && VEC && sizeof(IO) == 2;
     Raw2<IO> r1[EARLY_U ? P : 1], r2[EARLY_U ? P : 1];
